@@ -1,0 +1,161 @@
+"""The GPU tile layout of packed W4A16 weights, written from its specification.
+
+Test infrastructure only (see the package docstring). The HIP repack kernel
+must produce exactly these bytes; nothing here is shared with it.
+
+The pages describe a one-time reorder after loading (vLLM note "Carga de capas
+cuantizadas", "Responsabilidades" and "Flujo de datos": process_weights_after_loading
+rewrites qweight into the layout the kernel expects) but the layout is the
+kernel's own. This library's layout, version 1, for a K x N weight with group
+size G (G = K for group_size = -1; G a multiple of 128 dividing K):
+
+  KB = K / 128 row blocks, NB = N / 16 column blocks.
+
+  Weight plane, bytes [0, K*N/2):
+    block (nb, kb) is 1024 bytes at offset 1024 * (nb * KB + kb); so the whole K
+    range of one 16-column block is contiguous.
+    Inside a block, lane L in 0..63 owns bytes 16L .. 16L+15 = four little-endian
+    uint32 words i = 0..3. Word i of lane L holds column n = 16 nb + (L mod 16)
+    and rows k = 128 kb + 32 i + 8 (L div 16) + e for e = 0..7; nibble slot s
+    (bits 4s .. 4s+3) holds the code of row e = TILE_ORDER[s].
+    TILE_ORDER = (0, 2, 4, 6, 1, 3, 5, 7): slots t and t+4 hold rows 2t and 2t+1.
+
+  Metadata plane, bytes [K*N/2, K*N/2 + 4*KB*N):
+    uint32 number (nb * KB + kb) * 16 + c describes column n = 16 nb + c over
+    row block kb, whose group is g = (128 kb) div G:
+      bits 0..15  = the 16-bit pattern of S[g, n] (the scale, fp16 or bf16),
+      bits 16..19 = Z[g, n] (the zero point, 0..15),
+      bits 20..31 = 0.
+
+  Total size: K*N/2 + 4*(K/128)*N bytes.
+
+Column blocks are independent (as the n-blocks of the CPU layout are in the
+vllm-omni commit "cpu_int4: repack weights in n-blocks, to bound the load-time
+peak"): repacking a range of whole column blocks yields exactly the bytes of
+that range in both planes.
+"""
+
+import numpy as np
+
+TILE_ORDER = (0, 2, 4, 6, 1, 3, 5, 7)
+ROWS_PER_BLOCK = 128
+COLS_PER_BLOCK = 16
+BLOCK_BYTES = 1024
+LAYOUT_VERSION = 1
+
+
+def check_shape(K, N, group_size):
+    """Returns G; raises ValueError for shapes this layout does not cover."""
+    if K <= 0 or N <= 0:
+        raise ValueError("K and N must be positive")
+    if K % ROWS_PER_BLOCK != 0:
+        raise ValueError("K must be a multiple of 128")
+    if N % COLS_PER_BLOCK != 0:
+        raise ValueError("N must be a multiple of 16")
+    G = K if group_size == -1 else int(group_size)
+    if G <= 0 or G % ROWS_PER_BLOCK != 0 or K % G != 0:
+        raise ValueError("group size must be -1 or a multiple of 128 dividing K")
+    return G
+
+
+def packed_bytes(K, N, group_size):
+    check_shape(K, N, group_size)
+    return K * N // 2 + 4 * (K // ROWS_PER_BLOCK) * N
+
+
+def repack(Q, Z, scale_bits, group_size):
+    """Codes Q uint8 [K, N], zeros Z uint8 [K/G, N], scale bits uint16 [K/G, N]
+    -> packed buffer as uint8 [packed_bytes]."""
+    Q = np.asarray(Q, dtype=np.uint8)
+    K, N = Q.shape
+    G = check_shape(K, N, group_size)
+    Z = np.asarray(Z, dtype=np.uint8)
+    scale_bits = np.asarray(scale_bits, dtype=np.uint16)
+    if Z.shape != (K // G, N) or scale_bits.shape != (K // G, N):
+        raise ValueError("zeros and scales must be [K/G, N]")
+    KB, NB = K // ROWS_PER_BLOCK, N // COLS_PER_BLOCK
+
+    # Name the axes of Q by the layout: k = 128 kb + 32 i + 8 h + e, n = 16 nb + c.
+    q = Q.reshape(KB, 4, 4, 8, NB, 16)                  # [kb, i, h, e, nb, c]
+    words = np.zeros((NB, KB, 4, 16, 4), dtype=np.uint32)   # [nb, kb, h, c, i]
+    for s in range(8):
+        codes = q[:, :, :, TILE_ORDER[s], :, :]          # [kb, i, h, nb, c]
+        codes = codes.transpose(3, 0, 2, 4, 1)           # [nb, kb, h, c, i]
+        words |= codes.astype(np.uint32) << np.uint32(4 * s)
+    # lane L = 16 h + c, so [h, c] flattens to L in order
+    weight_plane = words.reshape(NB, KB, 64, 4)
+
+    group_of_block = (np.arange(KB) * ROWS_PER_BLOCK) // G             # [kb]
+    s_blk = scale_bits[group_of_block].astype(np.uint32)               # [kb, N]
+    z_blk = Z[group_of_block].astype(np.uint32)                        # [kb, N]
+    meta = (s_blk | (z_blk << np.uint32(16))).reshape(KB, NB, 16).transpose(1, 0, 2)
+
+    out = np.concatenate([
+        np.ascontiguousarray(weight_plane).astype("<u4").view(np.uint8).reshape(-1),
+        np.ascontiguousarray(meta).astype("<u4").view(np.uint8).reshape(-1),
+    ])
+    assert out.size == packed_bytes(K, N, group_size)
+    return out
+
+
+def repack_loops(Q, Z, scale_bits, group_size):
+    """The same layout with one Python loop per field: slow, for tiny shapes only.
+    Kept beside the array version so the two statements can be checked against
+    each other."""
+    Q = np.asarray(Q, dtype=np.uint8)
+    K, N = Q.shape
+    G = check_shape(K, N, group_size)
+    KB, NB = K // ROWS_PER_BLOCK, N // COLS_PER_BLOCK
+    out = bytearray(packed_bytes(K, N, group_size))
+    for nb in range(NB):
+        for kb in range(KB):
+            base = BLOCK_BYTES * (nb * KB + kb)
+            for lane in range(64):
+                n = 16 * nb + lane % 16
+                for i in range(4):
+                    word = 0
+                    for s in range(8):
+                        k = 128 * kb + 32 * i + 8 * (lane // 16) + TILE_ORDER[s]
+                        word |= int(Q[k, n]) << (4 * s)
+                    off = base + 16 * lane + 4 * i
+                    out[off:off + 4] = word.to_bytes(4, "little")
+    meta_base = K * N // 2
+    for nb in range(NB):
+        for kb in range(KB):
+            g = (128 * kb) // G
+            for c in range(16):
+                n = 16 * nb + c
+                word = int(scale_bits[g, n]) | (int(Z[g, n]) << 16)
+                off = meta_base + 4 * ((nb * KB + kb) * 16 + c)
+                out[off:off + 4] = word.to_bytes(4, "little")
+    return np.frombuffer(bytes(out), dtype=np.uint8)
+
+
+def decode(packed, K, N, group_size):
+    """Inverse of repack: packed bytes -> (Q uint8 [K, N], Z uint8 [K/G, N],
+    scale bits uint16 [K/G, N]). Raises ValueError if the buffer is not a valid
+    layout (nonzero reserved bits, or row blocks of one group disagreeing)."""
+    G = check_shape(K, N, group_size)
+    packed = np.asarray(packed, dtype=np.uint8)
+    if packed.size != packed_bytes(K, N, group_size):
+        raise ValueError("packed buffer has the wrong size")
+    KB, NB = K // ROWS_PER_BLOCK, N // COLS_PER_BLOCK
+    wbytes = K * N // 2
+    words = packed[:wbytes].view("<u4").reshape(NB, KB, 4, 16, 4)     # [nb, kb, h, c, i]
+    q = np.zeros((KB, 4, 4, 8, NB, 16), dtype=np.uint8)              # [kb, i, h, e, nb, c]
+    for s in range(8):
+        codes = ((words >> np.uint32(4 * s)) & np.uint32(0xF)).astype(np.uint8)
+        q[:, :, :, TILE_ORDER[s], :, :] = codes.transpose(1, 4, 2, 0, 3)
+    Q = q.reshape(K, N)
+
+    meta = packed[wbytes:].view("<u4").reshape(NB, KB, 16).transpose(1, 0, 2).reshape(KB, N)
+    if np.any(meta >> np.uint32(20)):
+        raise ValueError("reserved metadata bits are not zero")
+    blocks_per_group = G // ROWS_PER_BLOCK
+    meta_g = meta.reshape(K // G, blocks_per_group, N)
+    if np.any(meta_g != meta_g[:, :1, :]):
+        raise ValueError("row blocks of one group carry different metadata")
+    first = meta_g[:, 0, :]
+    S = (first & np.uint32(0xFFFF)).astype(np.uint16)
+    Z = ((first >> np.uint32(16)) & np.uint32(0xF)).astype(np.uint8)
+    return Q, Z, S

@@ -1,0 +1,275 @@
+"""Pin checks for the CPU oracle, as functions returning True when the oracle
+agrees with a fact fixed independently of it (a printed value, a hand-worked
+example, a closed form, an invariant, exact arithmetic).
+
+They are plain functions of the oracle's modules so that tests can run them both
+against the oracle and against copies of it with a planted mistake, to show that
+each plausible mistake trips at least one pin.
+"""
+
+import os
+from fractions import Fraction
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _lines(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                yield line
+
+
+def awq_golden_entries():
+    out = []
+    for line in _lines("awq_word_pins.txt"):
+        kind, rest = line.split(None, 1)
+        lhs, rhs = [p.strip() for p in rest.split("->")]
+        if kind == "pack":
+            out.append(("pack", [int(v) for v in lhs.split()], int(rhs, 16)))
+        else:
+            out.append(("unpack", int(lhs, 16), [int(v) for v in rhs.split()]))
+    return out
+
+
+def pin_awq_golden(awq):
+    for kind, a, b in awq_golden_entries():
+        if kind == "pack":
+            w = int(awq.pack_awq(np.array([a], dtype=np.uint8))[0, 0].view(np.uint32))
+            if w != b:
+                return False
+        else:
+            word = np.array([[a]], dtype=np.uint32).view(np.int32)
+            if awq.unpack_awq(word)[0].tolist() != b:
+                return False
+    return True
+
+
+def worked_example():
+    rows = [line.split() for line in _lines("worked_example_bf16.txt")]
+    s = [float(r[1]) for r in rows]
+    y = np.array([[float(r[2]) for r in rows], [float(r[3]) for r in rows]])
+    qweight = np.empty((128, 2), dtype=np.uint32)
+    qweight[0] = [0x75316420, 0xFFFFFFFF]
+    qweight[1] = [0x00000000, 0x11111111]
+    qweight[2:] = 0x88888888
+    qzeros = np.array([[0x33333333, 0x33333333]], dtype=np.uint32)
+    scale_bits = (np.array([s], dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    x = np.zeros((2, 128), dtype=np.float32)
+    x[0, 0], x[0, 1] = 1.0, 2.0
+    x[1, :] = 1.0
+    x_bits = (x.view(np.uint32) >> 16).astype(np.uint16)
+    return dict(qweight=qweight.view(np.int32), qzeros=qzeros.view(np.int32),
+                scale_bits=scale_bits, x_bits=x_bits, y=y)
+
+
+def pin_worked_example(gemm_mod):
+    ex = worked_example()
+    y = gemm_mod.w4a16_reference(ex["x_bits"], ex["qweight"], ex["qzeros"], ex["scale_bits"],
+                                 "bf16", 128)
+    return y.shape == ex["y"].shape and np.array_equal(y, ex["y"])
+
+
+def page3_transients():
+    return [(r[0], int(r[1]), int(r[2]), int(r[3])) for r in (l.split() for l in _lines("page3_int32_transients.txt"))]
+
+
+def pin_page3_transients(awq):
+    for _, N, K, mib in page3_transients():
+        R, C = awq.unpacked_shape((K, N // 8))
+        if R * C * 4 != mib * 2**20:
+            return False
+    return True
+
+
+def _fraction_reference(x_bits, qweight, qzeros, scale_bits, G):
+    """Exact y from the AWQ words with Python integers and Fractions. Codes are
+    read per element with the slot-of-column table (the inverse view of the
+    packing order), bf16 values decoded with integer arithmetic."""
+    slot_of_column = (0, 4, 1, 5, 2, 6, 3, 7)
+
+    def code(words, r, n):
+        w = int(words[r, n // 8]) & 0xFFFFFFFF
+        return (w >> (4 * slot_of_column[n % 8])) & 0xF
+
+    def bf16(b):
+        b = int(b)
+        sign = -1 if b & 0x8000 else 1
+        e = (b >> 7) & 0xFF
+        m = b & 0x7F
+        if e == 0:
+            return sign * Fraction(m, 2**133)      # 2^-126 * m / 2^7
+        return sign * Fraction(128 + m, 128) * (Fraction(2) ** (e - 127))
+
+    M, K = x_bits.shape
+    N = qweight.shape[1] * 8
+    y = [[Fraction(0)] * N for _ in range(M)]
+    for m in range(M):
+        for n in range(N):
+            acc = Fraction(0)
+            for k in range(K):
+                g = k // G
+                w = (code(qweight, k, n) - code(qzeros, g, n)) * bf16(scale_bits[g, n])
+                acc += bf16(x_bits[m, k]) * w
+            y[m][n] = acc
+    return y
+
+
+def pin_fraction_bruteforce(gemm_mod, seed=7):
+    rng = np.random.default_rng(seed)
+    for (M, K, N, G) in [(2, 128, 16, 128), (3, 256, 8, 128), (1, 256, 24, 64)]:
+        qweight = rng.integers(0, 2**32, (K, N // 8), dtype=np.uint32).view(np.int32)
+        qzeros = rng.integers(0, 2**32, (K // G, N // 8), dtype=np.uint32).view(np.int32)
+        s = rng.uniform(0.005, 0.02, (K // G, N)).astype(np.float32)
+        scale_bits = (s.view(np.uint32) >> 16).astype(np.uint16)
+        x = rng.standard_normal((M, K)).astype(np.float32)
+        x_bits = (x.view(np.uint32) >> 16).astype(np.uint16)
+        y = gemm_mod.w4a16_reference(x_bits, qweight, qzeros, scale_bits, "bf16", G)
+        exact = _fraction_reference(x_bits, qweight, qzeros, scale_bits, G)
+        for m in range(M):
+            for n in range(N):
+                e = float(exact[m][n])
+                if abs(y[m, n] - e) > 1e-12 * max(1.0, abs(e)):
+                    return False
+    return True
+
+
+def pin_closed_form_constant_codes(gemm_mod, awq):
+    """Q = c and Z = z0 everywhere: y[m, n] = (c - z0) * sum_g S[g, n] * sum_{k in g} x[m, k]."""
+    rng = np.random.default_rng(11)
+    M, K, N, G = 3, 512, 32, 128
+    c, z0 = 13, 4
+    qweight = awq.pack_awq(np.full((K, N), c, dtype=np.uint8))
+    qzeros = awq.pack_awq(np.full((K // G, N), z0, dtype=np.uint8))
+    s = rng.uniform(0.005, 0.02, (K // G, N)).astype(np.float32)
+    scale_bits = (s.view(np.uint32) >> 16).astype(np.uint16)
+    S = (scale_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    x_bits = (x.view(np.uint32) >> 16).astype(np.uint16)
+    X = (x_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    group_sums = X.reshape(M, K // G, G).sum(axis=2)               # [M, K/G]
+    expect = (c - z0) * np.einsum("mg,gn->mn", group_sums, S)
+    y = gemm_mod.w4a16_reference(x_bits, qweight, qzeros, scale_bits, "bf16", G)
+    return np.allclose(y, expect, rtol=1e-12, atol=1e-12)
+
+
+def pin_integer_special_case(gemm_mod, awq):
+    """S = 1, Z = 0 and integer activations: y = x . Q, an integer matrix product
+    computed exactly with int64."""
+    rng = np.random.default_rng(5)
+    M, K, N, G = 4, 256, 48, 128
+    Q = rng.integers(0, 16, (K, N), dtype=np.uint8)
+    qweight = awq.pack_awq(Q)
+    qzeros = awq.pack_awq(np.zeros((K // G, N), dtype=np.uint8))
+    scale_bits = np.full((K // G, N), 0x3F80, dtype=np.uint16)   # bf16 1.0
+    xi = rng.integers(-3, 4, (M, K)).astype(np.int64)
+    x_bits = (xi.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    y = gemm_mod.w4a16_reference(x_bits, qweight, qzeros, scale_bits, "bf16", G)
+    return np.array_equal(y, (xi @ Q.astype(np.int64)).astype(np.float64))
+
+
+def pin_zero_point_cancels(gemm_mod, awq):
+    """Z equal to the (per group, per column constant) code: every weight is 0, y = 0."""
+    rng = np.random.default_rng(3)
+    M, K, N, G = 2, 256, 16, 128
+    Zc = rng.integers(0, 16, (K // G, N), dtype=np.uint8)
+    Q = np.repeat(Zc, G, axis=0)
+    s = rng.uniform(0.005, 0.02, (K // G, N)).astype(np.float32)
+    scale_bits = (s.view(np.uint32) >> 16).astype(np.uint16)
+    x_bits = (rng.standard_normal((M, K)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    y = gemm_mod.w4a16_reference(x_bits, awq.pack_awq(Q), awq.pack_awq(Zc), scale_bits, "bf16", G)
+    return np.array_equal(y, np.zeros((M, N)))
+
+
+def pin_group_index(gemm_mod, awq):
+    """Only group g's scale is nonzero: y must equal the contribution of rows in g
+    alone, which (Q = 1, Z = 0, scale 1) is the plain sum of x over those rows."""
+    rng = np.random.default_rng(9)
+    M, K, N, G = 2, 512, 16, 128
+    ok = True
+    for g in range(K // G):
+        scale_bits = np.zeros((K // G, N), dtype=np.uint16)
+        scale_bits[g] = 0x3F80
+        qweight = awq.pack_awq(np.ones((K, N), dtype=np.uint8))
+        qzeros = awq.pack_awq(np.zeros((K // G, N), dtype=np.uint8))
+        xi = rng.integers(-4, 5, (M, K)).astype(np.int64)
+        x_bits = (xi.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        y = gemm_mod.w4a16_reference(x_bits, qweight, qzeros, scale_bits, "bf16", G)
+        expect = np.repeat(xi[:, g * G:(g + 1) * G].sum(axis=1, keepdims=True), N, axis=1)
+        ok &= np.array_equal(y, expect.astype(np.float64))
+    return bool(ok)
+
+
+ALL_GEMM_PINS = ("pin_worked_example", "pin_fraction_bruteforce", "pin_closed_form_constant_codes",
+                 "pin_integer_special_case", "pin_zero_point_cancels", "pin_group_index")
+
+
+def run_gemm_pins(gemm_mod, awq):
+    res = {}
+    res["pin_worked_example"] = pin_worked_example(gemm_mod)
+    res["pin_fraction_bruteforce"] = pin_fraction_bruteforce(gemm_mod)
+    res["pin_closed_form_constant_codes"] = pin_closed_form_constant_codes(gemm_mod, awq)
+    res["pin_integer_special_case"] = pin_integer_special_case(gemm_mod, awq)
+    res["pin_zero_point_cancels"] = pin_zero_point_cancels(gemm_mod, awq)
+    res["pin_group_index"] = pin_group_index(gemm_mod, awq)
+    return res
+
+
+# ---- tile layout pins: closed-form byte patterns for index-pattern code matrices ----
+
+def layout_index_pattern_cases(K=256, N=48):
+    """(description, Q, expected weight-plane check) triples. Each Q is chosen so
+    that every byte of the repacked weight plane has a closed-form value."""
+    k = np.arange(K)[:, None]
+    n = np.arange(N)[None, :]
+    KB, NB = K // 128, N // 16
+    lane = np.arange(64)
+
+    def expect_by_lane(f):      # byte value of every byte of lane L's 16 bytes
+        e = np.repeat(f(lane)[:, None], 16, axis=1).reshape(-1).astype(np.uint8)
+        return np.tile(e, NB * KB)
+
+    cases = []
+    cases.append(("code = column within block -> lane L all nibbles L mod 16",
+                  (n % 16) + 0 * k, expect_by_lane(lambda L: 0x11 * (L % 16))))
+    cases.append(("code = (k div 8) mod 4 -> lane L all nibbles L div 16",
+                  ((k // 8) % 4) + 0 * n, expect_by_lane(lambda L: 0x11 * (L // 16))))
+    w_i = np.array([0x11111111 * i for i in range(4)], dtype="<u4").view(np.uint8)
+    cases.append(("code = (k div 32) mod 4 -> word i is 0x11111111 * i",
+                  ((k // 32) % 4) + 0 * n, np.tile(w_i, 64 * NB * KB)))
+    w_o = np.array([0x75316420], dtype="<u4").view(np.uint8)
+    cases.append(("code = k mod 8 -> every word 0x75316420",
+                  (k % 8) + 0 * n, np.tile(w_o, 4 * 64 * NB * KB)))
+    blk = np.array([0x11 * (kb % 16) for nb in range(NB) for kb in range(KB)], dtype=np.uint8)
+    cases.append(("code = row block kb -> block (nb, kb) all bytes 0x11 * kb (nb-major order)",
+                  (k // 128) % 16 + 0 * n, np.repeat(blk, 1024)))
+    blk = np.array([0x11 * (nb % 16) for nb in range(NB) for kb in range(KB)], dtype=np.uint8)
+    cases.append(("code = column block nb -> block (nb, kb) all bytes 0x11 * nb",
+                  (n // 16) % 16 + 0 * k, np.repeat(blk, 1024)))
+    return [(d, q.astype(np.uint8), e) for d, q, e in cases]
+
+
+def pin_layout_index_patterns(tile_layout, K=256, N=48, G=128):
+    zeros = np.zeros((K // G, N), dtype=np.uint8)
+    sbits = np.zeros((K // G, N), dtype=np.uint16)
+    for _, Q, expect in layout_index_pattern_cases(K, N):
+        out = tile_layout.repack(Q, zeros, sbits, G)
+        if not np.array_equal(out[:K * N // 2], expect):
+            return False
+    return True
+
+
+def pin_layout_metadata(tile_layout, K=512, N=32, G=256):
+    """scale bits = column index, zero = group mod 16: metadata word of (nb, kb, c)
+    must be (16 nb + c) | ((128 kb div G) mod 16) << 16, stored nb-major."""
+    KG, KB, NB = K // G, K // 128, N // 16
+    sbits = np.tile(np.arange(N, dtype=np.uint16), (KG, 1))
+    Z = np.repeat((np.arange(KG) % 16).astype(np.uint8)[:, None], N, axis=1)
+    out = tile_layout.repack(np.zeros((K, N), np.uint8), Z, sbits, G)
+    meta = out[K * N // 2:].view("<u4")
+    expect = [(16 * nb + c) | ((((128 * kb) // G) % 16) << 16)
+              for nb in range(NB) for kb in range(KB) for c in range(16)]
+    return meta.tolist() == expect
