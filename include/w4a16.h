@@ -1,0 +1,137 @@
+/*
+ * w4a16.h — C ABI of the MI355X (gfx950) W4A16 library: group-wise asymmetric
+ * int4 weight-only GEMM with 16-bit activations, and the one-time repack of
+ * AWQ-packed weights into this library's GPU tile layout.
+ *
+ *   y[m, n] = sum_k x[m, k] * W[k, n],   W[k, n] = (q[k, n] - z[g, n]) * s[g, n],
+ *   g = k div G  (G = group size, 128 in the common case; -1 means G = K).
+ *
+ * Lifecycle, after the three phases of a quantised linear layer in the vLLM
+ * note "Carga de capas cuantizadas: AWQ / GPTQ / Marlin / fp8" (section
+ * "Responsabilidades": create_weights builds qweight / scales / qzeros,
+ * process_weights_after_loading reorders once after loading, apply runs the
+ * quantised GEMM in the forward):
+ *   1. the caller holds the checkpoint tensors with the shapes of section
+ *      "Flujo de datos": qweight int32 [K, N/8], qzeros int32 [K/G, N/8],
+ *      scales fp16/bf16 [K/G, N];
+ *   2. w4a16_repack writes them once into a packed buffer of
+ *      w4a16_packed_bytes(K, N, G) bytes (the caller may free the three
+ *      checkpoint tensors once the stream has passed the repack);
+ *   3. w4a16_gemm runs the product from the packed buffer, as often as needed.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller. The library
+ *     never allocates, frees or retains them after the call returns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Work
+ *     is enqueued asynchronously on it; nothing synchronises the host. The
+ *     caller keeps every buffer alive until the stream has passed the call.
+ *   - Every argument is validated on the host before anything is launched; an
+ *     invalid call returns its status and touches no memory.
+ *   - Calls on different streams touch only the buffers they are given, so
+ *     they may run concurrently when their outputs do not overlap.
+ *   - Status codes are returned; nothing is thrown across the ABI.
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    W4A16_OK = 0,
+    W4A16_ERR_NULL = 1,         /* a required pointer is NULL                       */
+    W4A16_ERR_SHAPE = 2,        /* M < 0, K or N <= 0, K % 128 != 0 or N % 16 != 0   */
+    W4A16_ERR_GROUP = 3,        /* group size not -1 and not a multiple of 128 dividing K */
+    W4A16_ERR_DTYPE = 4,        /* dtype is neither W4A16_FP16 nor W4A16_BF16        */
+    W4A16_ERR_ALIGN = 5,        /* a pointer is not aligned as documented            */
+    W4A16_ERR_BUFFER_SIZE = 6,  /* a caller buffer is smaller than required          */
+    W4A16_ERR_DEVICE = 7,       /* the current device is not a gfx950 GPU            */
+    W4A16_ERR_HIP = 8,          /* the HIP runtime reported an error at launch       */
+    W4A16_ERR_PATH = 9          /* unknown path, or the forced path cannot take M    */
+} w4a16_status;
+
+typedef enum {
+    W4A16_FP16 = 0,             /* IEEE binary16 activations, scales, bias, output  */
+    W4A16_BF16 = 1              /* bfloat16 activations, scales, bias, output       */
+} w4a16_dtype;
+
+typedef enum {
+    W4A16_PATH_AUTO = 0,        /* M <= gemv_max_m: GEMV, otherwise MFMA GEMM      */
+    W4A16_PATH_GEMV = 1,        /* weight-streaming split-K GEMV, M <= 16          */
+    W4A16_PATH_MFMA = 2         /* LDS-staged dequantise -> MFMA GEMM, any M       */
+} w4a16_path;
+
+/* Version of the packed tile layout. A buffer written by one version must not be
+ * read by another; callers that persist packed buffers store this number with them. */
+int w4a16_layout_version(void);
+
+/* Bytes of the packed buffer for a K x N weight with group size `group_size`:
+ * K*N/2 (4-bit codes) + 4*(K/128)*N (one 32-bit scale/zero word per column per
+ * 128-row block). Returns 0 if the shape or group size is not supported. */
+size_t w4a16_packed_bytes(int64_t K, int64_t N, int64_t group_size);
+
+/* One-time repack of AWQ checkpoint tensors into the packed tile layout
+ * ("process_weights_after_loading" of the vLLM note: the AWQ packing order along
+ * the output dimension is undone and the codes are rewritten in the layout the
+ * GEMM kernels read with 128-bit loads).
+ *
+ *   qweight  int32 [K, N/8], row-major. Word j of row k holds the 4-bit codes of
+ *            columns 8j .. 8j+7; nibble slot s (bits 4s..4s+3) holds column
+ *            8j + ORDER[s], ORDER = 0,2,4,6,1,3,5,7 (the AWQ interleave).
+ *   qzeros   int32 [K/G, N/8], row-major, packed exactly like qweight.
+ *   scales   [K/G, N] row-major, of `dtype`.
+ *   packed   output, `packed_bytes` >= w4a16_packed_bytes(K, N, group_size).
+ *            Only the first w4a16_packed_bytes(...) bytes are written.
+ *
+ * Alignment: qweight, qzeros 4 bytes; scales 2 bytes; packed 16 bytes.
+ * The result is a pure function of the inputs (bit-for-bit reproducible). */
+w4a16_status w4a16_repack(const int32_t* qweight, const int32_t* qzeros, const void* scales,
+                          w4a16_dtype dtype, int64_t K, int64_t N, int64_t group_size,
+                          void* packed, size_t packed_bytes, void* stream);
+
+/* Device workspace the GEMM needs for this shape, in bytes. The current kernels
+ * reduce split-K partial sums on chip, so this is 0 for every shape; the
+ * argument pair stays in the ABI for kernels that will need scratch memory. */
+size_t w4a16_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t group_size);
+
+/* y = x . dequant(W) (+ bias), from a buffer written by w4a16_repack
+ * ("apply(layer, x, bias)" of the vLLM note, section "Flujo de datos").
+ *
+ *   x        [M, K] row-major, `dtype`. 16-byte aligned.
+ *   packed   the repacked weight, `packed_bytes` >= w4a16_packed_bytes(K, N, G).
+ *            16-byte aligned.
+ *   y        [M, N] row-major, `dtype`, written in full. 16-byte aligned. Must not
+ *            overlap x, packed or bias.
+ *   bias     [N] of `dtype`, or NULL. 2-byte aligned. Added in fp32 before rounding.
+ *   group_size must be the value the buffer was repacked with (checked for shape
+ *            validity only: the metadata of the buffer carries the groups).
+ *   workspace / workspace_bytes: may be NULL / 0 when w4a16_workspace_bytes is 0.
+ *
+ * Products accumulate in fp32; the output is rounded to `dtype` once, to nearest
+ * even. For fixed inputs and shape the result is bit-for-bit reproducible from run
+ * to run. M = 0 is a valid no-op. */
+w4a16_status w4a16_gemm(const void* x, const void* packed, size_t packed_bytes, w4a16_dtype dtype,
+                        void* y, int64_t M, int64_t K, int64_t N, int64_t group_size,
+                        const void* bias, void* workspace, size_t workspace_bytes, void* stream);
+
+/* w4a16_gemm with the kernel choice exposed (tests, tuning). With
+ * W4A16_PATH_AUTO, M <= gemv_max_m takes the GEMV (gemv_max_m in 0..16; a
+ * negative value selects the default, 8). W4A16_PATH_GEMV requires M <= 16.
+ * Both paths read the same packed buffer. */
+w4a16_status w4a16_gemm_ex(const void* x, const void* packed, size_t packed_bytes, w4a16_dtype dtype,
+                           void* y, int64_t M, int64_t K, int64_t N, int64_t group_size,
+                           const void* bias, void* workspace, size_t workspace_bytes, void* stream,
+                           w4a16_path path, int64_t gemv_max_m);
+
+/* Static, NUL-terminated description of a status code ("unknown status" otherwise). */
+const char* w4a16_status_str(w4a16_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */

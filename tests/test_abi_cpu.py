@@ -1,0 +1,120 @@
+"""The C-ABI library on the host: it loads without a GPU, exports every entry point
+the header declares, and rejects invalid arguments before touching a device."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a16.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w4a16_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def w():
+    import w4a16_int4_weight_amd as mod
+    return mod
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted([
+        "w4a16_gemm", "w4a16_gemm_ex", "w4a16_layout_version", "w4a16_packed_bytes",
+        "w4a16_repack", "w4a16_status_str", "w4a16_workspace_bytes"])
+
+
+def test_library_exports_every_declared_symbol(w):
+    for name in declared_functions():
+        assert hasattr(w.lib, name), name
+    # and the binding mirrors each name
+    for name in declared_functions():
+        assert callable(getattr(w, name)), name
+
+
+def test_exports_are_c_symbols():
+    # no C++ mangling on the entry points
+    import subprocess
+    from w4a16_int4_weight_amd.build import LIB_PATH
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in declared_functions():
+        assert name in exported, name
+
+
+def test_layout_version_and_sizes(w):
+    from oracle import tile_layout
+    assert w.w4a16_layout_version() == tile_layout.LAYOUT_VERSION
+    for K, N, G in [(512, 512, 128), (2048, 13312, 128), (6656, 2048, 128), (2048, 131072, 128),
+                    (1024, 48, 256), (1024, 48, -1)]:
+        assert w.w4a16_packed_bytes(K, N, G) == tile_layout.packed_bytes(K, N, G)
+    for K, N, G in [(100, 16, 128), (256, 24, 128), (256, 16, 64), (384, 16, 256), (0, 16, 128), (128, 0, 128)]:
+        assert w.w4a16_packed_bytes(K, N, G) == 0
+    assert w.w4a16_workspace_bytes(512, 2048, 13312, 128) == 0
+
+
+def test_status_strings(w):
+    for code in range(10):
+        s = w.w4a16_status_str(code)
+        assert s and s != "unknown status"
+    assert w.w4a16_status_str(42) == "unknown status"
+
+
+P = ctypes.c_void_p
+
+
+def gemm(w, x=P(256), packed=P(512), pbytes=1 << 40, dtype=1, y=P(1024), M=4, K=512, N=512, G=128,
+         bias=None, ws=None, wsb=0, stream=None, path=None, gmax=-1):
+    args = (x, packed, pbytes, dtype, y, M, K, N, G, bias, ws, wsb, stream)
+    if path is None:
+        return w.lib.w4a16_gemm(*args)
+    return w.lib.w4a16_gemm_ex(*args, path, gmax)
+
+
+def test_gemm_validation_before_any_device_call(w):
+    # each invalid call returns its status; none reaches the device check (7)
+    assert gemm(w, M=-1) == 2
+    assert gemm(w, K=500) == 2
+    assert gemm(w, N=24) == 2
+    assert gemm(w, K=0) == 2
+    assert gemm(w, G=64) == 3
+    assert gemm(w, G=384) == 3
+    assert gemm(w, dtype=2) == 4
+    assert gemm(w, x=None) == 1
+    assert gemm(w, packed=None) == 1
+    assert gemm(w, y=None) == 1
+    assert gemm(w, x=P(258)) == 5
+    assert gemm(w, packed=P(520)) == 5
+    assert gemm(w, y=P(1032)) == 5
+    assert gemm(w, bias=P(1025)) == 5
+    assert gemm(w, pbytes=512 * 512 // 2) == 6
+    assert gemm(w, path=3) == 9
+    assert gemm(w, path=1, M=17) == 9
+    assert gemm(w, path=0, gmax=17) == 9
+    # M = 0 is a valid no-op, even with NULL buffers
+    assert gemm(w, M=0, x=None, y=None, packed=None) == 0
+    # a fully valid call on this GPU-less host stops at the device check
+    assert gemm(w) == 7
+
+
+def test_repack_validation_before_any_device_call(w):
+    def repack(qw=P(256), qz=P(512), sc=P(768), dtype=1, K=512, N=512, G=128, packed=P(1024), pbytes=1 << 40):
+        return w.lib.w4a16_repack(qw, qz, sc, dtype, K, N, G, packed, pbytes, None)
+    assert repack(K=100) == 2
+    assert repack(N=8) == 2
+    assert repack(G=32) == 3
+    assert repack(dtype=-1) == 4
+    assert repack(qw=None) == 1
+    assert repack(qz=None) == 1
+    assert repack(sc=None) == 1
+    assert repack(packed=None) == 1
+    assert repack(qw=P(258)) == 5
+    assert repack(sc=P(769)) == 5
+    assert repack(packed=P(1032)) == 5
+    assert repack(pbytes=1000) == 6
+    assert repack() == 7

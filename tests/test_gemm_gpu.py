@@ -1,0 +1,205 @@
+"""GPU W4A16 GEMM against the float64 oracle.
+
+Bar: max |y_gpu - y_ref| <= 1e-2 * max |y_ref| over each output tensor, where
+y_ref is the oracle's unrounded float64 product; exact special cases must be
+bit-identical to the correctly rounded exact result.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import awq, gemm as ogemm, numerics
+from gpu_util import (DEV, TORCH_DTYPE, bits_to_device, device_to_bits, int32_to_device, oracle_repack,
+                      oracle_y, sample_column_blocks, weights_to_device, y_to_f64)
+
+pytestmark = pytest.mark.gpu
+TOL = ogemm.TOLERANCE
+
+
+@pytest.fixture(scope="module")
+def w():
+    import w4a16_int4_weight_amd as mod
+    return mod
+
+
+def pack_on_gpu(w, ws):
+    qw, qz, sc = weights_to_device(ws)
+    return w.w4a16_repack(qw, qz, sc, ws.group_size)
+
+
+def run(w, ws, packed, x_bits, path="auto", bias=None, stream=None):
+    x = bits_to_device(x_bits, ws.dtype)
+    y = w.w4a16_gemm_ex(x, packed, ws.N, ws.group_size, bias=bias, path=path, stream=stream)
+    torch.cuda.synchronize()
+    return y
+
+
+WORKLOAD_CASES = [(name, M) for name, wl in synth.WORKLOADS.items() for M in wl.Ms]
+
+
+@pytest.mark.parametrize("name,M", WORKLOAD_CASES, ids=[f"{n}-M{m}" for n, m in WORKLOAD_CASES])
+def test_gemm_workloads(w, name, M):
+    print(f"gemm workload {name} M={M}", flush=True)
+    ws = synth.make(name)
+    packed = pack_on_gpu(w, ws)
+    y = run(w, ws, packed, ws.x_bits[M])
+    got = y_to_f64(y, ws.dtype)
+    if ws.N > 16384:
+        cols = sample_column_blocks(ws.N, 256, seed=M)
+        ref = oracle_y(ws, ws.x_bits[M], cols)
+        got = got[:, cols]
+    else:
+        ref = oracle_y(ws, ws.x_bits[M])
+    err = ogemm.max_rel_error(got, ref)
+    print(f"  max rel err {err:.3e}", flush=True)
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("M", list(range(1, 18)) + [24, 31, 32, 33, 63, 64, 65, 100, 128, 129, 200])
+def test_gemm_m_sweep_auto(w, M):
+    ws = synth.make_custom(500 + M, M, 1152, 272, "bf16", 128)   # 9 row blocks, 17 column blocks (ragged tile)
+    packed = pack_on_gpu(w, ws)
+    got = y_to_f64(run(w, ws, packed, ws.x_bits[M]), "bf16")
+    assert ogemm.max_rel_error(got, oracle_y(ws, ws.x_bits[M])) <= TOL
+
+
+@pytest.mark.parametrize("path", ["gemv", "mfma"])
+@pytest.mark.parametrize("M", [1, 2, 4, 7, 8, 9, 15, 16])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_gemm_forced_paths(w, path, M, dtype):
+    ws = synth.make_custom(900 + M, M, 6656, 48, dtype, 128)        # down-projection K, 52 row blocks
+    packed = pack_on_gpu(w, ws)
+    got = y_to_f64(run(w, ws, packed, ws.x_bits[M], path=path), dtype)
+    assert ogemm.max_rel_error(got, oracle_y(ws, ws.x_bits[M])) <= TOL
+
+
+def test_gemm_from_oracle_packed_buffer(w):
+    # the GEMM alone, fed the oracle's packed bytes (no GPU repack involved)
+    ws = synth.make_custom(41, 24, 1024, 512, "bf16", 128)
+    packed = torch.from_numpy(oracle_repack(ws)).to(DEV)
+    for path in ("gemv", "mfma"):
+        M = 16 if path == "gemv" else 24
+        xb = ws.x_bits[24][:M]
+        got = y_to_f64(run(w, ws, packed, xb, path=path), "bf16")
+        assert ogemm.max_rel_error(got, oracle_y(ws, xb)) <= TOL
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("path", ["gemv", "mfma"])
+def test_one_hot_rows_are_exact(w, dtype, path):
+    # x = e_k: y[m, :] = W[k_m, :] = (q - z) * s exactly, so the output must be the
+    # correctly rounded weight row, bit for bit; pins the k <-> lane/slot mapping
+    K, N, G = 512, 64, 128
+    rng = np.random.default_rng(3)
+    ws = synth.make_custom(3, 1, K, N, dtype, G)
+    M = 16
+    ks = rng.choice(K, size=M, replace=False)
+    x = np.zeros((M, K), dtype=np.float64)
+    x[np.arange(M), ks] = 1.0
+    xb = numerics.f64_to_half_bits_rne(x, dtype)
+    packed = pack_on_gpu(w, ws)
+    got = device_to_bits(run(w, ws, packed, xb, path=path))
+    ref = oracle_y(ws, xb)
+    assert np.array_equal(got, numerics.f64_to_half_bits_rne(ref, dtype))
+
+
+@pytest.mark.parametrize("path", ["gemv", "mfma"])
+def test_small_integer_case_is_exact(w, path):
+    # x in {-1, 0, 1}, s = 2^-6: every product and partial sum is exact in fp32,
+    # so any summation order gives the exact result and the output is RNE(y)
+    K, N, G, M = 1024, 96, 128, 12
+    rng = np.random.default_rng(12)
+    Q = rng.integers(0, 16, (K, N), dtype=np.uint8)
+    Z = rng.integers(0, 16, (K // G, N), dtype=np.uint8)
+    ws = synth.make_custom(12, M, K, N, "bf16", G)
+    ws.qweight, ws.qzeros = awq.pack_awq(Q), awq.pack_awq(Z)
+    ws.scale_bits = np.full((K // G, N), 0x3C80, np.uint16)        # bf16 2^-6
+    xb = numerics.f64_to_half_bits_rne(rng.integers(-1, 2, (M, K)).astype(np.float64), "bf16")
+    packed = pack_on_gpu(w, ws)
+    got = device_to_bits(run(w, ws, packed, xb, path=path))
+    assert np.array_equal(got, numerics.f64_to_half_bits_rne(oracle_y(ws, xb), "bf16"))
+
+
+@pytest.mark.parametrize("path", ["gemv", "mfma"])
+def test_bias(w, path):
+    ws = synth.make_custom(60, 8, 1024, 272, "bf16", 128)
+    rng = np.random.default_rng(60)
+    bias_bits = numerics.f64_to_half_bits_rne(rng.standard_normal(272), "bf16")
+    packed = pack_on_gpu(w, ws)
+    got = y_to_f64(run(w, ws, packed, ws.x_bits[8], path=path, bias=bits_to_device(bias_bits, "bf16")), "bf16")
+    assert ogemm.max_rel_error(got, oracle_y(ws, ws.x_bits[8], bias_bits=bias_bits)) <= TOL
+
+
+@pytest.mark.parametrize("M", [1, 8, 16, 512])
+def test_deterministic_and_in_bounds(w, M):
+    ws = synth.make_custom(70 + M, M, 2048, 1040, "bf16", 128)
+    packed = pack_on_gpu(w, ws)
+    x = bits_to_device(ws.x_bits[M], "bf16")
+    pad = 4096
+    outs = []
+    for _ in range(2):
+        buf = torch.full((M * 1040 + 2 * pad,), -7.0, dtype=torch.bfloat16, device=DEV)
+        y = buf[pad:pad + M * 1040].view(M, 1040)
+        w.w4a16_gemm(x, packed, 1040, 128, y=y)
+        torch.cuda.synchronize()
+        b = buf.cpu()
+        assert torch.all(b[:pad] == -7.0) and torch.all(b[-pad:] == -7.0), "write outside y"
+        outs.append(device_to_bits(y))
+    assert np.array_equal(outs[0], outs[1])
+
+
+def test_side_stream(w):
+    ws = synth.make_custom(80, 64, 1024, 512, "bf16", 128)
+    packed = pack_on_gpu(w, ws)
+    x = bits_to_device(ws.x_bits[64], "bf16")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        y1 = w.w4a16_gemm(x[:4].contiguous(), packed, 512, 128, stream=s)
+        y2 = w.w4a16_gemm(x, packed, 512, 128, stream=s)
+    s.synchronize()
+    assert ogemm.max_rel_error(y_to_f64(y2, "bf16"), oracle_y(ws, ws.x_bits[64])) <= TOL
+    assert ogemm.max_rel_error(y_to_f64(y1, "bf16"), oracle_y(ws, ws.x_bits[64][:4])) <= TOL
+
+
+def test_edge_shapes(w):
+    # one row block and one column block; M = 0 is a no-op
+    ws = synth.make_custom(90, 3, 128, 16, "fp16", 128)
+    packed = pack_on_gpu(w, ws)
+    for path in ("gemv", "mfma"):
+        got = y_to_f64(run(w, ws, packed, ws.x_bits[3], path=path), "fp16")
+        assert ogemm.max_rel_error(got, oracle_y(ws, ws.x_bits[3])) <= TOL
+    x0 = torch.empty((0, 128), dtype=torch.float16, device=DEV)
+    y0 = w.w4a16_gemm(x0, packed, 16, 128)
+    assert y0.shape == (0, 16)
+
+
+def test_per_channel_and_wide_groups(w):
+    for G in (-1, 256):
+        ws = synth.make_custom(95, 20, 1024, 64, "bf16", G)
+        packed = pack_on_gpu(w, ws)
+        for path, M in (("gemv", 5), ("mfma", 20)):
+            xb = ws.x_bits[20][:M]
+            got = y_to_f64(run(w, ws, packed, xb, path=path), "bf16")
+            assert ogemm.max_rel_error(got, oracle_y(ws, xb)) <= TOL
+
+
+def test_gemm_rejects_bad_calls(w):
+    ws = synth.make_custom(99, 4, 256, 32, "bf16", 128)
+    packed = pack_on_gpu(w, ws)
+    x = bits_to_device(ws.x_bits[4], "bf16")
+    with pytest.raises(w.W4A16Error) as e:
+        w.w4a16_gemm(x, packed[:100], 32, 128)
+    assert e.value.status == "W4A16_ERR_BUFFER_SIZE"
+    with pytest.raises(w.W4A16Error) as e:
+        w.w4a16_gemm_ex(x, packed, 32, 128, path="gemv", gemv_max_m=17)
+    assert e.value.status == "W4A16_ERR_PATH"
+    xbig = torch.zeros((17, 256), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(w.W4A16Error) as e:
+        w.w4a16_gemm_ex(xbig, packed, 32, 128, path="gemv")
+    assert e.value.status == "W4A16_ERR_PATH"
+    with pytest.raises(w.W4A16Error) as e:
+        w.w4a16_gemm(x, packed, 32, 64)
+    assert e.value.status == "W4A16_ERR_GROUP"

@@ -1,0 +1,158 @@
+"""Python binding of the MI355X W4A16 library (libw4a16.so): argument marshalling
+only. Every step of the repack and the GEMM runs in the HIP kernels behind the C
+ABI declared in include/w4a16.h; PyTorch provides device memory and streams.
+
+Functions keep the C names:
+  w4a16_layout_version()                         -> int
+  w4a16_packed_bytes(K, N, group_size)           -> int (0 if unsupported)
+  w4a16_workspace_bytes(M, K, N, group_size)     -> int
+  w4a16_repack(qweight, qzeros, scales, group_size, packed=None, stream=None) -> packed uint8 tensor
+  w4a16_gemm(x, packed, N, group_size, bias=None, y=None, workspace=None, stream=None) -> y
+  w4a16_gemm_ex(..., path="auto"|"gemv"|"mfma", gemv_max_m=-1)            -> y
+  w4a16_status_str(code)                         -> str
+
+There is no fallback: if the library is missing the import fails, and a call
+whose tensors are not on a gfx950 GPU returns the library's error, raised here.
+"""
+
+import ctypes
+import os
+
+import torch
+
+from .build import LIB_PATH
+
+__all__ = [
+    "W4A16Error", "lib", "w4a16_layout_version", "w4a16_packed_bytes", "w4a16_workspace_bytes",
+    "w4a16_repack", "w4a16_gemm", "w4a16_gemm_ex", "w4a16_status_str", "STATUS", "PATHS",
+]
+
+STATUS = {
+    0: "W4A16_OK", 1: "W4A16_ERR_NULL", 2: "W4A16_ERR_SHAPE", 3: "W4A16_ERR_GROUP",
+    4: "W4A16_ERR_DTYPE", 5: "W4A16_ERR_ALIGN", 6: "W4A16_ERR_BUFFER_SIZE",
+    7: "W4A16_ERR_DEVICE", 8: "W4A16_ERR_HIP", 9: "W4A16_ERR_PATH",
+}
+DTYPES = {torch.float16: 0, torch.bfloat16: 1}
+PATHS = {"auto": 0, "gemv": 1, "mfma": 2}
+
+
+class W4A16Error(RuntimeError):
+    def __init__(self, code, what):
+        self.code = code
+        self.status = STATUS.get(code, str(code))
+        super().__init__(f"{what}: {self.status} ({w4a16_status_str(code)})")
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m w4a16_int4_weight_amd.build` "
+                      "(the W4A16 path has no fallback)")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_vp, _i64, _sz, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+lib.w4a16_layout_version.argtypes = []
+lib.w4a16_layout_version.restype = _int
+lib.w4a16_packed_bytes.argtypes = [_i64, _i64, _i64]
+lib.w4a16_packed_bytes.restype = _sz
+lib.w4a16_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64]
+lib.w4a16_workspace_bytes.restype = _sz
+lib.w4a16_repack.argtypes = [_vp, _vp, _vp, _int, _i64, _i64, _i64, _vp, _sz, _vp]
+lib.w4a16_repack.restype = _int
+lib.w4a16_gemm.argtypes = [_vp, _vp, _sz, _int, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _sz, _vp]
+lib.w4a16_gemm.restype = _int
+lib.w4a16_gemm_ex.argtypes = lib.w4a16_gemm.argtypes + [_int, _i64]
+lib.w4a16_gemm_ex.restype = _int
+lib.w4a16_status_str.argtypes = [_int]
+lib.w4a16_status_str.restype = ctypes.c_char_p
+
+
+def w4a16_status_str(code):
+    return lib.w4a16_status_str(int(code)).decode()
+
+
+def w4a16_layout_version():
+    return lib.w4a16_layout_version()
+
+
+def w4a16_packed_bytes(K, N, group_size):
+    return lib.w4a16_packed_bytes(K, N, group_size)
+
+
+def w4a16_workspace_bytes(M, K, N, group_size):
+    return lib.w4a16_workspace_bytes(M, K, N, group_size)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(code, what):
+    if code != 0:
+        raise W4A16Error(code, what)
+
+
+def _dtype_code(dtype):
+    if dtype not in DTYPES:
+        raise W4A16Error(4, f"dtype {dtype}")
+    return DTYPES[dtype]
+
+
+def w4a16_repack(qweight, qzeros, scales, group_size=128, packed=None, stream=None):
+    """AWQ qweight int32 [K, N/8], qzeros int32 [K/G, N/8], scales [K/G, N] (fp16/bf16),
+    all on one GPU -> packed uint8 tensor of w4a16_packed_bytes(K, N, group_size) bytes."""
+    K, N = qweight.shape[0], qweight.shape[1] * 8
+    nbytes = w4a16_packed_bytes(K, N, group_size)
+    if packed is None:
+        packed = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=qweight.device)
+    for t, name in ((qweight, "qweight"), (qzeros, "qzeros"), (scales, "scales")):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if qweight.dtype != torch.int32 or qzeros.dtype != torch.int32:
+        raise ValueError("qweight and qzeros must be int32")
+    G = K if group_size == -1 else group_size
+    if G > 0 and K % G == 0 and (tuple(qzeros.shape) != (K // G, N // 8) or tuple(scales.shape) != (K // G, N)):
+        raise ValueError("qzeros must be [K/G, N/8] and scales [K/G, N]")
+    code = lib.w4a16_repack(_ptr(qweight), _ptr(qzeros), _ptr(scales), _dtype_code(scales.dtype),
+                            K, N, group_size, _ptr(packed), packed.numel() * packed.element_size(),
+                            _stream(stream, qweight.device))
+    _check(code, "w4a16_repack")
+    return packed
+
+
+def _gemm_args(x, packed, N, group_size, bias, y, workspace, stream):
+    if x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [M, K] tensor")
+    M, K = x.shape
+    if y is None:
+        y = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    if tuple(y.shape) != (M, N) or y.dtype != x.dtype or not y.is_contiguous():
+        raise ValueError("y must be a contiguous [M, N] tensor of x's dtype")
+    if bias is not None and (bias.dtype != x.dtype or tuple(bias.shape) != (N,) or not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous [N] tensor of x's dtype")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    args = (_ptr(x), _ptr(packed), packed.numel() * packed.element_size(), _dtype_code(x.dtype),
+            _ptr(y), M, K, N, group_size, _ptr(bias), _ptr(workspace), ws_bytes, _stream(stream, x.device))
+    return args, y
+
+
+def w4a16_gemm(x, packed, N, group_size=128, bias=None, y=None, workspace=None, stream=None):
+    """x [M, K] (fp16/bf16) times the packed weight (+ bias) -> y [M, N] of x's dtype."""
+    args, y = _gemm_args(x, packed, N, group_size, bias, y, workspace, stream)
+    _check(lib.w4a16_gemm(*args), "w4a16_gemm")
+    return y
+
+
+def w4a16_gemm_ex(x, packed, N, group_size=128, bias=None, y=None, workspace=None, stream=None,
+                  path="auto", gemv_max_m=-1):
+    """w4a16_gemm with the kernel path forced ("auto", "gemv" or "mfma")."""
+    if path not in PATHS:
+        raise W4A16Error(9, f"path {path!r}")
+    args, y = _gemm_args(x, packed, N, group_size, bias, y, workspace, stream)
+    _check(lib.w4a16_gemm_ex(*args, PATHS[path], gemv_max_m), "w4a16_gemm_ex")
+    return y

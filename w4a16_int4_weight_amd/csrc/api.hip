@@ -1,0 +1,153 @@
+// C ABI of the W4A16 library: argument validation, path dispatch, launches.
+// The entry points and their contracts are declared in include/w4a16.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "../../include/w4a16.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int kLayoutVersion = 1;
+constexpr int64_t kGemvMaxRows = 16;      // rows one GEMV A operand holds
+constexpr int64_t kDefaultGemvMaxM = 8;
+constexpr int kMaxDevices = 64;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Resolved group size, or 0 if (K, N, group_size) is outside the tile layout.
+w4a16_status check_shape(int64_t K, int64_t N, int64_t group_size, int64_t* G_out) {
+    if (K <= 0 || N <= 0 || K % 128 != 0 || N % 16 != 0) return W4A16_ERR_SHAPE;
+    if (K > (int64_t(1) << 40) || N > (int64_t(1) << 40) || (K / 2) > INT64_MAX / N) return W4A16_ERR_SHAPE;
+    const int64_t G = group_size == -1 ? K : group_size;
+    if (G <= 0 || G % 128 != 0 || K % G != 0) return W4A16_ERR_GROUP;
+    *G_out = G;
+    return W4A16_OK;
+}
+
+size_t packed_size(int64_t K, int64_t N) { return (size_t)(K * N / 2) + (size_t)4 * (size_t)(K / 128) * (size_t)N; }
+
+// 0 = unknown, 1 = gfx950, 2 = other; cached per device ordinal.
+std::atomic<int> g_device_kind[kMaxDevices];
+
+w4a16_status check_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return W4A16_ERR_DEVICE;
+    if (dev < 0 || dev >= kMaxDevices) return W4A16_ERR_DEVICE;
+    int kind = g_device_kind[dev].load(std::memory_order_relaxed);
+    if (kind == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return W4A16_ERR_DEVICE;
+        kind = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_device_kind[dev].store(kind, std::memory_order_relaxed);
+    }
+    return kind == 1 ? W4A16_OK : W4A16_ERR_DEVICE;
+}
+
+w4a16_status gemm_impl(const void* x, const void* packed, size_t packed_bytes, w4a16_dtype dtype, void* y,
+                       int64_t M, int64_t K, int64_t N, int64_t group_size, const void* bias, void* workspace,
+                       size_t workspace_bytes, void* stream, w4a16_path path, int64_t gemv_max_m) {
+    (void)workspace;
+    (void)workspace_bytes;
+    if (M < 0) return W4A16_ERR_SHAPE;
+    int64_t G = 0;
+    w4a16_status st = check_shape(K, N, group_size, &G);
+    if (st != W4A16_OK) return st;
+    if (dtype != W4A16_FP16 && dtype != W4A16_BF16) return W4A16_ERR_DTYPE;
+    if (path != W4A16_PATH_AUTO && path != W4A16_PATH_GEMV && path != W4A16_PATH_MFMA) return W4A16_ERR_PATH;
+    if (gemv_max_m < 0) gemv_max_m = kDefaultGemvMaxM;
+    if (gemv_max_m > kGemvMaxRows) return W4A16_ERR_PATH;
+    if (path == W4A16_PATH_GEMV && M > kGemvMaxRows) return W4A16_ERR_PATH;
+    if (M == 0) return W4A16_OK;
+    if (!x || !packed || !y) return W4A16_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(y, 16) || (bias && !aligned(bias, 2)))
+        return W4A16_ERR_ALIGN;
+    if (packed_bytes < packed_size(K, N)) return W4A16_ERR_BUFFER_SIZE;
+    st = check_device();
+    if (st != W4A16_OK) return st;
+
+    const bool bf16 = dtype == W4A16_BF16;
+    const bool use_gemv = path == W4A16_PATH_GEMV || (path == W4A16_PATH_AUTO && M <= gemv_max_m);
+    const auto* xp = static_cast<const uint16_t*>(x);
+    const auto* wp = static_cast<const uint8_t*>(packed);
+    const auto* bp = static_cast<const uint16_t*>(bias);
+    auto* yp = static_cast<uint16_t*>(y);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t err = use_gemv ? w4a16::launch_gemv(xp, wp, bp, yp, M, K, N, bf16, s)
+                                    : w4a16::launch_gemm(xp, wp, bp, yp, M, K, N, bf16, s);
+    return err == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int w4a16_layout_version(void) { return kLayoutVersion; }
+
+size_t w4a16_packed_bytes(int64_t K, int64_t N, int64_t group_size) {
+    int64_t G = 0;
+    if (check_shape(K, N, group_size, &G) != W4A16_OK) return 0;
+    return packed_size(K, N);
+}
+
+w4a16_status w4a16_repack(const int32_t* qweight, const int32_t* qzeros, const void* scales, w4a16_dtype dtype,
+                          int64_t K, int64_t N, int64_t group_size, void* packed, size_t packed_bytes,
+                          void* stream) {
+    int64_t G = 0;
+    w4a16_status st = check_shape(K, N, group_size, &G);
+    if (st != W4A16_OK) return st;
+    if (dtype != W4A16_FP16 && dtype != W4A16_BF16) return W4A16_ERR_DTYPE;
+    if (!qweight || !qzeros || !scales || !packed) return W4A16_ERR_NULL;
+    if (!aligned(qweight, 4) || !aligned(qzeros, 4) || !aligned(scales, 2) || !aligned(packed, 16))
+        return W4A16_ERR_ALIGN;
+    if (packed_bytes < packed_size(K, N)) return W4A16_ERR_BUFFER_SIZE;
+    st = check_device();
+    if (st != W4A16_OK) return st;
+    const hipError_t err = w4a16::launch_repack(qweight, qzeros, static_cast<const uint16_t*>(scales),
+                                                static_cast<uint8_t*>(packed), K, N, G,
+                                                static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
+size_t w4a16_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t group_size) {
+    (void)M;
+    (void)K;
+    (void)N;
+    (void)group_size;
+    return 0;
+}
+
+w4a16_status w4a16_gemm(const void* x, const void* packed, size_t packed_bytes, w4a16_dtype dtype, void* y,
+                        int64_t M, int64_t K, int64_t N, int64_t group_size, const void* bias, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+    return gemm_impl(x, packed, packed_bytes, dtype, y, M, K, N, group_size, bias, workspace, workspace_bytes,
+                     stream, W4A16_PATH_AUTO, kDefaultGemvMaxM);
+}
+
+w4a16_status w4a16_gemm_ex(const void* x, const void* packed, size_t packed_bytes, w4a16_dtype dtype, void* y,
+                           int64_t M, int64_t K, int64_t N, int64_t group_size, const void* bias, void* workspace,
+                           size_t workspace_bytes, void* stream, w4a16_path path, int64_t gemv_max_m) {
+    return gemm_impl(x, packed, packed_bytes, dtype, y, M, K, N, group_size, bias, workspace, workspace_bytes,
+                     stream, path, gemv_max_m);
+}
+
+const char* w4a16_status_str(w4a16_status status) {
+    switch (status) {
+        case W4A16_OK: return "ok";
+        case W4A16_ERR_NULL: return "a required pointer is NULL";
+        case W4A16_ERR_SHAPE: return "unsupported shape (need M >= 0, K % 128 == 0, N % 16 == 0)";
+        case W4A16_ERR_GROUP: return "unsupported group size (need -1 or a multiple of 128 dividing K)";
+        case W4A16_ERR_DTYPE: return "unsupported dtype (need fp16 or bf16)";
+        case W4A16_ERR_ALIGN: return "misaligned pointer";
+        case W4A16_ERR_BUFFER_SIZE: return "caller buffer too small";
+        case W4A16_ERR_DEVICE: return "current device is not a gfx950 GPU";
+        case W4A16_ERR_HIP: return "HIP launch error";
+        case W4A16_ERR_PATH: return "unknown path, or the forced path cannot take this M";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,99 @@
+// Device-side definitions shared by the W4A16 kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4a16 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Packed tile layout, version 1 (K x N weight, 128-row blocks, 16-column blocks):
+//   weight plane: block (nb, kb) = 1024 bytes at 1024 * (nb * KB + kb); lane L owns
+//   16 bytes = 4 words; word i of lane L holds column 16 nb + (L % 16), rows
+//   128 kb + 32 i + 8 (L / 16) + e, e = 0..7; nibble slot s holds row e = kTileOrder(s).
+//   metadata plane (after K*N/2 bytes): word (nb * KB + kb) * 16 + c =
+//   scale bits | zero << 16 for column 16 nb + c over row block kb.
+constexpr int kRowsPerBlock = 128;
+constexpr int kColsPerBlock = 16;
+constexpr int kBlockBytes = 1024;
+
+// Row e held by nibble slot s of a tile word: 0,2,4,6,1,3,5,7. Slots t and t+4
+// hold rows 2t and 2t+1, so (word >> 4t) & 0x000F000F puts the pair (2t, 2t+1)
+// in the low bits of the two 16-bit halves.
+__host__ __device__ constexpr int tile_row_of_slot(int s) { return 2 * (s & 3) + (s >> 2); }
+
+// AWQ: column 8j + t of an AWQ word sits in nibble slot awq_slot_of_column(t),
+// the inverse of the interleave 0,2,4,6,1,3,5,7 (slot s holds column ORDER[s]).
+__host__ __device__ constexpr int awq_slot_of_column(int t) { return (t >> 1) + 4 * (t & 1); }
+
+// 16-bit "magic" encodings: OR-ing a code q (0..15) into the low mantissa bits
+// gives the exact value base + q.
+//   bf16 0x4300 = 128.0, mantissa step 1 on [128, 256)
+//   fp16 0x6400 = 1024.0, mantissa step 1 on [1024, 2048)
+template <bool kBF16> struct Magic;
+template <> struct Magic<true> {
+    static constexpr uint32_t kBase2 = 0x43004300u;   // (128, 128)
+    static constexpr uint32_t kNegBase = 0xC300u;      // -128; OR z gives -(128 + z)
+    static constexpr float kBase = 128.0f;
+};
+template <> struct Magic<false> {
+    static constexpr uint32_t kBase2 = 0x64006400u;   // (1024, 1024)
+    static constexpr uint32_t kNegBase = 0xE400u;      // -1024; OR z gives -(1024 + z)
+    static constexpr float kBase = 1024.0f;
+};
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t b) {
+    _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)b);
+    return (float)h;
+}
+
+template <bool kBF16>
+__device__ __forceinline__ float half_bits_to_f32(uint32_t b) {
+    return kBF16 ? bf16_bits_to_f32(b) : f16_bits_to_f32(b);
+}
+
+// fp32 -> 16-bit, round to nearest even.
+template <bool kBF16>
+__device__ __forceinline__ uint16_t f32_to_half_bits(float v) {
+    if constexpr (kBF16) {
+        return __builtin_bit_cast(uint16_t, (__bf16)v);
+    } else {
+        return __builtin_bit_cast(uint16_t, (_Float16)v);
+    }
+}
+
+// Two fp32 -> packed pair of 16-bit values (lo = a, hi = b), round to nearest even.
+template <bool kBF16>
+__device__ __forceinline__ uint32_t pack2_rne(float a, float b) {
+    if constexpr (kBF16) {
+        f32x2 v = {a, b};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+    } else {
+        f32x2 v = {a, b};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+    }
+}
+
+// D = A(16x32) * B(32x16) + C, fp32 accumulate. Operand layout for lane l:
+// A row l%16 / B column l%16, eight consecutive k starting at 8*(l/16);
+// C/D: rows 4*(l/16) + r (r = register 0..3), column l%16.
+template <bool kBF16>
+__device__ __forceinline__ f32x4 mfma16x16x32(uint4 a, uint4 b, f32x4 c) {
+    if constexpr (kBF16) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    } else {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    }
+}
+
+}  // namespace w4a16

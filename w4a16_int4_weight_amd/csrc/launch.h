@@ -1,0 +1,22 @@
+// Host-side launchers of the W4A16 kernels. Arguments are assumed validated by the
+// C ABI layer (api.hip): shapes supported by the tile layout, pointers aligned.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4a16 {
+
+// AWQ tensors -> packed tile layout. G: resolved group size (multiple of 128, divides K).
+hipError_t launch_repack(const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
+                         uint8_t* packed, int64_t K, int64_t N, int64_t G, hipStream_t stream);
+
+// Weight-streaming split-K GEMV for 1 <= M <= 16.
+hipError_t launch_gemv(const uint16_t* x, const uint8_t* packed, const uint16_t* bias, uint16_t* y,
+                       int64_t M, int64_t K, int64_t N, bool bf16, hipStream_t stream);
+
+// LDS-staged dequantise -> MFMA GEMM for any M >= 1.
+hipError_t launch_gemm(const uint16_t* x, const uint8_t* packed, const uint16_t* bias, uint16_t* y,
+                       int64_t M, int64_t K, int64_t N, bool bf16, hipStream_t stream);
+
+}  // namespace w4a16
