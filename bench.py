@@ -1,0 +1,249 @@
+"""Benchmark of the W4A16 hot path on one MI355X.
+
+Headline (the JSON `value`): decode GEMV M=1 over the gate_up layer shape, K=2048,
+N=13312, group size 128, bf16, in algorithmic GB/s. A step is one w4a16_gemm call
+(dispatch, split-K GEMV, in-kernel reduction and epilogue) on one activation
+batch; the weights were repacked once before timing. Secondary entries in the same
+JSON line measure the other rows of the path on their own workloads: the LM-head
+repack (GB/s), the MFMA GEMM at M=512 (TFLOP/s) and the GEMV on the other shapes.
+
+Timing: warm-up calls, then K calls captured in one HIP graph and replayed once
+between two events on the launch stream, with a device synchronisation on both
+sides. Each call reads a different copy of the packed weights, rotating through
+at least 512 MiB of copies, so the 256 MiB Infinity Cache cannot serve repeats:
+the bytes come from HBM.
+
+Algorithmic bytes of a GEMM (AWQ-sized): K*N/2 codes + (K/G)*N/2 zeros
++ (K/G)*N*2 scales + M*K*2 activations + M*N*2 outputs; flops 2*M*N*K.
+Repack bytes: each AWQ byte read once and written once, 2*(K*N/2 + (K/G)*N/2 + (K/G)*N*2).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--quick]
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "W4A16 GEMM GB/s (M=1) & TFLOP/s (M=512) vs roofline; repack GB/s"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+ROTATE_BYTES = 512 << 20
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def gemm_bytes(M, K, N, G):
+    KG = K // G
+    return K * N // 2 + KG * N // 2 + KG * N * 2 + M * K * 2 + M * N * 2
+
+
+def repack_bytes(K, N, G):
+    KG = K // G
+    return 2 * (K * N // 2 + KG * N // 2 + KG * N * 2)
+
+
+def to_dev_bits(bits, dtype, dev):
+    import numpy as np
+    import torch
+    td = {"bf16": torch.bfloat16, "fp16": torch.float16}[dtype]
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(td).to(dev)
+
+
+def time_graph(fn_list, warmup):
+    """Runs warm-up calls eagerly, captures the timed calls in a graph and replays it
+    once between events. Returns (elapsed_ms, launches)."""
+    import torch
+    for i in range(warmup):
+        fn_list[i % len(fn_list)]()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for fn in fn_list:
+            fn()
+    torch.cuda.synchronize()
+    g.replay()                       # one untimed replay: graph upload, first-use costs
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    g.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end), len(fn_list)
+
+
+def measure_gemm(w, workload, M, steps, warmup, dev, path="auto"):
+    import torch
+    import synth
+    ws = synth.make(workload, Ms=(M,))
+    K, N, G = ws.K, ws.N, ws.group_size
+    qw = torch.from_numpy(ws.qweight).to(dev)
+    qz = torch.from_numpy(ws.qzeros).to(dev)
+    sc = to_dev_bits(ws.scale_bits, ws.dtype, dev)
+    packed0 = w.w4a16_repack(qw, qz, sc, G)
+    del qw, qz, sc
+    pbytes = packed0.numel()
+    copies = max(1, min(64, math.ceil(ROTATE_BYTES / pbytes)))
+    packs = [packed0] + [packed0.clone() for _ in range(copies - 1)]
+    x = to_dev_bits(ws.x_bits[M], ws.dtype, dev)
+    y = torch.empty((M, N), dtype=x.dtype, device=dev)
+    calls = [(lambda p=packs[i % copies]: w.w4a16_gemm_ex(x, p, N, G, y=y, path=path)) for i in range(steps)]
+    ms, n = time_graph(calls, warmup)
+    per_launch_s = ms / 1e3 / n
+    nbytes = gemm_bytes(M, K, N, G)
+    flops = 2 * M * N * K
+    del packs, packed0
+    torch.cuda.empty_cache()
+    return dict(workload=workload, M=M, K=K, N=N, group_size=G, dtype=ws.dtype, path=path,
+                kernel="w4a16_gemv" if (path == "gemv" or (path == "auto" and M <= 8)) else "w4a16_gemm_mfma",
+                weight_copies=copies, launches=n, us_per_launch=per_launch_s * 1e6,
+                algorithmic_bytes=nbytes, flops=flops,
+                GBps=nbytes / per_launch_s / 1e9, TFLOPs=flops / per_launch_s / 1e12)
+
+
+def measure_repack(w, workload, steps, warmup, dev):
+    import torch
+    import synth
+    ws = synth.make(workload, Ms=())
+    K, N, G = ws.K, ws.N, ws.group_size
+    qw = torch.from_numpy(ws.qweight).to(dev)
+    qz = torch.from_numpy(ws.qzeros).to(dev)
+    sc = to_dev_bits(ws.scale_bits, ws.dtype, dev)
+    pbytes = w.w4a16_packed_bytes(K, N, G)
+    in_bytes = qw.numel() * 4 + qz.numel() * 4 + sc.numel() * 2
+    copies = max(1, min(16, math.ceil(ROTATE_BYTES / (in_bytes + pbytes))))
+    ins = [(qw, qz, sc)] + [(qw.clone(), qz.clone(), sc.clone()) for _ in range(copies - 1)]
+    outs = [torch.empty(pbytes, dtype=torch.uint8, device=dev) for _ in range(copies)]
+    calls = [(lambda a=ins[i % copies], o=outs[i % copies]: w.w4a16_repack(a[0], a[1], a[2], G, packed=o))
+             for i in range(steps)]
+    ms, n = time_graph(calls, warmup)
+    per_launch_s = ms / 1e3 / n
+    nbytes = repack_bytes(K, N, G)
+    del ins, outs
+    torch.cuda.empty_cache()
+    return dict(workload=workload + " repack", K=K, N=N, group_size=G, dtype=ws.dtype, kernel="w4a16_repack",
+                copies=copies, launches=n, us_per_launch=per_launch_s * 1e6, algorithmic_bytes=nbytes,
+                GBps=nbytes / per_launch_s / 1e9)
+
+
+def roofline_hbm(entry, traffic=None):
+    return {"bound": "hbm", "achieved": round(entry["GBps"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(entry["GBps"] / HBM_PEAK_GBS, 4), "traffic": traffic}
+
+
+def roofline_mfma(entry):
+    return {"bound": "mfma", "achieved": round(entry["TFLOPs"], 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(entry["TFLOPs"] / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
+
+
+def cpu_baseline(workload, M, budget_s=15.0):
+    """The oracle as it stands (unpack, float64 dequant, float64 matmul), BLAS held
+    to one thread, timed on whole steps of the same workload until ~budget_s."""
+    import numpy as np
+    import synth
+    from oracle import gemm as ogemm
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    ws = synth.make(workload, Ms=(M,))
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    if ctx:
+        ctx.__enter__()
+    try:
+        t0 = time.perf_counter()
+        n = 0
+        while True:
+            ogemm.w4a16_reference(ws.x_bits[M], ws.qweight, ws.qzeros, ws.scale_bits, ws.dtype, ws.group_size)
+            n += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        dt = (time.perf_counter() - t0) / n
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    nbytes = gemm_bytes(M, ws.K, ws.N, ws.group_size)
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} whole steps of {workload} M={M} ({dt:.2f} s each): AWQ unpack, float64 dequant, "
+                      f"float64 matmul, BLAS limited to 1 thread, elementwise NumPy single-threaded"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--quick", action="store_true", help="headline only, no secondary entries")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this library has no multi-GPU path, so --gpus {args.gpus} "
+              "is not supported (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import w4a16_int4_weight_amd as w
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    log(f"device {torch.cuda.get_device_name(0)}")
+
+    head = measure_gemm(w, "gate_up_decode", 1, args.steps, args.warmup, dev)
+    log(f"headline gate_up_decode M=1: {head['us_per_launch']:.2f} us, {head['GBps']:.0f} GB/s")
+    secondary = []
+    if not args.quick:
+        for wl, M in [("lm_head", 1), ("down_proj", 1), ("down_proj", 8), ("down_proj", 16),
+                      ("qkv_prefill", 512), ("gate_up_prefill", 512), ("lm_head", 512)]:
+            steps = args.steps if M <= 16 else max(20, args.steps // 4)
+            e = measure_gemm(w, wl, M, steps, min(args.warmup, 10), dev)
+            e["roofline"] = roofline_hbm(e) if M <= 16 else roofline_mfma(e)
+            log(f"{wl} M={M}: {e['us_per_launch']:.2f} us, {e['GBps']:.0f} GB/s, {e['TFLOPs']:.1f} TFLOP/s")
+            secondary.append(e)
+        r = measure_repack(w, "lm_head", max(10, args.steps // 10), 3, dev)
+        r["roofline"] = roofline_hbm(r)
+        log(f"lm_head repack: {r['us_per_launch']:.1f} us, {r['GBps']:.0f} GB/s")
+        secondary.append(r)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        cpu = cpu_baseline("gate_up_decode", 1)
+        log(f"cpu baseline: {cpu['value']} GB/s")
+
+    line = {
+        "metric": METRIC,
+        "value": round(head["GBps"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["us_per_launch"] / 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "gate_up_decode: W4A16 GEMV M=1 K=2048 N=13312 group_size=128 bf16",
+                   "M": 1, "K": 2048, "N": 13312, "group_size": 128,
+                   "weight_copies_rotated": head["weight_copies"], "timing": "HIP graph of K calls, events"},
+        "roofline": roofline_hbm(head),
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -44,7 +44,8 @@ extern "C" {
 typedef enum {
     W4A16_OK = 0,
     W4A16_ERR_NULL = 1,         /* a required pointer is NULL                       */
-    W4A16_ERR_SHAPE = 2,        /* M < 0, K or N <= 0, K % 128 != 0 or N % 16 != 0   */
+    W4A16_ERR_SHAPE = 2,        /* M < 0, K or N <= 0, K % 128 != 0, N % 16 != 0,
+                                   K > 2^20 or N > 2^28                               */
     W4A16_ERR_GROUP = 3,        /* group size not -1 and not a multiple of 128 dividing K */
     W4A16_ERR_DTYPE = 4,        /* dtype is neither W4A16_FP16 nor W4A16_BF16        */
     W4A16_ERR_ALIGN = 5,        /* a pointer is not aligned as documented            */
@@ -70,8 +71,9 @@ typedef enum {
 int w4a16_layout_version(void);
 
 /* Bytes of the packed buffer for a K x N weight with group size `group_size`:
- * K*N/2 (4-bit codes) + 4*(K/128)*N (one 32-bit scale/zero word per column per
- * 128-row block). Returns 0 if the shape or group size is not supported. */
+ * K*N/2 (4-bit codes) + 4*KBP*N (one 32-bit scale/zero word per column per
+ * 128-row block, KBP = K/128 rounded up to a multiple of 4).
+ * Returns 0 if the shape or group size is not supported. */
 size_t w4a16_packed_bytes(int64_t K, int64_t N, int64_t group_size);
 
 /* One-time repack of AWQ checkpoint tensors into the packed tile layout

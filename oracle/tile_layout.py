@@ -20,14 +20,17 @@ size G (G = K for group_size = -1; G a multiple of 128 dividing K):
     (bits 4s .. 4s+3) holds the code of row e = TILE_ORDER[s].
     TILE_ORDER = (0, 2, 4, 6, 1, 3, 5, 7): slots t and t+4 hold rows 2t and 2t+1.
 
-  Metadata plane, bytes [K*N/2, K*N/2 + 4*KB*N):
-    uint32 number (nb * KB + kb) * 16 + c describes column n = 16 nb + c over
-    row block kb, whose group is g = (128 kb) div G:
+  Metadata plane, bytes [K*N/2, K*N/2 + 4*N*KBP), KBP = KB rounded up to a
+  multiple of 4:
+    uint32 number n * KBP + kb describes column n over row block kb (so one
+    column's words for all row blocks are contiguous), whose group is
+    g = (128 kb) div G:
       bits 0..15  = the 16-bit pattern of S[g, n] (the scale, fp16 or bf16),
       bits 16..19 = Z[g, n] (the zero point, 0..15),
-      bits 20..31 = 0.
+      bits 20..31 = 0;
+    words kb = KB .. KBP-1 of every column are 0 (padding).
 
-  Total size: K*N/2 + 4*(K/128)*N bytes.
+  Total size: K*N/2 + 4*N*KBP bytes.
 
 Column blocks are independent (as the n-blocks of the CPU layout are in the
 vllm-omni commit "cpu_int4: repack weights in n-blocks, to bound the load-time
@@ -41,7 +44,7 @@ TILE_ORDER = (0, 2, 4, 6, 1, 3, 5, 7)
 ROWS_PER_BLOCK = 128
 COLS_PER_BLOCK = 16
 BLOCK_BYTES = 1024
-LAYOUT_VERSION = 1
+LAYOUT_VERSION = 2
 
 
 def check_shape(K, N, group_size):
@@ -58,9 +61,14 @@ def check_shape(K, N, group_size):
     return G
 
 
+def padded_row_blocks(K):
+    KB = K // ROWS_PER_BLOCK
+    return (KB + 3) // 4 * 4
+
+
 def packed_bytes(K, N, group_size):
     check_shape(K, N, group_size)
-    return K * N // 2 + 4 * (K // ROWS_PER_BLOCK) * N
+    return K * N // 2 + 4 * N * padded_row_blocks(K)
 
 
 def repack(Q, Z, scale_bits, group_size):
@@ -88,7 +96,8 @@ def repack(Q, Z, scale_bits, group_size):
     group_of_block = (np.arange(KB) * ROWS_PER_BLOCK) // G             # [kb]
     s_blk = scale_bits[group_of_block].astype(np.uint32)               # [kb, N]
     z_blk = Z[group_of_block].astype(np.uint32)                        # [kb, N]
-    meta = (s_blk | (z_blk << np.uint32(16))).reshape(KB, NB, 16).transpose(1, 0, 2)
+    meta = np.zeros((N, padded_row_blocks(K)), dtype=np.uint32)        # [n, kb], padding 0
+    meta[:, :KB] = (s_blk | (z_blk << np.uint32(16))).T
 
     out = np.concatenate([
         np.ascontiguousarray(weight_plane).astype("<u4").view(np.uint8).reshape(-1),
@@ -120,14 +129,13 @@ def repack_loops(Q, Z, scale_bits, group_size):
                     off = base + 16 * lane + 4 * i
                     out[off:off + 4] = word.to_bytes(4, "little")
     meta_base = K * N // 2
-    for nb in range(NB):
-        for kb in range(KB):
+    KBP = padded_row_blocks(K)
+    for n in range(N):
+        for kb in range(KB):           # words kb >= KB stay 0
             g = (128 * kb) // G
-            for c in range(16):
-                n = 16 * nb + c
-                word = int(scale_bits[g, n]) | (int(Z[g, n]) << 16)
-                off = meta_base + 4 * ((nb * KB + kb) * 16 + c)
-                out[off:off + 4] = word.to_bytes(4, "little")
+            word = int(scale_bits[g, n]) | (int(Z[g, n]) << 16)
+            off = meta_base + 4 * (n * KBP + kb)
+            out[off:off + 4] = word.to_bytes(4, "little")
     return np.frombuffer(bytes(out), dtype=np.uint8)
 
 
@@ -148,7 +156,10 @@ def decode(packed, K, N, group_size):
         q[:, :, :, TILE_ORDER[s], :, :] = codes.transpose(1, 4, 2, 0, 3)
     Q = q.reshape(K, N)
 
-    meta = packed[wbytes:].view("<u4").reshape(NB, KB, 16).transpose(1, 0, 2).reshape(KB, N)
+    meta_all = packed[wbytes:].view("<u4").reshape(N, padded_row_blocks(K))
+    if np.any(meta_all[:, KB:]):
+        raise ValueError("metadata padding is not zero")
+    meta = meta_all[:, :KB].T                                          # [kb, n]
     if np.any(meta >> np.uint32(20)):
         raise ValueError("reserved metadata bits are not zero")
     blocks_per_group = G // ROWS_PER_BLOCK

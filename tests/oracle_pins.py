@@ -262,14 +262,16 @@ def pin_layout_index_patterns(tile_layout, K=256, N=48, G=128):
     return True
 
 
-def pin_layout_metadata(tile_layout, K=512, N=32, G=256):
-    """scale bits = column index, zero = group mod 16: metadata word of (nb, kb, c)
-    must be (16 nb + c) | ((128 kb div G) mod 16) << 16, stored nb-major."""
-    KG, KB, NB = K // G, K // 128, N // 16
+def pin_layout_metadata(tile_layout, K=768, N=32, G=256):
+    """scale bits = column index, zero = group mod 16: metadata word of (n, kb)
+    must be n | ((128 kb div G) mod 16) << 16 at position n * KBP + kb, with the
+    padding words of each column zero (K = 768: 6 row blocks, padded to 8)."""
+    KG, KB = K // G, K // 128
+    KBP = (KB + 3) // 4 * 4
     sbits = np.tile(np.arange(N, dtype=np.uint16), (KG, 1))
     Z = np.repeat((np.arange(KG) % 16).astype(np.uint8)[:, None], N, axis=1)
     out = tile_layout.repack(np.zeros((K, N), np.uint8), Z, sbits, G)
     meta = out[K * N // 2:].view("<u4")
-    expect = [(16 * nb + c) | ((((128 * kb) // G) % 16) << 16)
-              for nb in range(NB) for kb in range(KB) for c in range(16)]
+    expect = [(n | ((((128 * kb) // G) % 16) << 16)) if kb < KB else 0
+              for n in range(N) for kb in range(KBP)]
     return meta.tolist() == expect

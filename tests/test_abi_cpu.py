@@ -82,6 +82,8 @@ def test_gemm_validation_before_any_device_call(w):
     assert gemm(w, K=500) == 2
     assert gemm(w, N=24) == 2
     assert gemm(w, K=0) == 2
+    assert gemm(w, K=(1 << 20) + 128) == 2
+    assert gemm(w, N=(1 << 28) + 16) == 2
     assert gemm(w, G=64) == 3
     assert gemm(w, G=384) == 3
     assert gemm(w, dtype=2) == 4
@@ -118,3 +120,19 @@ def test_repack_validation_before_any_device_call(w):
     assert repack(packed=P(1032)) == 5
     assert repack(pbytes=1000) == 6
     assert repack() == 7
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    import w4a16_int4_weight_amd as mod
+    monkeypatch.setattr(mod, "LIB_PATH", "/nonexistent/libw4a16.so")
+    monkeypatch.setattr(mod, "_lib", None)
+    with pytest.raises(ImportError):
+        mod.w4a16_packed_bytes(512, 512, 128)
+    with pytest.raises(ImportError):
+        mod.lib
+
+
+def test_build_module_and_binding_agree_on_library_path():
+    import w4a16_int4_weight_amd as mod
+    from w4a16_int4_weight_amd import build
+    assert mod.LIB_PATH == build.LIB_PATH

@@ -190,6 +190,8 @@ def test_layout_column_chunks_are_independent():
 
 def test_layout_sizes_and_rejections():
     assert tile_layout.packed_bytes(2048, 13312, 128) == 2048 * 13312 // 2 + 4 * 16 * 13312
+    assert tile_layout.packed_bytes(6656, 2048, 128) == 6656 * 2048 // 2 + 4 * 52 * 2048
+    assert tile_layout.packed_bytes(384, 16, 128) == 384 * 16 // 2 + 4 * 4 * 16      # 3 row blocks padded to 4
     for K, N, G in [(100, 16, 128), (256, 24, 128), (256, 16, 64), (384, 16, 256)]:
         with pytest.raises(ValueError):
             tile_layout.packed_bytes(K, N, G)
@@ -200,6 +202,11 @@ def test_layout_decode_rejects_reserved_bits():
     buf = tile_layout.repack(np.zeros((K, N), np.uint8), np.zeros((1, N), np.uint8),
                              np.zeros((1, N), np.uint16), G).copy()
     buf[K * N // 2 + 3] = 0x10
+    with pytest.raises(ValueError):
+        tile_layout.decode(buf, K, N, G)
+    buf = tile_layout.repack(np.zeros((K, N), np.uint8), np.zeros((1, N), np.uint8),
+                             np.zeros((1, N), np.uint16), G).copy()
+    buf[K * N // 2 + 4] = 1            # padding word kb = 1 of column 0 (KB = 1, KBP = 4)
     with pytest.raises(ValueError):
         tile_layout.decode(buf, K, N, G)
 
@@ -275,8 +282,10 @@ LAYOUT_MUTANTS = [
     ("blocks kb-major", "words = np.zeros((NB, KB, 4, 16, 4), dtype=np.uint32)   # [nb, kb, h, c, i]",
      "words = np.zeros((KB, NB, 4, 16, 4), dtype=np.uint32)"),
     ("metadata zero in bits 12..15", "(z_blk << np.uint32(16))", "(z_blk << np.uint32(12))"),
-    ("metadata kb-major", "meta = (s_blk | (z_blk << np.uint32(16))).reshape(KB, NB, 16).transpose(1, 0, 2)",
-     "meta = (s_blk | (z_blk << np.uint32(16))).reshape(KB, NB, 16)"),
+    ("metadata row-block-major", "meta[:, :KB] = (s_blk | (z_blk << np.uint32(16))).T",
+     "meta[:, :KB] = (s_blk | (z_blk << np.uint32(16))).reshape(N, KB)"),
+    ("metadata unpadded", "meta = np.zeros((N, padded_row_blocks(K)), dtype=np.uint32)",
+     "meta = np.zeros((N, KB), dtype=np.uint32)"),
 ]
 
 

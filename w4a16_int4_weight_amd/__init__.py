@@ -11,8 +11,9 @@ Functions keep the C names:
   w4a16_gemm_ex(..., path="auto"|"gemv"|"mfma", gemv_max_m=-1)            -> y
   w4a16_status_str(code)                         -> str
 
-There is no fallback: if the library is missing the import fails, and a call
-whose tensors are not on a gfx950 GPU returns the library's error, raised here.
+There is no fallback: if the library is missing, the first call (or access to
+`lib`) raises ImportError; a call whose tensors are not on a gfx950 GPU returns the
+library's error, raised here as W4A16Error.
 """
 
 import ctypes
@@ -20,7 +21,7 @@ import os
 
 import torch
 
-from .build import LIB_PATH
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4a16.so")   # built by build.py
 
 __all__ = [
     "W4A16Error", "lib", "w4a16_layout_version", "w4a16_packed_bytes", "w4a16_workspace_bytes",
@@ -43,43 +44,59 @@ class W4A16Error(RuntimeError):
         super().__init__(f"{what}: {self.status} ({w4a16_status_str(code)})")
 
 
-if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built; run `python -m w4a16_int4_weight_amd.build` "
-                      "(the W4A16 path has no fallback)")
+_lib = None
 
-lib = ctypes.CDLL(LIB_PATH)
 
-_vp, _i64, _sz, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
-lib.w4a16_layout_version.argtypes = []
-lib.w4a16_layout_version.restype = _int
-lib.w4a16_packed_bytes.argtypes = [_i64, _i64, _i64]
-lib.w4a16_packed_bytes.restype = _sz
-lib.w4a16_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64]
-lib.w4a16_workspace_bytes.restype = _sz
-lib.w4a16_repack.argtypes = [_vp, _vp, _vp, _int, _i64, _i64, _i64, _vp, _sz, _vp]
-lib.w4a16_repack.restype = _int
-lib.w4a16_gemm.argtypes = [_vp, _vp, _sz, _int, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _sz, _vp]
-lib.w4a16_gemm.restype = _int
-lib.w4a16_gemm_ex.argtypes = lib.w4a16_gemm.argtypes + [_int, _i64]
-lib.w4a16_gemm_ex.restype = _int
-lib.w4a16_status_str.argtypes = [_int]
-lib.w4a16_status_str.restype = ctypes.c_char_p
+def _load():
+    """Loads libw4a16.so on first use. There is no fallback: a missing library is an
+    error the caller sees, never a silent switch to another implementation."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m w4a16_int4_weight_amd.build` "
+                          "(the W4A16 path has no fallback)")
+    h = ctypes.CDLL(LIB_PATH)
+    _vp, _i64, _sz, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+    h.w4a16_layout_version.argtypes = []
+    h.w4a16_layout_version.restype = _int
+    h.w4a16_packed_bytes.argtypes = [_i64, _i64, _i64]
+    h.w4a16_packed_bytes.restype = _sz
+    h.w4a16_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64]
+    h.w4a16_workspace_bytes.restype = _sz
+    h.w4a16_repack.argtypes = [_vp, _vp, _vp, _int, _i64, _i64, _i64, _vp, _sz, _vp]
+    h.w4a16_repack.restype = _int
+    h.w4a16_gemm.argtypes = [_vp, _vp, _sz, _int, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _sz, _vp]
+    h.w4a16_gemm.restype = _int
+    h.w4a16_gemm_ex.argtypes = h.w4a16_gemm.argtypes + [_int, _i64]
+    h.w4a16_gemm_ex.restype = _int
+    h.w4a16_status_str.argtypes = [_int]
+    h.w4a16_status_str.restype = ctypes.c_char_p
+    _lib = h
+    return h
+
+
+def __getattr__(name):
+    # `lib` is the loaded library handle, loaded on first access
+    if name == "lib":
+        return _load()
+    raise AttributeError(name)
 
 
 def w4a16_status_str(code):
-    return lib.w4a16_status_str(int(code)).decode()
+    return _load().w4a16_status_str(int(code)).decode()
 
 
 def w4a16_layout_version():
-    return lib.w4a16_layout_version()
+    return _load().w4a16_layout_version()
 
 
 def w4a16_packed_bytes(K, N, group_size):
-    return lib.w4a16_packed_bytes(K, N, group_size)
+    return _load().w4a16_packed_bytes(K, N, group_size)
 
 
 def w4a16_workspace_bytes(M, K, N, group_size):
-    return lib.w4a16_workspace_bytes(M, K, N, group_size)
+    return _load().w4a16_workspace_bytes(M, K, N, group_size)
 
 
 def _ptr(t):
@@ -118,7 +135,7 @@ def w4a16_repack(qweight, qzeros, scales, group_size=128, packed=None, stream=No
     G = K if group_size == -1 else group_size
     if G > 0 and K % G == 0 and (tuple(qzeros.shape) != (K // G, N // 8) or tuple(scales.shape) != (K // G, N)):
         raise ValueError("qzeros must be [K/G, N/8] and scales [K/G, N]")
-    code = lib.w4a16_repack(_ptr(qweight), _ptr(qzeros), _ptr(scales), _dtype_code(scales.dtype),
+    code = _load().w4a16_repack(_ptr(qweight), _ptr(qzeros), _ptr(scales), _dtype_code(scales.dtype),
                             K, N, group_size, _ptr(packed), packed.numel() * packed.element_size(),
                             _stream(stream, qweight.device))
     _check(code, "w4a16_repack")
@@ -144,7 +161,7 @@ def _gemm_args(x, packed, N, group_size, bias, y, workspace, stream):
 def w4a16_gemm(x, packed, N, group_size=128, bias=None, y=None, workspace=None, stream=None):
     """x [M, K] (fp16/bf16) times the packed weight (+ bias) -> y [M, N] of x's dtype."""
     args, y = _gemm_args(x, packed, N, group_size, bias, y, workspace, stream)
-    _check(lib.w4a16_gemm(*args), "w4a16_gemm")
+    _check(_load().w4a16_gemm(*args), "w4a16_gemm")
     return y
 
 
@@ -154,5 +171,5 @@ def w4a16_gemm_ex(x, packed, N, group_size=128, bias=None, y=None, workspace=Non
     if path not in PATHS:
         raise W4A16Error(9, f"path {path!r}")
     args, y = _gemm_args(x, packed, N, group_size, bias, y, workspace, stream)
-    _check(lib.w4a16_gemm_ex(*args, PATHS[path], gemv_max_m), "w4a16_gemm_ex")
+    _check(_load().w4a16_gemm_ex(*args, PATHS[path], gemv_max_m), "w4a16_gemm_ex")
     return y

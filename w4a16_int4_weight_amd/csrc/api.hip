@@ -11,24 +11,29 @@
 
 namespace {
 
-constexpr int kLayoutVersion = 1;
+constexpr int kLayoutVersion = 2;
 constexpr int64_t kGemvMaxRows = 16;      // rows one GEMV A operand holds
 constexpr int64_t kDefaultGemvMaxM = 8;
 constexpr int kMaxDevices = 64;
+constexpr int64_t kMaxK = int64_t(1) << 20;   // kernels index rows and columns with 32-bit integers
+constexpr int64_t kMaxN = int64_t(1) << 28;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 // Resolved group size, or 0 if (K, N, group_size) is outside the tile layout.
 w4a16_status check_shape(int64_t K, int64_t N, int64_t group_size, int64_t* G_out) {
     if (K <= 0 || N <= 0 || K % 128 != 0 || N % 16 != 0) return W4A16_ERR_SHAPE;
-    if (K > (int64_t(1) << 40) || N > (int64_t(1) << 40) || (K / 2) > INT64_MAX / N) return W4A16_ERR_SHAPE;
+    if (K > kMaxK || N > kMaxN) return W4A16_ERR_SHAPE;
     const int64_t G = group_size == -1 ? K : group_size;
     if (G <= 0 || G % 128 != 0 || K % G != 0) return W4A16_ERR_GROUP;
     *G_out = G;
     return W4A16_OK;
 }
 
-size_t packed_size(int64_t K, int64_t N) { return (size_t)(K * N / 2) + (size_t)4 * (size_t)(K / 128) * (size_t)N; }
+size_t packed_size(int64_t K, int64_t N) {
+    const size_t kbp = (size_t)((K / 128 + 3) / 4 * 4);
+    return (size_t)(K * N / 2) + (size_t)4 * kbp * (size_t)N;
+}
 
 // 0 = unknown, 1 = gfx950, 2 = other; cached per device ordinal.
 std::atomic<int> g_device_kind[kMaxDevices];

@@ -13,15 +13,18 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// Packed tile layout, version 1 (K x N weight, 128-row blocks, 16-column blocks):
+// Packed tile layout, version 2 (K x N weight, 128-row blocks, 16-column blocks):
 //   weight plane: block (nb, kb) = 1024 bytes at 1024 * (nb * KB + kb); lane L owns
 //   16 bytes = 4 words; word i of lane L holds column 16 nb + (L % 16), rows
-//   128 kb + 32 i + 8 (L / 16) + e, e = 0..7; nibble slot s holds row e = kTileOrder(s).
-//   metadata plane (after K*N/2 bytes): word (nb * KB + kb) * 16 + c =
-//   scale bits | zero << 16 for column 16 nb + c over row block kb.
+//   128 kb + 32 i + 8 (L / 16) + e, e = 0..7; nibble slot s holds row e = tile_row_of_slot(s).
+//   metadata plane (after K*N/2 bytes): word n * KBP + kb = scale bits | zero << 16
+//   for column n over row block kb; KBP = KB rounded up to a multiple of 4, the
+//   padding words are 0. One 16-byte load gives a column's words for 4 row blocks.
 constexpr int kRowsPerBlock = 128;
 constexpr int kColsPerBlock = 16;
 constexpr int kBlockBytes = 1024;
+
+__host__ __device__ constexpr int64_t padded_row_blocks(int64_t K) { return ((K / kRowsPerBlock) + 3) / 4 * 4; }
 
 // Row e held by nibble slot s of a tile word: 0,2,4,6,1,3,5,7. Slots t and t+4
 // hold rows 2t and 2t+1, so (word >> 4t) & 0x000F000F puts the pair (2t, 2t+1)

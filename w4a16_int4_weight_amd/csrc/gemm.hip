@@ -92,6 +92,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM][kLdsRowElems];
 
     const int64_t KB = K / kRowsPerBlock;
+    const int64_t KBP = padded_row_blocks(K);
     const int64_t NB = N / kColsPerBlock;
     const int tid = threadIdx.x;
     const int w = tid >> 6;
@@ -136,7 +137,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
         for (int j = 0; j < kColBlocksPerWave; ++j) {
             const int64_t blk = (nbw + j) * KB + kb;
             wq[j] = cb_valid[j] ? wplane[blk * 64 + lane] : make_uint4(0, 0, 0, 0);
-            md[j] = cb_valid[j] ? meta[blk * kColsPerBlock + c] : 0u;
+            md[j] = cb_valid[j] ? meta[((nbw + j) * kColsPerBlock + c) * KBP + kb] : 0u;
         }
     };
 

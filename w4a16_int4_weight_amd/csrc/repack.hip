@@ -73,17 +73,19 @@ __global__ __launch_bounds__(kRepackThreads) void repack_kernel(
         *dst = make_uint4(out[0], out[1], out[2], out[3]);
     }
 
-    // 3. Metadata of the tile's blocks: one word per column.
+    // 3. Metadata word of row block kb for each column of the tile; the workgroup
+    //    of the last row block also writes the zero padding words.
     const int64_t g = (kb * kRowsPerBlock) / G;
+    const int64_t KBP = padded_row_blocks(K);
     uint32_t* meta = reinterpret_cast<uint32_t*>(packed + K * N / 2);
     for (int t = tid; t < nbt * kColsPerBlock; t += kRepackThreads) {
-        const int j = t >> 4;
-        const int c = t & 15;
-        const int64_t n = (nb0 + j) * kColsPerBlock + c;
+        const int64_t n = nb0 * kColsPerBlock + t;
         const uint32_t zword = qzeros[g * words_per_row + (n >> 3)];
         const uint32_t z = (zword >> (4 * awq_slot_of_column((int)(n & 7)))) & 0xFu;
         const uint32_t sbits = scales[g * N + n];
-        meta[((nb0 + j) * KB + kb) * kColsPerBlock + c] = sbits | (z << 16);
+        meta[n * KBP + kb] = sbits | (z << 16);
+        if (kb == KB - 1)
+            for (int64_t p = KB; p < KBP; ++p) meta[n * KBP + p] = 0u;
     }
 }
 
