@@ -45,7 +45,7 @@ typedef enum {
     W4A16_OK = 0,
     W4A16_ERR_NULL = 1,         /* a required pointer is NULL                       */
     W4A16_ERR_SHAPE = 2,        /* M < 0, K or N <= 0, K % 128 != 0, N % 16 != 0,
-                                   K > 2^20 or N > 2^28                               */
+                                   K > 2^20, N > 2^28, K*N > 2^37 or M*K > 2^32       */
     W4A16_ERR_GROUP = 3,        /* group size not -1 and not a multiple of 128 dividing K */
     W4A16_ERR_DTYPE = 4,        /* dtype is neither W4A16_FP16 nor W4A16_BF16        */
     W4A16_ERR_ALIGN = 5,        /* a pointer is not aligned as documented            */

@@ -84,6 +84,8 @@ def test_gemm_validation_before_any_device_call(w):
     assert gemm(w, K=0) == 2
     assert gemm(w, K=(1 << 20) + 128) == 2
     assert gemm(w, N=(1 << 28) + 16) == 2
+    assert gemm(w, K=1 << 20, N=1 << 18) == 2
+    assert gemm(w, M=1 << 13, K=1 << 20) == 2
     assert gemm(w, G=64) == 3
     assert gemm(w, G=384) == 3
     assert gemm(w, dtype=2) == 4

@@ -17,13 +17,15 @@ constexpr int64_t kDefaultGemvMaxM = 8;
 constexpr int kMaxDevices = 64;
 constexpr int64_t kMaxK = int64_t(1) << 20;   // kernels index rows and columns with 32-bit integers
 constexpr int64_t kMaxN = int64_t(1) << 28;
+constexpr int64_t kMaxKN = int64_t(1) << 37;  // packed codes index in 32-bit 16-byte units
+constexpr int64_t kMaxMK = int64_t(1) << 32;  // activations index in 32-bit elements
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 // Resolved group size, or 0 if (K, N, group_size) is outside the tile layout.
 w4a16_status check_shape(int64_t K, int64_t N, int64_t group_size, int64_t* G_out) {
     if (K <= 0 || N <= 0 || K % 128 != 0 || N % 16 != 0) return W4A16_ERR_SHAPE;
-    if (K > kMaxK || N > kMaxN) return W4A16_ERR_SHAPE;
+    if (K > kMaxK || N > kMaxN || K * N > kMaxKN) return W4A16_ERR_SHAPE;
     const int64_t G = group_size == -1 ? K : group_size;
     if (G <= 0 || G % 128 != 0 || K % G != 0) return W4A16_ERR_GROUP;
     *G_out = G;
@@ -66,6 +68,7 @@ w4a16_status gemm_impl(const void* x, const void* packed, size_t packed_bytes, w
     if (gemv_max_m < 0) gemv_max_m = kDefaultGemvMaxM;
     if (gemv_max_m > kGemvMaxRows) return W4A16_ERR_PATH;
     if (path == W4A16_PATH_GEMV && M > kGemvMaxRows) return W4A16_ERR_PATH;
+    if (M >= (int64_t(1) << 31) || M * K > kMaxMK) return W4A16_ERR_SHAPE;
     if (M == 0) return W4A16_OK;
     if (!x || !packed || !y) return W4A16_ERR_NULL;
     if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(y, 16) || (bias && !aligned(bias, 2)))

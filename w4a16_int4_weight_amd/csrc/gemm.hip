@@ -11,13 +11,22 @@
 //
 // Workgroup: 4 waves side by side along N, each owning 4 column blocks (64
 // columns) and all 16*MR rows of the tile. Per 128-row block of K:
-//   * the activation tile [16*MR x 128] is staged in LDS (double buffered, the next
-//     block's tile loaded into registers while the current one is consumed);
-//   * each wave loads its own 4 x 16 bytes of packed codes and 4 metadata words
-//     per lane (also one block ahead), and per 32-row step decodes one word per
-//     column block into 8 fp16/bf16 weights (q - z) * s rounded once to the dtype;
-//   * MR x 4 MFMAs (16x16x32) per step, fp32 accumulators in registers.
+//   * the activation tile [16*MR x 128] is staged in LDS, double buffered: the next
+//     block's tile is loaded into registers while the current one is consumed;
+//   * each wave keeps three register sets of packed codes and metadata in rotation,
+//     so the codes of block kb+2 are in flight while block kb is computed;
+//   * per 32-row step a wave decodes one word per column block into 8 fp16/bf16
+//     weights (q - z) * s, each rounded once to the dtype, and issues MR x 4 MFMAs
+//     (16x16x32, fp32 accumulators);
+//   * the MFMA is given the weights as its first operand and the activations as its
+//     second, so it produces the transposed tile: each lane then holds 4 adjacent
+//     output columns of one row and the epilogue writes 8 bytes per lane.
+// Workgroups are numbered so that the M tiles of one N tile land on the same XCD
+// (the hardware deals workgroup ids round-robin over the 8 XCDs), where they share
+// the packed codes through that XCD's L2.
 // Epilogue: bias in fp32, one rounding to the dtype.
+#include <stddef.h>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -28,14 +37,14 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kColBlocksPerWave = 4;
 constexpr int kColBlocksPerWG = kWaves * kColBlocksPerWave;   // 16 -> 256 columns
-constexpr int kLdsRowElems = kRowsPerBlock + 8;               // 272-byte rows: spreads LDS banks
+constexpr int kXcds = 8;
 
-// Decode one tile word (8 codes of one column, rows 8 apart in k order given by the
-// slot order) into the B operand of a 16x16x32 MFMA: 8 values (q - z) * s.
+// Decode one tile word (8 codes of one column, rows in slot order) into the operand
+// of a 16x16x32 MFMA: 8 values (q - z) * s.
 template <bool kBF16> struct Dequant;
 
 template <> struct Dequant<true> {
-    // bf16: codes -> fp32 via the byte converters, (q - z) * s = fma(q, s, -z*s) is
+    // bf16: codes -> fp32 with the byte converters, (q - z) * s = fma(q, s, -z*s) is
     // exact in fp32 (a 4-bit integer times an 8-bit significand), then one RNE
     // conversion per pair. Byte b of (d & 0x0F0F0F0F) is slot 2b and byte b of
     // (d >> 4) & 0x0F0F0F0F is slot 2b+1; slot -> row: 0,2,4,6,1,3,5,7.
@@ -45,8 +54,11 @@ template <> struct Dequant<true> {
         nzs = -(float)((md >> 16) & 0xFu) * s;
     }
     __device__ __forceinline__ uint4 operator()(uint32_t d) const {
-        const uint32_t lo = d & 0x0F0F0F0Fu;          // rows 0, 4, 1, 5 in bytes 0..3
-        const uint32_t hi = (d >> 4) & 0x0F0F0F0Fu;   // rows 2, 6, 3, 7 in bytes 0..3
+        uint32_t lo = d & 0x0F0F0F0Fu;          // rows 0, 4, 1, 5 in bytes 0..3
+        uint32_t hi = (d >> 4) & 0x0F0F0F0Fu;   // rows 2, 6, 3, 7 in bytes 0..3
+        // hide the masks from the optimiser so each byte converts with one
+        // v_cvt_f32_ubyteN instead of an extract and a convert
+        asm volatile("" : "+v"(lo), "+v"(hi));
         const float r0 = fmaf((float)(lo & 0xFFu), s, nzs);
         const float r4 = fmaf((float)((lo >> 8) & 0xFFu), s, nzs);
         const float r1 = fmaf((float)((lo >> 16) & 0xFFu), s, nzs);
@@ -82,63 +94,112 @@ template <> struct Dequant<false> {
     }
 };
 
+__device__ __forceinline__ uint32_t pick(const uint4 v, int i) {
+    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// Direct global -> LDS copies (global_load_lds): each lane's 4 or 16 bytes land at
+// M0 + 4*lane or M0 + 16*lane, M0 being uniform over the wave. They count in vmcnt
+// like loads but occupy no registers, so several k blocks can be in flight. They are
+// issued through inline assembly so that the compiler does not guard every later LDS
+// read with a wait for all of them: the kernel waits for exactly the copies it needs.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" : : "v"(g), "s"(lds) : "memory", "m0");
+}
+
+// Workgroup barrier that is also a compiler barrier for memory operations, without
+// the vmcnt(0) a full __syncthreads() fence would add.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" : : : "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" : : : "memory");
+}
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt low bits [3:0], high
+// bits [15:14], expcnt [6:4] = 7, lgkmcnt [11:8] = 15).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// One stage of the LDS ring: the activation tile of one 128-row block of K, the
+// workgroup's 16 blocks of packed codes and its 256 metadata words.
+template <int BM>
+struct Stage {
+    // [BM rows][16 chunks of 16 bytes], chunk j of row r stored at chunk j ^ (r % 16)
+    uint4 x[BM * 16];
+    uint4 w[kColBlocksPerWG * 64];          // 16 blocks x 1 KiB, as in global memory
+    uint32_t meta[kColBlocksPerWG * kColsPerBlock];
+};
+
 template <bool kBF16, int MR>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed, const uint16_t* __restrict__ bias,
-    uint16_t* __restrict__ y, int64_t M, int64_t K, int64_t N) {
+    uint16_t* __restrict__ y, int M, int K, int N, int tiles_m, int tiles_n) {
     constexpr int BM = 16 * MR;
-    constexpr int kChunks = BM * (kRowsPerBlock / 8) / kThreads;   // 16-byte x-tile chunks per thread
-    static_assert(kChunks * kThreads == BM * (kRowsPerBlock / 8), "x tile must split evenly");
-    __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM][kLdsRowElems];
+    constexpr int kSlabsPerWave = BM / 4 / kWaves;      // 1 KiB slabs (4 rows) of the x tile per wave
+    static_assert(kSlabsPerWave * 4 * kWaves == BM, "x tile must split over the waves");
+    constexpr int kDmaPerStage = kSlabsPerWave + kColBlocksPerWave + 1;   // copies per wave per stage
+    constexpr int kStages = 3;
+    __shared__ Stage<BM> ring[kStages];
 
-    const int64_t KB = K / kRowsPerBlock;
-    const int64_t KBP = padded_row_blocks(K);
-    const int64_t NB = N / kColsPerBlock;
+    const int id = blockIdx.x;
+    const int local = id / kXcds;
+    const int m_tile = local % tiles_m;
+    const int n_tile = (local / tiles_m) * kXcds + id % kXcds;
+    if (n_tile >= tiles_n) return;
+
+    const int KB = K / kRowsPerBlock;
+    const int KBP = (int)padded_row_blocks(K);
+    const int NB = N / kColsPerBlock;
     const int tid = threadIdx.x;
-    const int w = tid >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);    // wave index, uniform
     const int lane = tid & 63;
     const int c = lane & 15;
     const int h = lane >> 4;
-    const int64_t m0 = (int64_t)blockIdx.y * BM;
-    const int64_t nbw = (int64_t)blockIdx.x * kColBlocksPerWG + w * kColBlocksPerWave;
+    const int m0 = m_tile * BM;
+    const int nbw = n_tile * kColBlocksPerWG + w * kColBlocksPerWave;   // first column block of this wave
 
-    const uint4* wplane = reinterpret_cast<const uint4*>(packed);
-    const uint32_t* meta = reinterpret_cast<const uint32_t*>(packed + K * N / 2);
-    bool cb_valid[kColBlocksPerWave];
+    // ---- per-lane sources of one stage's copies (k block kb adds kb * stride) ----
+    // x: slab `slab` covers tile rows 4 slab .. 4 slab + 3; lane (row 4 slab + lane/16,
+    // stored chunk lane%16) fetches logical chunk (lane%16) ^ (row%16). Rows past M
+    // read row M-1: they only feed output rows that are not written.
+    const uint16_t* xsrc[kSlabsPerWave];
 #pragma unroll
-    for (int j = 0; j < kColBlocksPerWave; ++j) cb_valid[j] = (nbw + j) < NB;
+    for (int t = 0; t < kSlabsPerWave; ++t) {
+        const int row = 4 * (w * kSlabsPerWave + t) + (lane >> 4);
+        const int m = m0 + row < M ? m0 + row : M - 1;
+        xsrc[t] = x + (size_t)m * K + 8 * ((lane & 15) ^ (row & 15));
+    }
+    const uint4* wsrc[kColBlocksPerWave];
+#pragma unroll
+    for (int j = 0; j < kColBlocksPerWave; ++j) {
+        const int nbj = nbw + j < NB ? nbw + j : NB - 1;
+        wsrc[j] = reinterpret_cast<const uint4*>(packed) + (size_t)nbj * KB * 64 + lane;
+    }
+    const int ncol = nbw * kColsPerBlock + lane;            // this wave's 64 columns
+    const uint32_t* msrc = reinterpret_cast<const uint32_t*>(packed + (size_t)K * N / 2) +
+                           (size_t)(ncol < N ? ncol : N - 1) * KBP;
+    const uint32_t ring_base = lds_addr(&ring[0]);
 
-    // x tile chunk q (0 .. BM*16-1): row q / 16, 16-byte column q % 16.
-    auto load_x = [&](int64_t kb, uint4 (&regs)[kChunks]) {
+    auto issue = [&](int slot, int kb) {
+        const uint32_t st = ring_base + (uint32_t)slot * (uint32_t)sizeof(Stage<BM>);
 #pragma unroll
-        for (int p = 0; p < kChunks; ++p) {
-            const int q = tid + p * kThreads;
-            const int row = q >> 4;
-            const int col = q & 15;
-            const int64_t m = m0 + row;
-            regs[p] = (q < BM * 16 && m < M)
-                          ? *reinterpret_cast<const uint4*>(x + m * K + kb * kRowsPerBlock + 8 * col)
-                          : make_uint4(0, 0, 0, 0);
-        }
-    };
-    auto store_x = [&](int buf, const uint4 (&regs)[kChunks]) {
+        for (int t = 0; t < kSlabsPerWave; ++t)
+            dma16(xsrc[t] + (size_t)kb * kRowsPerBlock,
+                  st + (uint32_t)offsetof(Stage<BM>, x) + (uint32_t)(w * kSlabsPerWave + t) * 1024u);
 #pragma unroll
-        for (int p = 0; p < kChunks; ++p) {
-            const int q = tid + p * kThreads;
-            if (q < BM * 16) {
-                const int row = q >> 4;
-                const int col = q & 15;
-                *reinterpret_cast<uint4*>(&xs[buf][row][8 * col]) = regs[p];
-            }
-        }
-    };
-    auto load_w = [&](int64_t kb, uint4 (&wq)[kColBlocksPerWave], uint32_t (&md)[kColBlocksPerWave]) {
-#pragma unroll
-        for (int j = 0; j < kColBlocksPerWave; ++j) {
-            const int64_t blk = (nbw + j) * KB + kb;
-            wq[j] = cb_valid[j] ? wplane[blk * 64 + lane] : make_uint4(0, 0, 0, 0);
-            md[j] = cb_valid[j] ? meta[((nbw + j) * kColsPerBlock + c) * KBP + kb] : 0u;
-        }
+        for (int j = 0; j < kColBlocksPerWave; ++j)
+            dma16(wsrc[j] + (size_t)kb * 64,
+                  st + (uint32_t)offsetof(Stage<BM>, w) + (uint32_t)(w * kColBlocksPerWave + j) * 1024u);
+        dma4(msrc + kb, st + (uint32_t)offsetof(Stage<BM>, meta) + (uint32_t)w * 256u);
     };
 
     f32x4 acc[MR][kColBlocksPerWave];
@@ -147,63 +208,58 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
 #pragma unroll
         for (int j = 0; j < kColBlocksPerWave; ++j) acc[r][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    uint4 xr[kChunks];
-    uint4 wq[kColBlocksPerWave], wq_next[kColBlocksPerWave];
-    uint32_t md[kColBlocksPerWave], md_next[kColBlocksPerWave];
+    issue(0, 0);
+    if (KB > 1) issue(1, 1);
+    for (int kb = 0; kb < KB; ++kb) {
+        // this wave's copies of stage kb are done (stage kb+1's may be in flight); the
+        // barrier makes every wave's copies visible and retires the reads of stage
+        // kb-1, whose slot is then refilled with stage kb+2
+        if (kb + 1 < KB) wait_vmcnt<kDmaPerStage>();
+        else wait_vmcnt<0>();
+        lds_barrier();
+        if (kb + 2 < KB) issue((kb + 2) % kStages, kb + 2);
 
-    load_x(0, xr);
-    load_w(0, wq, md);
-    store_x(0, xr);
-    __syncthreads();
-
-    for (int64_t kb = 0; kb < KB; ++kb) {
-        const int cur = (int)(kb & 1);
-        const bool has_next = kb + 1 < KB;
-        if (has_next) {
-            load_x(kb + 1, xr);
-            load_w(kb + 1, wq_next, md_next);
-        }
-
-        Dequant<kBF16> dq[kColBlocksPerWave] = {Dequant<kBF16>(md[0]), Dequant<kBF16>(md[1]),
-                                                Dequant<kBF16>(md[2]), Dequant<kBF16>(md[3])};
+        const Stage<BM>& st = ring[kb % kStages];
+        Dequant<kBF16> dq[kColBlocksPerWave] = {Dequant<kBF16>(st.meta[w * 64 + c]),
+                                                Dequant<kBF16>(st.meta[w * 64 + 16 + c]),
+                                                Dequant<kBF16>(st.meta[w * 64 + 32 + c]),
+                                                Dequant<kBF16>(st.meta[w * 64 + 48 + c])};
+        uint4 wq[kColBlocksPerWave];
+#pragma unroll
+        for (int j = 0; j < kColBlocksPerWave; ++j) wq[j] = st.w[(w * kColBlocksPerWave + j) * 64 + lane];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             uint4 b[kColBlocksPerWave];
 #pragma unroll
-            for (int j = 0; j < kColBlocksPerWave; ++j) {
-                const uint32_t d = i == 0 ? wq[j].x : i == 1 ? wq[j].y : i == 2 ? wq[j].z : wq[j].w;
-                b[j] = dq[j](d);
-            }
+            for (int j = 0; j < kColBlocksPerWave; ++j) b[j] = dq[j](pick(wq[j], i));
+            const int chunk = (4 * i + h) ^ c;              // row 16 r + c has row % 16 == c
 #pragma unroll
             for (int r = 0; r < MR; ++r) {
-                const uint4 a = *reinterpret_cast<const uint4*>(&xs[cur][16 * r + c][32 * i + 8 * h]);
+                const uint4 a = st.x[(16 * r + c) * 16 + chunk];
 #pragma unroll
-                for (int j = 0; j < kColBlocksPerWave; ++j) acc[r][j] = mfma16x16x32<kBF16>(a, b[j], acc[r][j]);
+                for (int j = 0; j < kColBlocksPerWave; ++j) acc[r][j] = mfma16x16x32<kBF16>(b[j], a, acc[r][j]);
             }
         }
-
-        if (has_next) {
-            store_x(cur ^ 1, xr);
-#pragma unroll
-            for (int j = 0; j < kColBlocksPerWave; ++j) {
-                wq[j] = wq_next[j];
-                md[j] = md_next[j];
-            }
-        }
-        __syncthreads();
     }
 
+    // transposed tiles: lane (c, h), register e -> row 16 r + c, column 16 j + 4 h + e
 #pragma unroll
     for (int j = 0; j < kColBlocksPerWave; ++j) {
-        if (!cb_valid[j]) continue;
-        const int64_t n = (nbw + j) * kColsPerBlock + c;
-        const float bv = bias ? half_bits_to_f32<kBF16>(bias[n]) : 0.f;
+        if (nbw + j >= NB) continue;
+        const int n = (nbw + j) * kColsPerBlock + 4 * h;
+        float bv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (bias) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) bv[e] = half_bits_to_f32<kBF16>(bias[n + e]);
+        }
 #pragma unroll
         for (int r = 0; r < MR; ++r) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int64_t m = m0 + 16 * r + 4 * h + e;
-                if (m < M) y[m * N + n] = f32_to_half_bits<kBF16>(acc[r][j][e] + bv);
+            const int m = m0 + 16 * r + c;
+            if (m < M) {
+                const f32x4 v = acc[r][j];
+                const uint2 o = make_uint2(pack2_rne<kBF16>(v[0] + bv[0], v[1] + bv[1]),
+                                           pack2_rne<kBF16>(v[2] + bv[2], v[3] + bv[3]));
+                *reinterpret_cast<uint2*>(y + (size_t)m * N + n) = o;
             }
         }
     }
@@ -211,18 +267,23 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
 
 template <bool kBF16>
 hipError_t launch_typed(const uint16_t* x, const uint8_t* packed, const uint16_t* bias, uint16_t* y,
-                        int64_t M, int64_t K, int64_t N, hipStream_t stream) {
-    const int64_t NB = N / kColsPerBlock;
-    const unsigned gx = (unsigned)((NB + kColBlocksPerWG - 1) / kColBlocksPerWG);
-    auto grid_for = [&](int bm) { return dim3(gx, (unsigned)((M + bm - 1) / bm)); };
+                        int M, int K, int N, hipStream_t stream) {
+    const int NB = N / kColsPerBlock;
+    const int tiles_n = (NB + kColBlocksPerWG - 1) / kColBlocksPerWG;
+    const int tiles_n_pad = (tiles_n + kXcds - 1) / kXcds * kXcds;
+    auto grid_for = [&](int bm) {
+        const int tiles_m = (M + bm - 1) / bm;
+        return dim3((unsigned)(tiles_m * tiles_n_pad));
+    };
+    const int tm16 = (M + 15) / 16, tm32 = (M + 31) / 32, tm64 = (M + 63) / 64, tm128 = (M + 127) / 128;
     if (M <= 16)
-        hipLaunchKernelGGL((gemm_kernel<kBF16, 1>), grid_for(16), dim3(kThreads), 0, stream, x, packed, bias, y, M, K, N);
+        hipLaunchKernelGGL((gemm_kernel<kBF16, 1>), grid_for(16), dim3(kThreads), 0, stream, x, packed, bias, y, M, K, N, tm16, tiles_n);
     else if (M <= 32)
-        hipLaunchKernelGGL((gemm_kernel<kBF16, 2>), grid_for(32), dim3(kThreads), 0, stream, x, packed, bias, y, M, K, N);
+        hipLaunchKernelGGL((gemm_kernel<kBF16, 2>), grid_for(32), dim3(kThreads), 0, stream, x, packed, bias, y, M, K, N, tm32, tiles_n);
     else if (M <= 64)
-        hipLaunchKernelGGL((gemm_kernel<kBF16, 4>), grid_for(64), dim3(kThreads), 0, stream, x, packed, bias, y, M, K, N);
+        hipLaunchKernelGGL((gemm_kernel<kBF16, 4>), grid_for(64), dim3(kThreads), 0, stream, x, packed, bias, y, M, K, N, tm64, tiles_n);
     else
-        hipLaunchKernelGGL((gemm_kernel<kBF16, 8>), grid_for(128), dim3(kThreads), 0, stream, x, packed, bias, y, M, K, N);
+        hipLaunchKernelGGL((gemm_kernel<kBF16, 8>), grid_for(128), dim3(kThreads), 0, stream, x, packed, bias, y, M, K, N, tm128, tiles_n);
     return hipGetLastError();
 }
 
@@ -230,8 +291,8 @@ hipError_t launch_typed(const uint16_t* x, const uint8_t* packed, const uint16_t
 
 hipError_t launch_gemm(const uint16_t* x, const uint8_t* packed, const uint16_t* bias, uint16_t* y,
                        int64_t M, int64_t K, int64_t N, bool bf16, hipStream_t stream) {
-    return bf16 ? launch_typed<true>(x, packed, bias, y, M, K, N, stream)
-                : launch_typed<false>(x, packed, bias, y, M, K, N, stream);
+    return bf16 ? launch_typed<true>(x, packed, bias, y, (int)M, (int)K, (int)N, stream)
+                : launch_typed<false>(x, packed, bias, y, (int)M, (int)K, (int)N, stream);
 }
 
 }  // namespace w4a16
