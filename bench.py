@@ -18,12 +18,20 @@ Algorithmic bytes of a GEMM (AWQ-sized): K*N/2 codes + (K/G)*N/2 zeros
 Repack bytes: each AWQ byte read once and written once, 2*(K*N/2 + (K/G)*N/2 + (K/G)*N*2).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--quick]
+       python bench.py --pmc-probe     (launches for hardware-counter runs, no timing)
+
+--pmc-probe runs, without graphs or timing, a 256 MiB device copy (the calibration
+kernel for the byte counters: it reads and writes exactly 256 MiB) three times, then
+the headline GEMV ten times on rotating weight copies, so that counter runs see one
+dispatch per launch.
 """
 
 import argparse
+import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -146,6 +154,59 @@ def roofline_mfma(entry):
             "unit": "TFLOP/s", "frac": round(entry["TFLOPs"] / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
 
 
+CALIBRATION_COPY_BYTES = 256 << 20
+COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "gemv_gate_up_decode_M1_counters.md")
+GEMV_SOURCES = ("w4a16_int4_weight_amd/csrc/gemv.hip", "w4a16_int4_weight_amd/csrc/device_common.h")
+
+
+def gemv_source_hash():
+    h = hashlib.sha256()
+    for f in GEMV_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic():
+    """HBM bytes per headline launch from the committed byte-counter summary, or None
+    when there is none or the GEMV source changed since the counters were taken."""
+    try:
+        with open(COUNTER_SUMMARY) as f:
+            text = f.read()
+    except OSError:
+        return None
+    vals = dict(re.findall(r"^(traffic_bytes_per_launch|kernel_source_sha256_16): (\S+)$", text, re.M))
+    if vals.get("kernel_source_sha256_16") != gemv_source_hash() or "traffic_bytes_per_launch" not in vals:
+        return None
+    return int(vals["traffic_bytes_per_launch"])
+
+
+def pmc_probe(dev):
+    import torch
+    import synth
+    import w4a16_int4_weight_amd as w
+    src = torch.empty(CALIBRATION_COPY_BYTES, dtype=torch.uint8, device=dev).fill_(7)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    ws = synth.make("gate_up_decode", Ms=(1,))
+    qw = torch.from_numpy(ws.qweight).to(dev)
+    qz = torch.from_numpy(ws.qzeros).to(dev)
+    sc = to_dev_bits(ws.scale_bits, ws.dtype, dev)
+    packed0 = w.w4a16_repack(qw, qz, sc, ws.group_size)
+    packs = [packed0] + [packed0.clone() for _ in range(9)]
+    x = to_dev_bits(ws.x_bits[1], ws.dtype, dev)
+    y = torch.empty((1, ws.N), dtype=x.dtype, device=dev)
+    torch.cuda.synchronize()
+    for i in range(10):
+        w.w4a16_gemm(x, packs[i], ws.N, ws.group_size, y=y)
+    torch.cuda.synchronize()
+    log("pmc probe done: 3 x 256 MiB copy, 10 x gate_up_decode GEMV")
+
+
 def cpu_baseline(workload, M, budget_s=15.0):
     """The oracle as it stands (unpack, float64 dequant, float64 matmul), BLAS held
     to one thread, timed on whole steps of the same workload until ~budget_s."""
@@ -185,6 +246,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true", help="headline only, no secondary entries")
+    ap.add_argument("--pmc-probe", action="store_true", help="launches for counter runs, no timing")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this library has no multi-GPU path, so --gpus {args.gpus} "
@@ -199,6 +261,9 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     log(f"device {torch.cuda.get_device_name(0)}")
+    if args.pmc_probe:
+        pmc_probe(dev)
+        return
 
     head = measure_gemm(w, "gate_up_decode", 1, args.steps, args.warmup, dev)
     log(f"headline gate_up_decode M=1: {head['us_per_launch']:.2f} us, {head['GBps']:.0f} GB/s")
@@ -238,7 +303,7 @@ def main():
         "config": {"workload": "gate_up_decode: W4A16 GEMV M=1 K=2048 N=13312 group_size=128 bf16",
                    "M": 1, "K": 2048, "N": 13312, "group_size": 128,
                    "weight_copies_rotated": head["weight_copies"], "timing": "HIP graph of K calls, events"},
-        "roofline": roofline_hbm(head),
+        "roofline": roofline_hbm(head, counter_traffic()),
         "cpu_baseline": cpu,
         "secondary": secondary,
     }

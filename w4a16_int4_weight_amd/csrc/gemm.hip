@@ -11,10 +11,10 @@
 //
 // Workgroup: 4 waves side by side along N, each owning 4 column blocks (64
 // columns) and all 16*MR rows of the tile. Per 128-row block of K:
-//   * the activation tile [16*MR x 128] is staged in LDS, double buffered: the next
-//     block's tile is loaded into registers while the current one is consumed;
-//   * each wave keeps three register sets of packed codes and metadata in rotation,
-//     so the codes of block kb+2 are in flight while block kb is computed;
+//   * a 3-stage LDS ring holds, per k block, the activation tile [16*MR x 128]
+//     (16-byte chunks XOR-swizzled by row, so the fragment reads of a wave spread
+//     over all banks), the workgroup's 16 blocks of packed codes and its metadata;
+//     the ring is filled by direct global -> LDS copies, two k blocks ahead;
 //   * per 32-row step a wave decodes one word per column block into 8 fp16/bf16
 //     weights (q - z) * s, each rounded once to the dtype, and issues MR x 4 MFMAs
 //     (16x16x32, fp32 accumulators);
@@ -227,17 +227,20 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
         uint4 wq[kColBlocksPerWave];
 #pragma unroll
         for (int j = 0; j < kColBlocksPerWave; ++j) wq[j] = st.w[(w * kColBlocksPerWave + j) * 64 + lane];
+        // per 32-row step: the MR activation fragments, then column block by column
+        // block one decoded operand and its MR MFMAs (decoding the next block overlaps
+        // the previous block's MFMAs)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            uint4 b[kColBlocksPerWave];
-#pragma unroll
-            for (int j = 0; j < kColBlocksPerWave; ++j) b[j] = dq[j](pick(wq[j], i));
             const int chunk = (4 * i + h) ^ c;              // row 16 r + c has row % 16 == c
+            uint4 a[MR];
 #pragma unroll
-            for (int r = 0; r < MR; ++r) {
-                const uint4 a = st.x[(16 * r + c) * 16 + chunk];
+            for (int r = 0; r < MR; ++r) a[r] = st.x[(16 * r + c) * 16 + chunk];
 #pragma unroll
-                for (int j = 0; j < kColBlocksPerWave; ++j) acc[r][j] = mfma16x16x32<kBF16>(b[j], a, acc[r][j]);
+            for (int j = 0; j < kColBlocksPerWave; ++j) {
+                const uint4 b = dq[j](pick(wq[j], i));
+#pragma unroll
+                for (int r = 0; r < MR; ++r) acc[r][j] = mfma16x16x32<kBF16>(b, a[r], acc[r][j]);
             }
         }
     }
