@@ -95,9 +95,16 @@ w4a16_status w4a16_repack(const int32_t* qweight, const int32_t* qzeros, const v
                           w4a16_dtype dtype, int64_t K, int64_t N, int64_t group_size,
                           void* packed, size_t packed_bytes, void* stream);
 
-/* Device workspace the GEMM needs for this shape, in bytes. The current kernels
- * reduce split-K partial sums on chip, so this is 0 for every shape; the
- * argument pair stays in the ABI for kernels that will need scratch memory. */
+/* Device workspace the GEMM needs for this shape, in bytes (0 for most shapes).
+ * It is non-zero when the MFMA GEMM splits K over workgroups because the output has
+ * too few tiles to fill the GPU (small N and M, long K); the split partial sums
+ * (fp32) and one counter per output tile live there. Independent of the path that
+ * w4a16_gemm_ex would choose: the value suffices for every path.
+ *
+ * Contract: the workspace must be zero-filled before its first use and is left
+ * zero-filled (in its counter part) by every call, so one zeroed allocation can be
+ * reused by consecutive calls on one stream. Calls that overlap in time (different
+ * streams) need different workspaces. 16-byte alignment. */
 size_t w4a16_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t group_size);
 
 /* y = x . dequant(W) (+ bias), from a buffer written by w4a16_repack
@@ -111,7 +118,8 @@ size_t w4a16_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t group_size
  *   bias     [N] of `dtype`, or NULL. 2-byte aligned. Added in fp32 before rounding.
  *   group_size must be the value the buffer was repacked with (checked for shape
  *            validity only: the metadata of the buffer carries the groups).
- *   workspace / workspace_bytes: may be NULL / 0 when w4a16_workspace_bytes is 0.
+ *   workspace / workspace_bytes: at least w4a16_workspace_bytes(M, K, N, group_size)
+ *            bytes under the contract stated there; may be NULL / 0 when that is 0.
  *
  * Products accumulate in fp32; the output is rounded to `dtype` once, to nearest
  * even. For fixed inputs and shape the result is bit-for-bit reproducible from run

@@ -55,7 +55,13 @@ def test_layout_version_and_sizes(w):
         assert w.w4a16_packed_bytes(K, N, G) == tile_layout.packed_bytes(K, N, G)
     for K, N, G in [(100, 16, 128), (256, 24, 128), (256, 16, 64), (384, 16, 256), (0, 16, 128), (128, 0, 128)]:
         assert w.w4a16_packed_bytes(K, N, G) == 0
+    # K split over workgroups only when the output has too few tiles for the GPU
+    assert w.w4a16_workspace_bytes(512, 2048, 131072, 128) == 0
     assert w.w4a16_workspace_bytes(512, 2048, 13312, 128) == 0
+    ws = w.w4a16_workspace_bytes(16, 6656, 2048, 128)
+    assert ws > 16 * 2048 * 4 and ws % 4 == 0
+    assert w.w4a16_workspace_bytes(16, 6656, 2048, 64) == 0          # invalid group size
+    assert w.w4a16_workspace_bytes(0, 6656, 2048, 128) == 0
 
 
 def test_status_strings(w):
@@ -100,6 +106,11 @@ def test_gemm_validation_before_any_device_call(w):
     assert gemm(w, path=3) == 9
     assert gemm(w, path=1, M=17) == 9
     assert gemm(w, path=0, gmax=17) == 9
+    # a shape whose MFMA GEMM splits K needs the workspace
+    assert gemm(w, M=16, K=6656, N=2048, path=2) == 1
+    assert gemm(w, M=16, K=6656, N=2048, path=2, ws=P(4096), wsb=64) == 6
+    assert gemm(w, M=16, K=6656, N=2048, path=2, ws=P(4100), wsb=1 << 30) == 5
+    assert gemm(w, M=16, K=6656, N=2048, path=1) == 7                   # GEMV needs none
     # M = 0 is a valid no-op, even with NULL buffers
     assert gemm(w, M=0, x=None, y=None, packed=None) == 0
     # a fully valid call on this GPU-less host stops at the device check

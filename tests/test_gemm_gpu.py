@@ -203,3 +203,42 @@ def test_gemm_rejects_bad_calls(w):
     with pytest.raises(w.W4A16Error) as e:
         w.w4a16_gemm(x, packed, 32, 64)
     assert e.value.status == "W4A16_ERR_GROUP"
+
+
+def test_split_k_workspace_is_reused_and_left_zero(w):
+    # a skinny shape whose MFMA GEMM splits K over workgroups: three calls on one
+    # zeroed workspace must agree bit for bit (the tile counters are reset each call),
+    # then another split shape on the same workspace
+    ws = synth.make_custom(110, 16, 6656, 2048, "bf16", 128)
+    need = w.w4a16_workspace_bytes(16, 6656, 2048, 128)
+    assert need > 0
+    work = torch.zeros(need + 4096, dtype=torch.uint8, device=DEV)
+    packed = pack_on_gpu(w, ws)
+    x = bits_to_device(ws.x_bits[16], "bf16")
+    outs = []
+    for _ in range(3):
+        y = w.w4a16_gemm_ex(x, packed, 2048, 128, workspace=work, path="mfma")
+        torch.cuda.synchronize()
+        outs.append(device_to_bits(y))
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[1], outs[2])
+    ref = oracle_y(ws, ws.x_bits[16])
+    assert ogemm.max_rel_error(numerics.half_bits_to_f64(outs[0], "bf16"), ref) <= TOL
+    ws2 = synth.make_custom(111, 40, 2560, 96, "bf16", 128)
+    assert w.w4a16_workspace_bytes(40, 2560, 96, 128) > 0
+    packed2 = pack_on_gpu(w, ws2)
+    y2 = w.w4a16_gemm_ex(bits_to_device(ws2.x_bits[40], "bf16"), packed2, 96, 128, workspace=work, path="mfma")
+    torch.cuda.synchronize()
+    assert ogemm.max_rel_error(y_to_f64(y2, "bf16"), oracle_y(ws2, ws2.x_bits[40])) <= TOL
+    # the counter part of the workspace is zero again
+    tiles_bytes = 256
+    assert int(work[:tiles_bytes].count_nonzero()) == 0
+
+
+def test_split_k_rejects_small_workspace(w):
+    ws = synth.make_custom(112, 16, 6656, 2048, "bf16", 128)
+    packed = pack_on_gpu(w, ws)
+    x = bits_to_device(ws.x_bits[16], "bf16")
+    small = torch.zeros(64, dtype=torch.uint8, device=DEV)
+    with pytest.raises(w.W4A16Error) as e:
+        w.w4a16_gemm_ex(x, packed, 2048, 128, workspace=small, path="mfma")
+    assert e.value.status == "W4A16_ERR_BUFFER_SIZE"

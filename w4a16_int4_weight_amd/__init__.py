@@ -8,6 +8,7 @@ Functions keep the C names:
   w4a16_workspace_bytes(M, K, N, group_size)     -> int
   w4a16_repack(qweight, qzeros, scales, group_size, packed=None, stream=None) -> packed uint8 tensor
   w4a16_gemm(x, packed, N, group_size, bias=None, y=None, workspace=None, stream=None) -> y
+      (workspace=None: a zero-filled per-device workspace is allocated on demand)
   w4a16_gemm_ex(..., path="auto"|"gemv"|"mfma", gemv_max_m=-1)            -> y
   w4a16_status_str(code)                         -> str
 
@@ -142,10 +143,29 @@ def w4a16_repack(qweight, qzeros, scales, group_size=128, packed=None, stream=No
     return packed
 
 
+_workspaces = {}
+
+
+def _default_workspace(device, nbytes):
+    """A zero-filled workspace per device, grown on demand. The kernels leave its
+    counters at zero, so it is reused by consecutive calls; calls overlapping on
+    different streams must pass their own `workspace`."""
+    key = torch.device(device).index
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
 def _gemm_args(x, packed, N, group_size, bias, y, workspace, stream):
     if x.dim() != 2 or not x.is_contiguous():
         raise ValueError("x must be a contiguous [M, K] tensor")
     M, K = x.shape
+    if workspace is None and M > 0:
+        need = w4a16_workspace_bytes(M, K, N, group_size)
+        if need > 0:
+            workspace = _default_workspace(x.device, need)
     if y is None:
         y = torch.empty((M, N), dtype=x.dtype, device=x.device)
     if tuple(y.shape) != (M, N) or y.dtype != x.dtype or not y.is_contiguous():

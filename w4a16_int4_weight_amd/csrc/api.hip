@@ -57,8 +57,6 @@ w4a16_status check_device() {
 w4a16_status gemm_impl(const void* x, const void* packed, size_t packed_bytes, w4a16_dtype dtype, void* y,
                        int64_t M, int64_t K, int64_t N, int64_t group_size, const void* bias, void* workspace,
                        size_t workspace_bytes, void* stream, w4a16_path path, int64_t gemv_max_m) {
-    (void)workspace;
-    (void)workspace_bytes;
     if (M < 0) return W4A16_ERR_SHAPE;
     int64_t G = 0;
     w4a16_status st = check_shape(K, N, group_size, &G);
@@ -74,18 +72,26 @@ w4a16_status gemm_impl(const void* x, const void* packed, size_t packed_bytes, w
     if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(y, 16) || (bias && !aligned(bias, 2)))
         return W4A16_ERR_ALIGN;
     if (packed_bytes < packed_size(K, N)) return W4A16_ERR_BUFFER_SIZE;
+    const bool use_gemv = path == W4A16_PATH_GEMV || (path == W4A16_PATH_AUTO && M <= gemv_max_m);
+    if (!use_gemv) {
+        const size_t need = w4a16::plan_gemm(M, K, N).workspace_bytes;
+        if (need > 0) {
+            if (!workspace) return W4A16_ERR_NULL;
+            if (!aligned(workspace, 16)) return W4A16_ERR_ALIGN;
+            if (workspace_bytes < need) return W4A16_ERR_BUFFER_SIZE;
+        }
+    }
     st = check_device();
     if (st != W4A16_OK) return st;
 
     const bool bf16 = dtype == W4A16_BF16;
-    const bool use_gemv = path == W4A16_PATH_GEMV || (path == W4A16_PATH_AUTO && M <= gemv_max_m);
     const auto* xp = static_cast<const uint16_t*>(x);
     const auto* wp = static_cast<const uint8_t*>(packed);
     const auto* bp = static_cast<const uint16_t*>(bias);
     auto* yp = static_cast<uint16_t*>(y);
     hipStream_t s = static_cast<hipStream_t>(stream);
     const hipError_t err = use_gemv ? w4a16::launch_gemv(xp, wp, bp, yp, M, K, N, bf16, s)
-                                    : w4a16::launch_gemm(xp, wp, bp, yp, M, K, N, bf16, s);
+                                    : w4a16::launch_gemm(xp, wp, bp, yp, M, K, N, bf16, workspace, s);
     return err == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
 }
 
@@ -121,11 +127,10 @@ w4a16_status w4a16_repack(const int32_t* qweight, const int32_t* qzeros, const v
 }
 
 size_t w4a16_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t group_size) {
-    (void)M;
-    (void)K;
-    (void)N;
-    (void)group_size;
-    return 0;
+    int64_t G = 0;
+    if (M <= 0 || check_shape(K, N, group_size, &G) != W4A16_OK) return 0;
+    if (M >= (int64_t(1) << 31) || M * K > kMaxMK) return 0;
+    return w4a16::plan_gemm(M, K, N).workspace_bytes;
 }
 
 w4a16_status w4a16_gemm(const void* x, const void* packed, size_t packed_bytes, w4a16_dtype dtype, void* y,

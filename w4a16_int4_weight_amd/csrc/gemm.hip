@@ -35,8 +35,6 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kColBlocksPerWave = 4;
-constexpr int kColBlocksPerWG = kWaves * kColBlocksPerWave;   // 16 -> 256 columns
 constexpr int kXcds = 8;
 
 // Decode one tile word (8 codes of one column, rows in slot order) into the operand
@@ -49,6 +47,7 @@ template <> struct Dequant<true> {
     // conversion per pair. Byte b of (d & 0x0F0F0F0F) is slot 2b and byte b of
     // (d >> 4) & 0x0F0F0F0F is slot 2b+1; slot -> row: 0,2,4,6,1,3,5,7.
     float s, nzs;
+    Dequant() = default;
     __device__ __forceinline__ Dequant(uint32_t md) {
         s = bf16_bits_to_f32(md & 0xFFFFu);
         nzs = -(float)((md >> 16) & 0xFu) * s;
@@ -77,6 +76,7 @@ template <> struct Dequant<false> {
     // fp16 subtract of (1024 + z) gives q - z exactly; a packed multiply by s rounds
     // (q - z) * s once, to nearest even.
     f16x2 zz, ss;
+    Dequant() = default;
     __device__ __forceinline__ Dequant(uint32_t md) {
         const _Float16 s = __builtin_bit_cast(_Float16, (uint16_t)(md & 0xFFFFu));
         const _Float16 zb = (_Float16)(1024.0f + (float)((md >> 16) & 0xFu));
@@ -130,47 +130,63 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // One stage of the LDS ring: the activation tile of one 128-row block of K, the
-// workgroup's 16 blocks of packed codes and its 256 metadata words.
-template <int BM>
+// workgroup's blocks of packed codes (4 waves x CBW) and its metadata words (64 per
+// wave, of which the first 16 * CBW are used).
+template <int BM, int CBW>
 struct Stage {
     // [BM rows][16 chunks of 16 bytes], chunk j of row r stored at chunk j ^ (r % 16)
     uint4 x[BM * 16];
-    uint4 w[kColBlocksPerWG * 64];          // 16 blocks x 1 KiB, as in global memory
-    uint32_t meta[kColBlocksPerWG * kColsPerBlock];
+    uint4 w[kWaves * CBW * 64];             // 1 KiB per block, as in global memory
+    uint32_t meta[kWaves * 64];
 };
 
-template <bool kBF16, int MR>
+// Workgroup tile: 16*MR rows x 64*CBW columns, 4 waves side by side along N, each
+// owning CBW column blocks and all rows. `splits` > 1 splits the K range over
+// workgroups; their fp32 partial tiles meet in `workspace` and the last workgroup of
+// a tile to finish adds them in split order (deterministic) and writes y.
+template <bool kBF16, int MR, int CBW>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed, const uint16_t* __restrict__ bias,
-    uint16_t* __restrict__ y, int M, int K, int N, int tiles_m, int tiles_n) {
+    uint16_t* __restrict__ y, int M, int K, int N, int tiles_m, int tiles_n, int splits,
+    uint32_t* __restrict__ counters, float* __restrict__ partials) {
     constexpr int BM = 16 * MR;
     constexpr int kSlabsPerWave = BM / 4 / kWaves;      // 1 KiB slabs (4 rows) of the x tile per wave
     static_assert(kSlabsPerWave * 4 * kWaves == BM, "x tile must split over the waves");
-    constexpr int kDmaPerStage = kSlabsPerWave + kColBlocksPerWave + 1;   // copies per wave per stage
+    constexpr int kDmaPerStage = kSlabsPerWave + CBW + 1;   // copies per wave per stage
     constexpr int kStages = 3;
-    __shared__ Stage<BM> ring[kStages];
+    using StageT = Stage<BM, CBW>;
+    __shared__ StageT ring[kStages];
+    __shared__ int last_split;
 
+    // XCD-aware order: ids id, id+8, id+16, ... share an XCD; they take the M tiles and
+    // the K splits of one N tile. Ids past the last N tile (grid padding) exit.
     const int id = blockIdx.x;
     const int local = id / kXcds;
     const int m_tile = local % tiles_m;
-    const int n_tile = (local / tiles_m) * kXcds + id % kXcds;
+    const int rest = local / tiles_m;
+    const int split = rest % splits;
+    const int n_tile = (rest / splits) * kXcds + id % kXcds;
     if (n_tile >= tiles_n) return;
 
     const int KB = K / kRowsPerBlock;
     const int KBP = (int)padded_row_blocks(K);
     const int NB = N / kColsPerBlock;
+    const int kb_begin = (int)((int64_t)KB * split / splits);
+    const int kb_end = (int)((int64_t)KB * (split + 1) / splits);
+    const int nkb = kb_end - kb_begin;
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);    // wave index, uniform
     const int lane = tid & 63;
     const int c = lane & 15;
     const int h = lane >> 4;
     const int m0 = m_tile * BM;
-    const int nbw = n_tile * kColBlocksPerWG + w * kColBlocksPerWave;   // first column block of this wave
+    const int nbw = (n_tile * kWaves + w) * CBW;               // first column block of this wave
 
     // ---- per-lane sources of one stage's copies (k block kb adds kb * stride) ----
     // x: slab `slab` covers tile rows 4 slab .. 4 slab + 3; lane (row 4 slab + lane/16,
     // stored chunk lane%16) fetches logical chunk (lane%16) ^ (row%16). Rows past M
-    // read row M-1: they only feed output rows that are not written.
+    // read row M-1 and columns past N read column N-1: they only feed outputs that
+    // are not written.
     const uint16_t* xsrc[kSlabsPerWave];
 #pragma unroll
     for (int t = 0; t < kSlabsPerWave; ++t) {
@@ -178,55 +194,54 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
         const int m = m0 + row < M ? m0 + row : M - 1;
         xsrc[t] = x + (size_t)m * K + 8 * ((lane & 15) ^ (row & 15));
     }
-    const uint4* wsrc[kColBlocksPerWave];
+    const uint4* wsrc[CBW];
 #pragma unroll
-    for (int j = 0; j < kColBlocksPerWave; ++j) {
+    for (int j = 0; j < CBW; ++j) {
         const int nbj = nbw + j < NB ? nbw + j : NB - 1;
         wsrc[j] = reinterpret_cast<const uint4*>(packed) + (size_t)nbj * KB * 64 + lane;
     }
-    const int ncol = nbw * kColsPerBlock + lane;            // this wave's 64 columns
+    const int ncol = nbw * kColsPerBlock + (lane < 16 * CBW ? lane : 0);   // this wave's columns
     const uint32_t* msrc = reinterpret_cast<const uint32_t*>(packed + (size_t)K * N / 2) +
                            (size_t)(ncol < N ? ncol : N - 1) * KBP;
     const uint32_t ring_base = lds_addr(&ring[0]);
 
     auto issue = [&](int slot, int kb) {
-        const uint32_t st = ring_base + (uint32_t)slot * (uint32_t)sizeof(Stage<BM>);
+        const uint32_t st = ring_base + (uint32_t)slot * (uint32_t)sizeof(StageT);
 #pragma unroll
         for (int t = 0; t < kSlabsPerWave; ++t)
             dma16(xsrc[t] + (size_t)kb * kRowsPerBlock,
-                  st + (uint32_t)offsetof(Stage<BM>, x) + (uint32_t)(w * kSlabsPerWave + t) * 1024u);
+                  st + (uint32_t)offsetof(StageT, x) + (uint32_t)(w * kSlabsPerWave + t) * 1024u);
 #pragma unroll
-        for (int j = 0; j < kColBlocksPerWave; ++j)
-            dma16(wsrc[j] + (size_t)kb * 64,
-                  st + (uint32_t)offsetof(Stage<BM>, w) + (uint32_t)(w * kColBlocksPerWave + j) * 1024u);
-        dma4(msrc + kb, st + (uint32_t)offsetof(Stage<BM>, meta) + (uint32_t)w * 256u);
+        for (int j = 0; j < CBW; ++j)
+            dma16(wsrc[j] + (size_t)kb * 64, st + (uint32_t)offsetof(StageT, w) + (uint32_t)(w * CBW + j) * 1024u);
+        dma4(msrc + kb, st + (uint32_t)offsetof(StageT, meta) + (uint32_t)w * 256u);
     };
 
-    f32x4 acc[MR][kColBlocksPerWave];
+    f32x4 acc[MR][CBW];
 #pragma unroll
     for (int r = 0; r < MR; ++r)
 #pragma unroll
-        for (int j = 0; j < kColBlocksPerWave; ++j) acc[r][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < CBW; ++j) acc[r][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    issue(0, 0);
-    if (KB > 1) issue(1, 1);
-    for (int kb = 0; kb < KB; ++kb) {
-        // this wave's copies of stage kb are done (stage kb+1's may be in flight); the
-        // barrier makes every wave's copies visible and retires the reads of stage
-        // kb-1, whose slot is then refilled with stage kb+2
-        if (kb + 1 < KB) wait_vmcnt<kDmaPerStage>();
+    issue(0, kb_begin);
+    if (nkb > 1) issue(1, kb_begin + 1);
+    for (int t = 0; t < nkb; ++t) {
+        // this wave's copies of step t are done (step t+1's may be in flight); the
+        // barrier makes every wave's copies visible and retires the reads of step
+        // t-1, whose slot is then refilled with step t+2
+        if (t + 1 < nkb) wait_vmcnt<kDmaPerStage>();
         else wait_vmcnt<0>();
         lds_barrier();
-        if (kb + 2 < KB) issue((kb + 2) % kStages, kb + 2);
+        if (t + 2 < nkb) issue((t + 2) % kStages, kb_begin + t + 2);
 
-        const Stage<BM>& st = ring[kb % kStages];
-        Dequant<kBF16> dq[kColBlocksPerWave] = {Dequant<kBF16>(st.meta[w * 64 + c]),
-                                                Dequant<kBF16>(st.meta[w * 64 + 16 + c]),
-                                                Dequant<kBF16>(st.meta[w * 64 + 32 + c]),
-                                                Dequant<kBF16>(st.meta[w * 64 + 48 + c])};
-        uint4 wq[kColBlocksPerWave];
+        const StageT& st = ring[t % kStages];
+        Dequant<kBF16> dq[CBW];
+        uint4 wq[CBW];
 #pragma unroll
-        for (int j = 0; j < kColBlocksPerWave; ++j) wq[j] = st.w[(w * kColBlocksPerWave + j) * 64 + lane];
+        for (int j = 0; j < CBW; ++j) {
+            dq[j] = Dequant<kBF16>(st.meta[w * 64 + 16 * j + c]);
+            wq[j] = st.w[(w * CBW + j) * 64 + lane];
+        }
         // per 32-row step: the MR activation fragments, then column block by column
         // block one decoded operand and its MR MFMAs (decoding the next block overlaps
         // the previous block's MFMAs)
@@ -237,7 +252,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
 #pragma unroll
             for (int r = 0; r < MR; ++r) a[r] = st.x[(16 * r + c) * 16 + chunk];
 #pragma unroll
-            for (int j = 0; j < kColBlocksPerWave; ++j) {
+            for (int j = 0; j < CBW; ++j) {
                 const uint4 b = dq[j](pick(wq[j], i));
 #pragma unroll
                 for (int r = 0; r < MR; ++r) acc[r][j] = mfma16x16x32<kBF16>(b, a[r], acc[r][j]);
@@ -246,8 +261,63 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     }
 
     // transposed tiles: lane (c, h), register e -> row 16 r + c, column 16 j + 4 h + e
+    if (splits > 1) {
+        // Publish this split's partial tile with agent-scope stores (coherent across the
+        // XCDs' L2s without writing back a whole L2), wait until they have completed,
+        // then count the tile's finished splits; the last split to arrive reads all
+        // partials back (agent-scope loads), adds them in split order and writes y.
+        auto part = [&](int sp, int m, int n) {
+            return reinterpret_cast<uint64_t*>(partials + ((size_t)sp * M + m) * N + n);
+        };
 #pragma unroll
-    for (int j = 0; j < kColBlocksPerWave; ++j) {
+        for (int j = 0; j < CBW; ++j) {
+            if (nbw + j >= NB) continue;
+            const int n = (nbw + j) * kColsPerBlock + 4 * h;
+#pragma unroll
+            for (int r = 0; r < MR; ++r) {
+                const int m = m0 + 16 * r + c;
+                if (m < M) {
+                    uint64_t* p = part(split, m, n);
+                    const f32x4 v = acc[r][j];
+                    __hip_atomic_store(p, __builtin_bit_cast(uint64_t, f32x2{v[0], v[1]}), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(p + 1, __builtin_bit_cast(uint64_t, f32x2{v[2], v[3]}), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0);          // this thread's partial stores have completed
+        __syncthreads();
+        const int tile = m_tile * tiles_n + n_tile;
+        if (tid == 0)
+            last_split = __hip_atomic_fetch_add(&counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                         (uint32_t)(splits - 1);
+        __syncthreads();
+        if (!last_split) return;
+#pragma unroll
+        for (int j = 0; j < CBW; ++j) {
+            const int n = (nbw + j) * kColsPerBlock + 4 * h;
+#pragma unroll
+            for (int r = 0; r < MR; ++r) {
+                const int m = m0 + 16 * r + c;
+                f32x4 v = {0.f, 0.f, 0.f, 0.f};
+                if (nbw + j < NB && m < M) {
+                    for (int sp = 0; sp < splits; ++sp) {
+                        const uint64_t* p = part(sp, m, n);
+                        const f32x2 lo = __builtin_bit_cast(f32x2, __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+                        const f32x2 hi = __builtin_bit_cast(f32x2, __hip_atomic_load(p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+                        v += f32x4{lo[0], lo[1], hi[0], hi[1]};
+                    }
+                }
+                acc[r][j] = v;
+            }
+        }
+        if (tid == 0)      // leave the counter at zero for the next call
+            __hip_atomic_store(&counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+
+#pragma unroll
+    for (int j = 0; j < CBW; ++j) {
         if (nbw + j >= NB) continue;
         const int n = (nbw + j) * kColsPerBlock + 4 * h;
         float bv[4] = {0.f, 0.f, 0.f, 0.f};
@@ -268,34 +338,80 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     }
 }
 
+constexpr int kTargetWorkgroups = 256;   // one per CU
+
+template <bool kBF16, int MR, int CBW>
+void launch_cfg(const GemmPlan& p, const uint16_t* x, const uint8_t* packed, const uint16_t* bias, uint16_t* y,
+                int M, int K, int N, uint32_t* counters, float* partials, hipStream_t stream) {
+    const int tiles_n_pad = (p.tiles_n + kXcds - 1) / kXcds * kXcds;
+    const dim3 grid((unsigned)(p.tiles_m * p.splits * tiles_n_pad));
+    hipLaunchKernelGGL((gemm_kernel<kBF16, MR, CBW>), grid, dim3(kThreads), 0, stream, x, packed, bias, y, M, K, N,
+                       p.tiles_m, p.tiles_n, p.splits, counters, partials);
+}
+
+template <bool kBF16, int MR>
+void launch_mr(const GemmPlan& p, const uint16_t* x, const uint8_t* packed, const uint16_t* bias, uint16_t* y,
+               int M, int K, int N, uint32_t* counters, float* partials, hipStream_t stream) {
+    if (p.cbw == 4) launch_cfg<kBF16, MR, 4>(p, x, packed, bias, y, M, K, N, counters, partials, stream);
+    else if (p.cbw == 2) launch_cfg<kBF16, MR, 2>(p, x, packed, bias, y, M, K, N, counters, partials, stream);
+    else launch_cfg<kBF16, MR, 1>(p, x, packed, bias, y, M, K, N, counters, partials, stream);
+}
+
 template <bool kBF16>
-hipError_t launch_typed(const uint16_t* x, const uint8_t* packed, const uint16_t* bias, uint16_t* y,
-                        int M, int K, int N, hipStream_t stream) {
-    const int NB = N / kColsPerBlock;
-    const int tiles_n = (NB + kColBlocksPerWG - 1) / kColBlocksPerWG;
-    const int tiles_n_pad = (tiles_n + kXcds - 1) / kXcds * kXcds;
-    auto grid_for = [&](int bm) {
-        const int tiles_m = (M + bm - 1) / bm;
-        return dim3((unsigned)(tiles_m * tiles_n_pad));
-    };
-    const int tm16 = (M + 15) / 16, tm32 = (M + 31) / 32, tm64 = (M + 63) / 64, tm128 = (M + 127) / 128;
-    if (M <= 16)
-        hipLaunchKernelGGL((gemm_kernel<kBF16, 1>), grid_for(16), dim3(kThreads), 0, stream, x, packed, bias, y, M, K, N, tm16, tiles_n);
-    else if (M <= 32)
-        hipLaunchKernelGGL((gemm_kernel<kBF16, 2>), grid_for(32), dim3(kThreads), 0, stream, x, packed, bias, y, M, K, N, tm32, tiles_n);
-    else if (M <= 64)
-        hipLaunchKernelGGL((gemm_kernel<kBF16, 4>), grid_for(64), dim3(kThreads), 0, stream, x, packed, bias, y, M, K, N, tm64, tiles_n);
-    else
-        hipLaunchKernelGGL((gemm_kernel<kBF16, 8>), grid_for(128), dim3(kThreads), 0, stream, x, packed, bias, y, M, K, N, tm128, tiles_n);
-    return hipGetLastError();
+void launch_typed(const GemmPlan& p, const uint16_t* x, const uint8_t* packed, const uint16_t* bias, uint16_t* y,
+                  int M, int K, int N, uint32_t* counters, float* partials, hipStream_t stream) {
+    if (p.mr == 1) launch_mr<kBF16, 1>(p, x, packed, bias, y, M, K, N, counters, partials, stream);
+    else if (p.mr == 2) launch_mr<kBF16, 2>(p, x, packed, bias, y, M, K, N, counters, partials, stream);
+    else if (p.mr == 4) launch_mr<kBF16, 4>(p, x, packed, bias, y, M, K, N, counters, partials, stream);
+    else launch_mr<kBF16, 8>(p, x, packed, bias, y, M, K, N, counters, partials, stream);
 }
 
 }  // namespace
 
+GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N) {
+    GemmPlan p;
+    p.mr = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
+    p.tiles_m = (int)((M + 16 * p.mr - 1) / (16 * p.mr));
+    const int64_t NB = N / kColsPerBlock;
+    const int64_t KB = K / kRowsPerBlock;
+    // widest column tile that still occupies 3/4 of the CUs, else the narrowest (a wider
+    // tile decodes each weight for as many rows but reads the activations less often)
+    p.cbw = 1;
+    for (int cbw : {4, 2}) {
+        if (p.tiles_m * ((NB + kWaves * cbw - 1) / (kWaves * cbw)) >= kTargetWorkgroups * 3 / 4) {
+            p.cbw = cbw;
+            break;
+        }
+    }
+    p.tiles_n = (int)((NB + kWaves * p.cbw - 1) / (kWaves * p.cbw));
+    const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
+    // too few tiles for the chip: split K, at least 4 row blocks per split
+    p.splits = 1;
+    if (tiles < kTargetWorkgroups / 2 && KB >= 8) {
+        const int64_t want = (kTargetWorkgroups + tiles - 1) / tiles;
+        const int64_t most = KB / 4;
+        p.splits = (int)(want < most ? want : most);
+    }
+    p.workspace_bytes = 0;
+    if (p.splits > 1) {
+        const size_t counters = ((size_t)tiles * 4 + 255) / 256 * 256;
+        p.workspace_bytes = counters + (size_t)p.splits * (size_t)M * (size_t)N * 4;
+    }
+    return p;
+}
+
 hipError_t launch_gemm(const uint16_t* x, const uint8_t* packed, const uint16_t* bias, uint16_t* y,
-                       int64_t M, int64_t K, int64_t N, bool bf16, hipStream_t stream) {
-    return bf16 ? launch_typed<true>(x, packed, bias, y, (int)M, (int)K, (int)N, stream)
-                : launch_typed<false>(x, packed, bias, y, (int)M, (int)K, (int)N, stream);
+                       int64_t M, int64_t K, int64_t N, bool bf16, void* workspace, hipStream_t stream) {
+    const GemmPlan p = plan_gemm(M, K, N);
+    uint32_t* counters = static_cast<uint32_t*>(workspace);
+    float* partials = nullptr;
+    if (p.splits > 1) {
+        const size_t counter_bytes = ((size_t)p.tiles_m * p.tiles_n * 4 + 255) / 256 * 256;
+        partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + counter_bytes);
+    }
+    if (bf16) launch_typed<true>(p, x, packed, bias, y, (int)M, (int)K, (int)N, counters, partials, stream);
+    else launch_typed<false>(p, x, packed, bias, y, (int)M, (int)K, (int)N, counters, partials, stream);
+    return hipGetLastError();
 }
 
 }  // namespace w4a16

@@ -15,8 +15,20 @@ hipError_t launch_repack(const int32_t* qweight, const int32_t* qzeros, const ui
 hipError_t launch_gemv(const uint16_t* x, const uint8_t* packed, const uint16_t* bias, uint16_t* y,
                        int64_t M, int64_t K, int64_t N, bool bf16, hipStream_t stream);
 
-// LDS-staged dequantise -> MFMA GEMM for any M >= 1.
+// LDS-staged dequantise -> MFMA GEMM for any M >= 1: tile shape and K split chosen
+// from the shape; workspace_bytes > 0 when K is split over workgroups.
+struct GemmPlan {
+    int mr;            // row fragments of 16 per tile (tile rows = 16 * mr)
+    int cbw;           // 16-column blocks per wave (tile columns = 64 * cbw)
+    int tiles_m, tiles_n;
+    int splits;        // workgroups per tile along K
+    size_t workspace_bytes;   // [tile counters, 256-byte aligned][splits x M x N fp32 partials]
+};
+GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N);
+
+// `workspace` must hold plan_gemm(M, K, N).workspace_bytes bytes whose counter part is
+// zero; the kernel leaves it zero.
 hipError_t launch_gemm(const uint16_t* x, const uint8_t* packed, const uint16_t* bias, uint16_t* y,
-                       int64_t M, int64_t K, int64_t N, bool bf16, hipStream_t stream);
+                       int64_t M, int64_t K, int64_t N, bool bf16, void* workspace, hipStream_t stream);
 
 }  // namespace w4a16
