@@ -8,84 +8,125 @@
 // vllm-omni commit "cpu_int4: repack weights in n-blocks ..." shows that transient
 // reaching 1 GiB for a 131072 x 2048 head).
 //
-// Work split: one workgroup per (128-row block kb, tile of up to 16 column blocks).
-//   1. 128 rows x (2 * tile) AWQ words are read, row by row, into LDS;
-//   2. each 16-byte lane chunk of the tile's 1 KiB output blocks is assembled from
-//      LDS (32 nibbles: 4 words x 8 slots) and written with one 128-bit store, a
-//      wave writing one contiguous 1 KiB block;
-//   3. the block's metadata words (scale bits | zero << 16) are written.
+// The reorder is an 8 x 8 transpose of 4-bit elements. Eight AWQ words of one word
+// column (8 output columns) and 8 consecutive rows hold nibble (row r, AWQ slot s);
+// a tile word holds one column and 8 rows. Transposing the 8 words in registers
+// (swap 16-bit halves, then bytes, then nibbles: three stages of pairwise swaps)
+// gives word s = the 8 rows of the column in AWQ slot s. Both orders are folded in
+// for free: feeding the rows in tile slot order makes nibble s' of every result hold
+// row tile_row_of_slot(s'), and the column t result is result word
+// awq_slot_of_column(t).
+//
+// Work split: workgroup = 128-row block kb x 64 AWQ words (512 columns); thread
+// (word j, lane group h) transposes rows 32 i + 8 h + 0..7 for i = 0..3 and places,
+// for each of its 8 columns, the 16-byte chunk of lane (column % 16) + 16 h in LDS;
+// the workgroup then writes its 32 blocks whole. Wave h reads 64 consecutive words
+// (256 bytes) of one row per load instruction. The workgroups of row block 0 also
+// write the metadata rows of their 512 columns (one column's row is contiguous).
 #include "device_common.h"
 #include "launch.h"
 
 namespace w4a16 {
 namespace {
 
-constexpr int kTileColBlocks = 16;            // column blocks per workgroup
-constexpr int kTileWords = 2 * kTileColBlocks; // AWQ words per row of the tile
-constexpr int kRepackThreads = 256;
+constexpr int kWordsPerTile = 64;                    // AWQ words (8 columns each) per workgroup
+constexpr int kRepackThreads = kWordsPerTile * 4;    // x 4 lane groups
+
+// 8 x 8 transpose of nibbles: on return nibble r of word s = nibble s of word r on entry.
+__device__ __forceinline__ void transpose8x8_nibbles(uint32_t (&v)[8]) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {            // 4x4 blocks: 16-bit halves
+        const uint32_t a = v[r], b = v[r + 4];
+        v[r] = (a & 0x0000FFFFu) | (b << 16);
+        v[r + 4] = (a >> 16) | (b & 0xFFFF0000u);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {            // 2x2 blocks: bytes within halves
+        const int r = (q & 1) + 4 * (q >> 1);
+        const uint32_t a = v[r], b = v[r + 2];
+        v[r] = (a & 0x00FF00FFu) | ((b & 0x00FF00FFu) << 8);
+        v[r + 2] = ((a >> 8) & 0x00FF00FFu) | (b & 0xFF00FF00u);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {            // single nibbles within bytes
+        const int r = 2 * q;
+        const uint32_t a = v[r], b = v[r + 1];
+        v[r] = (a & 0x0F0F0F0Fu) | ((b & 0x0F0F0F0Fu) << 4);
+        v[r + 1] = ((a >> 4) & 0x0F0F0F0Fu) | (b & 0xF0F0F0F0u);
+    }
+}
 
 __global__ __launch_bounds__(kRepackThreads) void repack_kernel(
     const uint32_t* __restrict__ qweight, const uint32_t* __restrict__ qzeros,
     const uint16_t* __restrict__ scales, uint8_t* __restrict__ packed,
     int64_t K, int64_t N, int64_t G) {
-    // +1 word of padding per row: rows 8 apart (the four lane groups of a wave)
-    // land in different LDS banks.
-    __shared__ uint32_t tile[kRowsPerBlock][kTileWords + 1];
-
     const int64_t KB = K / kRowsPerBlock;
-    const int64_t NB = N / kColsPerBlock;
     const int64_t words_per_row = N / 8;
     const int64_t kb = blockIdx.y;
-    const int64_t nb0 = (int64_t)blockIdx.x * kTileColBlocks;
-    const int nbt = (int)((NB - nb0) < kTileColBlocks ? (NB - nb0) : kTileColBlocks);
-    const int tw = 2 * nbt;
+    const int64_t j0 = (int64_t)blockIdx.x * kWordsPerTile;     // first AWQ word of the tile
     const int tid = threadIdx.x;
+    const int jl = tid & (kWordsPerTile - 1);
+    const int h = tid / kWordsPerTile;                            // lane group (wave) 0..3
+    const int64_t j = j0 + jl;
+    const bool active = j < words_per_row;
+    const int64_t jc = active ? j : words_per_row - 1;            // clamped: loads stay in bounds
 
-    // 1. AWQ words of rows 128 kb .. 128 kb + 127, words 2 nb0 .. 2 nb0 + tw - 1.
-    const uint32_t* src = qweight + (kb * kRowsPerBlock) * words_per_row + 2 * nb0;
-    for (int idx = tid; idx < kRowsPerBlock * tw; idx += kRepackThreads) {
-        const int r = idx / tw;
-        const int wcol = idx - r * tw;
-        tile[r][wcol] = src[(int64_t)r * words_per_row + wcol];
+    // 1. rows 128 kb + 32 i + 8 h + e of word column jc, fed in tile slot order
+    uint32_t t[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t* src = qweight + (kb * kRowsPerBlock + 32 * i + 8 * h) * words_per_row + jc;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) t[i][s] = src[(int64_t)tile_row_of_slot(s) * words_per_row];
+    }
+    // 2. transpose: t[i][s] = column in AWQ slot s, its 8 rows in tile slot order
+#pragma unroll
+    for (int i = 0; i < 4; ++i) transpose8x8_nibbles(t[i]);
+
+    // 3. column 8 j + c8 -> block (j / 2), lane (8 (j % 2) + c8) + 16 h: words i = 0..3.
+    //    The tile's 32 blocks are assembled in LDS and written out whole, each wave
+    //    storing contiguous 1 KiB blocks.
+    __shared__ uint4 stage[kWordsPerTile / 2 * 64];
+    if (active) {
+#pragma unroll
+        for (int c8 = 0; c8 < 8; ++c8) {
+            const int s = awq_slot_of_column(c8);
+            const int lane = 8 * (jl & 1) + c8 + 16 * h;
+            stage[(jl >> 1) * 64 + lane] = make_uint4(t[0][s], t[1][s], t[2][s], t[3][s]);
+        }
     }
     __syncthreads();
-
-    // 2. Output chunks: block j of the tile, lane L.
-    for (int idx = tid; idx < nbt * 64; idx += kRepackThreads) {
-        const int j = idx >> 6;
-        const int lane = idx & 63;
-        const int c = lane & 15;
-        const int h = lane >> 4;
-        const int wcol = 2 * j + (c >> 3);
-        const int shift = 4 * awq_slot_of_column(c & 7);
-        uint32_t out[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint32_t word = 0;
-#pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                const int r = 32 * i + 8 * h + tile_row_of_slot(s);
-                word |= ((tile[r][wcol] >> shift) & 0xFu) << (4 * s);
-            }
-            out[i] = word;
-        }
-        uint4* dst = reinterpret_cast<uint4*>(packed + ((nb0 + j) * KB + kb) * kBlockBytes) + lane;
-        *dst = make_uint4(out[0], out[1], out[2], out[3]);
+    const int64_t tile_words = words_per_row - j0 < kWordsPerTile ? words_per_row - j0 : kWordsPerTile;
+    const int nblk = (int)(tile_words / 2);                       // N % 16 == 0: whole blocks
+    for (int q = tid; q < nblk * 64; q += kRepackThreads) {
+        const int64_t nb = (j0 >> 1) + (q >> 6);
+        reinterpret_cast<uint4*>(packed + (nb * KB + kb) * kBlockBytes)[q & 63] = stage[q];
     }
 
-    // 3. Metadata word of row block kb for each column of the tile; the workgroup
-    //    of the last row block also writes the zero padding words.
-    const int64_t g = (kb * kRowsPerBlock) / G;
+    // 4. metadata: the workgroups of row block 0 write, for each column of their tile,
+    //    its whole row of KBP words (scale bits | zero << 16 per row block, then zero
+    //    padding), 16 bytes at a time
+    if (kb != 0) return;
     const int64_t KBP = padded_row_blocks(K);
     uint32_t* meta = reinterpret_cast<uint32_t*>(packed + K * N / 2);
-    for (int t = tid; t < nbt * kColsPerBlock; t += kRepackThreads) {
-        const int64_t n = nb0 * kColsPerBlock + t;
-        const uint32_t zword = qzeros[g * words_per_row + (n >> 3)];
-        const uint32_t z = (zword >> (4 * awq_slot_of_column((int)(n & 7)))) & 0xFu;
-        const uint32_t sbits = scales[g * N + n];
-        meta[n * KBP + kb] = sbits | (z << 16);
-        if (kb == KB - 1)
-            for (int64_t p = KB; p < KBP; ++p) meta[n * KBP + p] = 0u;
+    for (int q = tid; q < tile_words * 8; q += kRepackThreads) {
+        const int64_t n = j0 * 8 + q;
+        const int zshift = 4 * awq_slot_of_column((int)(n & 7));
+        uint4* row = reinterpret_cast<uint4*>(meta + n * KBP);
+        for (int64_t p0 = 0; p0 < KBP; p0 += 4) {
+            uint32_t word[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t b = p0 + e;
+                word[e] = 0u;
+                if (b < KB) {
+                    const int64_t g = (b * kRowsPerBlock) / G;
+                    const uint32_t z = (qzeros[g * words_per_row + (n >> 3)] >> zshift) & 0xFu;
+                    word[e] = (uint32_t)scales[g * N + n] | (z << 16);
+                }
+            }
+            row[p0 / 4] = make_uint4(word[0], word[1], word[2], word[3]);
+        }
     }
 }
 
@@ -94,8 +135,8 @@ __global__ __launch_bounds__(kRepackThreads) void repack_kernel(
 hipError_t launch_repack(const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
                          uint8_t* packed, int64_t K, int64_t N, int64_t G, hipStream_t stream) {
     const int64_t KB = K / kRowsPerBlock;
-    const int64_t NB = N / kColsPerBlock;
-    dim3 grid((unsigned)((NB + kTileColBlocks - 1) / kTileColBlocks), (unsigned)KB);
+    const int64_t words = N / 8;
+    dim3 grid((unsigned)((words + kWordsPerTile - 1) / kWordsPerTile), (unsigned)KB);
     hipLaunchKernelGGL(repack_kernel, grid, dim3(kRepackThreads), 0, stream,
                        reinterpret_cast<const uint32_t*>(qweight), reinterpret_cast<const uint32_t*>(qzeros),
                        scales, packed, K, N, G);
