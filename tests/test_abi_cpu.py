@@ -61,6 +61,8 @@ def test_layout_version_and_sizes(w):
     ws = w.w4a16_workspace_bytes(16, 6656, 2048, 128)
     assert ws > 16 * 2048 * 4 and ws % 4 == 0
     assert w.w4a16_workspace_bytes(16, 6656, 2048, 64) == 0          # invalid group size
+    # sized for the MFMA GEMM, which any M may be sent to; the GEMV needs none
+    assert w.w4a16_workspace_bytes(1, 2048, 131072, 128) == 0
     assert w.w4a16_workspace_bytes(0, 6656, 2048, 128) == 0
 
 
@@ -111,6 +113,7 @@ def test_gemm_validation_before_any_device_call(w):
     assert gemm(w, M=16, K=6656, N=2048, path=2, ws=P(4096), wsb=64) == 6
     assert gemm(w, M=16, K=6656, N=2048, path=2, ws=P(4100), wsb=1 << 30) == 5
     assert gemm(w, M=16, K=6656, N=2048, path=1) == 7                   # GEMV needs none
+    assert gemm(w, M=1, K=6656, N=2048) == 7
     # M = 0 is a valid no-op, even with NULL buffers
     assert gemm(w, M=0, x=None, y=None, packed=None) == 0
     # a fully valid call on this GPU-less host stops at the device check

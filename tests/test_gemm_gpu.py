@@ -242,3 +242,24 @@ def test_split_k_rejects_small_workspace(w):
     with pytest.raises(w.W4A16Error) as e:
         w.w4a16_gemm_ex(x, packed, 2048, 128, workspace=small, path="mfma")
     assert e.value.status == "W4A16_ERR_BUFFER_SIZE"
+
+
+@pytest.mark.parametrize("K", [8320, 9216])
+@pytest.mark.parametrize("M", [1, 5, 16])
+def test_gemv_long_k(w, K, M):
+    # more than 64 row blocks: each wave takes several runs of 4 row blocks, the next
+    # run's loads in flight during the current one (65 row blocks: 9 waves of 8, the
+    # last with one valid block); M = 16 does not fit in LDS and reads x directly
+    ws = synth.make_custom(700 + M + K // 128, M, K, 48, "bf16", 128)
+    packed = pack_on_gpu(w, ws)
+    got = y_to_f64(run(w, ws, packed, ws.x_bits[M], path="gemv"), "bf16")
+    assert ogemm.max_rel_error(got, oracle_y(ws, ws.x_bits[M])) <= TOL
+
+
+def test_gemv_needs_no_workspace(w):
+    ws = synth.make_custom(140, 8, 6656, 2048, "bf16", 128)
+    packed = pack_on_gpu(w, ws)
+    x = bits_to_device(ws.x_bits[8], "bf16")
+    y = w.w4a16_gemm_ex(x, packed, 2048, 128, workspace=None, path="gemv")
+    torch.cuda.synchronize()
+    assert ogemm.max_rel_error(y_to_f64(y, "bf16"), oracle_y(ws, ws.x_bits[8])) <= TOL

@@ -73,13 +73,11 @@ w4a16_status gemm_impl(const void* x, const void* packed, size_t packed_bytes, w
         return W4A16_ERR_ALIGN;
     if (packed_bytes < packed_size(K, N)) return W4A16_ERR_BUFFER_SIZE;
     const bool use_gemv = path == W4A16_PATH_GEMV || (path == W4A16_PATH_AUTO && M <= gemv_max_m);
-    if (!use_gemv) {
-        const size_t need = w4a16::plan_gemm(M, K, N).workspace_bytes;
-        if (need > 0) {
-            if (!workspace) return W4A16_ERR_NULL;
-            if (!aligned(workspace, 16)) return W4A16_ERR_ALIGN;
-            if (workspace_bytes < need) return W4A16_ERR_BUFFER_SIZE;
-        }
+    const size_t need = use_gemv ? 0 : w4a16::plan_gemm(M, K, N).workspace_bytes;
+    if (need > 0) {
+        if (!workspace) return W4A16_ERR_NULL;
+        if (!aligned(workspace, 16)) return W4A16_ERR_ALIGN;
+        if (workspace_bytes < need) return W4A16_ERR_BUFFER_SIZE;
     }
     st = check_device();
     if (st != W4A16_OK) return st;
@@ -130,6 +128,7 @@ size_t w4a16_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t group_size
     int64_t G = 0;
     if (M <= 0 || check_shape(K, N, group_size, &G) != W4A16_OK) return 0;
     if (M >= (int64_t(1) << 31) || M * K > kMaxMK) return 0;
+    // only the MFMA GEMM uses one (when it splits K over workgroups); the GEMV needs none
     return w4a16::plan_gemm(M, K, N).workspace_bytes;
 }
 

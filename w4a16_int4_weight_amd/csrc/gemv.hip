@@ -7,24 +7,31 @@
 // possible:
 //
 //   * one workgroup per 16-column block; its waves split the K range (split-K) in
-//     runs of 4 row blocks, loading a column's 4 metadata words with one 16-byte
-//     load. Every load is unconditional (indices clamped into the buffer), so the
-//     loads of a run are all in flight before the first is consumed;
+//     runs of 4 row blocks, loading a column's metadata words for the run with one
+//     16-byte load. Every load is unconditional (indices clamped into the buffer,
+//     out-of-range row blocks weighted by a zero scale), so all of a run's loads are
+//     in flight before the first is consumed. Codes and metadata are read once,
+//     with nontemporal loads;
 //   * per 32-row step a lane turns its packed word into the B operand of a
 //     16x16x32 MFMA with one shift and one AND-OR per pair of codes: OR-ing a code
 //     into the mantissa of the 16-bit value 128.0 (bf16) or 1024.0 (fp16) gives
 //     exactly base + q, so the MFMA sums T = sum_k x (base + q) with exact products;
-//   * the activations (<= 16 rows) are the A operand, zero beyond row M;
+//     the run's row blocks are independent MFMA chains, interleaved;
+//   * the activations are the A operand; rows >= M repeat row 0 and their results
+//     are dropped (a row of the product depends on that row of A only);
 //   * per 128-row block, y += s * (T - (base + z) * X), X = sum_k x over the block:
 //     the offset and the zero point leave in one correction, because
 //     sum_k x (base + q) - (base + z) sum_k x = sum_k x (q - z);
 //   * the waves' partial sums are added in wave order through LDS (deterministic),
 //     bias is added in fp32 and the result rounded once to the output dtype.
+//     (Splitting K over workgroups as well, with fp32 partials in a workspace and a
+//     last-arriver reduction, measured slower on every decode shape here, narrow N
+//     included: the extra pass costs more than the idle compute units.)
 //
 // Two variants:
-//   staged  (activations fit in LDS): the workgroup copies x [M, K] to LDS and
+//   staged  (the activations fit in LDS): the workgroup copies x to LDS and
 //           computes the row-block sums X there once (16 lanes per sum, reduced
-//           with DPP lane moves), while the first run of codes is in flight;
+//           with DPP lane moves), while the codes are in flight;
 //   direct  (otherwise): each lane loads its activation fragments from global
 //           memory, and X is folded into the MFMA as a second product with B equal
 //           to -(base + z) in every entry.
@@ -39,18 +46,33 @@ constexpr int kRun = 4;                      // row blocks per load batch (one m
 constexpr int kMaxStagedChunksPerThread = 8; // 16-byte activation chunks a thread stages
 constexpr size_t kStagedLdsLimit = 128 * 1024;
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Data read exactly once: nontemporal 16-byte load.
+__device__ __forceinline__ uint4 load_once(const uint4* p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ uint32_t pick(const uint4 v, int i) {
     return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
-__device__ __forceinline__ uint4 and4(const uint4 v, uint32_t m) { return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m); }
+// The nibble-pair mask 0x000F000F held in a VGPR. A three-operand instruction on
+// this architecture reads at most one scalar or literal constant, so with the mask
+// in a VGPR and the magic base in an SGPR each pair of codes decodes with a single
+// v_and_or_b32 (after its shift) instead of a separate AND and OR.
+__device__ __forceinline__ uint32_t pair_mask_vgpr() {
+    uint32_t m;
+    asm volatile("v_mov_b32 %0, 0x000f000f" : "=v"(m));
+    return m;
+}
 
 // B operand of step i: codes of rows 32i + 8(l/16) + 0..7 as base + q pairs.
 template <bool kBF16>
-__device__ __forceinline__ uint4 magic_operand(uint32_t v) {
+__device__ __forceinline__ uint4 magic_operand(uint32_t v, uint32_t mask) {
     constexpr uint32_t B = Magic<kBF16>::kBase2;
-    return make_uint4((v & 0x000F000Fu) | B, ((v >> 4) & 0x000F000Fu) | B,
-                      ((v >> 8) & 0x000F000Fu) | B, ((v >> 12) & 0x000F000Fu) | B);
+    return make_uint4((v & mask) | B, ((v >> 4) & mask) | B, ((v >> 8) & mask) | B, ((v >> 12) & mask) | B);
 }
 
 // Sum of the 8 16-bit values in a uint4, in fp32.
@@ -73,27 +95,36 @@ __device__ __forceinline__ float row16_sum(float v) {
     return v;
 }
 
+struct GemvArgs {
+    const uint16_t* x;
+    const uint8_t* packed;
+    const uint16_t* bias;
+    uint16_t* y;
+    int M, K, N;
+    int kb_per_wave;        // row blocks per wave (multiple of kRun)
+};
+
 template <bool kBF16, bool kStaged, int kChunks>
-__global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(
-    const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed, const uint16_t* __restrict__ bias,
-    uint16_t* __restrict__ y, int M, int K, int N, int kb_per_wave) {
+__global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(const GemvArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     using Mg = Magic<kBF16>;
 
+    const int M = a.M, K = a.K, N = a.N;
     const int KB = K / kRowsPerBlock;
     const int KBP = (int)padded_row_blocks(K);
     const int nb = blockIdx.x;
     const int waves = blockDim.x >> 6;
-    const int w = threadIdx.x >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);     // wave-uniform
     const int lane = threadIdx.x & 63;
     const int c = lane & 15;         // column in the block, and activation row of the A operand
     const int h = lane >> 4;         // which 8 of every 32 rows
-    const int kb_begin = w * kb_per_wave;                       // multiple of 4
-    const int kb_end = kb_begin + kb_per_wave < KB ? kb_begin + kb_per_wave : KB;
-    const uint32_t row_mask = c < M ? 0xFFFFFFFFu : 0u;
+    // row blocks of this wave [kb_begin, kb_end)
+    const int kb_begin = w * a.kb_per_wave;
+    const int kb_end = kb_begin + a.kb_per_wave < KB ? kb_begin + a.kb_per_wave : KB;
+    const int xr = c < M ? c : 0;    // activation row this lane feeds to the MFMA
 
-    // LDS: [staged x, M*K 16-bit][row-block sums X, KB x 16 fp32][wave partials]
-    const int xs_bytes = kStaged ? ((M * K * 2 + 15) & ~15) : 0;
+    // LDS: [staged x, M x K 16-bit][row-block sums X, KB x 16 fp32][wave partials]
+    const int xs_bytes = kStaged ? M * K * 2 : 0;                // multiple of 256
     const int xsum_bytes = kStaged ? KB * 16 * 4 : 0;
     uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
     float* xsum = reinterpret_cast<float*>(smem + xs_bytes);
@@ -103,34 +134,40 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(
     const int row_chunks = K / 8;
     const int chunks = M * row_chunks;
     uint4 xv[kStaged ? kChunks : 1];
+    int xm[kStaged ? kChunks : 1];
     if constexpr (kStaged) {
+        const float inv_row_chunks = 1.0f / (float)row_chunks;
 #pragma unroll
         for (int p = 0; p < kChunks; ++p) {
             const int q = threadIdx.x + p * blockDim.x;
-            xv[p] = reinterpret_cast<const uint4*>(x)[q < chunks ? q : chunks - 1];
+            // row of chunk q: a float estimate (q < 2^22, off by at most one) corrected exactly
+            int m = (int)((float)q * inv_row_chunks);
+            m -= m * row_chunks > q ? 1 : 0;
+            m += (m + 1) * row_chunks <= q ? 1 : 0;
+            m = q < chunks ? m : 0;
+            xm[p] = m;
+            xv[p] = reinterpret_cast<const uint4*>(a.x)[q < chunks ? q : chunks - 1];
         }
     }
 
-    // 2. codes and metadata of this wave's first run of 4 row blocks (clamped into
-    //    the column block; blocks past kb_end are loaded but not used)
-    const uint4* wcol = reinterpret_cast<const uint4*>(packed) + (size_t)nb * KB * 64 + lane;
-    const uint4* mcol = reinterpret_cast<const uint4*>(packed + (size_t)K * N / 2) + ((size_t)(nb * kColsPerBlock + c) * KBP) / 4;
+    // 2. codes and metadata of this wave's first run (clamped into the column block;
+    //    row blocks past kb_end are loaded but weighted by zero)
+    const uint4* wcol = reinterpret_cast<const uint4*>(a.packed) + (size_t)nb * KB * 64 + lane;
+    const uint4* mcol = reinterpret_cast<const uint4*>(a.packed + (size_t)K * N / 2) + ((size_t)(nb * kColsPerBlock + c) * KBP) / 4;
     auto load_run = [&](int kb0, uint4 (&wq)[kRun], uint4& md) {
-        md = mcol[kb0 / 4];
+        md = load_once(mcol + (kb0 < KB ? kb0 : KB - 1) / 4);
 #pragma unroll
         for (int u = 0; u < kRun; ++u) {
             const int kb = kb0 + u < KB ? kb0 + u : KB - 1;
-            wq[u] = wcol[(size_t)kb * 64];
+            wq[u] = load_once(wcol + (size_t)kb * 64);
         }
     };
-    const int kb_first = kb_begin < KB ? kb_begin : (KB - 1) / 4 * 4;
     uint4 wq[kRun], md;
-    load_run(kb_first, wq, md);
+    load_run(kb_begin, wq, md);
 
-    // 3. staged variant: x -> LDS and the row-block sums; rows >= M of the sums are 0
+    // 3. staged variant: x -> LDS and the row-block sums (rows < M; the sums of the
+    //    repeated rows are never read into a kept result)
     if constexpr (kStaged) {
-        for (int t = threadIdx.x; t < KB * 16; t += blockDim.x)
-            if ((t & 15) >= M) xsum[t] = 0.f;
 #pragma unroll
         for (int p = 0; p < kChunks; ++p) {
             const int q = threadIdx.x + p * blockDim.x;
@@ -140,59 +177,81 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(
                 reinterpret_cast<uint4*>(xs)[q] = xv[p];
                 const float s = row16_sum(sum8<kBF16>(xv[p]));
                 if ((q & 15) == 0) {
-                    const int m = q / row_chunks;
-                    const int kb = (q - m * row_chunks) >> 4;
-                    xsum[kb * 16 + m] = s;
+                    const int kb = (q - xm[p] * row_chunks) >> 4;
+                    xsum[kb * 16 + xm[p]] = s;
                 }
             }
         }
         __syncthreads();
     }
 
-    // 4. runs of 4 row blocks, the next run's loads in flight during the current one
-    const uint16_t* xrow = (kStaged ? (const uint16_t*)xs : x) + (c < M ? c : 0) * K + 8 * h;
+    // 4. runs of row blocks, the next run's loads in flight during the current one
+    const uint32_t mask = pair_mask_vgpr();
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int kb0 = kb_begin; kb0 < kb_end; kb0 += kRun) {
-        uint4 wqn[kRun], mdn;
-        const bool more = kb0 + kRun < kb_end;
-        if (more) load_run(kb0 + kRun, wqn, mdn);
+    auto compute_run = [&](const int kb0, const uint4 (&wr)[kRun], const uint4 mr) {
+        // row block of each run entry (entries past kb_end read block 0's activations:
+        // finite values, weighted by zero)
+        int kbl[kRun];
+        float s[kRun];
+        uint32_t z[kRun];
 #pragma unroll
         for (int u = 0; u < kRun; ++u) {
-            const int kb = kb0 + u;
-            if (kb >= kb_end) break;
-            uint4 xa[4];
+            const bool valid = kb0 + u < kb_end;
+            kbl[u] = valid ? kb0 + u : 0;
+            const uint32_t mdv = pick(mr, u);             // kb0 is a multiple of 4
+            s[u] = valid ? half_bits_to_f32<kBF16>(mdv & 0xFFFFu) : 0.f;
+            z[u] = (mdv >> 16) & 0xFu;
+        }
+        f32x4 t[kRun];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                xa[i] = and4(*reinterpret_cast<const uint4*>(xrow + kb * kRowsPerBlock + 32 * i), row_mask);
-            const uint32_t mdv = pick(md, u);
-            const float s = half_bits_to_f32<kBF16>(mdv & 0xFFFFu);
-            const uint32_t z = (mdv >> 16) & 0xFu;
-            const uint4 d = wq[u];
-            f32x4 t = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (kStaged) {
+        for (int u = 0; u < kRun; ++u) t[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) t = mfma16x16x32<kBF16>(xa[i], magic_operand<kBF16>(pick(d, i)), t);
-                const f32x4 xsv = *reinterpret_cast<const f32x4*>(xsum + kb * 16 + 4 * h);
-                const float zb = Mg::kBase + (float)z;
-                acc += s * (t - zb * xsv);
-            } else {
-                const uint32_t nz = Mg::kNegBase | z;            // -(base + z), exact
-                const uint4 bz = make_uint4(nz | (nz << 16), nz | (nz << 16), nz | (nz << 16), nz | (nz << 16));
+        for (int i = 0; i < 4; ++i) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    t = mfma16x16x32<kBF16>(xa[i], magic_operand<kBF16>(pick(d, i)), t);
-                    t = mfma16x16x32<kBF16>(xa[i], bz, t);
+            for (int u = 0; u < kRun; ++u) {
+                uint4 xa;
+                if constexpr (kStaged)
+                    xa = *reinterpret_cast<const uint4*>(xs + xr * K + kbl[u] * kRowsPerBlock + 32 * i + 8 * h);
+                else
+                    xa = *reinterpret_cast<const uint4*>(a.x + (size_t)xr * K + kbl[u] * kRowsPerBlock + 32 * i + 8 * h);
+                t[u] = mfma16x16x32<kBF16>(xa, magic_operand<kBF16>(pick(wr[u], i), mask), t[u]);
+                if constexpr (!kStaged) {
+                    const uint32_t nz = Mg::kNegBase | z[u];            // -(base + z), exact
+                    const uint32_t nz2 = nz | (nz << 16);
+                    t[u] = mfma16x16x32<kBF16>(xa, make_uint4(nz2, nz2, nz2, nz2), t[u]);
                 }
-                acc += s * t;
             }
         }
-        if (more) {
+        if constexpr (kStaged) {
+            if (M == 1) {      // only register 0 of lanes 0..15 holds a kept result
 #pragma unroll
-            for (int u = 0; u < kRun; ++u) wq[u] = wqn[u];
-            md = mdn;
+                for (int u = 0; u < kRun; ++u)
+                    acc[0] += s[u] * (t[u][0] - (Mg::kBase + (float)z[u]) * xsum[kbl[u] * 16]);
+            } else {
+#pragma unroll
+                for (int u = 0; u < kRun; ++u) {
+                    const f32x4 xsv = *reinterpret_cast<const f32x4*>(xsum + kbl[u] * 16 + 4 * h);
+                    acc += s[u] * (t[u] - (Mg::kBase + (float)z[u]) * xsv);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < kRun; ++u) acc += s[u] * t[u];
         }
+    };
+    const int runs = a.kb_per_wave / kRun;
+    int kb0 = kb_begin;
+    for (int r = 1; r < runs; ++r, kb0 += kRun) {
+        uint4 wqn[kRun], mdn;
+        load_run(kb0 + kRun, wqn, mdn);
+        compute_run(kb0, wq, md);
+#pragma unroll
+        for (int u = 0; u < kRun; ++u) wq[u] = wqn[u];
+        md = mdn;
     }
+    compute_run(kb0, wq, md);
 
+    // 5. waves' partials in wave order
     if (waves > 1) {
         partial[w * 64 + lane] = acc;
         __syncthreads();
@@ -201,54 +260,66 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(
         for (int v = 1; v < waves; ++v) acc += partial[v * 64 + lane];
     }
 
+    // lane (c, h), register r -> row 4h + r, column 16 nb + c
     const int n = nb * kColsPerBlock + c;
-    const float b = bias ? half_bits_to_f32<kBF16>(bias[n]) : 0.f;
+    const float b = a.bias ? half_bits_to_f32<kBF16>(a.bias[n]) : 0.f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int row = 4 * h + r;
-        if (row < M) y[(size_t)row * N + n] = f32_to_half_bits<kBF16>(acc[r] + b);
+        if (row < M) a.y[(size_t)row * N + n] = f32_to_half_bits<kBF16>(acc[r] + b);
     }
 }
 
 template <bool kBF16>
-void launch_typed(const dim3 grid, const dim3 block, size_t lds, bool staged, int chunks_per_thread, hipStream_t s,
-                  const uint16_t* x, const uint8_t* packed, const uint16_t* bias, uint16_t* y, int M, int K, int N,
-                  int kpw) {
-    if (!staged)
-        hipLaunchKernelGGL((gemv_kernel<kBF16, false, 1>), grid, block, lds, s, x, packed, bias, y, M, K, N, kpw);
-    else if (chunks_per_thread <= 1)
-        hipLaunchKernelGGL((gemv_kernel<kBF16, true, 1>), grid, block, lds, s, x, packed, bias, y, M, K, N, kpw);
-    else if (chunks_per_thread <= 2)
-        hipLaunchKernelGGL((gemv_kernel<kBF16, true, 2>), grid, block, lds, s, x, packed, bias, y, M, K, N, kpw);
-    else if (chunks_per_thread <= 4)
-        hipLaunchKernelGGL((gemv_kernel<kBF16, true, 4>), grid, block, lds, s, x, packed, bias, y, M, K, N, kpw);
+void launch_typed(const GemvPlan& p, const GemvArgs& args, hipStream_t s) {
+    const dim3 grid((unsigned)(args.N / kColsPerBlock));
+    const dim3 block((unsigned)(64 * p.waves));
+    if (!p.staged)
+        hipLaunchKernelGGL((gemv_kernel<kBF16, false, 1>), grid, block, p.lds_bytes, s, args);
+    else if (p.chunks_per_thread <= 1)
+        hipLaunchKernelGGL((gemv_kernel<kBF16, true, 1>), grid, block, p.lds_bytes, s, args);
+    else if (p.chunks_per_thread <= 2)
+        hipLaunchKernelGGL((gemv_kernel<kBF16, true, 2>), grid, block, p.lds_bytes, s, args);
+    else if (p.chunks_per_thread <= 4)
+        hipLaunchKernelGGL((gemv_kernel<kBF16, true, 4>), grid, block, p.lds_bytes, s, args);
     else
-        hipLaunchKernelGGL((gemv_kernel<kBF16, true, 8>), grid, block, lds, s, x, packed, bias, y, M, K, N, kpw);
+        hipLaunchKernelGGL((gemv_kernel<kBF16, true, 8>), grid, block, p.lds_bytes, s, args);
 }
 
 }  // namespace
 
-hipError_t launch_gemv(const uint16_t* x, const uint8_t* packed, const uint16_t* bias, uint16_t* y,
-                       int64_t M, int64_t K, int64_t N, bool bf16, hipStream_t stream) {
+GemvPlan plan_gemv(int64_t M, int64_t K, int64_t N) {
+    (void)N;
+    GemvPlan p;
     const int64_t KB = K / kRowsPerBlock;
     // runs of 4 row blocks per wave, at most 16 waves
     int64_t kpw = kRun;
     while ((KB + kpw - 1) / kpw > kMaxWaves) kpw += kRun;
-    const int64_t waves = (KB + kpw - 1) / kpw;
-    const int64_t threads = 64 * waves;
-    const size_t partial_bytes = waves > 1 ? (size_t)waves * 64 * 16 : 0;
-    const size_t staged_bytes = (((size_t)M * K * 2 + 15) & ~(size_t)15) + (size_t)KB * 16 * 4 + partial_bytes;
-    const int64_t chunks_per_thread = (M * K / 8 + threads - 1) / threads;
-    const bool staged = staged_bytes <= kStagedLdsLimit && chunks_per_thread <= kMaxStagedChunksPerThread;
-    const size_t lds = staged ? staged_bytes : partial_bytes;
-    const dim3 grid((unsigned)(N / kColsPerBlock));
-    const dim3 block((unsigned)threads);
-    if (bf16)
-        launch_typed<true>(grid, block, lds, staged, (int)chunks_per_thread, stream, x, packed, bias, y, (int)M, (int)K,
-                           (int)N, (int)kpw);
-    else
-        launch_typed<false>(grid, block, lds, staged, (int)chunks_per_thread, stream, x, packed, bias, y, (int)M, (int)K,
-                            (int)N, (int)kpw);
+    p.kb_per_wave = (int)kpw;
+    p.waves = (int)((KB + kpw - 1) / kpw);
+    const int64_t threads = 64 * p.waves;
+    const size_t partial_bytes = p.waves > 1 ? (size_t)p.waves * 64 * 16 : 0;
+    const size_t staged_bytes = (size_t)M * K * 2 + (size_t)KB * 16 * 4 + partial_bytes;
+    p.chunks_per_thread = (int)((M * K / 8 + threads - 1) / threads);
+    p.staged = staged_bytes <= kStagedLdsLimit && p.chunks_per_thread <= kMaxStagedChunksPerThread;
+    p.lds_bytes = p.staged ? staged_bytes : partial_bytes;
+    return p;
+}
+
+hipError_t launch_gemv(const uint16_t* x, const uint8_t* packed, const uint16_t* bias, uint16_t* y,
+                       int64_t M, int64_t K, int64_t N, bool bf16, hipStream_t stream) {
+    const GemvPlan p = plan_gemv(M, K, N);
+    GemvArgs args;
+    args.x = x;
+    args.packed = packed;
+    args.bias = bias;
+    args.y = y;
+    args.M = (int)M;
+    args.K = (int)K;
+    args.N = (int)N;
+    args.kb_per_wave = p.kb_per_wave;
+    if (bf16) launch_typed<true>(p, args, stream);
+    else launch_typed<false>(p, args, stream);
     return hipGetLastError();
 }
 

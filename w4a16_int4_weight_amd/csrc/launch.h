@@ -11,7 +11,17 @@ namespace w4a16 {
 hipError_t launch_repack(const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
                          uint8_t* packed, int64_t K, int64_t N, int64_t G, hipStream_t stream);
 
-// Weight-streaming split-K GEMV for 1 <= M <= 16.
+// Weight-streaming split-K GEMV for 1 <= M <= 16 (K split over the waves of a
+// workgroup; no workspace).
+struct GemvPlan {
+    int kb_per_wave;       // row blocks per wave (multiple of 4)
+    int waves;             // waves per workgroup
+    bool staged;           // activations staged in LDS
+    int chunks_per_thread; // 16-byte activation chunks each thread stages
+    size_t lds_bytes;
+};
+GemvPlan plan_gemv(int64_t M, int64_t K, int64_t N);
+
 hipError_t launch_gemv(const uint16_t* x, const uint8_t* packed, const uint16_t* bias, uint16_t* y,
                        int64_t M, int64_t K, int64_t N, bool bf16, hipStream_t stream);
 
