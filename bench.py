@@ -10,8 +10,9 @@ repack (GB/s), the MFMA GEMM at M=512 (TFLOP/s) and the GEMV on the other shapes
 Timing: warm-up calls, then K calls captured in one HIP graph and replayed once
 between two events on the launch stream, with a device synchronisation on both
 sides. Each call reads a different copy of the packed weights, rotating through
-at least 512 MiB of copies, so the 256 MiB Infinity Cache cannot serve repeats:
-the bytes come from HBM.
+at least 1 GiB of copies (at least 8 for the LM head), so the 256 MiB Infinity Cache
+cannot serve repeats: the bytes come from HBM. (A rotation of only 4 x 139 MB ran
+the LM-head GEMV about 8% slower than 8 copies; more copies only remove reuse.)
 
 Algorithmic bytes of a GEMM (AWQ-sized): K*N/2 codes + (K/G)*N/2 zeros
 + (K/G)*N*2 scales + M*K*2 activations + M*N*2 outputs; flops 2*M*N*K.
@@ -22,8 +23,8 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [
 
 --pmc-probe runs, without graphs or timing, a 256 MiB device copy (the calibration
 kernel for the byte counters: it reads and writes exactly 256 MiB) three times, then
-the headline GEMV ten times on rotating weight copies, so that counter runs see one
-dispatch per launch.
+the headline GEMV ten times on rotating weight copies and the LM-head M=512 GEMM three
+times, so that counter runs see one dispatch per launch.
 """
 
 import argparse
@@ -41,7 +42,8 @@ sys.path.insert(0, ROOT)
 METRIC = "W4A16 GEMM GB/s (M=1) & TFLOP/s (M=512) vs roofline; repack GB/s"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
-ROTATE_BYTES = 512 << 20
+ROTATE_BYTES = 1 << 30
+MAX_COPIES = 128
 
 
 def log(msg):
@@ -101,7 +103,7 @@ def measure_gemm(w, workload, M, steps, warmup, dev, path="auto"):
     packed0 = w.w4a16_repack(qw, qz, sc, G)
     del qw, qz, sc
     pbytes = packed0.numel()
-    copies = max(1, min(64, math.ceil(ROTATE_BYTES / pbytes)))
+    copies = max(1, min(MAX_COPIES, math.ceil(ROTATE_BYTES / pbytes)))
     packs = [packed0] + [packed0.clone() for _ in range(copies - 1)]
     x = to_dev_bits(ws.x_bits[M], ws.dtype, dev)
     y = torch.empty((M, N), dtype=x.dtype, device=dev)
@@ -204,7 +206,21 @@ def pmc_probe(dev):
     for i in range(10):
         w.w4a16_gemm(x, packs[i], ws.N, ws.group_size, y=y)
     torch.cuda.synchronize()
-    log("pmc probe done: 3 x 256 MiB copy, 10 x gate_up_decode GEMV")
+    del packs, packed0
+    # the MFMA GEMM on the LM-head prefill (M=512), three launches on one weight copy
+    ws = synth.make("lm_head", Ms=(512,))
+    qw = torch.from_numpy(ws.qweight).to(dev)
+    qz = torch.from_numpy(ws.qzeros).to(dev)
+    sc = to_dev_bits(ws.scale_bits, ws.dtype, dev)
+    packed = w.w4a16_repack(qw, qz, sc, ws.group_size)
+    del qw, qz, sc
+    x = to_dev_bits(ws.x_bits[512], ws.dtype, dev)
+    y = torch.empty((512, ws.N), dtype=x.dtype, device=dev)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        w.w4a16_gemm(x, packed, ws.N, ws.group_size, y=y)
+    torch.cuda.synchronize()
+    log("pmc probe done: 3 x 256 MiB copy, 10 x gate_up_decode GEMV, 3 x lm_head M=512 GEMM")
 
 
 def cpu_baseline(workload, M, budget_s=15.0):

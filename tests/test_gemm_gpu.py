@@ -263,3 +263,16 @@ def test_gemv_needs_no_workspace(w):
     y = w.w4a16_gemm_ex(x, packed, 2048, 128, workspace=None, path="gemv")
     torch.cuda.synchronize()
     assert ogemm.max_rel_error(y_to_f64(y, "bf16"), oracle_y(ws, ws.x_bits[8])) <= TOL
+
+
+@pytest.mark.parametrize("M", [300, 512])
+def test_gemm_256_row_tiles(w, M):
+    # a wide N (8192 column blocks, 2 x 512 tiles of 256 x 256) gives the 256-row tiles
+    # with the two-stage ring and register metadata; M = 300 leaves a ragged second row
+    # tile; sampled column blocks
+    ws = synth.make_custom(800 + M, M, 256, 131072, "bf16", 128)
+    packed = pack_on_gpu(w, ws)
+    got = y_to_f64(run(w, ws, packed, ws.x_bits[M], path="mfma"), "bf16")
+    cols = sample_column_blocks(ws.N, 128, seed=M)
+    err = ogemm.max_rel_error(got[:, cols], oracle_y(ws, ws.x_bits[M], cols))
+    assert err <= TOL

@@ -130,14 +130,21 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // One stage of the LDS ring: the activation tile of one 128-row block of K, the
-// workgroup's blocks of packed codes (4 waves x CBW) and its metadata words (64 per
-// wave, of which the first 16 * CBW are used).
-template <int BM, int CBW>
+// workgroup's blocks of packed codes (4 waves x CBW) and, with kMeta, its metadata
+// words (64 per wave, of which the first 16 * CBW are used). Without kMeta (the
+// 256-row tiles, whose two stages fill the 160 KiB of LDS) each lane loads its
+// metadata words into registers instead.
+template <int BM, int CBW, bool kMeta>
 struct Stage {
     // [BM rows][16 chunks of 16 bytes], chunk j of row r stored at chunk j ^ (r % 16)
     uint4 x[BM * 16];
     uint4 w[kWaves * CBW * 64];             // 1 KiB per block, as in global memory
     uint32_t meta[kWaves * 64];
+};
+template <int BM, int CBW>
+struct Stage<BM, CBW, false> {
+    uint4 x[BM * 16];
+    uint4 w[kWaves * CBW * 64];
 };
 
 // Workgroup tile: 16*MR rows x 64*CBW columns, 4 waves side by side along N, each
@@ -152,11 +159,15 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     constexpr int BM = 16 * MR;
     constexpr int kSlabsPerWave = BM / 4 / kWaves;      // 1 KiB slabs (4 rows) of the x tile per wave
     static_assert(kSlabsPerWave * 4 * kWaves == BM, "x tile must split over the waves");
-    constexpr int kDmaPerStage = kSlabsPerWave + CBW + 1;   // copies per wave per stage
-    constexpr int kStages = 3;
-    using StageT = Stage<BM, CBW>;
+    // 256-row tiles: two stages (one k block ahead), metadata in registers; otherwise
+    // three stages (two ahead) with the metadata staged in LDS as well
+    constexpr int kStages = MR == 16 ? 2 : 3;
+    constexpr bool kMetaInLds = kStages == 3;
+    constexpr int kDmaPerStage = kSlabsPerWave + CBW + (kMetaInLds ? 1 : 0);   // copies per wave per stage
+    using StageT = Stage<BM, CBW, kMetaInLds>;
     __shared__ StageT ring[kStages];
-    __shared__ int last_split;
+    // split-K flag, in ring memory (written only after every wave has left the main loop)
+    int& last_split = *reinterpret_cast<int*>(&ring[0]);
 
     // XCD-aware order: ids id, id+8, id+16, ... share an XCD; they take the M tiles and
     // the K splits of one N tile. Ids past the last N tile (grid padding) exit.
@@ -187,34 +198,48 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     // stored chunk lane%16) fetches logical chunk (lane%16) ^ (row%16). Rows past M
     // read row M-1 and columns past N read column N-1: they only feed outputs that
     // are not written.
-    const uint16_t* xsrc[kSlabsPerWave];
+    // (32-bit element offsets rather than pointers: M * K <= 2^32 and K * N / 32 < 2^32,
+    // and they leave registers for the 256-row tiles)
+    uint32_t xoff[kSlabsPerWave];
 #pragma unroll
     for (int t = 0; t < kSlabsPerWave; ++t) {
         const int row = 4 * (w * kSlabsPerWave + t) + (lane >> 4);
         const int m = m0 + row < M ? m0 + row : M - 1;
-        xsrc[t] = x + (size_t)m * K + 8 * ((lane & 15) ^ (row & 15));
+        xoff[t] = (uint32_t)m * (uint32_t)K + 8u * (uint32_t)((lane & 15) ^ (row & 15));
     }
-    const uint4* wsrc[CBW];
+    uint32_t woff[CBW];
 #pragma unroll
     for (int j = 0; j < CBW; ++j) {
         const int nbj = nbw + j < NB ? nbw + j : NB - 1;
-        wsrc[j] = reinterpret_cast<const uint4*>(packed) + (size_t)nbj * KB * 64 + lane;
+        woff[j] = (uint32_t)nbj * (uint32_t)KB * 64u + (uint32_t)lane;
     }
+    const uint4* wbase = reinterpret_cast<const uint4*>(packed);
     const int ncol = nbw * kColsPerBlock + (lane < 16 * CBW ? lane : 0);   // this wave's columns
     const uint32_t* msrc = reinterpret_cast<const uint32_t*>(packed + (size_t)K * N / 2) +
                            (size_t)(ncol < N ? ncol : N - 1) * KBP;
     const uint32_t ring_base = lds_addr(&ring[0]);
 
+    // metadata in registers: lane (c, h) takes column 16 (nbw + j) + c of each block j
+    const uint32_t* mbase = reinterpret_cast<const uint32_t*>(packed + (size_t)K * N / 2);
+    uint32_t moff[kMetaInLds ? 1 : CBW];
+    if constexpr (!kMetaInLds) {
+#pragma unroll
+        for (int j = 0; j < CBW; ++j) {
+            const int nbj = nbw + j < NB ? nbw + j : NB - 1;
+            moff[j] = (uint32_t)(nbj * kColsPerBlock + c) * (uint32_t)KBP;
+        }
+    }
+
     auto issue = [&](int slot, int kb) {
         const uint32_t st = ring_base + (uint32_t)slot * (uint32_t)sizeof(StageT);
 #pragma unroll
         for (int t = 0; t < kSlabsPerWave; ++t)
-            dma16(xsrc[t] + (size_t)kb * kRowsPerBlock,
+            dma16(x + xoff[t] + (size_t)kb * kRowsPerBlock,
                   st + (uint32_t)offsetof(StageT, x) + (uint32_t)(w * kSlabsPerWave + t) * 1024u);
 #pragma unroll
         for (int j = 0; j < CBW; ++j)
-            dma16(wsrc[j] + (size_t)kb * 64, st + (uint32_t)offsetof(StageT, w) + (uint32_t)(w * CBW + j) * 1024u);
-        dma4(msrc + kb, st + (uint32_t)offsetof(StageT, meta) + (uint32_t)w * 256u);
+            dma16(wbase + woff[j] + (size_t)kb * 64, st + (uint32_t)offsetof(StageT, w) + (uint32_t)(w * CBW + j) * 1024u);
+        if constexpr (kMetaInLds) dma4(msrc + kb, st + (uint32_t)offsetof(StageT, meta) + (uint32_t)w * 256u);
     };
 
     f32x4 acc[MR][CBW];
@@ -223,23 +248,44 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
 #pragma unroll
         for (int j = 0; j < CBW; ++j) acc[r][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    uint32_t md[CBW], mdn[CBW];        // register metadata (two-stage ring only)
     issue(0, kb_begin);
-    if (nkb > 1) issue(1, kb_begin + 1);
+    if constexpr (kMetaInLds) {
+        if (nkb > 1) issue(1, kb_begin + 1);
+    } else {
+#pragma unroll
+        for (int j = 0; j < CBW; ++j) mdn[j] = mbase[moff[j] + kb_begin];
+    }
     for (int t = 0; t < nkb; ++t) {
-        // this wave's copies of step t are done (step t+1's may be in flight); the
-        // barrier makes every wave's copies visible and retires the reads of step
-        // t-1, whose slot is then refilled with step t+2
-        if (t + 1 < nkb) wait_vmcnt<kDmaPerStage>();
-        else wait_vmcnt<0>();
-        lds_barrier();
-        if (t + 2 < nkb) issue((t + 2) % kStages, kb_begin + t + 2);
+        if constexpr (kMetaInLds) {
+            // this wave's copies of step t are done (step t+1's may be in flight); the
+            // barrier makes every wave's copies visible and retires the reads of step
+            // t-1, whose slot is then refilled with step t+2
+            if (t + 1 < nkb) wait_vmcnt<kDmaPerStage>();
+            else wait_vmcnt<0>();
+            lds_barrier();
+            if (t + 2 < nkb) issue((t + 2) % kStages, kb_begin + t + 2);
+        } else {
+            // step t's copies and metadata have landed; after the barrier the other
+            // slot (step t-1) is free for step t+1
+            wait_vmcnt<0>();
+            lds_barrier();
+#pragma unroll
+            for (int j = 0; j < CBW; ++j) md[j] = mdn[j];
+            if (t + 1 < nkb) {
+                issue((t + 1) % kStages, kb_begin + t + 1);
+#pragma unroll
+                for (int j = 0; j < CBW; ++j) mdn[j] = mbase[moff[j] + kb_begin + t + 1];
+            }
+        }
 
         const StageT& st = ring[t % kStages];
         Dequant<kBF16> dq[CBW];
         uint4 wq[CBW];
 #pragma unroll
         for (int j = 0; j < CBW; ++j) {
-            dq[j] = Dequant<kBF16>(st.meta[w * 64 + 16 * j + c]);
+            if constexpr (kMetaInLds) dq[j] = Dequant<kBF16>(st.meta[w * 64 + 16 * j + c]);
+            else dq[j] = Dequant<kBF16>(md[j]);
             wq[j] = st.w[(w * CBW + j) * 64 + lane];
         }
         // per 32-row step: the MR activation fragments, then column block by column
@@ -363,17 +409,21 @@ void launch_typed(const GemmPlan& p, const uint16_t* x, const uint8_t* packed, c
     if (p.mr == 1) launch_mr<kBF16, 1>(p, x, packed, bias, y, M, K, N, counters, partials, stream);
     else if (p.mr == 2) launch_mr<kBF16, 2>(p, x, packed, bias, y, M, K, N, counters, partials, stream);
     else if (p.mr == 4) launch_mr<kBF16, 4>(p, x, packed, bias, y, M, K, N, counters, partials, stream);
-    else launch_mr<kBF16, 8>(p, x, packed, bias, y, M, K, N, counters, partials, stream);
+    else if (p.mr == 8) launch_mr<kBF16, 8>(p, x, packed, bias, y, M, K, N, counters, partials, stream);
+    else launch_mr<kBF16, 16>(p, x, packed, bias, y, M, K, N, counters, partials, stream);
 }
 
 }  // namespace
 
 GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N) {
     GemmPlan p;
-    p.mr = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
-    p.tiles_m = (int)((M + 16 * p.mr - 1) / (16 * p.mr));
     const int64_t NB = N / kColsPerBlock;
     const int64_t KB = K / kRowsPerBlock;
+    p.mr = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
+    // 256-row tiles (half the decode work per MFMA) when M has at least two full
+    // 128-row tiles and the 256 x 256 tiles alone give every CU 4 of them
+    if (M >= 256 && ((M + 255) / 256) * ((NB + 4 * kWaves - 1) / (4 * kWaves)) >= 4 * kTargetWorkgroups) p.mr = 16;
+    p.tiles_m = (int)((M + 16 * p.mr - 1) / (16 * p.mr));
     // widest column tile that still occupies 3/4 of the CUs, else the narrowest (a wider
     // tile decodes each weight for as many rows but reads the activations less often)
     p.cbw = 1;
