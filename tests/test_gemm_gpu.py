@@ -266,10 +266,9 @@ def test_gemv_needs_no_workspace(w):
 
 
 @pytest.mark.parametrize("M", [300, 512])
-def test_gemm_256_row_tiles(w, M):
-    # a wide N (8192 column blocks, 2 x 512 tiles of 256 x 256) gives the 256-row tiles
-    # with the two-stage ring and register metadata; M = 300 leaves a ragged second row
-    # tile; sampled column blocks
+def test_gemm_wide_n(w, M):
+    # LM-head width (8192 column blocks, 512 column tiles of 256) with a short K;
+    # M = 300 leaves a ragged third row tile; sampled column blocks
     ws = synth.make_custom(800 + M, M, 256, 131072, "bf16", 128)
     packed = pack_on_gpu(w, ws)
     got = y_to_f64(run(w, ws, packed, ws.x_bits[M], path="mfma"), "bf16")

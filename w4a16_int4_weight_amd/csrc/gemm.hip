@@ -9,15 +9,19 @@
 // weight is dequantised once per workgroup tile of up to 128 rows, straight from
 // the packed layout, which is already in MFMA operand order: no per-call shuffle.
 //
-// Workgroup: 4 waves side by side along N, each owning 4 column blocks (64
+// Workgroup: 4 waves side by side along N, each owning CBW column blocks (16 CBW
 // columns) and all 16*MR rows of the tile. Per 128-row block of K:
 //   * a 3-stage LDS ring holds, per k block, the activation tile [16*MR x 128]
 //     (16-byte chunks XOR-swizzled by row, so the fragment reads of a wave spread
-//     over all banks), the workgroup's 16 blocks of packed codes and its metadata;
+//     over all banks), the workgroup's blocks of packed codes and its metadata;
 //     the ring is filled by direct global -> LDS copies, two k blocks ahead;
 //   * per 32-row step a wave decodes one word per column block into 8 fp16/bf16
-//     weights (q - z) * s, each rounded once to the dtype, and issues MR x 4 MFMAs
-//     (16x16x32, fp32 accumulators);
+//     weights (q - z) * s, each rounded once to the dtype, and issues MR x CBW
+//     MFMAs (16x16x32, fp32 accumulators). For bf16 the decoding of the next
+//     operand is cut into single-instruction slices placed between the MFMAs of the
+//     current one (a wave hides about two VALU instructions behind each MFMA, and
+//     the decode is ~3 per MFMA at MR = 8: issued in a burst it stalled the matrix
+//     cores);
 //   * the MFMA is given the weights as its first operand and the activations as its
 //     second, so it produces the transposed tile: each lane then holds 4 adjacent
 //     output columns of one row and the epilogue writes 8 bytes per lane.
@@ -130,21 +134,14 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // One stage of the LDS ring: the activation tile of one 128-row block of K, the
-// workgroup's blocks of packed codes (4 waves x CBW) and, with kMeta, its metadata
-// words (64 per wave, of which the first 16 * CBW are used). Without kMeta (the
-// 256-row tiles, whose two stages fill the 160 KiB of LDS) each lane loads its
-// metadata words into registers instead.
-template <int BM, int CBW, bool kMeta>
+// workgroup's blocks of packed codes (4 waves x CBW) and its metadata words (64 per
+// wave, of which the first 16 * CBW are used).
+template <int BM, int CBW>
 struct Stage {
     // [BM rows][16 chunks of 16 bytes], chunk j of row r stored at chunk j ^ (r % 16)
     uint4 x[BM * 16];
     uint4 w[kWaves * CBW * 64];             // 1 KiB per block, as in global memory
     uint32_t meta[kWaves * 64];
-};
-template <int BM, int CBW>
-struct Stage<BM, CBW, false> {
-    uint4 x[BM * 16];
-    uint4 w[kWaves * CBW * 64];
 };
 
 // Workgroup tile: 16*MR rows x 64*CBW columns, 4 waves side by side along N, each
@@ -159,15 +156,11 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     constexpr int BM = 16 * MR;
     constexpr int kSlabsPerWave = BM / 4 / kWaves;      // 1 KiB slabs (4 rows) of the x tile per wave
     static_assert(kSlabsPerWave * 4 * kWaves == BM, "x tile must split over the waves");
-    // 256-row tiles: two stages (one k block ahead), metadata in registers; otherwise
-    // three stages (two ahead) with the metadata staged in LDS as well
-    constexpr int kStages = MR == 16 ? 2 : 3;
-    constexpr bool kMetaInLds = kStages == 3;
-    constexpr int kDmaPerStage = kSlabsPerWave + CBW + (kMetaInLds ? 1 : 0);   // copies per wave per stage
-    using StageT = Stage<BM, CBW, kMetaInLds>;
+    constexpr int kDmaPerStage = kSlabsPerWave + CBW + 1;   // copies per wave per stage
+    constexpr int kStages = 3;
+    using StageT = Stage<BM, CBW>;
     __shared__ StageT ring[kStages];
-    // split-K flag, in ring memory (written only after every wave has left the main loop)
-    int& last_split = *reinterpret_cast<int*>(&ring[0]);
+    __shared__ int last_split;
 
     // XCD-aware order: ids id, id+8, id+16, ... share an XCD; they take the M tiles and
     // the K splits of one N tile. Ids past the last N tile (grid padding) exit.
@@ -198,8 +191,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     // stored chunk lane%16) fetches logical chunk (lane%16) ^ (row%16). Rows past M
     // read row M-1 and columns past N read column N-1: they only feed outputs that
     // are not written.
-    // (32-bit element offsets rather than pointers: M * K <= 2^32 and K * N / 32 < 2^32,
-    // and they leave registers for the 256-row tiles)
+    // (32-bit element offsets rather than pointers: M * K <= 2^32 and K * N / 32 < 2^32)
     uint32_t xoff[kSlabsPerWave];
 #pragma unroll
     for (int t = 0; t < kSlabsPerWave; ++t) {
@@ -219,17 +211,6 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
                            (size_t)(ncol < N ? ncol : N - 1) * KBP;
     const uint32_t ring_base = lds_addr(&ring[0]);
 
-    // metadata in registers: lane (c, h) takes column 16 (nbw + j) + c of each block j
-    const uint32_t* mbase = reinterpret_cast<const uint32_t*>(packed + (size_t)K * N / 2);
-    uint32_t moff[kMetaInLds ? 1 : CBW];
-    if constexpr (!kMetaInLds) {
-#pragma unroll
-        for (int j = 0; j < CBW; ++j) {
-            const int nbj = nbw + j < NB ? nbw + j : NB - 1;
-            moff[j] = (uint32_t)(nbj * kColsPerBlock + c) * (uint32_t)KBP;
-        }
-    }
-
     auto issue = [&](int slot, int kb) {
         const uint32_t st = ring_base + (uint32_t)slot * (uint32_t)sizeof(StageT);
 #pragma unroll
@@ -239,7 +220,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
 #pragma unroll
         for (int j = 0; j < CBW; ++j)
             dma16(wbase + woff[j] + (size_t)kb * 64, st + (uint32_t)offsetof(StageT, w) + (uint32_t)(w * CBW + j) * 1024u);
-        if constexpr (kMetaInLds) dma4(msrc + kb, st + (uint32_t)offsetof(StageT, meta) + (uint32_t)w * 256u);
+        dma4(msrc + kb, st + (uint32_t)offsetof(StageT, meta) + (uint32_t)w * 256u);
     };
 
     f32x4 acc[MR][CBW];
@@ -248,60 +229,104 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
 #pragma unroll
         for (int j = 0; j < CBW; ++j) acc[r][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    uint32_t md[CBW], mdn[CBW];        // register metadata (two-stage ring only)
     issue(0, kb_begin);
-    if constexpr (kMetaInLds) {
-        if (nkb > 1) issue(1, kb_begin + 1);
-    } else {
-#pragma unroll
-        for (int j = 0; j < CBW; ++j) mdn[j] = mbase[moff[j] + kb_begin];
-    }
+    if (nkb > 1) issue(1, kb_begin + 1);
     for (int t = 0; t < nkb; ++t) {
-        if constexpr (kMetaInLds) {
-            // this wave's copies of step t are done (step t+1's may be in flight); the
-            // barrier makes every wave's copies visible and retires the reads of step
-            // t-1, whose slot is then refilled with step t+2
-            if (t + 1 < nkb) wait_vmcnt<kDmaPerStage>();
-            else wait_vmcnt<0>();
-            lds_barrier();
-            if (t + 2 < nkb) issue((t + 2) % kStages, kb_begin + t + 2);
-        } else {
-            // step t's copies and metadata have landed; after the barrier the other
-            // slot (step t-1) is free for step t+1
-            wait_vmcnt<0>();
-            lds_barrier();
-#pragma unroll
-            for (int j = 0; j < CBW; ++j) md[j] = mdn[j];
-            if (t + 1 < nkb) {
-                issue((t + 1) % kStages, kb_begin + t + 1);
-#pragma unroll
-                for (int j = 0; j < CBW; ++j) mdn[j] = mbase[moff[j] + kb_begin + t + 1];
-            }
-        }
+        // this wave's copies of step t are done (step t+1's may be in flight); the
+        // barrier makes every wave's copies visible and retires the reads of step
+        // t-1, whose slot is then refilled with step t+2
+        if (t + 1 < nkb) wait_vmcnt<kDmaPerStage>();
+        else wait_vmcnt<0>();
+        lds_barrier();
+        if (t + 2 < nkb) issue((t + 2) % kStages, kb_begin + t + 2);
 
         const StageT& st = ring[t % kStages];
         Dequant<kBF16> dq[CBW];
         uint4 wq[CBW];
 #pragma unroll
         for (int j = 0; j < CBW; ++j) {
-            if constexpr (kMetaInLds) dq[j] = Dequant<kBF16>(st.meta[w * 64 + 16 * j + c]);
-            else dq[j] = Dequant<kBF16>(md[j]);
+            dq[j] = Dequant<kBF16>(st.meta[w * 64 + 16 * j + c]);
             wq[j] = st.w[(w * CBW + j) * 64 + lane];
         }
-        // per 32-row step: the MR activation fragments, then column block by column
-        // block one decoded operand and its MR MFMAs (decoding the next block overlaps
-        // the previous block's MFMAs)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int chunk = (4 * i + h) ^ c;              // row 16 r + c has row % 16 == c
+        if constexpr (kBF16) {
+            // Unit (i, j) = 32-row step i, column block j: MR MFMAs on one decoded
+            // operand b. While they run, the next unit's word is decoded in independent
+            // slices, one after each MFMA (masks; two byte converts; two fmas one slot
+            // later; a pair pack after both fmas), and in a step's last unit each
+            // fragment a[r] is refilled with the next step's right after its last use.
+            // sched_barrier(0) after each slot keeps this order: one wave hides about
+            // two VALU instructions behind each MFMA, not a burst of twenty.
             uint4 a[MR];
 #pragma unroll
-            for (int r = 0; r < MR; ++r) a[r] = st.x[(16 * r + c) * 16 + chunk];
+            for (int r = 0; r < MR; ++r) a[r] = st.x[(16 * r + c) * 16 + (h ^ c)];
+            uint4 b = dq[0](pick(wq[0], 0));
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int j = 0; j < CBW; ++j) {
-                const uint4 b = dq[j](pick(wq[j], i));
+            for (int i = 0; i < 4; ++i) {
 #pragma unroll
-                for (int r = 0; r < MR; ++r) acc[r][j] = mfma16x16x32<kBF16>(b, a[r], acc[r][j]);
+                for (int j = 0; j < CBW; ++j) {
+                    const bool has_next = !(i == 3 && j == CBW - 1);
+                    const int jn = j + 1 < CBW ? j + 1 : 0;
+                    const int in = j + 1 < CBW ? i : i + 1;
+                    const uint32_t dn = has_next ? pick(wq[jn], in & 3) : 0u;
+                    const float sn = dq[jn].s, zn = dq[jn].nzs;
+                    uint32_t lo = 0u, hi = 0u;
+                    float cv[8], fv[8];
+                    uint32_t o[4] = {0u, 0u, 0u, 0u};
+                    const int chunk = (4 * (i + 1) + h) ^ c;
+#pragma unroll
+                    for (int r = 0; r < MR; ++r) {
+                        acc[r][j] = mfma16x16x32<kBF16>(b, a[r], acc[r][j]);
+                        if (has_next) {
+                            // 12 ticks spread over the MR slots: 0 masks, 1..4 converts
+                            // (values v = 2(t-1), +1), 4..7 fmas (v = 2(t-4), +1), 8..11 packs.
+                            // Values 0..3 are the bytes of lo (rows 0,4,1,5), 4..7 of hi
+                            // (rows 2,6,3,7); output word e holds rows (2e, 2e+1).
+                            constexpr int kTicks = 12;
+#pragma unroll
+                            for (int tk = r * kTicks / MR; tk < (r + 1) * kTicks / MR; ++tk) {
+                                if (tk == 0) {
+                                    lo = dn & 0x0F0F0F0Fu;
+                                    hi = (dn >> 4) & 0x0F0F0F0Fu;
+                                    asm volatile("" : "+v"(lo), "+v"(hi));   // one byte convert per value
+                                } else if (tk <= 4) {
+                                    const int v0 = 2 * (tk - 1), v1 = v0 + 1;
+                                    cv[v0] = (float)((((v0 < 4) ? lo : hi) >> (8 * (v0 & 3))) & 0xFFu);
+                                    cv[v1] = (float)((((v1 < 4) ? lo : hi) >> (8 * (v1 & 3))) & 0xFFu);
+                                }
+                                if (tk >= 4 && tk <= 7) {
+                                    const int v0 = 2 * (tk - 4), v1 = v0 + 1;
+                                    fv[v0] = fmaf(cv[v0], sn, zn);
+                                    fv[v1] = fmaf(cv[v1], sn, zn);
+                                }
+                                if (tk >= 8) {
+                                    const int e = tk - 8;
+                                    const int va = e == 0 ? 0 : e == 1 ? 4 : e == 2 ? 1 : 5;
+                                    o[e] = pack2_rne<true>(fv[va], fv[va + 2]);
+                                }
+                            }
+                        }
+                        if (j == CBW - 1 && i < 3) a[r] = st.x[(16 * r + c) * 16 + chunk];
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    if (has_next) b = make_uint4(o[0], o[1], o[2], o[3]);
+                }
+            }
+        } else {
+            // fp16: per 32-row step the MR fragments, then column block by column block
+            // one decoded operand (three packed-fp16 instructions per pair) and its MFMAs
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int chunk = (4 * i + h) ^ c;          // row 16 r + c has row % 16 == c
+                uint4 a[MR];
+#pragma unroll
+                for (int r = 0; r < MR; ++r) a[r] = st.x[(16 * r + c) * 16 + chunk];
+#pragma unroll
+                for (int j = 0; j < CBW; ++j) {
+                    const uint4 b = dq[j](pick(wq[j], i));
+#pragma unroll
+                    for (int r = 0; r < MR; ++r) acc[r][j] = mfma16x16x32<kBF16>(b, a[r], acc[r][j]);
+                }
             }
         }
     }
@@ -409,8 +434,7 @@ void launch_typed(const GemmPlan& p, const uint16_t* x, const uint8_t* packed, c
     if (p.mr == 1) launch_mr<kBF16, 1>(p, x, packed, bias, y, M, K, N, counters, partials, stream);
     else if (p.mr == 2) launch_mr<kBF16, 2>(p, x, packed, bias, y, M, K, N, counters, partials, stream);
     else if (p.mr == 4) launch_mr<kBF16, 4>(p, x, packed, bias, y, M, K, N, counters, partials, stream);
-    else if (p.mr == 8) launch_mr<kBF16, 8>(p, x, packed, bias, y, M, K, N, counters, partials, stream);
-    else launch_mr<kBF16, 16>(p, x, packed, bias, y, M, K, N, counters, partials, stream);
+    else launch_mr<kBF16, 8>(p, x, packed, bias, y, M, K, N, counters, partials, stream);
 }
 
 }  // namespace
@@ -420,9 +444,6 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N) {
     const int64_t NB = N / kColsPerBlock;
     const int64_t KB = K / kRowsPerBlock;
     p.mr = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
-    // 256-row tiles (half the decode work per MFMA) when M has at least two full
-    // 128-row tiles and the 256 x 256 tiles alone give every CU 4 of them
-    if (M >= 256 && ((M + 255) / 256) * ((NB + 4 * kWaves - 1) / (4 * kWaves)) >= 4 * kTargetWorkgroups) p.mr = 16;
     p.tiles_m = (int)((M + 16 * p.mr - 1) / (16 * p.mr));
     // widest column tile that still occupies 3/4 of the CUs, else the narrowest (a wider
     // tile decodes each weight for as many rows but reads the activations less often)
