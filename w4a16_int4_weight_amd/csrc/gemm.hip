@@ -107,14 +107,26 @@ __device__ __forceinline__ uint32_t pick(const uint4 v, int i) {
 // like loads but occupy no registers, so several k blocks can be in flight. They are
 // issued through inline assembly so that the compiler does not guard every later LDS
 // read with a wait for all of them: the kernel waits for exactly the copies it needs.
+// Scalar-base form: a wave-uniform 64-bit base in SGPRs plus a loop-invariant 32-bit
+// byte offset per lane. (With a 64-bit address per copy the compiler rebuilt every
+// address in one VGPR pair, so each copy waited until the previous one had read it:
+// ~55 cycles a copy, a sixth of the k loop.)
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(lds) : "memory", "m0");
+// (readfirstlane returns int: each half goes through uint32_t so that a low half
+// with bit 31 set is not sign-extended over the high half)
+__device__ __forceinline__ const uint8_t* uniform_ptr(const void* p) {
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<const uint8_t*>((hi << 32) | lo);
 }
-__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" : : "v"(g), "s"(lds) : "memory", "m0");
+__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(base), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const uint8_t* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" : : "v"(voff), "s"(base), "s"(lds) : "memory", "m0");
 }
 
 // Workgroup barrier that is also a compiler barrier for memory operations, without
@@ -186,41 +198,52 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     const int m0 = m_tile * BM;
     const int nbw = (n_tile * kWaves + w) * CBW;               // first column block of this wave
 
-    // ---- per-lane sources of one stage's copies (k block kb adds kb * stride) ----
+    // ---- sources of one stage's copies: wave-uniform bases (k block kb adds kb * stride)
+    // plus per-lane byte offsets ----
     // x: slab `slab` covers tile rows 4 slab .. 4 slab + 3; lane (row 4 slab + lane/16,
     // stored chunk lane%16) fetches logical chunk (lane%16) ^ (row%16). Rows past M
     // read row M-1 and columns past N read column N-1: they only feed outputs that
-    // are not written.
-    // (32-bit element offsets rather than pointers: M * K <= 2^32 and K * N / 32 < 2^32)
+    // are not written. Offsets from the tile's first row stay below 2^28 (128 rows of
+    // at most 2^20 elements).
+    const uint8_t* xbase = uniform_ptr(x + (size_t)m0 * K);
     uint32_t xoff[kSlabsPerWave];
 #pragma unroll
     for (int t = 0; t < kSlabsPerWave; ++t) {
         const int row = 4 * (w * kSlabsPerWave + t) + (lane >> 4);
         const int m = m0 + row < M ? m0 + row : M - 1;
-        xoff[t] = (uint32_t)m * (uint32_t)K + 8u * (uint32_t)((lane & 15) ^ (row & 15));
+        xoff[t] = 2u * ((uint32_t)(m - m0) * (uint32_t)K + 8u * (uint32_t)((lane & 15) ^ (row & 15)));
     }
+    // codes: this wave's blocks from its first (clamped) column block
+    const int nbw0 = nbw < NB ? nbw : NB - 1;
+    const uint8_t* wbase = uniform_ptr(packed + (size_t)nbw0 * KB * kBlockBytes);
     uint32_t woff[CBW];
 #pragma unroll
     for (int j = 0; j < CBW; ++j) {
         const int nbj = nbw + j < NB ? nbw + j : NB - 1;
-        woff[j] = (uint32_t)nbj * (uint32_t)KB * 64u + (uint32_t)lane;
+        woff[j] = (uint32_t)(nbj - nbw0) * (uint32_t)KB * kBlockBytes + 16u * (uint32_t)lane;
     }
-    const uint4* wbase = reinterpret_cast<const uint4*>(packed);
-    const int ncol = nbw * kColsPerBlock + (lane < 16 * CBW ? lane : 0);   // this wave's columns
-    const uint32_t* msrc = reinterpret_cast<const uint32_t*>(packed + (size_t)K * N / 2) +
-                           (size_t)(ncol < N ? ncol : N - 1) * KBP;
+    // metadata: column words of this wave's columns (lanes past 16 * CBW repeat one)
+    const int col0 = nbw * kColsPerBlock < N ? nbw * kColsPerBlock : N - kColsPerBlock;
+    const int ncol = nbw * kColsPerBlock + (lane < 16 * CBW ? lane : 0);
+    const uint8_t* mbase = uniform_ptr(packed + (size_t)K * N / 2 + (size_t)col0 * KBP * 4);
+    const uint32_t moff = (uint32_t)((ncol < N ? ncol : N - 1) - col0) * (uint32_t)KBP * 4u;
     const uint32_t ring_base = lds_addr(&ring[0]);
 
-    auto issue = [&](int slot, int kb) {
+    // copy q (0 .. kDmaPerStage-1) of k block kb into ring slot `slot`
+    auto issue_one = [&](int slot, int kb, int q) {
         const uint32_t st = ring_base + (uint32_t)slot * (uint32_t)sizeof(StageT);
+        if (q < kSlabsPerWave)
+            dma16(xbase + (size_t)kb * kRowsPerBlock * 2, xoff[q],
+                  st + (uint32_t)offsetof(StageT, x) + (uint32_t)(w * kSlabsPerWave + q) * 1024u);
+        else if (q < kSlabsPerWave + CBW)
+            dma16(wbase + (size_t)kb * kBlockBytes, woff[q - kSlabsPerWave],
+                  st + (uint32_t)offsetof(StageT, w) + (uint32_t)(w * CBW + q - kSlabsPerWave) * 1024u);
+        else
+            dma4(mbase + (size_t)kb * 4, moff, st + (uint32_t)offsetof(StageT, meta) + (uint32_t)w * 256u);
+    };
+    auto issue = [&](int slot, int kb) {
 #pragma unroll
-        for (int t = 0; t < kSlabsPerWave; ++t)
-            dma16(x + xoff[t] + (size_t)kb * kRowsPerBlock,
-                  st + (uint32_t)offsetof(StageT, x) + (uint32_t)(w * kSlabsPerWave + t) * 1024u);
-#pragma unroll
-        for (int j = 0; j < CBW; ++j)
-            dma16(wbase + woff[j] + (size_t)kb * 64, st + (uint32_t)offsetof(StageT, w) + (uint32_t)(w * CBW + j) * 1024u);
-        dma4(msrc + kb, st + (uint32_t)offsetof(StageT, meta) + (uint32_t)w * 256u);
+        for (int q = 0; q < kDmaPerStage; ++q) issue_one(slot, kb, q);
     };
 
     f32x4 acc[MR][CBW];
@@ -238,6 +261,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
         if (t + 1 < nkb) wait_vmcnt<kDmaPerStage>();
         else wait_vmcnt<0>();
         lds_barrier();
+        // The copies queue at the CU's address unit (about 16 cycles per 1 KiB copy, the
+        // 4 waves' together) and each wave waits until its own are accepted: about a
+        // sixth of the loop. Spreading them between the MFMAs measured slower.
         if (t + 2 < nkb) issue((t + 2) % kStages, kb_begin + t + 2);
 
         const StageT& st = ring[t % kStages];
