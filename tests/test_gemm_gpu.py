@@ -275,3 +275,19 @@ def test_gemm_wide_n(w, M):
     cols = sample_column_blocks(ws.N, 128, seed=M)
     err = ogemm.max_rel_error(got[:, cols], oracle_y(ws, ws.x_bits[M], cols))
     assert err <= TOL
+
+
+@pytest.mark.parametrize("M,N,dtype", [(3000, 2608, "bf16"), (3000, 2608, "fp16"), (20, 131072, "bf16")])
+def test_gemm_eight_wave_tiles(w, M, N, dtype):
+    # 256-column tiles run as 8 waves of 2 column blocks: N = 2608 (163 blocks) leaves
+    # a last tile whose later waves lie wholly past N; M = 20 is the shortest such tile
+    # (32 rows: one activation copy per wave). Wide N on sampled column blocks.
+    ws = synth.make_custom(900 + M % 97, M, 256, N, dtype, 128)
+    packed = pack_on_gpu(w, ws)
+    got = y_to_f64(run(w, ws, packed, ws.x_bits[M], path="mfma"), dtype)
+    if N > 16384:
+        cols = sample_column_blocks(N, 128, seed=M)
+        err = ogemm.max_rel_error(got[:, cols], oracle_y(ws, ws.x_bits[M], cols))
+    else:
+        err = ogemm.max_rel_error(got, oracle_y(ws, ws.x_bits[M]))
+    assert err <= TOL

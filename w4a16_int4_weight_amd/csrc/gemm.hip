@@ -9,8 +9,10 @@
 // weight is dequantised once per workgroup tile of up to 128 rows, straight from
 // the packed layout, which is already in MFMA operand order: no per-call shuffle.
 //
-// Workgroup: 4 waves side by side along N, each owning CBW column blocks (16 CBW
-// columns) and all 16*MR rows of the tile. Per 128-row block of K:
+// Workgroup: 4 or 8 waves side by side along N, each owning CBW column blocks (16 CBW
+// columns) and all 16*MR rows of the tile; the 256-column tile runs as 8 waves of
+// 2 blocks, two per SIMD, so that one computes while the other waits on its copies
+// or the barrier. Per 128-row block of K:
 //   * a 3-stage LDS ring holds, per k block, the activation tile [16*MR x 128]
 //     (16-byte chunks XOR-swizzled by row, so the fragment reads of a wave spread
 //     over all banks), the workgroup's blocks of packed codes and its metadata;
@@ -37,8 +39,6 @@
 namespace w4a16 {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
 constexpr int kXcds = 8;
 
 // Decode one tile word (8 codes of one column, rows in slot order) into the operand
@@ -146,22 +146,22 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // One stage of the LDS ring: the activation tile of one 128-row block of K, the
-// workgroup's blocks of packed codes (4 waves x CBW) and its metadata words (64 per
+// workgroup's blocks of packed codes (W waves x CBW) and its metadata words (64 per
 // wave, of which the first 16 * CBW are used).
-template <int BM, int CBW>
+template <int BM, int CBW, int W>
 struct Stage {
     // [BM rows][16 chunks of 16 bytes], chunk j of row r stored at chunk j ^ (r % 16)
     uint4 x[BM * 16];
-    uint4 w[kWaves * CBW * 64];             // 1 KiB per block, as in global memory
-    uint32_t meta[kWaves * 64];
+    uint4 w[W * CBW * 64];                  // 1 KiB per block, as in global memory
+    uint32_t meta[W * 64];
 };
 
 // Workgroup tile: 16*MR rows x 64*CBW columns, 4 waves side by side along N, each
 // owning CBW column blocks and all rows. `splits` > 1 splits the K range over
 // workgroups; their fp32 partial tiles meet in `workspace` and the last workgroup of
 // a tile to finish adds them in split order (deterministic) and writes y.
-template <bool kBF16, int MR, int CBW>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(
+template <bool kBF16, int MR, int CBW, int kWaves>
+__global__ __launch_bounds__(64 * kWaves) void gemm_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed, const uint16_t* __restrict__ bias,
     uint16_t* __restrict__ y, int M, int K, int N, int tiles_m, int tiles_n, int splits,
     uint32_t* __restrict__ counters, float* __restrict__ partials) {
@@ -170,7 +170,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     static_assert(kSlabsPerWave * 4 * kWaves == BM, "x tile must split over the waves");
     constexpr int kDmaPerStage = kSlabsPerWave + CBW + 1;   // copies per wave per stage
     constexpr int kStages = 3;
-    using StageT = Stage<BM, CBW>;
+    using StageT = Stage<BM, CBW, kWaves>;
     __shared__ StageT ring[kStages];
     __shared__ int last_split;
 
@@ -437,21 +437,27 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
 
 constexpr int kTargetWorkgroups = 256;   // one per CU
 
-template <bool kBF16, int MR, int CBW>
+template <bool kBF16, int MR, int CBW, int W>
 void launch_cfg(const GemmPlan& p, const uint16_t* x, const uint8_t* packed, const uint16_t* bias, uint16_t* y,
                 int M, int K, int N, uint32_t* counters, float* partials, hipStream_t stream) {
     const int tiles_n_pad = (p.tiles_n + kXcds - 1) / kXcds * kXcds;
     const dim3 grid((unsigned)(p.tiles_m * p.splits * tiles_n_pad));
-    hipLaunchKernelGGL((gemm_kernel<kBF16, MR, CBW>), grid, dim3(kThreads), 0, stream, x, packed, bias, y, M, K, N,
+    hipLaunchKernelGGL((gemm_kernel<kBF16, MR, CBW, W>), grid, dim3(64 * W), 0, stream, x, packed, bias, y, M, K, N,
                        p.tiles_m, p.tiles_n, p.splits, counters, partials);
 }
 
 template <bool kBF16, int MR>
 void launch_mr(const GemmPlan& p, const uint16_t* x, const uint8_t* packed, const uint16_t* bias, uint16_t* y,
                int M, int K, int N, uint32_t* counters, float* partials, hipStream_t stream) {
-    if (p.cbw == 4) launch_cfg<kBF16, MR, 4>(p, x, packed, bias, y, M, K, N, counters, partials, stream);
-    else if (p.cbw == 2) launch_cfg<kBF16, MR, 2>(p, x, packed, bias, y, M, K, N, counters, partials, stream);
-    else launch_cfg<kBF16, MR, 1>(p, x, packed, bias, y, M, K, N, counters, partials, stream);
+    if constexpr (MR >= 2) {
+        if (p.waves == 8) {
+            launch_cfg<kBF16, MR, 2, 8>(p, x, packed, bias, y, M, K, N, counters, partials, stream);
+            return;
+        }
+    }
+    if (p.cbw == 4) launch_cfg<kBF16, MR, 4, 4>(p, x, packed, bias, y, M, K, N, counters, partials, stream);
+    else if (p.cbw == 2) launch_cfg<kBF16, MR, 2, 4>(p, x, packed, bias, y, M, K, N, counters, partials, stream);
+    else launch_cfg<kBF16, MR, 1, 4>(p, x, packed, bias, y, M, K, N, counters, partials, stream);
 }
 
 template <bool kBF16>
@@ -471,16 +477,25 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N) {
     const int64_t KB = K / kRowsPerBlock;
     p.mr = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
     p.tiles_m = (int)((M + 16 * p.mr - 1) / (16 * p.mr));
-    // widest column tile that still occupies 3/4 of the CUs, else the narrowest (a wider
-    // tile decodes each weight for as many rows but reads the activations less often)
+    // widest column tile (4 waves x cbw blocks) that still occupies 3/4 of the CUs, else
+    // the narrowest (a wider tile decodes each weight for as many rows but reads the
+    // activations less often)
+    p.waves = 4;
     p.cbw = 1;
     for (int cbw : {4, 2}) {
-        if (p.tiles_m * ((NB + kWaves * cbw - 1) / (kWaves * cbw)) >= kTargetWorkgroups * 3 / 4) {
+        if (p.tiles_m * ((NB + 4 * cbw - 1) / (4 * cbw)) >= kTargetWorkgroups * 3 / 4) {
             p.cbw = cbw;
             break;
         }
     }
-    p.tiles_n = (int)((NB + kWaves * p.cbw - 1) / (kWaves * p.cbw));
+    // the 256-column tile as 8 waves of 2 blocks rather than 4 of 4: two waves per SIMD,
+    // so one computes while the other waits on its copies, the barrier or LDS (needs
+    // 16 * mr >= 32 rows for the activation copies to split over 8 waves)
+    if (p.cbw == 4 && p.mr >= 2) {
+        p.waves = 8;
+        p.cbw = 2;
+    }
+    p.tiles_n = (int)((NB + p.waves * p.cbw - 1) / (p.waves * p.cbw));
     const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
     // too few tiles for the chip: split K, at least 4 row blocks per split
     p.splits = 1;

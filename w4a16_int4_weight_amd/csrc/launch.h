@@ -29,7 +29,8 @@ hipError_t launch_gemv(const uint16_t* x, const uint8_t* packed, const uint16_t*
 // from the shape; workspace_bytes > 0 when K is split over workgroups.
 struct GemmPlan {
     int mr;            // row fragments of 16 per tile (tile rows = 16 * mr)
-    int cbw;           // 16-column blocks per wave (tile columns = 64 * cbw)
+    int cbw;           // 16-column blocks per wave (tile columns = 16 * waves * cbw)
+    int waves;         // waves per workgroup, side by side along N (4 or 8)
     int tiles_m, tiles_n;
     int splits;        // workgroups per tile along K
     size_t workspace_bytes;   // [tile counters, 256-byte aligned][splits x M x N fp32 partials]
