@@ -265,6 +265,27 @@ def test_gemv_needs_no_workspace(w):
     assert ogemm.max_rel_error(y_to_f64(y, "bf16"), oracle_y(ws, ws.x_bits[8])) <= TOL
 
 
+@pytest.mark.parametrize("K,M,dtype", [(2048, 1, "bf16"), (2048, 8, "bf16"), (2048, 3, "fp16"),
+                                       (512, 2, "bf16"), (1024, 5, "bf16")])
+def test_gemv_several_column_blocks_per_workgroup(w, K, M, dtype):
+    # N = 13280 (830 column blocks) runs 4 blocks per workgroup: the last workgroup has
+    # 2 blocks past N, which repeat the last block and must store nothing. K = 512 has
+    # one wave per block (no K split), K = 1024 two.
+    print(f"gemv 4 blocks per workgroup K={K} M={M} {dtype}", flush=True)
+    N = 13280
+    ws = synth.make_custom(1000 + K // 128 + M, M, K, N, dtype, 128)
+    packed = pack_on_gpu(w, ws)
+    x = bits_to_device(ws.x_bits[M], dtype)
+    pad = 4096
+    buf = torch.full((M * N + 2 * pad,), -7.0, dtype=TORCH_DTYPE[dtype], device=DEV)
+    y = buf[pad:pad + M * N].view(M, N)
+    w.w4a16_gemm_ex(x, packed, N, 128, y=y, path="gemv")
+    torch.cuda.synchronize()
+    b = buf.cpu()
+    assert torch.all(b[:pad] == -7.0) and torch.all(b[-pad:] == -7.0), "write outside y"
+    assert ogemm.max_rel_error(y_to_f64(y, dtype), oracle_y(ws, ws.x_bits[M])) <= TOL
+
+
 @pytest.mark.parametrize("M", [300, 512])
 def test_gemm_wide_n(w, M):
     # LM-head width (8192 column blocks, 512 column tiles of 256) with a short K;

@@ -15,7 +15,8 @@ hipError_t launch_repack(const int32_t* qweight, const int32_t* qzeros, const ui
 // workgroup; no workspace).
 struct GemvPlan {
     int kb_per_wave;       // row blocks per wave (multiple of 4)
-    int waves;             // waves per workgroup
+    int waves;             // waves per workgroup (waves_k per column block)
+    int waves_k;           // waves splitting K for one 16-column block
     bool staged;           // activations staged in LDS
     int chunks_per_thread; // 16-byte activation chunks each thread stages
     size_t lds_bytes;
