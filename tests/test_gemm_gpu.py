@@ -268,11 +268,11 @@ def test_gemv_needs_no_workspace(w):
 @pytest.mark.parametrize("K,M,dtype", [(2048, 1, "bf16"), (2048, 8, "bf16"), (2048, 3, "fp16"),
                                        (512, 2, "bf16"), (1024, 5, "bf16")])
 def test_gemv_several_column_blocks_per_workgroup(w, K, M, dtype):
-    # N = 13280 (830 column blocks) runs 4 blocks per workgroup: the last workgroup has
-    # 2 blocks past N, which repeat the last block and must store nothing. K = 512 has
+    # N = 13296 (831 column blocks) runs 2 blocks per workgroup: the last workgroup has
+    # a block past N, which repeats the last block and must store nothing. K = 512 has
     # one wave per block (no K split), K = 1024 two.
-    print(f"gemv 4 blocks per workgroup K={K} M={M} {dtype}", flush=True)
-    N = 13280
+    print(f"gemv 2 blocks per workgroup K={K} M={M} {dtype}", flush=True)
+    N = 13296
     ws = synth.make_custom(1000 + K // 128 + M, M, K, N, dtype, 128)
     packed = pack_on_gpu(w, ws)
     x = bits_to_device(ws.x_bits[M], dtype)

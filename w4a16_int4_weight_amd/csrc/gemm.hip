@@ -361,54 +361,78 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(
     if (splits > 1) {
         // Publish this split's partial tile with agent-scope stores (coherent across the
         // XCDs' L2s without writing back a whole L2), wait until they have completed,
-        // then count the tile's finished splits; the last split to arrive reads all
-        // partials back (agent-scope loads), adds them in split order and writes y.
-        auto part = [&](int sp, int m, int n) {
-            return reinterpret_cast<uint64_t*>(partials + ((size_t)sp * M + m) * N + n);
+        // then count the tile's finished splits; the last split to arrive reads the
+        // other splits' partials back (agent-scope loads), adds them in split order and
+        // writes y. Partials are kept per (tile, split, wave, fragment) in the lanes'
+        // own order, 1 KiB per fragment: every store and load instruction covers 512
+        // contiguous bytes (whole cache lines), the low and high halves of the lanes'
+        // 16 bytes in two such runs.
+        const int tile = m_tile * tiles_n + n_tile;
+        auto part = [&](int sp, int f) {
+            const size_t slot = (((size_t)tile * splits + sp) * kWaves + w) * (MR * CBW) + f;
+            return reinterpret_cast<uint64_t*>(reinterpret_cast<uint8_t*>(partials) + slot * 1024) + lane;
         };
 #pragma unroll
         for (int j = 0; j < CBW; ++j) {
-            if (nbw + j >= NB) continue;
-            const int n = (nbw + j) * kColsPerBlock + 4 * h;
 #pragma unroll
             for (int r = 0; r < MR; ++r) {
-                const int m = m0 + 16 * r + c;
-                if (m < M) {
-                    uint64_t* p = part(split, m, n);
-                    const f32x4 v = acc[r][j];
-                    __hip_atomic_store(p, __builtin_bit_cast(uint64_t, f32x2{v[0], v[1]}), __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-                    __hip_atomic_store(p + 1, __builtin_bit_cast(uint64_t, f32x2{v[2], v[3]}), __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-                }
+                uint64_t* q = part(split, r * CBW + j);
+                const f32x4 v = acc[r][j];
+                __hip_atomic_store(q, __builtin_bit_cast(uint64_t, f32x2{v[0], v[1]}), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(q + 64, __builtin_bit_cast(uint64_t, f32x2{v[2], v[3]}), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
             }
         }
         __builtin_amdgcn_s_waitcnt(0);          // this thread's partial stores have completed
         __syncthreads();
-        const int tile = m_tile * tiles_n + n_tile;
         if (tid == 0)
             last_split = __hip_atomic_fetch_add(&counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
                          (uint32_t)(splits - 1);
         __syncthreads();
         if (!last_split) return;
+        // Sum in split order; this workgroup's own split comes from its registers. The
+        // loads of a batch of splits are all issued before the first is used: kBatch
+        // splits x MR x CBW fragments in flight (one memory round trip per batch).
+        constexpr int kBatch = MR * CBW >= 16 ? 1 : 16 / (MR * CBW);
+        f32x4 sum[MR][CBW];
 #pragma unroll
-        for (int j = 0; j < CBW; ++j) {
-            const int n = (nbw + j) * kColsPerBlock + 4 * h;
+        for (int j = 0; j < CBW; ++j)
 #pragma unroll
-            for (int r = 0; r < MR; ++r) {
-                const int m = m0 + 16 * r + c;
-                f32x4 v = {0.f, 0.f, 0.f, 0.f};
-                if (nbw + j < NB && m < M) {
-                    for (int sp = 0; sp < splits; ++sp) {
-                        const uint64_t* p = part(sp, m, n);
-                        const f32x2 lo = __builtin_bit_cast(f32x2, __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-                        const f32x2 hi = __builtin_bit_cast(f32x2, __hip_atomic_load(p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-                        v += f32x4{lo[0], lo[1], hi[0], hi[1]};
+            for (int r = 0; r < MR; ++r) sum[r][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int sp0 = 0; sp0 < splits; sp0 += kBatch) {
+            f32x4 got[kBatch][MR][CBW];
+#pragma unroll
+            for (int b = 0; b < kBatch; ++b) {
+                const int sp = sp0 + b;
+#pragma unroll
+                for (int j = 0; j < CBW; ++j) {
+#pragma unroll
+                    for (int r = 0; r < MR; ++r) {
+                        got[b][r][j] = acc[r][j];
+                        if (sp < splits && sp != split) {
+                            const uint64_t* q = part(sp, r * CBW + j);
+                            const f32x2 lo = __builtin_bit_cast(f32x2, __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+                            const f32x2 hi = __builtin_bit_cast(f32x2, __hip_atomic_load(q + 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+                            got[b][r][j] = f32x4{lo[0], lo[1], hi[0], hi[1]};
+                        }
                     }
                 }
-                acc[r][j] = v;
+            }
+#pragma unroll
+            for (int b = 0; b < kBatch; ++b) {
+                if (sp0 + b < splits) {
+#pragma unroll
+                    for (int j = 0; j < CBW; ++j)
+#pragma unroll
+                        for (int r = 0; r < MR; ++r) sum[r][j] += got[b][r][j];
+                }
             }
         }
+#pragma unroll
+        for (int j = 0; j < CBW; ++j)
+#pragma unroll
+            for (int r = 0; r < MR; ++r) acc[r][j] = sum[r][j];
         if (tid == 0)      // leave the counter at zero for the next call
             __hip_atomic_store(&counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -507,7 +531,9 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N) {
     p.workspace_bytes = 0;
     if (p.splits > 1) {
         const size_t counters = ((size_t)tiles * 4 + 255) / 256 * 256;
-        p.workspace_bytes = counters + (size_t)p.splits * (size_t)M * (size_t)N * 4;
+        // fp32 partial tiles: splits x tiles x (16 mr) x (16 waves cbw)
+        p.workspace_bytes = counters + (size_t)p.splits * (size_t)tiles * (size_t)(16 * p.mr) *
+                                           (size_t)(16 * p.waves * p.cbw) * 4;
     }
     return p;
 }

@@ -54,6 +54,23 @@ __device__ __forceinline__ uint4 load_once(const uint4* p) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Activation chunk load, kept where it is written (before the code loads). The
+// compiler would otherwise sink it below them into the staging branch; since vector
+// loads complete in order, waiting for it would then wait for the codes too. Its
+// result is claimed with wait_x_chunk.
+__device__ __forceinline__ u32x4 load_x_chunk(const void* p) {
+    u32x4 v;
+    asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(p) : "memory");
+    return v;
+}
+
+// Wait until at most `kAfter` vector loads are outstanding (those issued after the
+// activation chunks) and hand the chunk to the code that reads it.
+template <int kAfter>
+__device__ __forceinline__ void wait_x_chunk(u32x4& v) {
+    asm volatile("s_waitcnt vmcnt(%1)" : "+v"(v) : "n"(kAfter) : "memory");
+}
+
 __device__ __forceinline__ uint32_t pick(const uint4 v, int i) {
     return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
@@ -139,7 +156,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(const GemvArgs a) 
     // 1. staged variant: this thread's activation chunks, loaded first
     const int row_chunks = K / 8;
     const int chunks = M * row_chunks;
-    uint4 xv[kStaged ? kChunks : 1];
+    u32x4 xv[kStaged ? kChunks : 1];
     int xm[kStaged ? kChunks : 1];
     if constexpr (kStaged) {
         const float inv_row_chunks = 1.0f / (float)row_chunks;
@@ -152,7 +169,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(const GemvArgs a) 
             m += (m + 1) * row_chunks <= q ? 1 : 0;
             m = q < chunks ? m : 0;
             xm[p] = m;
-            xv[p] = reinterpret_cast<const uint4*>(a.x)[q < chunks ? q : chunks - 1];
+            xv[p] = load_x_chunk(reinterpret_cast<const uint4*>(a.x) + (q < chunks ? q : chunks - 1));
         }
     }
 
@@ -174,14 +191,18 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(const GemvArgs a) 
     // 3. staged variant: x -> LDS and the row-block sums (rows < M; the sums of the
     //    repeated rows are never read into a kept result)
     if constexpr (kStaged) {
+        // the run's metadata and kRun code loads stay in flight
+#pragma unroll
+        for (int p = 0; p < kChunks; ++p) wait_x_chunk<kRun + 1>(xv[p]);
 #pragma unroll
         for (int p = 0; p < kChunks; ++p) {
             const int q = threadIdx.x + p * blockDim.x;
+            const uint4 xc = make_uint4(xv[p].x, xv[p].y, xv[p].z, xv[p].w);
             // chunks of one (row, row block) are 16 consecutive q: one row of 16 lanes,
             // all valid or all past the end together (row_chunks is a multiple of 16)
             if (q < chunks) {
-                reinterpret_cast<uint4*>(xs)[q] = xv[p];
-                const float s = row16_sum(sum8<kBF16>(xv[p]));
+                reinterpret_cast<uint4*>(xs)[q] = xc;
+                const float s = row16_sum(sum8<kBF16>(xc));
                 if ((q & 15) == 0) {
                     const int kb = (q - xm[p] * row_chunks) >> 4;
                     xsum[kb * 16 + xm[p]] = s;
@@ -317,19 +338,14 @@ GemvPlan plan_gemv_with(int64_t M, int64_t K, int64_t N, int cols_per_wg) {
     return p;
 }
 
-// Several column blocks per workgroup when the grid would otherwise put a few small
-// workgroups on each compute unit (mid-size N): one workgroup per unit then issues
-// the activation loads before any weight load on that unit, instead of queueing a
-// later workgroup's activations behind an earlier one's weights. Measured on the
-// 2048 x 13312 decode shape: -6% at M = 1, -8% at M = 8; slower for N = 131072 and
-// N = 3072, so those keep one block per workgroup.
+// Two column blocks per workgroup when N is mid-sized (at most 1024 blocks, at least
+// 400): fewer, larger workgroups per compute unit share one copy of the activations.
+// Measured on the 2048 x 13312 decode shape: M = 8 -9%, M = 4 -4%, M = 1 even; four
+// blocks per workgroup, or two for N = 131072 or N = 3072, measured slower.
 GemvPlan plan_gemv(int64_t M, int64_t K, int64_t N) {
     const int64_t NB = N / kColsPerBlock;
     const GemvPlan one = plan_gemv_with(M, K, N, 1);
-    if (NB <= 1024) {
-        for (int c = 4; c >= 2; c /= 2)
-            if (c * one.waves_k <= kMaxWaves && NB / c >= 200) return plan_gemv_with(M, K, N, c);
-    }
+    if (NB <= 1024 && NB / 2 >= 200 && 2 * one.waves_k <= kMaxWaves) return plan_gemv_with(M, K, N, 2);
     return one;
 }
 
