@@ -501,23 +501,53 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N) {
     const int64_t KB = K / kRowsPerBlock;
     p.mr = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
     p.tiles_m = (int)((M + 16 * p.mr - 1) / (16 * p.mr));
-    // widest column tile (4 waves x cbw blocks) that still occupies 3/4 of the CUs, else
-    // the narrowest (a wider tile decodes each weight for as many rows but reads the
-    // activations less often)
     p.waves = 4;
     p.cbw = 1;
-    for (int cbw : {4, 2}) {
-        if (p.tiles_m * ((NB + 4 * cbw - 1) / (4 * cbw)) >= kTargetWorkgroups * 3 / 4) {
-            p.cbw = cbw;
-            break;
+    if (p.mr >= 4) {
+        // Tile shape from a cost model: rounds of tiles over the CUs (one workgroup per
+        // CU) x tile area / throughput of that shape. Throughputs are relative output
+        // elements per unit time, per k block, measured with one tile per CU on MI355X:
+        // wider and taller tiles decode each weight for more rows and copy the
+        // activations less often, but leave CUs idle on small outputs.
+        struct Shape { int mr, cbw, waves; double rate; };
+        static constexpr Shape kShapes[] = {
+            {8, 2, 8, 13.1},   // 128 x 256
+            {8, 2, 4, 10.4},   // 128 x 128
+            {8, 1, 4, 7.2},    // 128 x 64
+            {4, 2, 8, 10.8},   // 64 x 256
+            {4, 2, 4, 7.4},    // 64 x 128
+            {4, 1, 4, 5.4},    // 64 x 64
+        };
+        double best = 0.0;
+        for (const Shape& c : kShapes) {
+            if (c.mr > p.mr) continue;
+            const int64_t tm = (M + 16 * c.mr - 1) / (16 * c.mr);
+            const int64_t tn = (NB + c.waves * c.cbw - 1) / (c.waves * c.cbw);
+            const int64_t rounds = (tm * tn + kTargetWorkgroups - 1) / kTargetWorkgroups;
+            const double cost = (double)rounds * (16.0 * c.mr) * (16.0 * c.waves * c.cbw) / c.rate;
+            if (best == 0.0 || cost < best) {
+                best = cost;
+                p.mr = c.mr;
+                p.cbw = c.cbw;
+                p.waves = c.waves;
+                p.tiles_m = (int)tm;
+            }
         }
-    }
-    // the 256-column tile as 8 waves of 2 blocks rather than 4 of 4: two waves per SIMD,
-    // so one computes while the other waits on its copies, the barrier or LDS (needs
-    // 16 * mr >= 32 rows for the activation copies to split over 8 waves)
-    if (p.cbw == 4 && p.mr >= 2) {
-        p.waves = 8;
-        p.cbw = 2;
+    } else {
+        // 16- and 32-row tiles (M <= 32, weight-bound): the widest column tile (4 waves
+        // x cbw blocks) that still occupies 3/4 of the CUs, else the narrowest
+        for (int cbw : {4, 2}) {
+            if (p.tiles_m * ((NB + 4 * cbw - 1) / (4 * cbw)) >= kTargetWorkgroups * 3 / 4) {
+                p.cbw = cbw;
+                break;
+            }
+        }
+        // the 256-column tile as 8 waves of 2 blocks rather than 4 of 4: two waves per
+        // SIMD (needs 16 * mr >= 32 rows for the activation copies to split over 8 waves)
+        if (p.cbw == 4 && p.mr >= 2) {
+            p.waves = 8;
+            p.cbw = 2;
+        }
     }
     p.tiles_n = (int)((NB + p.waves * p.cbw - 1) / (p.waves * p.cbw));
     const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
