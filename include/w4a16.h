@@ -137,6 +137,31 @@ w4a16_status w4a16_gemm_ex(const void* x, const void* packed, size_t packed_byte
                            const void* bias, void* workspace, size_t workspace_bytes, void* stream,
                            w4a16_path path, int64_t gemv_max_m);
 
+/* Tied-embedding gather from the packed head weight: a model whose input embedding
+ * is tied to its output head keeps one quantised matrix for both (vllm-omni commit
+ * "cpu_int4: repack weights in n-blocks, to bound the load-time peak": the
+ * 131072 x 2048 embedding is "tied, so it is also the head"; commit "Add cpu_int4,
+ * an asymmetric 4-bit weight path for vLLM's CPU backend": the quantised tied
+ * embedding is checked end to end). With the head stored for y = x . W, W [K, N]
+ * (K hidden, N vocabulary), the embedding of token t is column t of dequant(W):
+ *
+ *   out[i, k] = (q[k, ids[i]] - z[k div G, ids[i]]) * s[k div G, ids[i]]
+ *
+ * computed exactly and rounded once to `dtype` (nearest even): bit-for-bit the
+ * correctly rounded value.
+ *
+ *   ids      int32 [T] token ids, device memory, 4-byte aligned. An id outside
+ *            [0, N) yields a row of zeros (no error is reported for it).
+ *   packed   the buffer w4a16_repack wrote for the head, `packed_bytes` >=
+ *            w4a16_packed_bytes(K, N, G), 16-byte aligned; read only.
+ *   out      [T, K] row-major, `dtype`, written in full, 16-byte aligned. Must not
+ *            overlap ids or packed.
+ *   T        number of tokens, 0 <= T < 2^31 (T = 0 is a valid no-op).
+ *   dtype and group_size must be those the buffer was repacked with. */
+w4a16_status w4a16_embedding(const int32_t* ids, int64_t T, const void* packed, size_t packed_bytes,
+                             w4a16_dtype dtype, int64_t K, int64_t N, int64_t group_size, void* out,
+                             void* stream);
+
 /* Static, NUL-terminated description of a status code ("unknown status" otherwise). */
 const char* w4a16_status_str(w4a16_status status);
 

@@ -28,6 +28,7 @@ Modules:
   awq          pack_awq / unpack_awq: the AWQ int32 nibble packing
   tile_layout  repack / decode: the GPU tile layout, written from its spec
   gemm         dequant / gemm / tolerance check
+  embedding    tied-embedding gather: dequantised columns of the head weight
 """
 
-from . import numerics, awq, tile_layout, gemm  # noqa: F401
+from . import numerics, awq, tile_layout, gemm, embedding  # noqa: F401

@@ -123,3 +123,10 @@ def make_custom(seed, M, K, N, dtype=BF16, group_size=128):
     ws = draw_weights(rng, K, N, group_size, dtype)
     ws.x_bits[M] = draw_activations(rng, M, K, dtype)
     return ws
+
+
+def draw_token_ids(seed, T, N):
+    """Token ids for an embedding lookup: T ids uniform on [0, N), int32, from their
+    own generator Generator(PCG64(seed)) (prompt tokens of a vocabulary of N)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return rng.integers(0, N, size=T, dtype=np.int64).astype(np.int32)

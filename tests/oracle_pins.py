@@ -275,3 +275,77 @@ def pin_layout_metadata(tile_layout, K=768, N=32, G=256):
     expect = [(n | ((((128 * kb) // G) % 16) << 16)) if kb < KB else 0
               for n in range(N) for kb in range(KBP)]
     return meta.tolist() == expect
+
+
+# ---------------------------------------------------------------- tied embedding
+
+def _bf16_bits_of(v):
+    return int(np.array([v], dtype=np.float32).view(np.uint32)[0] >> 16)
+
+
+def embedding_golden():
+    weights, rounding = [], []
+    for line in _lines("worked_example_embedding.txt"):
+        f = line.split()
+        if f[0] == "weights":
+            weights.append((int(f[1]), float(f[2]), float(f[3]), float(f[4])))
+        else:
+            rounding.append((f[1], int(f[2], 16), int(f[3]), int(f[4]), int(f[5], 16)))
+    return weights, rounding
+
+
+def pin_embedding_worked_example(emb):
+    """The hand-worked rows: exact values, so their bf16 bits are known."""
+    ex = worked_example()
+    weights, _ = embedding_golden()
+    ids = np.array([w[0] for w in weights])
+    got = emb.embedding(ids, ex["qweight"], ex["qzeros"], ex["scale_bits"], "bf16", 128)
+    if got.shape != (len(ids), 128):
+        return False
+    for i, (_, e0, e1, rest) in enumerate(weights):
+        want = [_bf16_bits_of(e0), _bf16_bits_of(e1)] + [_bf16_bits_of(rest)] * 126
+        if got[i].tolist() != want:
+            return False
+    return True
+
+
+def pin_embedding_rounding(emb):
+    """(q - z) * s needing a rounding step: hand-rounded results (ties to even)."""
+    _, rounding = embedding_golden()
+    for dtype, sbits, q, z, want in rounding:
+        qweight = np.full((128, 1), q * 0x11111111, dtype=np.uint32).view(np.int32)   # every column code q
+        qzeros = np.full((1, 1), z * 0x11111111, dtype=np.uint32).view(np.int32)
+        scale_bits = np.full((1, 8), sbits, dtype=np.uint16)
+        got = emb.embedding(np.array([0, 5]), qweight, qzeros, scale_bits, dtype, 128)
+        if not np.all(got == want):
+            return False
+    return True
+
+
+def pin_embedding_matches_gemm(emb, gemm_mod, seed=11):
+    """Row t of the embedding is column t of the GEMM oracle's product with the
+    identity activation (x = I_K gives y = W exactly), zeros for ids out of range."""
+    rng = np.random.default_rng(seed)
+    for (K, N, G, dtype) in [(256, 24, 128, "bf16"), (128, 16, 128, "fp16"), (256, 8, -1, "bf16")]:
+        GG = K if G == -1 else G
+        qweight = rng.integers(0, 2**32, (K, N // 8), dtype=np.uint32).view(np.int32)
+        qzeros = rng.integers(0, 2**32, (K // GG, N // 8), dtype=np.uint32).view(np.int32)
+        s = rng.uniform(0.005, 0.02, (K // GG, N))
+        scale_bits = (s.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16) if dtype == "bf16" \
+            else s.astype(np.float16).view(np.uint16)
+        one = 0x3F80 if dtype == "bf16" else 0x3C00
+        x_bits = np.where(np.eye(K, dtype=bool), one, 0).astype(np.uint16)
+        y = gemm_mod.w4a16_reference(x_bits, qweight, qzeros, scale_bits, dtype, G)    # = W
+        ids = np.array([N - 1, 0, 3, 3, N, -2, 5])
+        e = emb.embedding_f64(ids, qweight, qzeros, scale_bits, dtype, G)
+        for i, t in enumerate(ids):
+            want = y[:, t] if 0 <= t < N else np.zeros(K)
+            if not np.array_equal(e[i], want):
+                return False
+    return True
+
+
+def run_embedding_pins(emb, gemm_mod):
+    return {"worked example": pin_embedding_worked_example(emb),
+            "rounding": pin_embedding_rounding(emb),
+            "identity product": pin_embedding_matches_gemm(emb, gemm_mod)}

@@ -25,7 +25,7 @@ def w():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
-        "w4a16_gemm", "w4a16_gemm_ex", "w4a16_layout_version", "w4a16_packed_bytes",
+        "w4a16_embedding", "w4a16_gemm", "w4a16_gemm_ex", "w4a16_layout_version", "w4a16_packed_bytes",
         "w4a16_repack", "w4a16_status_str", "w4a16_workspace_bytes"])
 
 
@@ -152,3 +152,25 @@ def test_build_module_and_binding_agree_on_library_path():
     import w4a16_int4_weight_amd as mod
     from w4a16_int4_weight_amd import build
     assert mod.LIB_PATH == build.LIB_PATH
+
+
+def test_embedding_validation_before_any_device_call(w):
+    def emb(ids=P(256), T=4, packed=P(1024), pbytes=1 << 40, dtype=1, K=512, N=512, G=128, out=P(2048)):
+        return w.lib.w4a16_embedding(ids, T, packed, pbytes, dtype, K, N, G, out, None)
+    assert emb(K=100) == 2
+    assert emb(N=8) == 2
+    assert emb(G=32) == 3
+    assert emb(dtype=2) == 4
+    assert emb(T=-1) == 2
+    assert emb(T=1 << 31) == 2
+    assert emb(ids=None) == 1
+    assert emb(packed=None) == 1
+    assert emb(out=None) == 1
+    assert emb(ids=P(258)) == 5
+    assert emb(packed=P(1032)) == 5
+    assert emb(out=P(2056)) == 5
+    assert emb(pbytes=512 * 512 // 2) == 6
+    # T = 0 is a valid no-op, even with NULL buffers
+    assert emb(T=0, ids=None, packed=None, out=None) == 0
+    # a fully valid call on this GPU-less host stops at the device check
+    assert emb() == 7

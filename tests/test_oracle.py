@@ -11,7 +11,7 @@ import types
 import numpy as np
 import pytest
 
-from oracle import awq, gemm, numerics, tile_layout
+from oracle import awq, embedding, gemm, numerics, tile_layout
 import oracle_pins as pins
 
 ORACLE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
@@ -296,4 +296,51 @@ def test_planted_layout_mistakes_are_caught(desc, old, new):
         ok = pins.pin_layout_index_patterns(mut) and pins.pin_layout_metadata(mut)
     except (ValueError, AssertionError):
         ok = False    # a mutant that breaks the layout's own size check is caught too
+    assert not ok
+
+
+# ---------------------------------------------------------------- tied embedding
+
+def test_embedding_worked_example():
+    assert pins.pin_embedding_worked_example(embedding)
+
+
+def test_embedding_rounding_by_hand():
+    assert pins.pin_embedding_rounding(embedding)
+
+
+def test_embedding_is_the_identity_product():
+    assert pins.pin_embedding_matches_gemm(embedding, gemm)
+
+
+def test_embedding_empty_and_all_out_of_range():
+    ex = pins.worked_example()
+    assert embedding.embedding(np.array([], dtype=np.int64), ex["qweight"], ex["qzeros"], ex["scale_bits"],
+                               "bf16", 128).shape == (0, 128)
+    e = embedding.embedding(np.array([16, -1, 1 << 40]), ex["qweight"], ex["qzeros"], ex["scale_bits"],
+                            "bf16", 128)
+    assert e.shape == (3, 128) and not e.any()
+
+
+EMBEDDING_MUTANTS = [
+    ("neighbouring column", "where = np.searchsorted(words, ids[valid] // 8) * 8 + ids[valid] % 8",
+     "where = np.searchsorted(words, ids[valid] // 8) * 8 + (ids[valid] + 1) % 8"),
+    ("negative ids wrap around", "valid = (ids >= 0) & (ids < N)", "valid = (ids >= -N) & (ids < N)"),
+    ("truncation instead of rounding",
+     "return f64_to_half_bits_rne(embedding_f64(ids, qweight, qzeros, scale_bits, dtype, group_size), dtype)",
+     "return (embedding_f64(ids, qweight, qzeros, scale_bits, dtype, group_size).astype(np.float32)"
+     ".view(np.uint32) >> 16).astype(np.uint16) if dtype == 'bf16' else "
+     "f64_to_half_bits_rne(embedding_f64(ids, qweight, qzeros, scale_bits, dtype, group_size), dtype)"),
+    ("row of W instead of column", "E[valid] = W[:, where].T", "E[valid] = W[where % W.shape[0], :K]"),
+]
+
+
+@pytest.mark.parametrize("desc,old,new", EMBEDDING_MUTANTS, ids=[m[0] for m in EMBEDDING_MUTANTS])
+def test_planted_embedding_mistakes_are_caught(desc, old, new):
+    try:
+        mut = _mutant("embedding", old, new)
+        results = pins.run_embedding_pins(mut, gemm)
+        ok = all(results.values())
+    except (ValueError, IndexError):
+        ok = False    # a mutant that breaks the gather's shapes is caught too
     assert not ok

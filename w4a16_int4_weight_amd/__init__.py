@@ -10,6 +10,7 @@ Functions keep the C names:
   w4a16_gemm(x, packed, N, group_size, bias=None, y=None, workspace=None, stream=None) -> y
       (workspace=None: a zero-filled per-device workspace is allocated on demand)
   w4a16_gemm_ex(..., path="auto"|"gemv"|"mfma", gemv_max_m=-1)            -> y
+  w4a16_embedding(ids, packed, K, N, group_size, dtype, out=None, stream=None) -> out [T, K]
   w4a16_status_str(code)                         -> str
 
 There is no fallback: if the library is missing, the first call (or access to
@@ -26,7 +27,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4a16.so
 
 __all__ = [
     "W4A16Error", "lib", "w4a16_layout_version", "w4a16_packed_bytes", "w4a16_workspace_bytes",
-    "w4a16_repack", "w4a16_gemm", "w4a16_gemm_ex", "w4a16_status_str", "STATUS", "PATHS",
+    "w4a16_repack", "w4a16_gemm", "w4a16_gemm_ex", "w4a16_embedding", "w4a16_status_str", "STATUS", "PATHS",
 ]
 
 STATUS = {
@@ -71,6 +72,8 @@ def _load():
     h.w4a16_gemm.restype = _int
     h.w4a16_gemm_ex.argtypes = h.w4a16_gemm.argtypes + [_int, _i64]
     h.w4a16_gemm_ex.restype = _int
+    h.w4a16_embedding.argtypes = [_vp, _i64, _vp, _sz, _int, _i64, _i64, _i64, _vp, _vp]
+    h.w4a16_embedding.restype = _int
     h.w4a16_status_str.argtypes = [_int]
     h.w4a16_status_str.restype = ctypes.c_char_p
     _lib = h
@@ -193,3 +196,19 @@ def w4a16_gemm_ex(x, packed, N, group_size=128, bias=None, y=None, workspace=Non
     args, y = _gemm_args(x, packed, N, group_size, bias, y, workspace, stream)
     _check(_load().w4a16_gemm_ex(*args, PATHS[path], gemv_max_m), "w4a16_gemm_ex")
     return y
+
+
+def w4a16_embedding(ids, packed, K, N, group_size=128, dtype=torch.bfloat16, out=None, stream=None):
+    """Token ids int32 [T] -> out [T, K] of `dtype`: row i is column ids[i] of the
+    dequantised head weight the packed buffer holds (zeros for ids outside [0, N))."""
+    if ids.dim() != 1 or ids.dtype != torch.int32 or not ids.is_contiguous():
+        raise ValueError("ids must be a contiguous int32 [T] tensor")
+    T = ids.shape[0]
+    if out is None:
+        out = torch.empty((T, K), dtype=dtype, device=ids.device)
+    if tuple(out.shape) != (T, K) or out.dtype != dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [T, K] tensor of `dtype`")
+    code = _load().w4a16_embedding(_ptr(ids), T, _ptr(packed), packed.numel() * packed.element_size(),
+                                   _dtype_code(dtype), K, N, group_size, _ptr(out), _stream(stream, ids.device))
+    _check(code, "w4a16_embedding")
+    return out

@@ -146,6 +146,25 @@ w4a16_status w4a16_gemm_ex(const void* x, const void* packed, size_t packed_byte
                      stream, path, gemv_max_m);
 }
 
+w4a16_status w4a16_embedding(const int32_t* ids, int64_t T, const void* packed, size_t packed_bytes,
+                             w4a16_dtype dtype, int64_t K, int64_t N, int64_t group_size, void* out, void* stream) {
+    int64_t G = 0;
+    w4a16_status st = check_shape(K, N, group_size, &G);
+    if (st != W4A16_OK) return st;
+    if (dtype != W4A16_FP16 && dtype != W4A16_BF16) return W4A16_ERR_DTYPE;
+    if (T < 0 || T >= (int64_t(1) << 31)) return W4A16_ERR_SHAPE;
+    if (T == 0) return W4A16_OK;
+    if (!ids || !packed || !out) return W4A16_ERR_NULL;
+    if (!aligned(ids, 4) || !aligned(packed, 16) || !aligned(out, 16)) return W4A16_ERR_ALIGN;
+    if (packed_bytes < packed_size(K, N)) return W4A16_ERR_BUFFER_SIZE;
+    st = check_device();
+    if (st != W4A16_OK) return st;
+    const hipError_t err = w4a16::launch_embedding(ids, T, static_cast<const uint8_t*>(packed),
+                                                   static_cast<uint16_t*>(out), K, N, dtype == W4A16_BF16,
+                                                   static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
 const char* w4a16_status_str(w4a16_status status) {
     switch (status) {
         case W4A16_OK: return "ok";

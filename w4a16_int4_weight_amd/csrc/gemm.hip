@@ -41,63 +41,6 @@ namespace {
 
 constexpr int kXcds = 8;
 
-// Decode one tile word (8 codes of one column, rows in slot order) into the operand
-// of a 16x16x32 MFMA: 8 values (q - z) * s.
-template <bool kBF16> struct Dequant;
-
-template <> struct Dequant<true> {
-    // bf16: codes -> fp32 with the byte converters, (q - z) * s = fma(q, s, -z*s) is
-    // exact in fp32 (a 4-bit integer times an 8-bit significand), then one RNE
-    // conversion per pair. Byte b of (d & 0x0F0F0F0F) is slot 2b and byte b of
-    // (d >> 4) & 0x0F0F0F0F is slot 2b+1; slot -> row: 0,2,4,6,1,3,5,7.
-    float s, nzs;
-    Dequant() = default;
-    __device__ __forceinline__ Dequant(uint32_t md) {
-        s = bf16_bits_to_f32(md & 0xFFFFu);
-        nzs = -(float)((md >> 16) & 0xFu) * s;
-    }
-    __device__ __forceinline__ uint4 operator()(uint32_t d) const {
-        uint32_t lo = d & 0x0F0F0F0Fu;          // rows 0, 4, 1, 5 in bytes 0..3
-        uint32_t hi = (d >> 4) & 0x0F0F0F0Fu;   // rows 2, 6, 3, 7 in bytes 0..3
-        // hide the masks from the optimiser so each byte converts with one
-        // v_cvt_f32_ubyteN instead of an extract and a convert
-        asm volatile("" : "+v"(lo), "+v"(hi));
-        const float r0 = fmaf((float)(lo & 0xFFu), s, nzs);
-        const float r4 = fmaf((float)((lo >> 8) & 0xFFu), s, nzs);
-        const float r1 = fmaf((float)((lo >> 16) & 0xFFu), s, nzs);
-        const float r5 = fmaf((float)(lo >> 24), s, nzs);
-        const float r2 = fmaf((float)(hi & 0xFFu), s, nzs);
-        const float r6 = fmaf((float)((hi >> 8) & 0xFFu), s, nzs);
-        const float r3 = fmaf((float)((hi >> 16) & 0xFFu), s, nzs);
-        const float r7 = fmaf((float)(hi >> 24), s, nzs);
-        return make_uint4(pack2_rne<true>(r0, r1), pack2_rne<true>(r2, r3),
-                          pack2_rne<true>(r4, r5), pack2_rne<true>(r6, r7));
-    }
-};
-
-template <> struct Dequant<false> {
-    // fp16: OR-ing a pair of codes into 1024.0 gives (1024 + q) exactly; a packed
-    // fp16 subtract of (1024 + z) gives q - z exactly; a packed multiply by s rounds
-    // (q - z) * s once, to nearest even.
-    f16x2 zz, ss;
-    Dequant() = default;
-    __device__ __forceinline__ Dequant(uint32_t md) {
-        const _Float16 s = __builtin_bit_cast(_Float16, (uint16_t)(md & 0xFFFFu));
-        const _Float16 zb = (_Float16)(1024.0f + (float)((md >> 16) & 0xFu));
-        zz = f16x2{zb, zb};
-        ss = f16x2{s, s};
-    }
-    __device__ __forceinline__ uint32_t pair(uint32_t bits) const {
-        f16x2 v = __builtin_bit_cast(f16x2, bits | Magic<false>::kBase2);
-        v = (v - zz) * ss;
-        return __builtin_bit_cast(uint32_t, v);
-    }
-    __device__ __forceinline__ uint4 operator()(uint32_t d) const {
-        return make_uint4(pair(d & 0x000F000Fu), pair((d >> 4) & 0x000F000Fu),
-                          pair((d >> 8) & 0x000F000Fu), pair((d >> 12) & 0x000F000Fu));
-    }
-};
-
 __device__ __forceinline__ uint32_t pick(const uint4 v, int i) {
     return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }

@@ -26,6 +26,11 @@ GemvPlan plan_gemv(int64_t M, int64_t K, int64_t N);
 hipError_t launch_gemv(const uint16_t* x, const uint8_t* packed, const uint16_t* bias, uint16_t* y,
                        int64_t M, int64_t K, int64_t N, bool bf16, hipStream_t stream);
 
+// Tied-embedding gather: out[t, :] = dequantised column ids[t] of the packed [K, N]
+// weight (zeros for ids outside [0, N)).
+hipError_t launch_embedding(const int32_t* ids, int64_t T, const uint8_t* packed, uint16_t* out, int64_t K,
+                            int64_t N, bool bf16, hipStream_t stream);
+
 // LDS-staged dequantise -> MFMA GEMM for any M >= 1: tile shape and K split chosen
 // from the shape; workspace_bytes > 0 when K is split over workgroups.
 struct GemmPlan {
