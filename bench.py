@@ -5,7 +5,8 @@ N=13312, group size 128, bf16, in algorithmic GB/s. A step is one w4a16_gemm cal
 (dispatch, split-K GEMV, in-kernel reduction and epilogue) on one activation
 batch; the weights were repacked once before timing. Secondary entries in the same
 JSON line measure the other rows of the path on their own workloads: the LM-head
-repack (GB/s), the MFMA GEMM at M=512 (TFLOP/s) and the GEMV on the other shapes.
+repack (GB/s), the MFMA GEMM at M=512 (TFLOP/s), the GEMV on the other shapes and
+the tied-embedding gather of 512 tokens from the packed LM head (GB/s).
 
 Timing: warm-up calls, then K calls captured in one HIP graph and replayed once
 between two events on the launch stream, with a device synchronisation on both
@@ -17,6 +18,7 @@ the LM-head GEMV about 8% slower than 8 copies; more copies only remove reuse.)
 Algorithmic bytes of a GEMM (AWQ-sized): K*N/2 codes + (K/G)*N/2 zeros
 + (K/G)*N*2 scales + M*K*2 activations + M*N*2 outputs; flops 2*M*N*K.
 Repack bytes: each AWQ byte read once and written once, 2*(K*N/2 + (K/G)*N/2 + (K/G)*N*2).
+Gather bytes, per token: K/2 codes + (K/G)*2.5 zero and scale bytes + 4 (id) + 2K outputs.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--quick]
        python bench.py --pmc-probe     (launches for hardware-counter runs, no timing)
@@ -144,6 +146,41 @@ def measure_repack(w, workload, steps, warmup, dev):
     return dict(workload=workload + " repack", K=K, N=N, group_size=G, dtype=ws.dtype, kernel="w4a16_repack",
                 copies=copies, launches=n, us_per_launch=per_launch_s * 1e6, algorithmic_bytes=nbytes,
                 GBps=nbytes / per_launch_s / 1e9)
+
+
+def embedding_bytes(T, K, G):
+    """Algorithmic bytes of a T-token gather: per token its K codes (K/2 bytes), its
+    K/G zeros and scales (2.5 bytes each), the id (4 bytes) and the K outputs (2K)."""
+    return T * (K // 2 + (K // G) * 5 // 2 + 4 + 2 * K)
+
+
+def measure_embedding(w, workload, T, steps, warmup, dev):
+    import numpy as np
+    import torch
+    import synth
+    ws = synth.make(workload, Ms=())
+    K, N, G = ws.K, ws.N, ws.group_size
+    qw = torch.from_numpy(ws.qweight).to(dev)
+    qz = torch.from_numpy(ws.qzeros).to(dev)
+    sc = to_dev_bits(ws.scale_bits, ws.dtype, dev)
+    packed0 = w.w4a16_repack(qw, qz, sc, G)
+    del qw, qz, sc
+    copies = max(1, min(MAX_COPIES, math.ceil(ROTATE_BYTES / packed0.numel())))
+    packs = [packed0] + [packed0.clone() for _ in range(copies - 1)]
+    # a different set of prompt tokens per call, so repeated calls do not re-read the
+    # same columns from the caches
+    ids = [torch.from_numpy(synth.draw_token_ids(7000 + i, T, N)).to(dev) for i in range(steps)]
+    out = torch.empty((T, K), dtype=torch.bfloat16 if ws.dtype == "bf16" else torch.float16, device=dev)
+    calls = [(lambda p=packs[i % copies], t=ids[i]: w.w4a16_embedding(t, p, K, N, G, out.dtype, out=out))
+             for i in range(steps)]
+    ms, n = time_graph(calls, warmup)
+    per_launch_s = ms / 1e3 / n
+    nbytes = embedding_bytes(T, K, G)
+    del packs, packed0, ids
+    torch.cuda.empty_cache()
+    return dict(workload=workload + " tied-embedding gather", T=T, K=K, N=N, group_size=G, dtype=ws.dtype,
+                kernel="w4a16_embedding", weight_copies=copies, launches=n, us_per_launch=per_launch_s * 1e6,
+                algorithmic_bytes=nbytes, GBps=nbytes / per_launch_s / 1e9)
 
 
 def roofline_hbm(entry, traffic=None):
@@ -296,6 +333,10 @@ def main():
         r["roofline"] = roofline_hbm(r)
         log(f"lm_head repack: {r['us_per_launch']:.1f} us, {r['GBps']:.0f} GB/s")
         secondary.append(r)
+        e = measure_embedding(w, "lm_head", 512, args.steps, min(args.warmup, 10), dev)
+        e["roofline"] = roofline_hbm(e)
+        log(f"lm_head tied-embedding gather T=512: {e['us_per_launch']:.2f} us, {e['GBps']:.0f} GB/s")
+        secondary.append(e)
 
     cpu = None
     if not args.no_cpu_baseline:
