@@ -95,6 +95,27 @@ w4a16_status w4a16_repack(const int32_t* qweight, const int32_t* qzeros, const v
                           w4a16_dtype dtype, int64_t K, int64_t N, int64_t group_size,
                           void* packed, size_t packed_bytes, void* stream);
 
+/* The same one-time repack from GPTQ-standard tensors. GPTQ-style packing runs
+ * along the input dimension in standard bit order (vLLM note "Carga de capas
+ * cuantizadas", section "Motivación de diseño": the Marlin kernel takes only that
+ * style, so AWQ checkpoints are converted to it first). The packed buffer written
+ * is byte-for-byte the one w4a16_repack writes for the same codes, zero points and
+ * scales, so every other entry point reads it unchanged.
+ *
+ *   qweight  int32 [K/8, N], row-major. Word i of column n holds rows 8i .. 8i+7;
+ *            nibble j (bits 4j..4j+3) holds row 8i + j.
+ *   qzeros   int32 [K/G, N/8], row-major, packed along N in standard order:
+ *            nibble j of word w holds the zero point of column 8w + j, used as is
+ *            (w = (q - z) * s; no +1 offset is applied).
+ *   scales   [K/G, N] row-major, of `dtype`.
+ *   packed   output, `packed_bytes` >= w4a16_packed_bytes(K, N, group_size).
+ *
+ * Activation-order checkpoints (a g_idx permutation of K) are not supported: groups
+ * are contiguous runs of G rows. Alignment as for w4a16_repack. */
+w4a16_status w4a16_repack_gptq(const int32_t* qweight, const int32_t* qzeros, const void* scales,
+                               w4a16_dtype dtype, int64_t K, int64_t N, int64_t group_size,
+                               void* packed, size_t packed_bytes, void* stream);
+
 /* Device workspace the GEMM needs for this shape, in bytes (0 for most shapes).
  * It is non-zero when the MFMA GEMM splits K over workgroups because the output has
  * too few tiles to fill the GPU (small N and M, long K); the split partial sums

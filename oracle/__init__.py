@@ -26,9 +26,10 @@ Sources (pages, by title and section):
 Modules:
   numerics     16-bit float bit patterns -> float64 (definitions of fp16 / bf16)
   awq          pack_awq / unpack_awq: the AWQ int32 nibble packing
+  gptq         GPTQ-standard packing: codes along K, zero points along N, standard order
   tile_layout  repack / decode: the GPU tile layout, written from its spec
   gemm         dequant / gemm / tolerance check
   embedding    tied-embedding gather: dequantised columns of the head weight
 """
 
-from . import numerics, awq, tile_layout, gemm, embedding  # noqa: F401
+from . import numerics, awq, gptq, tile_layout, gemm, embedding  # noqa: F401

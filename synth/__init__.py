@@ -130,3 +130,26 @@ def draw_token_ids(seed, T, N):
     own generator Generator(PCG64(seed)) (prompt tokens of a vocabulary of N)."""
     rng = np.random.Generator(np.random.PCG64(seed))
     return rng.integers(0, N, size=T, dtype=np.int64).astype(np.int32)
+
+
+@dataclass
+class GptqWeightSet:
+    K: int
+    N: int
+    group_size: int
+    dtype: str
+    qweight: np.ndarray      # int32 [K/8, N]   (codes packed along K)
+    qzeros: np.ndarray       # int32 [K/G, N/8] (zero points packed along N)
+    scale_bits: np.ndarray   # uint16 [K/G, N]
+
+
+def draw_gptq_weights(seed, K, N, dtype=BF16, group_size=128):
+    """A GPTQ-standard weight set, same recipe as draw_weights: whole int32 words
+    uniform over all 2^32 patterns (so every code and zero point is uniform on 0..15
+    whatever the order inside the word), then scales uniform on [0.005, 0.02)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    G = K if group_size == -1 else group_size
+    qweight = rng.integers(0, 2**32, size=(K // 8, N), dtype=np.uint32).view(np.int32)
+    qzeros = rng.integers(0, 2**32, size=(K // G, N // 8), dtype=np.uint32).view(np.int32)
+    scales = rng.uniform(0.005, 0.02, size=(K // G, N)).astype(np.float32)
+    return GptqWeightSet(K, N, group_size, dtype, qweight, qzeros, f32_to_half_bits(scales, dtype))

@@ -349,3 +349,73 @@ def run_embedding_pins(emb, gemm_mod):
     return {"worked example": pin_embedding_worked_example(emb),
             "rounding": pin_embedding_rounding(emb),
             "identity product": pin_embedding_matches_gemm(emb, gemm_mod)}
+
+
+# ---------------------------------------------------------------- GPTQ-standard packing
+
+def gptq_golden_entries():
+    out = []
+    for line in _lines("gptq_word_pins.txt"):
+        kind, direction, rest = line.split(None, 2)
+        lhs, rhs = [p.strip() for p in rest.split("->")]
+        if direction == "pack":
+            out.append((kind, "pack", [int(v) for v in lhs.split()], int(rhs, 16)))
+        else:
+            out.append((kind, "unpack", int(lhs, 16), [int(v) for v in rhs.split()]))
+    return out
+
+
+def pin_gptq_golden(gptq):
+    """Hand-derived words: weights as one column of 8 rows, zeros as one row of 8 columns."""
+    for kind, direction, a, b in gptq_golden_entries():
+        if kind == "weight":
+            if direction == "pack":
+                w = gptq.pack_gptq_weight(np.array(a, dtype=np.uint8).reshape(8, 1))
+                if w.shape != (1, 1) or int(w.view(np.uint32)[0, 0]) != b:
+                    return False
+            else:
+                c = gptq.unpack_gptq_weight(np.array([[a]], dtype=np.uint32).view(np.int32))
+                if c.shape != (8, 1) or c[:, 0].tolist() != b:
+                    return False
+        else:
+            if direction == "pack":
+                w = gptq.pack_gptq_zeros(np.array([a], dtype=np.uint8))
+                if w.shape != (1, 1) or int(w.view(np.uint32)[0, 0]) != b:
+                    return False
+            else:
+                c = gptq.unpack_gptq_zeros(np.array([[a]], dtype=np.uint32).view(np.int32))
+                if c.shape != (1, 8) or c[0].tolist() != b:
+                    return False
+    return True
+
+
+def pin_gptq_roundtrips(gptq, seed=5):
+    rng = np.random.default_rng(seed)
+    Q = rng.integers(0, 16, (64, 24), dtype=np.uint8)
+    if not np.array_equal(gptq.unpack_gptq_weight(gptq.pack_gptq_weight(Q)), Q):
+        return False
+    W = rng.integers(0, 2**32, (5, 24), dtype=np.uint32).view(np.int32)
+    if not np.array_equal(gptq.pack_gptq_weight(gptq.unpack_gptq_weight(W)), W):
+        return False
+    Z = rng.integers(0, 16, (3, 40), dtype=np.uint8)
+    if not np.array_equal(gptq.unpack_gptq_zeros(gptq.pack_gptq_zeros(Z)), Z):
+        return False
+    return True
+
+
+def pin_gptq_row_moves_one_nibble(gptq):
+    """A single code in row r of a column block lands in word r // 8, nibble r % 8."""
+    for r in range(16):
+        Q = np.zeros((16, 8), dtype=np.uint8)
+        Q[r, 3] = 9
+        w = gptq.pack_gptq_weight(Q).view(np.uint32)
+        want = np.zeros((2, 8), dtype=np.uint32)
+        want[r // 8, 3] = 9 << (4 * (r % 8))
+        if not np.array_equal(w, want):
+            return False
+    return True
+
+
+def run_gptq_pins(gptq):
+    return {"golden": pin_gptq_golden(gptq), "roundtrips": pin_gptq_roundtrips(gptq),
+            "one nibble": pin_gptq_row_moves_one_nibble(gptq)}

@@ -26,7 +26,7 @@ def w():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "w4a16_embedding", "w4a16_gemm", "w4a16_gemm_ex", "w4a16_layout_version", "w4a16_packed_bytes",
-        "w4a16_repack", "w4a16_status_str", "w4a16_workspace_bytes"])
+        "w4a16_repack", "w4a16_repack_gptq", "w4a16_status_str", "w4a16_workspace_bytes"])
 
 
 def test_library_exports_every_declared_symbol(w):
@@ -152,6 +152,24 @@ def test_build_module_and_binding_agree_on_library_path():
     import w4a16_int4_weight_amd as mod
     from w4a16_int4_weight_amd import build
     assert mod.LIB_PATH == build.LIB_PATH
+
+
+def test_repack_gptq_validation_before_any_device_call(w):
+    def repack(qw=P(256), qz=P(512), sc=P(768), dtype=1, K=512, N=512, G=128, packed=P(1024), pbytes=1 << 40):
+        return w.lib.w4a16_repack_gptq(qw, qz, sc, dtype, K, N, G, packed, pbytes, None)
+    assert repack(K=100) == 2
+    assert repack(N=8) == 2
+    assert repack(G=32) == 3
+    assert repack(dtype=-1) == 4
+    assert repack(qw=None) == 1
+    assert repack(qz=None) == 1
+    assert repack(sc=None) == 1
+    assert repack(packed=None) == 1
+    assert repack(qw=P(258)) == 5
+    assert repack(sc=P(769)) == 5
+    assert repack(packed=P(1032)) == 5
+    assert repack(pbytes=1000) == 6
+    assert repack() == 7
 
 
 def test_embedding_validation_before_any_device_call(w):

@@ -11,7 +11,7 @@ import types
 import numpy as np
 import pytest
 
-from oracle import awq, embedding, gemm, numerics, tile_layout
+from oracle import awq, embedding, gemm, gptq, numerics, tile_layout
 import oracle_pins as pins
 
 ORACLE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
@@ -344,3 +344,60 @@ def test_planted_embedding_mistakes_are_caught(desc, old, new):
     except (ValueError, IndexError):
         ok = False    # a mutant that breaks the gather's shapes is caught too
     assert not ok
+
+
+# ---------------------------------------------------------------- GPTQ-standard packing
+
+def test_gptq_golden_words():
+    assert pins.pin_gptq_golden(gptq)
+
+
+def test_gptq_roundtrips():
+    assert pins.pin_gptq_roundtrips(gptq)
+
+
+def test_gptq_row_moves_one_nibble():
+    assert pins.pin_gptq_row_moves_one_nibble(gptq)
+
+
+def test_gptq_and_awq_repack_to_the_same_layout():
+    # the tile layout is a function of the codes alone: the same codes, zero points
+    # and scales reach the same packed buffer through either checkpoint format
+    rng = np.random.default_rng(3)
+    K, N, G = 256, 48, 128
+    Q = rng.integers(0, 16, (K, N), dtype=np.uint8)
+    Z = rng.integers(0, 16, (K // G, N), dtype=np.uint8)
+    S = rng.integers(0, 2**16, (K // G, N), dtype=np.uint16)
+    via_gptq = tile_layout.repack(gptq.unpack_gptq_weight(gptq.pack_gptq_weight(Q)),
+                                  gptq.unpack_gptq_zeros(gptq.pack_gptq_zeros(Z)), S, G)
+    via_awq = tile_layout.repack(awq.unpack_awq(awq.pack_awq(Q)), awq.unpack_awq(awq.pack_awq(Z)), S, G)
+    assert np.array_equal(via_gptq, via_awq)
+
+
+def test_gptq_rejects_bad_input():
+    with pytest.raises(ValueError):
+        gptq.pack_gptq_weight(np.zeros((12, 8), dtype=np.uint8))     # K not a multiple of 8
+    with pytest.raises(ValueError):
+        gptq.pack_gptq_zeros(np.zeros((1, 12), dtype=np.uint8))      # N not a multiple of 8
+    with pytest.raises(ValueError):
+        gptq.pack_gptq_weight(np.full((8, 8), 16, dtype=np.uint8))
+
+
+GPTQ_MUTANTS = [
+    ("weight nibbles from the top", "words |= grouped[:, j, :] << np.uint32(4 * j)",
+     "words |= grouped[:, j, :] << np.uint32(28 - 4 * j)"),
+    ("weight unpacked from the top", "codes[:, j, :] = ((w >> np.uint32(4 * j))",
+     "codes[:, j, :] = ((w >> np.uint32(28 - 4 * j))"),
+    ("zeros in AWQ's interleaved order", "words |= grouped[:, :, j] << np.uint32(4 * j)",
+     "words |= grouped[:, :, (0, 2, 4, 6, 1, 3, 5, 7)[j]] << np.uint32(4 * j)"),
+    ("zero point stored with a +1 offset", "codes[:, :, j] = ((w >> np.uint32(4 * j)) & np.uint32(0xF)).astype(np.uint8)",
+     "codes[:, :, j] = (((w >> np.uint32(4 * j)) & np.uint32(0xF)) + 1).astype(np.uint8)"),
+    ("rows of a word strided by K/8", "grouped = codes.astype(np.uint32).reshape(K // 8, 8, N)",
+     "grouped = codes.astype(np.uint32).reshape(8, K // 8, N).transpose(1, 0, 2)"),
+]
+
+
+@pytest.mark.parametrize("desc,old,new", GPTQ_MUTANTS, ids=[m[0] for m in GPTQ_MUTANTS])
+def test_planted_gptq_mistakes_are_caught(desc, old, new):
+    mut = _mutant("gptq", old, new)
+    assert not all(pins.run_gptq_pins(mut).values())

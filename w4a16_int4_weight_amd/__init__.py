@@ -7,6 +7,7 @@ Functions keep the C names:
   w4a16_packed_bytes(K, N, group_size)           -> int (0 if unsupported)
   w4a16_workspace_bytes(M, K, N, group_size)     -> int
   w4a16_repack(qweight, qzeros, scales, group_size, packed=None, stream=None) -> packed uint8 tensor
+  w4a16_repack_gptq(qweight, qzeros, scales, group_size, packed=None, stream=None) -> packed uint8 tensor
   w4a16_gemm(x, packed, N, group_size, bias=None, y=None, workspace=None, stream=None) -> y
       (workspace=None: a zero-filled per-device workspace is allocated on demand)
   w4a16_gemm_ex(..., path="auto"|"gemv"|"mfma", gemv_max_m=-1)            -> y
@@ -27,7 +28,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4a16.so
 
 __all__ = [
     "W4A16Error", "lib", "w4a16_layout_version", "w4a16_packed_bytes", "w4a16_workspace_bytes",
-    "w4a16_repack", "w4a16_gemm", "w4a16_gemm_ex", "w4a16_embedding", "w4a16_status_str", "STATUS", "PATHS",
+    "w4a16_repack", "w4a16_repack_gptq", "w4a16_gemm", "w4a16_gemm_ex", "w4a16_embedding", "w4a16_status_str", "STATUS", "PATHS",
 ]
 
 STATUS = {
@@ -68,6 +69,8 @@ def _load():
     h.w4a16_workspace_bytes.restype = _sz
     h.w4a16_repack.argtypes = [_vp, _vp, _vp, _int, _i64, _i64, _i64, _vp, _sz, _vp]
     h.w4a16_repack.restype = _int
+    h.w4a16_repack_gptq.argtypes = h.w4a16_repack.argtypes
+    h.w4a16_repack_gptq.restype = _int
     h.w4a16_gemm.argtypes = [_vp, _vp, _sz, _int, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _sz, _vp]
     h.w4a16_gemm.restype = _int
     h.w4a16_gemm_ex.argtypes = h.w4a16_gemm.argtypes + [_int, _i64]
@@ -143,6 +146,28 @@ def w4a16_repack(qweight, qzeros, scales, group_size=128, packed=None, stream=No
                             K, N, group_size, _ptr(packed), packed.numel() * packed.element_size(),
                             _stream(stream, qweight.device))
     _check(code, "w4a16_repack")
+    return packed
+
+
+def w4a16_repack_gptq(qweight, qzeros, scales, group_size=128, packed=None, stream=None):
+    """GPTQ-standard qweight int32 [K/8, N] (codes along K), qzeros int32 [K/G, N/8]
+    (standard order along N), scales [K/G, N] -> the same packed buffer as w4a16_repack."""
+    K, N = qweight.shape[0] * 8, qweight.shape[1]
+    nbytes = w4a16_packed_bytes(K, N, group_size)
+    if packed is None:
+        packed = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=qweight.device)
+    for t, name in ((qweight, "qweight"), (qzeros, "qzeros"), (scales, "scales")):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if qweight.dtype != torch.int32 or qzeros.dtype != torch.int32:
+        raise ValueError("qweight and qzeros must be int32")
+    G = K if group_size == -1 else group_size
+    if G > 0 and K % G == 0 and (tuple(qzeros.shape) != (K // G, N // 8) or tuple(scales.shape) != (K // G, N)):
+        raise ValueError("qzeros must be [K/G, N/8] and scales [K/G, N]")
+    code = _load().w4a16_repack_gptq(_ptr(qweight), _ptr(qzeros), _ptr(scales), _dtype_code(scales.dtype),
+                                     K, N, group_size, _ptr(packed), packed.numel() * packed.element_size(),
+                                     _stream(stream, qweight.device))
+    _check(code, "w4a16_repack_gptq")
     return packed
 
 

@@ -124,6 +124,25 @@ w4a16_status w4a16_repack(const int32_t* qweight, const int32_t* qzeros, const v
     return err == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
 }
 
+w4a16_status w4a16_repack_gptq(const int32_t* qweight, const int32_t* qzeros, const void* scales,
+                               w4a16_dtype dtype, int64_t K, int64_t N, int64_t group_size, void* packed,
+                               size_t packed_bytes, void* stream) {
+    int64_t G = 0;
+    w4a16_status st = check_shape(K, N, group_size, &G);
+    if (st != W4A16_OK) return st;
+    if (dtype != W4A16_FP16 && dtype != W4A16_BF16) return W4A16_ERR_DTYPE;
+    if (!qweight || !qzeros || !scales || !packed) return W4A16_ERR_NULL;
+    if (!aligned(qweight, 4) || !aligned(qzeros, 4) || !aligned(scales, 2) || !aligned(packed, 16))
+        return W4A16_ERR_ALIGN;
+    if (packed_bytes < packed_size(K, N)) return W4A16_ERR_BUFFER_SIZE;
+    st = check_device();
+    if (st != W4A16_OK) return st;
+    const hipError_t err = w4a16::launch_repack_gptq(qweight, qzeros, static_cast<const uint16_t*>(scales),
+                                                     static_cast<uint8_t*>(packed), K, N, G,
+                                                     static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
 size_t w4a16_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t group_size) {
     int64_t G = 0;
     if (M <= 0 || check_shape(K, N, group_size, &G) != W4A16_OK) return 0;

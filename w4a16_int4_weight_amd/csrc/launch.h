@@ -10,6 +10,9 @@ namespace w4a16 {
 // AWQ tensors -> packed tile layout. G: resolved group size (multiple of 128, divides K).
 hipError_t launch_repack(const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
                          uint8_t* packed, int64_t K, int64_t N, int64_t G, hipStream_t stream);
+// The same layout from GPTQ-standard tensors (codes packed along K, standard order).
+hipError_t launch_repack_gptq(const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
+                              uint8_t* packed, int64_t K, int64_t N, int64_t G, hipStream_t stream);
 
 // Weight-streaming split-K GEMV for 1 <= M <= 16 (K split over the waves of a
 // workgroup; no workspace).

@@ -130,7 +130,79 @@ __global__ __launch_bounds__(kRepackThreads) void repack_kernel(
     }
 }
 
+// ---- GPTQ-standard input: codes packed along K ----
+//
+// GPTQ-style packing runs along the input dimension in standard bit order (vLLM
+// note "Carga de capas cuantizadas", section "Motivación de diseño", on converting
+// AWQ to the GPTQ style the Marlin kernel takes): qweight int32 [K/8, N], word
+// (i, n) holding rows 8 i + j of column n in nibble j; qzeros int32 [K/G, N/8]
+// packed along N, nibble j = column 8 w + j. A tile word holds the same 8 rows of
+// one column (rows 32 w + 8 h + 0..7 of a row block, word w of lane c + 16 h), with
+// row e in nibble slot s where e = tile_row_of_slot(s): even rows in the low half,
+// odd rows in the high half. So each tile word is one GPTQ word with its nibbles
+// unzipped, and no transpose is needed.
+constexpr int kGptqColumns = 256;    // columns per workgroup, one per thread
+
+// nibbles 0,2,4,6 of v -> nibbles 0..3, nibbles 1,3,5,7 -> nibbles 4..7
+__device__ __forceinline__ uint32_t unzip_nibbles(uint32_t v) {
+    uint32_t e = v & 0x0F0F0F0Fu;            // even nibbles, one per byte
+    uint32_t o = (v >> 4) & 0x0F0F0F0Fu;     // odd nibbles
+    e = (e | (e >> 4)) & 0x00FF00FFu;
+    o = (o | (o >> 4)) & 0x00FF00FFu;
+    e = (e | (e >> 8)) & 0x0000FFFFu;
+    o = (o | (o >> 8)) & 0x0000FFFFu;
+    return e | (o << 16);
+}
+
+__global__ __launch_bounds__(kGptqColumns) void repack_gptq_kernel(
+    const uint32_t* __restrict__ qweight, const uint32_t* __restrict__ qzeros,
+    const uint16_t* __restrict__ scales, uint8_t* __restrict__ packed,
+    int64_t K, int64_t N, int64_t G) {
+    const int64_t KB = K / kRowsPerBlock;
+    const int64_t kb = blockIdx.y;
+    const int64_t n = (int64_t)blockIdx.x * kGptqColumns + threadIdx.x;
+    if (n >= N) return;
+    const int64_t nb = n / kColsPerBlock;
+    const int c = (int)(n % kColsPerBlock);
+    uint4* blk = reinterpret_cast<uint4*>(packed + (nb * KB + kb) * kBlockBytes);
+    // GPTQ word row i = 16 kb + 4 w + h: lane group h, word w of the tile
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        uint32_t t[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) t[w] = unzip_nibbles(qweight[(16 * kb + 4 * w + h) * N + n]);
+        blk[c + 16 * h] = make_uint4(t[0], t[1], t[2], t[3]);
+    }
+    if (kb != 0) return;
+    // metadata row of column n: scale bits | zero << 16 per row block, zero padding
+    const int64_t KBP = padded_row_blocks(K);
+    uint4* row = reinterpret_cast<uint4*>(packed + K * N / 2 + n * KBP * 4);
+    for (int64_t p0 = 0; p0 < KBP; p0 += 4) {
+        uint32_t word[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int64_t b = p0 + e;
+            word[e] = 0u;
+            if (b < KB) {
+                const int64_t g = (b * kRowsPerBlock) / G;
+                const uint32_t z = (qzeros[g * (N / 8) + n / 8] >> (4 * (n % 8))) & 0xFu;
+                word[e] = (uint32_t)scales[g * N + n] | (z << 16);
+            }
+        }
+        row[p0 / 4] = make_uint4(word[0], word[1], word[2], word[3]);
+    }
+}
+
 }  // namespace
+
+hipError_t launch_repack_gptq(const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
+                              uint8_t* packed, int64_t K, int64_t N, int64_t G, hipStream_t stream) {
+    const dim3 grid((unsigned)((N + kGptqColumns - 1) / kGptqColumns), (unsigned)(K / kRowsPerBlock));
+    hipLaunchKernelGGL(repack_gptq_kernel, grid, dim3(kGptqColumns), 0, stream,
+                       reinterpret_cast<const uint32_t*>(qweight), reinterpret_cast<const uint32_t*>(qzeros),
+                       scales, packed, K, N, G);
+    return hipGetLastError();
+}
 
 hipError_t launch_repack(const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
                          uint8_t* packed, int64_t K, int64_t N, int64_t G, hipStream_t stream) {
