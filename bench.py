@@ -5,8 +5,9 @@ N=13312, group size 128, bf16, in algorithmic GB/s. A step is one w4a16_gemm cal
 (dispatch, split-K GEMV, in-kernel reduction and epilogue) on one activation
 batch; the weights were repacked once before timing. Secondary entries in the same
 JSON line measure the other rows of the path on their own workloads: the LM-head
-repack (GB/s), the MFMA GEMM at M=512 (TFLOP/s), the GEMV on the other shapes and
-the tied-embedding gather of 512 tokens from the packed LM head (GB/s).
+repack from AWQ and from GPTQ-standard tensors (GB/s), the MFMA GEMM at M=512
+(TFLOP/s), the GEMV on the other shapes and the tied-embedding gather of 512 tokens
+from the packed LM head (GB/s).
 
 Timing: warm-up calls, then K calls captured in one HIP graph and replayed once
 between two events on the launch stream, with a device synchronisation on both
@@ -123,10 +124,18 @@ def measure_gemm(w, workload, M, steps, warmup, dev, path="auto"):
                 GBps=nbytes / per_launch_s / 1e9, TFLOPs=flops / per_launch_s / 1e12)
 
 
-def measure_repack(w, workload, steps, warmup, dev):
+def measure_repack(w, workload, steps, warmup, dev, fmt="awq"):
+    """fmt "awq": w4a16_repack from AWQ tensors; "gptq": w4a16_repack_gptq from
+    GPTQ-standard tensors of the same shape (same recipe, same byte count)."""
     import torch
     import synth
-    ws = synth.make(workload, Ms=())
+    if fmt == "awq":
+        ws = synth.make(workload, Ms=())
+        fn = w.w4a16_repack
+    else:
+        wl = synth.WORKLOADS[workload]
+        ws = synth.draw_gptq_weights(wl.seed, wl.K, wl.N, wl.dtype, wl.group_size)
+        fn = w.w4a16_repack_gptq
     K, N, G = ws.K, ws.N, ws.group_size
     qw = torch.from_numpy(ws.qweight).to(dev)
     qz = torch.from_numpy(ws.qzeros).to(dev)
@@ -136,14 +145,15 @@ def measure_repack(w, workload, steps, warmup, dev):
     copies = max(1, min(16, math.ceil(ROTATE_BYTES / (in_bytes + pbytes))))
     ins = [(qw, qz, sc)] + [(qw.clone(), qz.clone(), sc.clone()) for _ in range(copies - 1)]
     outs = [torch.empty(pbytes, dtype=torch.uint8, device=dev) for _ in range(copies)]
-    calls = [(lambda a=ins[i % copies], o=outs[i % copies]: w.w4a16_repack(a[0], a[1], a[2], G, packed=o))
+    calls = [(lambda a=ins[i % copies], o=outs[i % copies]: fn(a[0], a[1], a[2], G, packed=o))
              for i in range(steps)]
     ms, n = time_graph(calls, warmup)
     per_launch_s = ms / 1e3 / n
     nbytes = repack_bytes(K, N, G)
     del ins, outs
     torch.cuda.empty_cache()
-    return dict(workload=workload + " repack", K=K, N=N, group_size=G, dtype=ws.dtype, kernel="w4a16_repack",
+    return dict(workload=workload + (" repack" if fmt == "awq" else " repack from GPTQ"), K=K, N=N, group_size=G,
+                dtype=ws.dtype, kernel="w4a16_repack" if fmt == "awq" else "w4a16_repack_gptq",
                 copies=copies, launches=n, us_per_launch=per_launch_s * 1e6, algorithmic_bytes=nbytes,
                 GBps=nbytes / per_launch_s / 1e9)
 
@@ -332,6 +342,10 @@ def main():
         r = measure_repack(w, "lm_head", max(10, args.steps // 10), 3, dev)
         r["roofline"] = roofline_hbm(r)
         log(f"lm_head repack: {r['us_per_launch']:.1f} us, {r['GBps']:.0f} GB/s")
+        secondary.append(r)
+        r = measure_repack(w, "lm_head", max(10, args.steps // 10), 3, dev, fmt="gptq")
+        r["roofline"] = roofline_hbm(r)
+        log(f"lm_head repack from GPTQ: {r['us_per_launch']:.1f} us, {r['GBps']:.0f} GB/s")
         secondary.append(r)
         e = measure_embedding(w, "lm_head", 512, args.steps, min(args.warmup, 10), dev)
         e["roofline"] = roofline_hbm(e)
