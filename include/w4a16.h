@@ -44,7 +44,7 @@ extern "C" {
 typedef enum {
     W4A16_OK = 0,
     W4A16_ERR_NULL = 1,         /* a required pointer is NULL                       */
-    W4A16_ERR_SHAPE = 2,        /* M < 0, K or N <= 0, K % 128 != 0, N % 16 != 0,
+    W4A16_ERR_SHAPE = 2,        /* M < 0, K or N <= 0, K % 128 != 0, N % 8 != 0,
                                    K > 2^20, N > 2^28, K*N > 2^37 or M*K > 2^32       */
     W4A16_ERR_GROUP = 3,        /* group size not -1 and not a multiple of 128 dividing K */
     W4A16_ERR_DTYPE = 4,        /* dtype is neither W4A16_FP16 nor W4A16_BF16        */
@@ -71,8 +71,11 @@ typedef enum {
 int w4a16_layout_version(void);
 
 /* Bytes of the packed buffer for a K x N weight with group size `group_size`:
- * K*N/2 (4-bit codes) + 4*KBP*N (one 32-bit scale/zero word per column per
- * 128-row block, KBP = K/128 rounded up to a multiple of 4).
+ * K*Np/2 (4-bit codes) + 4*KBP*Np (one 32-bit scale/zero word per column per
+ * 128-row block), Np = N rounded up to a multiple of 16 and KBP = K/128 rounded up
+ * to a multiple of 4. N must be a multiple of 8 (the AWQ and GPTQ pack factor); with
+ * N % 16 == 8 the last 16-column block carries 8 zero columns that no entry point
+ * reads into a result.
  * Returns 0 if the shape or group size is not supported. */
 size_t w4a16_packed_bytes(int64_t K, int64_t N, int64_t group_size);
 

@@ -9,9 +9,15 @@ rewrites qweight into the layout the kernel expects) but the layout is the
 kernel's own. This library's layout, version 1, for a K x N weight with group
 size G (G = K for group_size = -1; G a multiple of 128 dividing K):
 
-  KB = K / 128 row blocks, NB = N / 16 column blocks.
+  KB = K / 128 row blocks; Np = N rounded up to a multiple of 16, NB = Np / 16
+  column blocks. N must be a multiple of 8, the pack factor of the checkpoint
+  words (vLLM note, "Flujo de datos": packed_factor 8). When N % 16 == 8 the last
+  block's columns N .. Np-1 are padding: code 0 in every row and metadata word 0
+  (the vllm-omni commit "cpu_int4: dequantize prefill weights from the tinygemm
+  layout, not a copy" reads an N that does not fill the last block as a case to be
+  handled, not silently mis-read; here it is handled by whole zero columns).
 
-  Weight plane, bytes [0, K*N/2):
+  Weight plane, bytes [0, K*Np/2):
     block (nb, kb) is 1024 bytes at offset 1024 * (nb * KB + kb); so the whole K
     range of one 16-column block is contiguous.
     Inside a block, lane L in 0..63 owns bytes 16L .. 16L+15 = four little-endian
@@ -20,7 +26,7 @@ size G (G = K for group_size = -1; G a multiple of 128 dividing K):
     (bits 4s .. 4s+3) holds the code of row e = TILE_ORDER[s].
     TILE_ORDER = (0, 2, 4, 6, 1, 3, 5, 7): slots t and t+4 hold rows 2t and 2t+1.
 
-  Metadata plane, bytes [K*N/2, K*N/2 + 4*N*KBP), KBP = KB rounded up to a
+  Metadata plane, bytes [K*Np/2, K*Np/2 + 4*Np*KBP), KBP = KB rounded up to a
   multiple of 4:
     uint32 number n * KBP + kb describes column n over row block kb (so one
     column's words for all row blocks are contiguous), whose group is
@@ -30,7 +36,7 @@ size G (G = K for group_size = -1; G a multiple of 128 dividing K):
       bits 20..31 = 0;
     words kb = KB .. KBP-1 of every column are 0 (padding).
 
-  Total size: K*N/2 + 4*N*KBP bytes.
+  Total size: K*Np/2 + 4*Np*KBP bytes.
 
 Column blocks are independent (as the n-blocks of the CPU layout are in the
 vllm-omni commit "cpu_int4: repack weights in n-blocks, to bound the load-time
@@ -53,8 +59,8 @@ def check_shape(K, N, group_size):
         raise ValueError("K and N must be positive")
     if K % ROWS_PER_BLOCK != 0:
         raise ValueError("K must be a multiple of 128")
-    if N % COLS_PER_BLOCK != 0:
-        raise ValueError("N must be a multiple of 16")
+    if N % 8 != 0:
+        raise ValueError("N must be a multiple of 8")
     G = K if group_size == -1 else int(group_size)
     if G <= 0 or G % ROWS_PER_BLOCK != 0 or K % G != 0:
         raise ValueError("group size must be -1 or a multiple of 128 dividing K")
@@ -66,9 +72,14 @@ def padded_row_blocks(K):
     return (KB + 3) // 4 * 4
 
 
+def padded_cols(N):
+    return (N + COLS_PER_BLOCK - 1) // COLS_PER_BLOCK * COLS_PER_BLOCK
+
+
 def packed_bytes(K, N, group_size):
     check_shape(K, N, group_size)
-    return K * N // 2 + 4 * N * padded_row_blocks(K)
+    Np = padded_cols(N)
+    return K * Np // 2 + 4 * Np * padded_row_blocks(K)
 
 
 def repack(Q, Z, scale_bits, group_size):
@@ -81,6 +92,10 @@ def repack(Q, Z, scale_bits, group_size):
     scale_bits = np.asarray(scale_bits, dtype=np.uint16)
     if Z.shape != (K // G, N) or scale_bits.shape != (K // G, N):
         raise ValueError("zeros and scales must be [K/G, N]")
+    N_real, N = N, padded_cols(N)
+    if N != N_real:       # zero padding columns: code 0, zero point 0, scale bits 0
+        pad = ((0, 0), (0, N - N_real))
+        Q, Z, scale_bits = np.pad(Q, pad), np.pad(Z, pad), np.pad(scale_bits, pad)
     KB, NB = K // ROWS_PER_BLOCK, N // COLS_PER_BLOCK
 
     # Name the axes of Q by the layout: k = 128 kb + 32 i + 8 h + e, n = 16 nb + c.
@@ -103,7 +118,7 @@ def repack(Q, Z, scale_bits, group_size):
         np.ascontiguousarray(weight_plane).astype("<u4").view(np.uint8).reshape(-1),
         np.ascontiguousarray(meta).astype("<u4").view(np.uint8).reshape(-1),
     ])
-    assert out.size == packed_bytes(K, N, group_size)
+    assert out.size == packed_bytes(K, N_real, group_size)
     return out
 
 
@@ -114,13 +129,16 @@ def repack_loops(Q, Z, scale_bits, group_size):
     Q = np.asarray(Q, dtype=np.uint8)
     K, N = Q.shape
     G = check_shape(K, N, group_size)
-    KB, NB = K // ROWS_PER_BLOCK, N // COLS_PER_BLOCK
+    Np = padded_cols(N)
+    KB, NB = K // ROWS_PER_BLOCK, Np // COLS_PER_BLOCK
     out = bytearray(packed_bytes(K, N, group_size))
     for nb in range(NB):
         for kb in range(KB):
             base = BLOCK_BYTES * (nb * KB + kb)
             for lane in range(64):
                 n = 16 * nb + lane % 16
+                if n >= N:
+                    continue           # padding column: its bytes stay 0
                 for i in range(4):
                     word = 0
                     for s in range(8):
@@ -128,9 +146,9 @@ def repack_loops(Q, Z, scale_bits, group_size):
                         word |= int(Q[k, n]) << (4 * s)
                     off = base + 16 * lane + 4 * i
                     out[off:off + 4] = word.to_bytes(4, "little")
-    meta_base = K * N // 2
+    meta_base = K * Np // 2
     KBP = padded_row_blocks(K)
-    for n in range(N):
+    for n in range(N):                 # padding columns' words stay 0
         for kb in range(KB):           # words kb >= KB stay 0
             g = (128 * kb) // G
             word = int(scale_bits[g, n]) | (int(Z[g, n]) << 16)
@@ -147,6 +165,7 @@ def decode(packed, K, N, group_size):
     packed = np.asarray(packed, dtype=np.uint8)
     if packed.size != packed_bytes(K, N, group_size):
         raise ValueError("packed buffer has the wrong size")
+    N_real, N = N, padded_cols(N)
     KB, NB = K // ROWS_PER_BLOCK, N // COLS_PER_BLOCK
     wbytes = K * N // 2
     words = packed[:wbytes].view("<u4").reshape(NB, KB, 4, 16, 4)     # [nb, kb, h, c, i]
@@ -169,4 +188,6 @@ def decode(packed, K, N, group_size):
     first = meta_g[:, 0, :]
     S = (first & np.uint32(0xFFFF)).astype(np.uint16)
     Z = ((first >> np.uint32(16)) & np.uint32(0xF)).astype(np.uint8)
-    return Q, Z, S
+    if np.any(Q[:, N_real:]) or np.any(meta[:, N_real:]):
+        raise ValueError("padding columns are not zero")
+    return Q[:, :N_real], Z[:, :N_real], S[:, :N_real]

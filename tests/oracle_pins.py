@@ -277,6 +277,33 @@ def pin_layout_metadata(tile_layout, K=768, N=32, G=256):
     return meta.tolist() == expect
 
 
+def pin_layout_half_block(tile_layout):
+    """N = 24 (a last half block): every real code 15, zero points 5, scale bits
+    0x1234 + n. Closed form: block 1 holds columns 16..23 in lanes c < 8 (every word
+    0xFFFFFFFF) and zero words in lanes c >= 8; the metadata plane starts at K*32/2
+    and columns 24..31 have all-zero words; the buffer is K*32/2 + 4*32*KBP bytes."""
+    K, N, G = 256, 24, 128
+    KB, KBP = K // 128, 4
+    Q = np.full((K, N), 15, dtype=np.uint8)
+    Z = np.full((K // G, N), 5, dtype=np.uint8)
+    S = np.tile((0x1234 + np.arange(N)).astype(np.uint16), (K // G, 1))
+    out = tile_layout.repack(Q, Z, S, G)
+    if out.size != K * 32 // 2 + 4 * 32 * KBP:
+        return False
+    words = out[:K * 32 // 2].view("<u4").reshape(2, KB, 64, 4)          # [nb, kb, lane, i]
+    c = np.arange(64) % 16
+    if not np.all(words[0] == 0xFFFFFFFF):
+        return False
+    if not (np.all(words[1][:, c < 8] == 0xFFFFFFFF) and np.all(words[1][:, c >= 8] == 0)):
+        return False
+    meta = out[K * 32 // 2:].view("<u4").reshape(32, KBP)
+    for n in range(32):
+        want = [(0x1234 + n) | (5 << 16) if (n < N and kb < KB) else 0 for kb in range(KBP)]
+        if meta[n].tolist() != want:
+            return False
+    return True
+
+
 # ---------------------------------------------------------------- tied embedding
 
 def _bf16_bits_of(v):

@@ -192,7 +192,8 @@ def test_layout_sizes_and_rejections():
     assert tile_layout.packed_bytes(2048, 13312, 128) == 2048 * 13312 // 2 + 4 * 16 * 13312
     assert tile_layout.packed_bytes(6656, 2048, 128) == 6656 * 2048 // 2 + 4 * 52 * 2048
     assert tile_layout.packed_bytes(384, 16, 128) == 384 * 16 // 2 + 4 * 4 * 16      # 3 row blocks padded to 4
-    for K, N, G in [(100, 16, 128), (256, 24, 128), (256, 16, 64), (384, 16, 256)]:
+    assert tile_layout.packed_bytes(256, 24, 128) == 256 * 32 // 2 + 4 * 4 * 32      # half block padded to 16
+    for K, N, G in [(100, 16, 128), (256, 20, 128), (256, 16, 64), (384, 16, 256)]:
         with pytest.raises(ValueError):
             tile_layout.packed_bytes(K, N, G)
 
@@ -401,3 +402,46 @@ GPTQ_MUTANTS = [
 def test_planted_gptq_mistakes_are_caught(desc, old, new):
     mut = _mutant("gptq", old, new)
     assert not all(pins.run_gptq_pins(mut).values())
+
+
+# ---------------------------------------------------------------- N % 16 == 8
+
+def test_layout_half_block_padding():
+    assert pins.pin_layout_half_block(tile_layout)
+
+
+def test_layout_half_block_decode_roundtrip():
+    rng = np.random.default_rng(12)
+    K, N, G = 384, 40, 128
+    Q = rng.integers(0, 16, (K, N), dtype=np.uint8)
+    Z = rng.integers(0, 16, (K // G, N), dtype=np.uint8)
+    S = rng.integers(0, 2**16, (K // G, N), dtype=np.uint16)
+    out = tile_layout.repack(Q, Z, S, G)
+    assert np.array_equal(out, tile_layout.repack_loops(Q, Z, S, G))
+    Q2, Z2, S2 = tile_layout.decode(out, K, N, G)
+    assert np.array_equal(Q2, Q) and np.array_equal(Z2, Z) and np.array_equal(S2, S)
+    bad = out.copy()
+    bad[(K * 48 // 2) + 4 * 4 * 47] = 1          # metadata word of padding column 47
+    with pytest.raises(ValueError):
+        tile_layout.decode(bad, K, N, G)
+
+
+HALF_BLOCK_MUTANTS = [
+    ("padding repeats the last column", "Q, Z, scale_bits = np.pad(Q, pad), np.pad(Z, pad), np.pad(scale_bits, pad)",
+     "Q, Z, scale_bits = np.pad(Q, pad, mode='edge'), np.pad(Z, pad), np.pad(scale_bits, pad)"),
+    ("padding metadata repeats the last column",
+     "Q, Z, scale_bits = np.pad(Q, pad), np.pad(Z, pad), np.pad(scale_bits, pad)",
+     "Q, Z, scale_bits = np.pad(Q, pad), np.pad(Z, pad), np.pad(scale_bits, pad, mode='edge')"),
+    ("metadata plane placed after K*N/2", "meta = np.zeros((N, padded_row_blocks(K)), dtype=np.uint32)",
+     "meta = np.zeros((N_real, padded_row_blocks(K)), dtype=np.uint32)"),
+]
+
+
+@pytest.mark.parametrize("desc,old,new", HALF_BLOCK_MUTANTS, ids=[m[0] for m in HALF_BLOCK_MUTANTS])
+def test_planted_half_block_mistakes_are_caught(desc, old, new):
+    try:
+        mut = _mutant("tile_layout", old, new)
+        ok = pins.pin_layout_half_block(mut)
+    except (ValueError, AssertionError, IndexError):
+        ok = False
+    assert not ok

@@ -24,7 +24,7 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 // Resolved group size, or 0 if (K, N, group_size) is outside the tile layout.
 w4a16_status check_shape(int64_t K, int64_t N, int64_t group_size, int64_t* G_out) {
-    if (K <= 0 || N <= 0 || K % 128 != 0 || N % 16 != 0) return W4A16_ERR_SHAPE;
+    if (K <= 0 || N <= 0 || K % 128 != 0 || N % 8 != 0) return W4A16_ERR_SHAPE;
     if (K > kMaxK || N > kMaxN || K * N > kMaxKN) return W4A16_ERR_SHAPE;
     const int64_t G = group_size == -1 ? K : group_size;
     if (G <= 0 || G % 128 != 0 || K % G != 0) return W4A16_ERR_GROUP;
@@ -32,9 +32,12 @@ w4a16_status check_shape(int64_t K, int64_t N, int64_t group_size, int64_t* G_ou
     return W4A16_OK;
 }
 
+// K x Np codes (Np = N rounded up to 16 columns) + one 32-bit word per column per
+// 128-row block, the row-block count rounded up to 4
 size_t packed_size(int64_t K, int64_t N) {
     const size_t kbp = (size_t)((K / 128 + 3) / 4 * 4);
-    return (size_t)(K * N / 2) + (size_t)4 * kbp * (size_t)N;
+    const size_t np = (size_t)((N + 15) / 16 * 16);
+    return (size_t)K * np / 2 + (size_t)4 * kbp * np;
 }
 
 // 0 = unknown, 1 = gfx950, 2 = other; cached per device ordinal.
@@ -188,7 +191,7 @@ const char* w4a16_status_str(w4a16_status status) {
     switch (status) {
         case W4A16_OK: return "ok";
         case W4A16_ERR_NULL: return "a required pointer is NULL";
-        case W4A16_ERR_SHAPE: return "unsupported shape (need M >= 0, K % 128 == 0, N % 16 == 0)";
+        case W4A16_ERR_SHAPE: return "unsupported shape (need M >= 0, K % 128 == 0, N % 8 == 0)";
         case W4A16_ERR_GROUP: return "unsupported group size (need -1 or a multiple of 128 dividing K)";
         case W4A16_ERR_DTYPE: return "unsupported dtype (need fp16 or bf16)";
         case W4A16_ERR_ALIGN: return "misaligned pointer";

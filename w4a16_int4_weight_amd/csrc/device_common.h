@@ -25,6 +25,9 @@ constexpr int kColsPerBlock = 16;
 constexpr int kBlockBytes = 1024;
 
 __host__ __device__ constexpr int64_t padded_row_blocks(int64_t K) { return ((K / kRowsPerBlock) + 3) / 4 * 4; }
+// Columns of the packed layout: N rounded up to whole 16-column blocks (N % 8 == 0;
+// a last block of 8 real columns carries 8 zero columns, code 0 and metadata 0).
+__host__ __device__ constexpr int64_t padded_cols(int64_t N) { return (N + kColsPerBlock - 1) / kColsPerBlock * kColsPerBlock; }
 
 // Row e held by nibble slot s of a tile word: 0,2,4,6,1,3,5,7. Slots t and t+4
 // hold rows 2t and 2t+1, so (word >> 4t) & 0x000F000F puts the pair (2t, 2t+1)

@@ -45,7 +45,7 @@ __global__ __launch_bounds__(64 * kTokensPerWorkgroup) void embedding_kernel(
     // this column's 16-byte chunk of lane group 0 in its first block; group h is
     // 256 h bytes further on, row block kb 1 KiB * kb
     const uint8_t* codes = packed + (size_t)(col / kColsPerBlock) * KB * kBlockBytes + 16 * (col % kColsPerBlock);
-    const uint32_t* meta = reinterpret_cast<const uint32_t*>(packed + (size_t)K * N / 2) + (size_t)col * KBP;
+    const uint32_t* meta = reinterpret_cast<const uint32_t*>(packed + (size_t)K * padded_cols(N) / 2) + (size_t)col * KBP;
     uint16_t* row = out + (size_t)t * K;
     for (int q = lane; q < KB * 4; q += 64) {
         const int kb = q >> 2;

@@ -129,7 +129,8 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(
 
     const int KB = K / kRowsPerBlock;
     const int KBP = (int)padded_row_blocks(K);
-    const int NB = N / kColsPerBlock;
+    const int Np = (int)padded_cols(N);                         // columns of the packed layout
+    const int NB = Np / kColsPerBlock;
     const int kb_begin = (int)((int64_t)KB * split / splits);
     const int kb_end = (int)((int64_t)KB * (split + 1) / splits);
     const int nkb = kb_end - kb_begin;
@@ -166,10 +167,10 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(
         woff[j] = (uint32_t)(nbj - nbw0) * (uint32_t)KB * kBlockBytes + 16u * (uint32_t)lane;
     }
     // metadata: column words of this wave's columns (lanes past 16 * CBW repeat one)
-    const int col0 = nbw * kColsPerBlock < N ? nbw * kColsPerBlock : N - kColsPerBlock;
+    const int col0 = nbw * kColsPerBlock < Np ? nbw * kColsPerBlock : Np - kColsPerBlock;
     const int ncol = nbw * kColsPerBlock + (lane < 16 * CBW ? lane : 0);
-    const uint8_t* mbase = uniform_ptr(packed + (size_t)K * N / 2 + (size_t)col0 * KBP * 4);
-    const uint32_t moff = (uint32_t)((ncol < N ? ncol : N - 1) - col0) * (uint32_t)KBP * 4u;
+    const uint8_t* mbase = uniform_ptr(packed + (size_t)K * Np / 2 + (size_t)col0 * KBP * 4);
+    const uint32_t moff = (uint32_t)((ncol < Np ? ncol : Np - 1) - col0) * (uint32_t)KBP * 4u;
     const uint32_t ring_base = lds_addr(&ring[0]);
 
     // copy q (0 .. kDmaPerStage-1) of k block kb into ring slot `slot`
@@ -384,6 +385,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(
     for (int j = 0; j < CBW; ++j) {
         if (nbw + j >= NB) continue;
         const int n = (nbw + j) * kColsPerBlock + 4 * h;
+        if (n >= N) continue;                  // zero padding of a last half block (N % 8 == 0)
         float bv[4] = {0.f, 0.f, 0.f, 0.f};
         if (bias) {
 #pragma unroll
@@ -440,7 +442,7 @@ void launch_typed(const GemmPlan& p, const uint16_t* x, const uint8_t* packed, c
 
 GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N) {
     GemmPlan p;
-    const int64_t NB = N / kColsPerBlock;
+    const int64_t NB = padded_cols(N) / kColsPerBlock;
     const int64_t KB = K / kRowsPerBlock;
     p.mr = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
     p.tiles_m = (int)((M + 16 * p.mr - 1) / (16 * p.mr));

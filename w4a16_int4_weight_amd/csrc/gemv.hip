@@ -135,8 +135,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(const GemvArgs a) 
     const int cbl = w / a.waves_k;                                       // column block in the workgroup
     const int wk = w - cbl * a.waves_k;                                  // K slice of this wave
     const int nb_raw = blockIdx.x * (waves / a.waves_k) + cbl;
-    const bool nb_valid = nb_raw < N / kColsPerBlock;
-    const int nb = nb_valid ? nb_raw : N / kColsPerBlock - 1;            // a ragged last workgroup
+    const int NB = (int)(padded_cols(N) / kColsPerBlock);
+    const bool nb_valid = nb_raw < NB;
+    const int nb = nb_valid ? nb_raw : NB - 1;                           // a ragged last workgroup
                                                                          // repeats the last block, unstored
     const int lane = threadIdx.x & 63;
     const int c = lane & 15;         // column in the block, and activation row of the A operand
@@ -176,7 +177,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(const GemvArgs a) 
     // 2. codes and metadata of this wave's first run (clamped into the column block;
     //    row blocks past kb_end are loaded but weighted by zero)
     const uint4* wcol = reinterpret_cast<const uint4*>(a.packed) + (size_t)nb * KB * 64 + lane;
-    const uint4* mcol = reinterpret_cast<const uint4*>(a.packed + (size_t)K * N / 2) + ((size_t)(nb * kColsPerBlock + c) * KBP) / 4;
+    const uint4* mcol = reinterpret_cast<const uint4*>(a.packed + (size_t)K * padded_cols(N) / 2) + ((size_t)(nb * kColsPerBlock + c) * KBP) / 4;
     auto load_run = [&](int kb0, uint4 (&wq)[kRun], uint4& md) {
         md = load_once(mcol + (kb0 < KB ? kb0 : KB - 1) / 4);
 #pragma unroll
@@ -289,8 +290,10 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(const GemvArgs a) 
     }
     if (!nb_valid) return;
 
-    // lane (c, h), register r -> row 4h + r, column 16 nb + c
+    // lane (c, h), register r -> row 4h + r, column 16 nb + c (columns past N: the
+    // zero padding of a last half block, not stored)
     const int n = nb * kColsPerBlock + c;
+    if (n >= N) return;
     const float b = a.bias ? half_bits_to_f32<kBF16>(a.bias[n]) : 0.f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -302,7 +305,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(const GemvArgs a) 
 template <bool kBF16>
 void launch_typed(const GemvPlan& p, const GemvArgs& args, hipStream_t s) {
     const int cols_per_wg = p.waves / p.waves_k;
-    const dim3 grid((unsigned)((args.N / kColsPerBlock + cols_per_wg - 1) / cols_per_wg));
+    const dim3 grid((unsigned)((padded_cols(args.N) / kColsPerBlock + cols_per_wg - 1) / cols_per_wg));
     const dim3 block((unsigned)(64 * p.waves));
     if (!p.staged)
         hipLaunchKernelGGL((gemv_kernel<kBF16, false, 1>), grid, block, p.lds_bytes, s, args);
@@ -343,7 +346,7 @@ GemvPlan plan_gemv_with(int64_t M, int64_t K, int64_t N, int cols_per_wg) {
 // Measured on the 2048 x 13312 decode shape: M = 8 -9%, M = 4 -4%, M = 1 even; four
 // blocks per workgroup, or two for N = 131072 or N = 3072, measured slower.
 GemvPlan plan_gemv(int64_t M, int64_t K, int64_t N) {
-    const int64_t NB = N / kColsPerBlock;
+    const int64_t NB = padded_cols(N) / kColsPerBlock;
     const GemvPlan one = plan_gemv_with(M, K, N, 1);
     if (NB <= 1024 && NB / 2 >= 200 && 2 * one.waves_k <= kMaxWaves) return plan_gemv_with(M, K, N, 2);
     return one;

@@ -86,31 +86,32 @@ __global__ __launch_bounds__(kRepackThreads) void repack_kernel(
     // 3. column 8 j + c8 -> block (j / 2), lane (8 (j % 2) + c8) + 16 h: words i = 0..3.
     //    The tile's 32 blocks are assembled in LDS and written out whole, each wave
     //    storing contiguous 1 KiB blocks.
+    //    With N % 16 == 8 the last block has one word: its other 8 columns are zero.
     __shared__ uint4 stage[kWordsPerTile / 2 * 64];
-    if (active) {
 #pragma unroll
-        for (int c8 = 0; c8 < 8; ++c8) {
-            const int s = awq_slot_of_column(c8);
-            const int lane = 8 * (jl & 1) + c8 + 16 * h;
-            stage[(jl >> 1) * 64 + lane] = make_uint4(t[0][s], t[1][s], t[2][s], t[3][s]);
-        }
+    for (int c8 = 0; c8 < 8; ++c8) {
+        const int s = awq_slot_of_column(c8);
+        const int lane = 8 * (jl & 1) + c8 + 16 * h;
+        stage[(jl >> 1) * 64 + lane] = active ? make_uint4(t[0][s], t[1][s], t[2][s], t[3][s]) : make_uint4(0, 0, 0, 0);
     }
     __syncthreads();
     const int64_t tile_words = words_per_row - j0 < kWordsPerTile ? words_per_row - j0 : kWordsPerTile;
-    const int nblk = (int)(tile_words / 2);                       // N % 16 == 0: whole blocks
+    const int nblk = (int)((tile_words + 1) / 2);                 // a last half block included
     for (int q = tid; q < nblk * 64; q += kRepackThreads) {
         const int64_t nb = (j0 >> 1) + (q >> 6);
         reinterpret_cast<uint4*>(packed + (nb * KB + kb) * kBlockBytes)[q & 63] = stage[q];
     }
 
-    // 4. metadata: the workgroups of row block 0 write, for each column of their tile,
-    //    its whole row of KBP words (scale bits | zero << 16 per row block, then zero
-    //    padding), 16 bytes at a time
+    // 4. metadata: the workgroups of row block 0 write, for each column of their tile's
+    //    blocks, its whole row of KBP words (scale bits | zero << 16 per row block, then
+    //    zero padding; all zero for the padding columns of a last half block), 16 bytes
+    //    at a time
     if (kb != 0) return;
     const int64_t KBP = padded_row_blocks(K);
-    uint32_t* meta = reinterpret_cast<uint32_t*>(packed + K * N / 2);
-    for (int q = tid; q < tile_words * 8; q += kRepackThreads) {
+    uint32_t* meta = reinterpret_cast<uint32_t*>(packed + K * padded_cols(N) / 2);
+    for (int q = tid; q < nblk * kColsPerBlock; q += kRepackThreads) {
         const int64_t n = j0 * 8 + q;
+        const bool real = n < N;
         const int zshift = 4 * awq_slot_of_column((int)(n & 7));
         uint4* row = reinterpret_cast<uint4*>(meta + n * KBP);
         for (int64_t p0 = 0; p0 < KBP; p0 += 4) {
@@ -119,7 +120,7 @@ __global__ __launch_bounds__(kRepackThreads) void repack_kernel(
             for (int e = 0; e < 4; ++e) {
                 const int64_t b = p0 + e;
                 word[e] = 0u;
-                if (b < KB) {
+                if (real && b < KB) {
                     const int64_t g = (b * kRowsPerBlock) / G;
                     const uint32_t z = (qzeros[g * words_per_row + (n >> 3)] >> zshift) & 0xFu;
                     word[e] = (uint32_t)scales[g * N + n] | (z << 16);
@@ -161,7 +162,8 @@ __global__ __launch_bounds__(kGptqColumns) void repack_gptq_kernel(
     const int64_t KB = K / kRowsPerBlock;
     const int64_t kb = blockIdx.y;
     const int64_t n = (int64_t)blockIdx.x * kGptqColumns + threadIdx.x;
-    if (n >= N) return;
+    if (n >= padded_cols(N)) return;
+    const bool real = n < N;          // else a zero padding column of a last half block
     const int64_t nb = n / kColsPerBlock;
     const int c = (int)(n % kColsPerBlock);
     uint4* blk = reinterpret_cast<uint4*>(packed + (nb * KB + kb) * kBlockBytes);
@@ -170,20 +172,20 @@ __global__ __launch_bounds__(kGptqColumns) void repack_gptq_kernel(
     for (int h = 0; h < 4; ++h) {
         uint32_t t[4];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) t[w] = unzip_nibbles(qweight[(16 * kb + 4 * w + h) * N + n]);
+        for (int w = 0; w < 4; ++w) t[w] = real ? unzip_nibbles(qweight[(16 * kb + 4 * w + h) * N + n]) : 0u;
         blk[c + 16 * h] = make_uint4(t[0], t[1], t[2], t[3]);
     }
     if (kb != 0) return;
     // metadata row of column n: scale bits | zero << 16 per row block, zero padding
     const int64_t KBP = padded_row_blocks(K);
-    uint4* row = reinterpret_cast<uint4*>(packed + K * N / 2 + n * KBP * 4);
+    uint4* row = reinterpret_cast<uint4*>(packed + K * padded_cols(N) / 2 + n * KBP * 4);
     for (int64_t p0 = 0; p0 < KBP; p0 += 4) {
         uint32_t word[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int64_t b = p0 + e;
             word[e] = 0u;
-            if (b < KB) {
+            if (real && b < KB) {
                 const int64_t g = (b * kRowsPerBlock) / G;
                 const uint32_t z = (qzeros[g * (N / 8) + n / 8] >> (4 * (n % 8))) & 0xFu;
                 word[e] = (uint32_t)scales[g * N + n] | (z << 16);
@@ -197,7 +199,7 @@ __global__ __launch_bounds__(kGptqColumns) void repack_gptq_kernel(
 
 hipError_t launch_repack_gptq(const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
                               uint8_t* packed, int64_t K, int64_t N, int64_t G, hipStream_t stream) {
-    const dim3 grid((unsigned)((N + kGptqColumns - 1) / kGptqColumns), (unsigned)(K / kRowsPerBlock));
+    const dim3 grid((unsigned)((padded_cols(N) + kGptqColumns - 1) / kGptqColumns), (unsigned)(K / kRowsPerBlock));
     hipLaunchKernelGGL(repack_gptq_kernel, grid, dim3(kGptqColumns), 0, stream,
                        reinterpret_cast<const uint32_t*>(qweight), reinterpret_cast<const uint32_t*>(qzeros),
                        scales, packed, K, N, G);
