@@ -52,7 +52,8 @@ typedef enum {
     W4A16_ERR_BUFFER_SIZE = 6,  /* a caller buffer is smaller than required          */
     W4A16_ERR_DEVICE = 7,       /* the current device is not a gfx950 GPU            */
     W4A16_ERR_HIP = 8,          /* the HIP runtime reported an error at launch       */
-    W4A16_ERR_PATH = 9          /* unknown path, or the forced path cannot take M    */
+    W4A16_ERR_PATH = 9,         /* unknown path, or the forced path cannot take M    */
+    W4A16_ERR_LAYOUT = 10       /* packed header bad, or from another layout version */
 } w4a16_status;
 
 typedef enum {
@@ -118,6 +119,47 @@ w4a16_status w4a16_repack(const int32_t* qweight, const int32_t* qzeros, const v
 w4a16_status w4a16_repack_gptq(const int32_t* qweight, const int32_t* qzeros, const void* scales,
                                w4a16_dtype dtype, int64_t K, int64_t N, int64_t group_size,
                                void* packed, size_t packed_bytes, void* stream);
+
+/* Column-chunked repack, to bound the device-side copy of the checkpoint tensors
+ * while loading (vllm-omni commit "cpu_int4: repack weights in n-blocks, to bound
+ * the load-time peak": column blocks are independent, so the expansion can cover one
+ * chunk at a time; the whole-matrix transient there was 1 GiB for the tied head).
+ * The tensors hold columns [n0, n0 + nc) of the K x N weight, contiguous:
+ *   w4a16_repack_columns:      qweight int32 [K, nc/8], qzeros int32 [K/G, nc/8]
+ *                              (AWQ order), scales [K/G, nc];
+ *   w4a16_repack_gptq_columns: qweight int32 [K/8, nc], qzeros int32 [K/G, nc/8]
+ *                              (standard order), scales [K/G, nc].
+ * They write exactly those columns' codes and metadata into `packed`, the buffer of
+ * the whole K x N weight (packed_bytes >= w4a16_packed_bytes(K, N, G)); the other
+ * columns' bytes are not touched. n0 % 16 == 0, nc % 8 == 0, n0 + nc <= N, and
+ * nc % 16 == 0 unless the chunk ends at N. Repacking all chunks of a partition of
+ * [0, N) gives the bytes w4a16_repack writes. Alignment as for w4a16_repack. */
+w4a16_status w4a16_repack_columns(const int32_t* qweight, const int32_t* qzeros, const void* scales,
+                                  w4a16_dtype dtype, int64_t K, int64_t N, int64_t group_size,
+                                  int64_t n0, int64_t nc, void* packed, size_t packed_bytes, void* stream);
+w4a16_status w4a16_repack_gptq_columns(const int32_t* qweight, const int32_t* qzeros, const void* scales,
+                                       w4a16_dtype dtype, int64_t K, int64_t N, int64_t group_size,
+                                       int64_t n0, int64_t nc, void* packed, size_t packed_bytes,
+                                       void* stream);
+
+/* Persisting a packed buffer, so a later load skips the repack (the AWQ-v2 PR
+ * "feat(quantization): add AWQ-v2 64KB DMA page-aligned zero-repack loader and
+ * specification", sections "Overview" and "Claims": weights stored pre-swizzled in
+ * the kernel's layout, with the legacy path still available). A stored buffer starts
+ * with this 64-byte header, host memory:
+ *   bytes 0..7 "W4A16PK\0", 8..11 layout version (w4a16_layout_version), 12..15
+ *   dtype, 16..23 K, 24..31 N, 32..39 group_size, 40..47 packed bytes (all
+ *   little-endian), 48..55 FNV-1a 64-bit hash of bytes 0..47, 56..63 zero.
+ * w4a16_packed_header fills `header` (header_bytes >= 64) for a valid shape.
+ * w4a16_parse_packed_header checks it and returns the fields; W4A16_ERR_LAYOUT if the
+ * magic, the hash, the reserved bytes, the fields or the layout version disagree (a
+ * buffer of another version must be repacked from the checkpoint). Host only: no
+ * device is touched. */
+#define W4A16_PACKED_HEADER_BYTES 64
+w4a16_status w4a16_packed_header(int64_t K, int64_t N, int64_t group_size, w4a16_dtype dtype,
+                                 void* header, size_t header_bytes);
+w4a16_status w4a16_parse_packed_header(const void* header, size_t header_bytes, int64_t* K, int64_t* N,
+                                       int64_t* group_size, w4a16_dtype* dtype, size_t* packed_bytes);
 
 /* Device workspace the GEMM needs for this shape, in bytes (0 for most shapes).
  * It is non-zero when the MFMA GEMM splits K over workgroups because the output has

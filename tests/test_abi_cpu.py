@@ -26,7 +26,8 @@ def w():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "w4a16_embedding", "w4a16_gemm", "w4a16_gemm_ex", "w4a16_layout_version", "w4a16_packed_bytes",
-        "w4a16_repack", "w4a16_repack_gptq", "w4a16_status_str", "w4a16_workspace_bytes"])
+        "w4a16_packed_header", "w4a16_parse_packed_header", "w4a16_repack", "w4a16_repack_columns",
+        "w4a16_repack_gptq", "w4a16_repack_gptq_columns", "w4a16_status_str", "w4a16_workspace_bytes"])
 
 
 def test_library_exports_every_declared_symbol(w):
@@ -67,7 +68,7 @@ def test_layout_version_and_sizes(w):
 
 
 def test_status_strings(w):
-    for code in range(10):
+    for code in range(11):
         s = w.w4a16_status_str(code)
         assert s and s != "unknown status"
     assert w.w4a16_status_str(42) == "unknown status"
@@ -192,3 +193,81 @@ def test_embedding_validation_before_any_device_call(w):
     assert emb(T=0, ids=None, packed=None, out=None) == 0
     # a fully valid call on this GPU-less host stops at the device check
     assert emb() == 7
+
+
+def test_repack_columns_validation_before_any_device_call(w):
+    for fn in (w.lib.w4a16_repack_columns, w.lib.w4a16_repack_gptq_columns):
+        def rc(n0=0, nc=512, K=512, N=1024, G=128, qw=P(256), packed=P(1024), pbytes=1 << 40):
+            return fn(qw, P(512), P(768), 1, K, N, G, n0, nc, packed, pbytes, None)
+        assert rc(n0=8) == 2                    # not a whole block
+        assert rc(nc=0) == 2
+        assert rc(nc=12) == 2                   # not a multiple of 8
+        assert rc(n0=512, nc=520) == 2          # past N
+        assert rc(n0=0, nc=24) == 2             # half block not at the end
+        assert rc(n0=-16) == 2
+        assert rc(qw=None) == 1
+        assert rc(pbytes=1000) == 6
+        assert rc(n0=1000, nc=24, N=1024) == 2  # n0 not a whole block
+        assert rc(n0=992, nc=24, N=1016) == 7   # last chunk ending in a half block: valid
+        assert rc() == 7
+
+
+def fnv1a64(data):
+    h = 0xcbf29ce484222325
+    for b in data:
+        h = ((h ^ b) * 0x100000001b3) & 0xFFFFFFFFFFFFFFFF
+    return h
+
+
+def test_packed_header_format(w):
+    import struct
+    import torch
+    h = w.w4a16_packed_header(2048, 13288, 128, torch.bfloat16)
+    assert len(h) == 64
+    magic, version, dtype, K, N, G, nbytes, digest = struct.unpack("<8sIIqqqQQ", h[:56])
+    assert magic == b"W4A16PK\0" and version == w.w4a16_layout_version() and dtype == 1
+    assert (K, N, G) == (2048, 13288, 128) and nbytes == w.w4a16_packed_bytes(2048, 13288, 128)
+    assert digest == fnv1a64(h[:48]) and h[56:] == bytes(8)
+    assert w.w4a16_parse_packed_header(h) == (2048, 13288, 128, torch.bfloat16, nbytes)
+    assert w.w4a16_parse_packed_header(w.w4a16_packed_header(512, 64, -1, torch.float16))[2:4] == (-1, torch.float16)
+
+
+def test_packed_header_rejections(w):
+    import struct
+    import torch
+    h = bytearray(w.w4a16_packed_header(1024, 272, 256, torch.bfloat16))
+    for i in (0, 9, 20, 44, 50, 60):              # magic, version, K, size, hash, reserved
+        bad = bytearray(h)
+        bad[i] ^= 1
+        with pytest.raises(w.W4A16Error) as e:
+            w.w4a16_parse_packed_header(bad)
+        assert e.value.status == "W4A16_ERR_LAYOUT"
+    # another layout version with a consistent hash is still refused
+    other = bytearray(h)
+    struct.pack_into("<I", other, 8, w.w4a16_layout_version() + 1)
+    struct.pack_into("<Q", other, 48, fnv1a64(bytes(other[:48])))
+    with pytest.raises(w.W4A16Error) as e:
+        w.w4a16_parse_packed_header(other)
+    assert e.value.status == "W4A16_ERR_LAYOUT"
+    with pytest.raises(w.W4A16Error) as e:
+        w.w4a16_parse_packed_header(bytes(h[:40]))
+    assert e.value.status == "W4A16_ERR_BUFFER_SIZE"
+    with pytest.raises(w.W4A16Error) as e:
+        w.w4a16_packed_header(1024, 270, 128, torch.bfloat16)
+    assert e.value.status == "W4A16_ERR_SHAPE"
+
+
+def test_save_and_load_packed_file_on_host(w, tmp_path):
+    import torch
+    K, N, G = 256, 40, 128
+    nbytes = w.w4a16_packed_bytes(K, N, G)
+    packed = torch.randint(0, 256, (nbytes,), dtype=torch.uint8)
+    path = tmp_path / "layer.w4a16"
+    w.save_packed(str(path), packed, K, N, G, torch.float16)
+    raw = path.read_bytes()
+    assert len(raw) == w.PAYLOAD_OFFSET + nbytes and raw[64:w.PAYLOAD_OFFSET] == bytes(w.PAYLOAD_OFFSET - 64)
+    got, K2, N2, G2, dt = w.load_packed(str(path), device="cpu")
+    assert (K2, N2, G2, dt) == (K, N, G, torch.float16) and torch.equal(got, packed)
+    path.write_bytes(raw[:-1])                      # truncated payload
+    with pytest.raises(w.W4A16Error):
+        w.load_packed(str(path), device="cpu")

@@ -8,11 +8,22 @@ Functions keep the C names:
   w4a16_workspace_bytes(M, K, N, group_size)     -> int
   w4a16_repack(qweight, qzeros, scales, group_size, packed=None, stream=None) -> packed uint8 tensor
   w4a16_repack_gptq(qweight, qzeros, scales, group_size, packed=None, stream=None) -> packed uint8 tensor
+  w4a16_repack_columns / w4a16_repack_gptq_columns(qweight, qzeros, scales, N, n0, group_size, packed, stream)
+      (one column chunk of the checkpoint into the whole weight's packed buffer)
+  w4a16_packed_header(K, N, group_size, dtype) -> 64 bytes
+  w4a16_parse_packed_header(header) -> (K, N, group_size, dtype, packed_bytes)
   w4a16_gemm(x, packed, N, group_size, bias=None, y=None, workspace=None, stream=None) -> y
       (workspace=None: a zero-filled per-device workspace is allocated on demand)
   w4a16_gemm_ex(..., path="auto"|"gemv"|"mfma", gemv_max_m=-1)            -> y
   w4a16_embedding(ids, packed, K, N, group_size, dtype, out=None, stream=None) -> out [T, K]
   w4a16_status_str(code)                         -> str
+
+Load-path helpers built on those calls (host-side data movement only):
+  repack_from_host(qweight, qzeros, scales, group_size, fmt, chunk_columns, device)
+      checkpoint tensors in host memory -> packed device buffer, one column chunk of
+      the checkpoint on the device at a time
+  save_packed(path, packed, K, N, group_size, dtype) / load_packed(path, device)
+      a packed buffer on disk: the 64-byte header, zero padding to 64 KiB, the bytes
 
 There is no fallback: if the library is missing, the first call (or access to
 `lib`) raises ImportError; a call whose tensors are not on a gfx950 GPU returns the
@@ -28,14 +39,18 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4a16.so
 
 __all__ = [
     "W4A16Error", "lib", "w4a16_layout_version", "w4a16_packed_bytes", "w4a16_workspace_bytes",
-    "w4a16_repack", "w4a16_repack_gptq", "w4a16_gemm", "w4a16_gemm_ex", "w4a16_embedding", "w4a16_status_str", "STATUS", "PATHS",
+    "w4a16_repack", "w4a16_repack_gptq", "w4a16_repack_columns", "w4a16_repack_gptq_columns",
+    "w4a16_packed_header", "w4a16_parse_packed_header", "repack_from_host", "save_packed", "load_packed",
+    "w4a16_gemm", "w4a16_gemm_ex", "w4a16_embedding", "w4a16_status_str", "STATUS", "PATHS",
 ]
 
 STATUS = {
     0: "W4A16_OK", 1: "W4A16_ERR_NULL", 2: "W4A16_ERR_SHAPE", 3: "W4A16_ERR_GROUP",
     4: "W4A16_ERR_DTYPE", 5: "W4A16_ERR_ALIGN", 6: "W4A16_ERR_BUFFER_SIZE",
-    7: "W4A16_ERR_DEVICE", 8: "W4A16_ERR_HIP", 9: "W4A16_ERR_PATH",
+    7: "W4A16_ERR_DEVICE", 8: "W4A16_ERR_HIP", 9: "W4A16_ERR_PATH", 10: "W4A16_ERR_LAYOUT",
 }
+HEADER_BYTES = 64
+PAYLOAD_OFFSET = 1 << 16       # packed bytes start 64 KiB into a saved file (page aligned)
 DTYPES = {torch.float16: 0, torch.bfloat16: 1}
 PATHS = {"auto": 0, "gemv": 1, "mfma": 2}
 
@@ -71,6 +86,16 @@ def _load():
     h.w4a16_repack.restype = _int
     h.w4a16_repack_gptq.argtypes = h.w4a16_repack.argtypes
     h.w4a16_repack_gptq.restype = _int
+    h.w4a16_repack_columns.argtypes = [_vp, _vp, _vp, _int, _i64, _i64, _i64, _i64, _i64, _vp, _sz, _vp]
+    h.w4a16_repack_columns.restype = _int
+    h.w4a16_repack_gptq_columns.argtypes = h.w4a16_repack_columns.argtypes
+    h.w4a16_repack_gptq_columns.restype = _int
+    h.w4a16_packed_header.argtypes = [_i64, _i64, _i64, _int, _vp, _sz]
+    h.w4a16_packed_header.restype = _int
+    _p64 = ctypes.POINTER(ctypes.c_int64)
+    h.w4a16_parse_packed_header.argtypes = [_vp, _sz, _p64, _p64, _p64, ctypes.POINTER(ctypes.c_int),
+                                            ctypes.POINTER(ctypes.c_size_t)]
+    h.w4a16_parse_packed_header.restype = _int
     h.w4a16_gemm.argtypes = [_vp, _vp, _sz, _int, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _sz, _vp]
     h.w4a16_gemm.restype = _int
     h.w4a16_gemm_ex.argtypes = h.w4a16_gemm.argtypes + [_int, _i64]
@@ -169,6 +194,116 @@ def w4a16_repack_gptq(qweight, qzeros, scales, group_size=128, packed=None, stre
                                      _stream(stream, qweight.device))
     _check(code, "w4a16_repack_gptq")
     return packed
+
+
+def _repack_columns(fn, name, qweight, qzeros, scales, K, N, n0, nc, group_size, packed, stream):
+    for t, tname in ((qweight, "qweight"), (qzeros, "qzeros"), (scales, "scales")):
+        if not t.is_contiguous():
+            raise ValueError(f"{tname} must be contiguous")
+    if qweight.dtype != torch.int32 or qzeros.dtype != torch.int32:
+        raise ValueError("qweight and qzeros must be int32")
+    code = fn(_ptr(qweight), _ptr(qzeros), _ptr(scales), _dtype_code(scales.dtype), K, N, group_size, n0, nc,
+              _ptr(packed), packed.numel() * packed.element_size(), _stream(stream, qweight.device))
+    _check(code, name)
+    return packed
+
+
+def w4a16_repack_columns(qweight, qzeros, scales, N, n0, group_size=128, packed=None, stream=None):
+    """AWQ tensors of columns [n0, n0 + nc) (qweight int32 [K, nc/8], qzeros [K/G, nc/8],
+    scales [K/G, nc]) -> those columns of the K x N weight's packed buffer."""
+    K, nc = qweight.shape[0], qweight.shape[1] * 8
+    if packed is None:
+        packed = torch.empty(max(w4a16_packed_bytes(K, N, group_size), 1), dtype=torch.uint8, device=qweight.device)
+    return _repack_columns(_load().w4a16_repack_columns, "w4a16_repack_columns", qweight, qzeros, scales, K, N,
+                           n0, nc, group_size, packed, stream)
+
+
+def w4a16_repack_gptq_columns(qweight, qzeros, scales, N, n0, group_size=128, packed=None, stream=None):
+    """GPTQ-standard tensors of columns [n0, n0 + nc) (qweight int32 [K/8, nc], qzeros
+    [K/G, nc/8], scales [K/G, nc]) -> those columns of the K x N weight's packed buffer."""
+    K, nc = qweight.shape[0] * 8, qweight.shape[1]
+    if packed is None:
+        packed = torch.empty(max(w4a16_packed_bytes(K, N, group_size), 1), dtype=torch.uint8, device=qweight.device)
+    return _repack_columns(_load().w4a16_repack_gptq_columns, "w4a16_repack_gptq_columns", qweight, qzeros, scales,
+                           K, N, n0, nc, group_size, packed, stream)
+
+
+def repack_from_host(qweight, qzeros, scales, group_size=128, fmt="awq", chunk_columns=4096, device="cuda:0",
+                     stream=None):
+    """Checkpoint tensors in host memory -> packed device buffer. Column chunks of
+    `chunk_columns` (a multiple of 16) are copied to the device and repacked one at a
+    time, so the device holds one chunk of the checkpoint tensors besides the packed
+    buffer. fmt "awq": qweight [K, N/8]; "gptq": qweight [K/8, N] (codes along K)."""
+    if fmt not in ("awq", "gptq"):
+        raise ValueError(f"fmt {fmt!r}")
+    if chunk_columns <= 0 or chunk_columns % 16 != 0:
+        raise ValueError("chunk_columns must be a positive multiple of 16")
+    K, N = (qweight.shape[0], qweight.shape[1] * 8) if fmt == "awq" else (qweight.shape[0] * 8, qweight.shape[1])
+    nbytes = w4a16_packed_bytes(K, N, group_size)
+    if nbytes == 0:
+        raise W4A16Error(2, "repack_from_host")
+    packed = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    for n0 in range(0, N, chunk_columns):
+        nc = min(chunk_columns, N - n0)
+        w0, w1 = n0 // 8, (n0 + nc) // 8
+        qw = qweight[:, w0:w1] if fmt == "awq" else qweight[:, n0:n0 + nc]
+        qw = qw.contiguous().to(device)
+        qz = qzeros[:, w0:w1].contiguous().to(device)
+        sc = scales[:, n0:n0 + nc].contiguous().to(device)
+        if fmt == "awq":
+            w4a16_repack_columns(qw, qz, sc, N, n0, group_size, packed, stream)
+        else:
+            w4a16_repack_gptq_columns(qw, qz, sc, N, n0, group_size, packed, stream)
+        del qw, qz, sc
+    return packed
+
+
+def w4a16_packed_header(K, N, group_size, dtype):
+    """The 64-byte header of a stored packed buffer (bytes)."""
+    buf = ctypes.create_string_buffer(HEADER_BYTES)
+    _check(_load().w4a16_packed_header(K, N, group_size, _dtype_code(dtype), buf, HEADER_BYTES),
+           "w4a16_packed_header")
+    return buf.raw
+
+
+def w4a16_parse_packed_header(header):
+    """bytes -> (K, N, group_size, torch dtype, packed_bytes); W4A16Error if invalid."""
+    header = bytes(header)
+    K, N, G = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    dt, nbytes = ctypes.c_int(), ctypes.c_size_t()
+    _check(_load().w4a16_parse_packed_header(header, len(header), ctypes.byref(K), ctypes.byref(N),
+                                             ctypes.byref(G), ctypes.byref(dt), ctypes.byref(nbytes)),
+           "w4a16_parse_packed_header")
+    dtype = {v: k for k, v in DTYPES.items()}[dt.value]
+    return K.value, N.value, G.value, dtype, nbytes.value
+
+
+def save_packed(path, packed, K, N, group_size, dtype):
+    """Writes the header, zero padding to 64 KiB and the packed bytes."""
+    header = w4a16_packed_header(K, N, group_size, dtype)
+    nbytes = w4a16_packed_bytes(K, N, group_size)
+    if packed.numel() * packed.element_size() < nbytes:
+        raise W4A16Error(6, "save_packed")
+    data = packed.reshape(-1).view(torch.uint8)[:nbytes].cpu().numpy().tobytes()
+    with open(path, "wb") as f:
+        f.write(header + bytes(PAYLOAD_OFFSET - HEADER_BYTES))
+        f.write(data)
+
+
+def load_packed(path, device="cuda:0"):
+    """-> (packed device tensor, K, N, group_size, dtype). W4A16Error (W4A16_ERR_LAYOUT)
+    if the file was written for another layout version or is damaged: repack from the
+    checkpoint instead."""
+    with open(path, "rb") as f:
+        head = f.read(PAYLOAD_OFFSET)
+        K, N, G, dtype, nbytes = w4a16_parse_packed_header(head[:HEADER_BYTES])
+        if len(head) != PAYLOAD_OFFSET or any(head[HEADER_BYTES:]):
+            raise W4A16Error(10, "load_packed")
+        data = f.read(nbytes)
+        if len(data) != nbytes or f.read(1):
+            raise W4A16Error(10, "load_packed")
+    packed = torch.frombuffer(bytearray(data), dtype=torch.uint8).to(device)
+    return packed, K, N, G, dtype
 
 
 _workspaces = {}

@@ -96,6 +96,32 @@ w4a16_status gemm_impl(const void* x, const void* packed, size_t packed_bytes, w
     return err == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
 }
 
+// One repack entry: AWQ (gptq = false) or GPTQ-standard tensors holding columns
+// [n0, n0 + nc) of a K x N weight, written into the packed layout of the K x N weight.
+w4a16_status repack_impl(bool gptq, const int32_t* qweight, const int32_t* qzeros, const void* scales,
+                         w4a16_dtype dtype, int64_t K, int64_t N, int64_t group_size, int64_t n0, int64_t nc,
+                         void* packed, size_t packed_bytes, void* stream) {
+    int64_t G = 0;
+    w4a16_status st = check_shape(K, N, group_size, &G);
+    if (st != W4A16_OK) return st;
+    if (dtype != W4A16_FP16 && dtype != W4A16_BF16) return W4A16_ERR_DTYPE;
+    // whole 16-column blocks, except that the last chunk may end in a half block
+    if (n0 < 0 || nc <= 0 || n0 % 16 != 0 || nc % 8 != 0 || nc > N - n0 || (nc % 16 != 0 && n0 + nc != N))
+        return W4A16_ERR_SHAPE;
+    if (!qweight || !qzeros || !scales || !packed) return W4A16_ERR_NULL;
+    if (!aligned(qweight, 4) || !aligned(qzeros, 4) || !aligned(scales, 2) || !aligned(packed, 16))
+        return W4A16_ERR_ALIGN;
+    if (packed_bytes < packed_size(K, N)) return W4A16_ERR_BUFFER_SIZE;
+    st = check_device();
+    if (st != W4A16_OK) return st;
+    const auto* sc = static_cast<const uint16_t*>(scales);
+    auto* out = static_cast<uint8_t*>(packed);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t err = gptq ? w4a16::launch_repack_gptq(qweight, qzeros, sc, out, K, nc, G, n0, N, s)
+                                : w4a16::launch_repack(qweight, qzeros, sc, out, K, nc, G, n0, N, s);
+    return err == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -111,39 +137,27 @@ size_t w4a16_packed_bytes(int64_t K, int64_t N, int64_t group_size) {
 w4a16_status w4a16_repack(const int32_t* qweight, const int32_t* qzeros, const void* scales, w4a16_dtype dtype,
                           int64_t K, int64_t N, int64_t group_size, void* packed, size_t packed_bytes,
                           void* stream) {
-    int64_t G = 0;
-    w4a16_status st = check_shape(K, N, group_size, &G);
-    if (st != W4A16_OK) return st;
-    if (dtype != W4A16_FP16 && dtype != W4A16_BF16) return W4A16_ERR_DTYPE;
-    if (!qweight || !qzeros || !scales || !packed) return W4A16_ERR_NULL;
-    if (!aligned(qweight, 4) || !aligned(qzeros, 4) || !aligned(scales, 2) || !aligned(packed, 16))
-        return W4A16_ERR_ALIGN;
-    if (packed_bytes < packed_size(K, N)) return W4A16_ERR_BUFFER_SIZE;
-    st = check_device();
-    if (st != W4A16_OK) return st;
-    const hipError_t err = w4a16::launch_repack(qweight, qzeros, static_cast<const uint16_t*>(scales),
-                                                static_cast<uint8_t*>(packed), K, N, G,
-                                                static_cast<hipStream_t>(stream));
-    return err == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+    return repack_impl(false, qweight, qzeros, scales, dtype, K, N, group_size, 0, N, packed, packed_bytes, stream);
 }
 
 w4a16_status w4a16_repack_gptq(const int32_t* qweight, const int32_t* qzeros, const void* scales,
                                w4a16_dtype dtype, int64_t K, int64_t N, int64_t group_size, void* packed,
                                size_t packed_bytes, void* stream) {
-    int64_t G = 0;
-    w4a16_status st = check_shape(K, N, group_size, &G);
-    if (st != W4A16_OK) return st;
-    if (dtype != W4A16_FP16 && dtype != W4A16_BF16) return W4A16_ERR_DTYPE;
-    if (!qweight || !qzeros || !scales || !packed) return W4A16_ERR_NULL;
-    if (!aligned(qweight, 4) || !aligned(qzeros, 4) || !aligned(scales, 2) || !aligned(packed, 16))
-        return W4A16_ERR_ALIGN;
-    if (packed_bytes < packed_size(K, N)) return W4A16_ERR_BUFFER_SIZE;
-    st = check_device();
-    if (st != W4A16_OK) return st;
-    const hipError_t err = w4a16::launch_repack_gptq(qweight, qzeros, static_cast<const uint16_t*>(scales),
-                                                     static_cast<uint8_t*>(packed), K, N, G,
-                                                     static_cast<hipStream_t>(stream));
-    return err == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+    return repack_impl(true, qweight, qzeros, scales, dtype, K, N, group_size, 0, N, packed, packed_bytes, stream);
+}
+
+w4a16_status w4a16_repack_columns(const int32_t* qweight, const int32_t* qzeros, const void* scales,
+                                  w4a16_dtype dtype, int64_t K, int64_t N, int64_t group_size, int64_t n0,
+                                  int64_t nc, void* packed, size_t packed_bytes, void* stream) {
+    return repack_impl(false, qweight, qzeros, scales, dtype, K, N, group_size, n0, nc, packed, packed_bytes,
+                       stream);
+}
+
+w4a16_status w4a16_repack_gptq_columns(const int32_t* qweight, const int32_t* qzeros, const void* scales,
+                                       w4a16_dtype dtype, int64_t K, int64_t N, int64_t group_size, int64_t n0,
+                                       int64_t nc, void* packed, size_t packed_bytes, void* stream) {
+    return repack_impl(true, qweight, qzeros, scales, dtype, K, N, group_size, n0, nc, packed, packed_bytes,
+                       stream);
 }
 
 size_t w4a16_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t group_size) {
@@ -187,6 +201,74 @@ w4a16_status w4a16_embedding(const int32_t* ids, int64_t T, const void* packed, 
     return err == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
 }
 
+// Packed-buffer header: magic, layout version, dtype, K, N, group size, buffer bytes,
+// an FNV-1a checksum of those 48 bytes, 8 reserved zero bytes.
+constexpr char kHeaderMagic[8] = {'W', '4', 'A', '1', '6', 'P', 'K', 0};
+
+uint64_t fnv1a64(const uint8_t* p, size_t n) {
+    uint64_t h = 0xcbf29ce484222325ull;
+    for (size_t i = 0; i < n; ++i) {
+        h ^= p[i];
+        h *= 0x100000001b3ull;
+    }
+    return h;
+}
+
+w4a16_status w4a16_packed_header(int64_t K, int64_t N, int64_t group_size, w4a16_dtype dtype, void* header,
+                                 size_t header_bytes) {
+    int64_t G = 0;
+    w4a16_status st = check_shape(K, N, group_size, &G);
+    if (st != W4A16_OK) return st;
+    if (dtype != W4A16_FP16 && dtype != W4A16_BF16) return W4A16_ERR_DTYPE;
+    if (!header) return W4A16_ERR_NULL;
+    if (header_bytes < W4A16_PACKED_HEADER_BYTES) return W4A16_ERR_BUFFER_SIZE;
+    uint8_t h[W4A16_PACKED_HEADER_BYTES] = {};
+    const uint32_t version = kLayoutVersion, dt = (uint32_t)dtype;
+    const uint64_t nbytes = packed_size(K, N);
+    memcpy(h, kHeaderMagic, 8);
+    memcpy(h + 8, &version, 4);
+    memcpy(h + 12, &dt, 4);
+    memcpy(h + 16, &K, 8);
+    memcpy(h + 24, &N, 8);
+    memcpy(h + 32, &group_size, 8);
+    memcpy(h + 40, &nbytes, 8);
+    const uint64_t sum = fnv1a64(h, 48);
+    memcpy(h + 48, &sum, 8);
+    memcpy(header, h, sizeof(h));
+    return W4A16_OK;
+}
+
+w4a16_status w4a16_parse_packed_header(const void* header, size_t header_bytes, int64_t* K, int64_t* N,
+                                       int64_t* group_size, w4a16_dtype* dtype, size_t* packed_bytes) {
+    if (!header || !K || !N || !group_size || !dtype || !packed_bytes) return W4A16_ERR_NULL;
+    if (header_bytes < W4A16_PACKED_HEADER_BYTES) return W4A16_ERR_BUFFER_SIZE;
+    const uint8_t* h = static_cast<const uint8_t*>(header);
+    uint64_t sum = 0, nbytes = 0;
+    memcpy(&sum, h + 48, 8);
+    if (memcmp(h, kHeaderMagic, 8) != 0 || sum != fnv1a64(h, 48)) return W4A16_ERR_LAYOUT;
+    for (int i = 56; i < 64; ++i)
+        if (h[i] != 0) return W4A16_ERR_LAYOUT;
+    uint32_t version = 0, dt = 0;
+    int64_t k = 0, n = 0, g = 0;
+    memcpy(&version, h + 8, 4);
+    memcpy(&dt, h + 12, 4);
+    memcpy(&k, h + 16, 8);
+    memcpy(&n, h + 24, 8);
+    memcpy(&g, h + 32, 8);
+    memcpy(&nbytes, h + 40, 8);
+    if (version != (uint32_t)kLayoutVersion) return W4A16_ERR_LAYOUT;
+    int64_t G = 0;
+    if (check_shape(k, n, g, &G) != W4A16_OK || (dt != W4A16_FP16 && dt != W4A16_BF16) ||
+        nbytes != packed_size(k, n))
+        return W4A16_ERR_LAYOUT;
+    *K = k;
+    *N = n;
+    *group_size = g;
+    *dtype = (w4a16_dtype)dt;
+    *packed_bytes = (size_t)nbytes;
+    return W4A16_OK;
+}
+
 const char* w4a16_status_str(w4a16_status status) {
     switch (status) {
         case W4A16_OK: return "ok";
@@ -199,6 +281,7 @@ const char* w4a16_status_str(w4a16_status status) {
         case W4A16_ERR_DEVICE: return "current device is not a gfx950 GPU";
         case W4A16_ERR_HIP: return "HIP launch error";
         case W4A16_ERR_PATH: return "unknown path, or the forced path cannot take this M";
+        case W4A16_ERR_LAYOUT: return "packed-buffer header invalid or from another layout version";
         default: return "unknown status";
     }
 }

@@ -56,10 +56,13 @@ __device__ __forceinline__ void transpose8x8_nibbles(uint32_t (&v)[8]) {
     }
 }
 
+// Input tensors hold columns [n0, n0 + N) of a K x Nt weight (the whole weight when
+// n0 = 0 and N = Nt): qweight [K, N/8], qzeros [K/G, N/8], scales [K/G, N]. Output:
+// those columns' blocks and metadata rows in the packed layout of the K x Nt weight.
 __global__ __launch_bounds__(kRepackThreads) void repack_kernel(
     const uint32_t* __restrict__ qweight, const uint32_t* __restrict__ qzeros,
     const uint16_t* __restrict__ scales, uint8_t* __restrict__ packed,
-    int64_t K, int64_t N, int64_t G) {
+    int64_t K, int64_t N, int64_t G, int64_t n0, int64_t Nt) {
     const int64_t KB = K / kRowsPerBlock;
     const int64_t words_per_row = N / 8;
     const int64_t kb = blockIdx.y;
@@ -98,7 +101,7 @@ __global__ __launch_bounds__(kRepackThreads) void repack_kernel(
     const int64_t tile_words = words_per_row - j0 < kWordsPerTile ? words_per_row - j0 : kWordsPerTile;
     const int nblk = (int)((tile_words + 1) / 2);                 // a last half block included
     for (int q = tid; q < nblk * 64; q += kRepackThreads) {
-        const int64_t nb = (j0 >> 1) + (q >> 6);
+        const int64_t nb = n0 / kColsPerBlock + (j0 >> 1) + (q >> 6);
         reinterpret_cast<uint4*>(packed + (nb * KB + kb) * kBlockBytes)[q & 63] = stage[q];
     }
 
@@ -108,12 +111,12 @@ __global__ __launch_bounds__(kRepackThreads) void repack_kernel(
     //    at a time
     if (kb != 0) return;
     const int64_t KBP = padded_row_blocks(K);
-    uint32_t* meta = reinterpret_cast<uint32_t*>(packed + K * padded_cols(N) / 2);
+    uint32_t* meta = reinterpret_cast<uint32_t*>(packed + K * padded_cols(Nt) / 2);
     for (int q = tid; q < nblk * kColsPerBlock; q += kRepackThreads) {
-        const int64_t n = j0 * 8 + q;
+        const int64_t n = j0 * 8 + q;                 // column of the input tensors
         const bool real = n < N;
         const int zshift = 4 * awq_slot_of_column((int)(n & 7));
-        uint4* row = reinterpret_cast<uint4*>(meta + n * KBP);
+        uint4* row = reinterpret_cast<uint4*>(meta + (n0 + n) * KBP);
         for (int64_t p0 = 0; p0 < KBP; p0 += 4) {
             uint32_t word[4];
 #pragma unroll
@@ -155,16 +158,18 @@ __device__ __forceinline__ uint32_t unzip_nibbles(uint32_t v) {
     return e | (o << 16);
 }
 
+// Input columns [n0, n0 + N) of a K x Nt weight, as for repack_kernel: qweight
+// [K/8, N], qzeros [K/G, N/8], scales [K/G, N].
 __global__ __launch_bounds__(kGptqColumns) void repack_gptq_kernel(
     const uint32_t* __restrict__ qweight, const uint32_t* __restrict__ qzeros,
     const uint16_t* __restrict__ scales, uint8_t* __restrict__ packed,
-    int64_t K, int64_t N, int64_t G) {
+    int64_t K, int64_t N, int64_t G, int64_t n0, int64_t Nt) {
     const int64_t KB = K / kRowsPerBlock;
     const int64_t kb = blockIdx.y;
     const int64_t n = (int64_t)blockIdx.x * kGptqColumns + threadIdx.x;
     if (n >= padded_cols(N)) return;
     const bool real = n < N;          // else a zero padding column of a last half block
-    const int64_t nb = n / kColsPerBlock;
+    const int64_t nb = (n0 + n) / kColsPerBlock;
     const int c = (int)(n % kColsPerBlock);
     uint4* blk = reinterpret_cast<uint4*>(packed + (nb * KB + kb) * kBlockBytes);
     // GPTQ word row i = 16 kb + 4 w + h: lane group h, word w of the tile
@@ -178,7 +183,7 @@ __global__ __launch_bounds__(kGptqColumns) void repack_gptq_kernel(
     if (kb != 0) return;
     // metadata row of column n: scale bits | zero << 16 per row block, zero padding
     const int64_t KBP = padded_row_blocks(K);
-    uint4* row = reinterpret_cast<uint4*>(packed + K * padded_cols(N) / 2 + n * KBP * 4);
+    uint4* row = reinterpret_cast<uint4*>(packed + K * padded_cols(Nt) / 2 + (n0 + n) * KBP * 4);
     for (int64_t p0 = 0; p0 < KBP; p0 += 4) {
         uint32_t word[4];
 #pragma unroll
@@ -198,22 +203,24 @@ __global__ __launch_bounds__(kGptqColumns) void repack_gptq_kernel(
 }  // namespace
 
 hipError_t launch_repack_gptq(const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
-                              uint8_t* packed, int64_t K, int64_t N, int64_t G, hipStream_t stream) {
+                              uint8_t* packed, int64_t K, int64_t N, int64_t G, int64_t n0, int64_t Nt,
+                              hipStream_t stream) {
     const dim3 grid((unsigned)((padded_cols(N) + kGptqColumns - 1) / kGptqColumns), (unsigned)(K / kRowsPerBlock));
     hipLaunchKernelGGL(repack_gptq_kernel, grid, dim3(kGptqColumns), 0, stream,
                        reinterpret_cast<const uint32_t*>(qweight), reinterpret_cast<const uint32_t*>(qzeros),
-                       scales, packed, K, N, G);
+                       scales, packed, K, N, G, n0, Nt);
     return hipGetLastError();
 }
 
 hipError_t launch_repack(const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
-                         uint8_t* packed, int64_t K, int64_t N, int64_t G, hipStream_t stream) {
+                         uint8_t* packed, int64_t K, int64_t N, int64_t G, int64_t n0, int64_t Nt,
+                         hipStream_t stream) {
     const int64_t KB = K / kRowsPerBlock;
     const int64_t words = N / 8;
     dim3 grid((unsigned)((words + kWordsPerTile - 1) / kWordsPerTile), (unsigned)KB);
     hipLaunchKernelGGL(repack_kernel, grid, dim3(kRepackThreads), 0, stream,
                        reinterpret_cast<const uint32_t*>(qweight), reinterpret_cast<const uint32_t*>(qzeros),
-                       scales, packed, K, N, G);
+                       scales, packed, K, N, G, n0, Nt);
     return hipGetLastError();
 }
 
