@@ -45,48 +45,6 @@ __device__ __forceinline__ uint32_t pick(const uint4 v, int i) {
     return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
-// Direct global -> LDS copies (global_load_lds): each lane's 4 or 16 bytes land at
-// M0 + 4*lane or M0 + 16*lane, M0 being uniform over the wave. They count in vmcnt
-// like loads but occupy no registers, so several k blocks can be in flight. They are
-// issued through inline assembly so that the compiler does not guard every later LDS
-// read with a wait for all of them: the kernel waits for exactly the copies it needs.
-// Scalar-base form: a wave-uniform 64-bit base in SGPRs plus a loop-invariant 32-bit
-// byte offset per lane. (With a 64-bit address per copy the compiler rebuilt every
-// address in one VGPR pair, so each copy waited until the previous one had read it:
-// ~55 cycles a copy, a sixth of the k loop.)
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-// (readfirstlane returns int: each half goes through uint32_t so that a low half
-// with bit 31 set is not sign-extended over the high half)
-__device__ __forceinline__ const uint8_t* uniform_ptr(const void* p) {
-    const uint64_t v = (uint64_t)(uintptr_t)p;
-    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
-    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-    return reinterpret_cast<const uint8_t*>((hi << 32) | lo);
-}
-__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(base), "s"(lds) : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(const uint8_t* base, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" : : "v"(voff), "s"(base), "s"(lds) : "memory", "m0");
-}
-
-// Workgroup barrier that is also a compiler barrier for memory operations, without
-// the vmcnt(0) a full __syncthreads() fence would add.
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("" : : : "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" : : : "memory");
-}
-
-// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt low bits [3:0], high
-// bits [15:14], expcnt [6:4] = 7, lgkmcnt [11:8] = 15).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
 
 // One stage of the LDS ring: the activation tile of one 128-row block of K, the
 // workgroup's blocks of packed codes (W waves x CBW) and its metadata words (64 per

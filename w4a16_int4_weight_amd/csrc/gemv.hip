@@ -54,22 +54,9 @@ __device__ __forceinline__ uint4 load_once(const uint4* p) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// Activation chunk load, kept where it is written (before the code loads). The
-// compiler would otherwise sink it below them into the staging branch; since vector
-// loads complete in order, waiting for it would then wait for the codes too. Its
-// result is claimed with wait_x_chunk.
-__device__ __forceinline__ u32x4 load_x_chunk(const void* p) {
-    u32x4 v;
-    asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(p) : "memory");
-    return v;
-}
-
-// Wait until at most `kAfter` vector loads are outstanding (those issued after the
-// activation chunks) and hand the chunk to the code that reads it.
-template <int kAfter>
-__device__ __forceinline__ void wait_x_chunk(u32x4& v) {
-    asm volatile("s_waitcnt vmcnt(%1)" : "+v"(v) : "n"(kAfter) : "memory");
-}
+// LDS bytes of the staged activations, `chunks` 16-byte chunks copied in whole waves
+// of 64 (the last wave's extra lanes land in the padding)
+__host__ __device__ constexpr int64_t staged_x_bytes(int64_t chunks) { return (chunks + 63) / 64 * 64 * 16; }
 
 __device__ __forceinline__ uint32_t pick(const uint4 v, int i) {
     return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
@@ -147,30 +134,34 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(const GemvArgs a) 
     const int kb_end = kb_begin + a.kb_per_wave < KB ? kb_begin + a.kb_per_wave : KB;
     const int xr = c < M ? c : 0;    // activation row this lane feeds to the MFMA
 
-    // LDS: [staged x, M x K 16-bit][row-block sums X, KB x 16 fp32][wave partials]
-    const int xs_bytes = kStaged ? M * K * 2 : 0;                // multiple of 256
+    // LDS: [staged x, M x K 16-bit, in whole 1 KiB wave copies][row-block sums X,
+    // KB x 16 fp32][wave partials]
+    const int row_chunks = K / 8;
+    const int chunks = M * row_chunks;                            // 16-byte activation chunks
+    const int xs_bytes = kStaged ? (int)staged_x_bytes(chunks) : 0;
     const int xsum_bytes = kStaged ? KB * 16 * 4 : 0;
     uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
     float* xsum = reinterpret_cast<float*>(smem + xs_bytes);
     f32x4* partial = reinterpret_cast<f32x4*>(smem + xs_bytes + xsum_bytes);
 
-    // 1. staged variant: this thread's activation chunks, loaded first
-    const int row_chunks = K / 8;
-    const int chunks = M * row_chunks;
-    u32x4 xv[kStaged ? kChunks : 1];
-    int xm[kStaged ? kChunks : 1];
+    // 1. staged variant: the activations are copied global -> LDS first, ahead of the
+    //    codes (chunk q to byte 16 q; wave w copies chunks 64 w + 0..63 + p blockDim.x,
+    //    lanes past the end re-reading the last chunk into the padding). The copies
+    //    hold no registers: an exact vmcnt wait and a barrier order them before their
+    //    readers, and the codes stay in flight meanwhile. (A register load was sunk by
+    //    the compiler below the code loads, whose completion it then also waited for;
+    //    an inline-assembly register load with a separate wait let the compiler copy
+    //    the result registers before the wait.)
     if constexpr (kStaged) {
-        const float inv_row_chunks = 1.0f / (float)row_chunks;
+        const uint8_t* xbase = uniform_ptr(a.x);
+        const uint32_t xs_lds = lds_addr(xs);
 #pragma unroll
         for (int p = 0; p < kChunks; ++p) {
-            const int q = threadIdx.x + p * blockDim.x;
-            // row of chunk q: a float estimate (q < 2^22, off by at most one) corrected exactly
-            int m = (int)((float)q * inv_row_chunks);
-            m -= m * row_chunks > q ? 1 : 0;
-            m += (m + 1) * row_chunks <= q ? 1 : 0;
-            m = q < chunks ? m : 0;
-            xm[p] = m;
-            xv[p] = load_x_chunk(reinterpret_cast<const uint4*>(a.x) + (q < chunks ? q : chunks - 1));
+            const int q0 = w * 64 + p * (int)blockDim.x;             // wave-uniform
+            if (q0 < chunks) {
+                const int q = q0 + lane < chunks ? q0 + lane : chunks - 1;
+                dma16(xbase, 16u * (uint32_t)q, xs_lds + 16u * (uint32_t)q0);
+            }
         }
     }
 
@@ -189,25 +180,27 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(const GemvArgs a) 
     uint4 wq[kRun], md;
     load_run(kb_begin, wq, md);
 
-    // 3. staged variant: x -> LDS and the row-block sums (rows < M; the sums of the
-    //    repeated rows are never read into a kept result)
+    // 3. staged variant: the row-block sums X of the staged activations (rows < M; the
+    //    sums of the repeated rows are never read into a kept result)
     if constexpr (kStaged) {
-        // the run's metadata and kRun code loads stay in flight
-#pragma unroll
-        for (int p = 0; p < kChunks; ++p) wait_x_chunk<kRun + 1>(xv[p]);
+        // this wave's copies are done (its run's loads may still be in flight); each
+        // lane sums the chunk its own copy wrote, so no barrier is needed before the
+        // sums, only after them
+        wait_vmcnt<kRun + 1>();
+        asm volatile("" : : : "memory");
+        const float inv_row_chunks = 1.0f / (float)row_chunks;
 #pragma unroll
         for (int p = 0; p < kChunks; ++p) {
             const int q = threadIdx.x + p * blockDim.x;
-            const uint4 xc = make_uint4(xv[p].x, xv[p].y, xv[p].z, xv[p].w);
             // chunks of one (row, row block) are 16 consecutive q: one row of 16 lanes,
             // all valid or all past the end together (row_chunks is a multiple of 16)
             if (q < chunks) {
-                reinterpret_cast<uint4*>(xs)[q] = xc;
-                const float s = row16_sum(sum8<kBF16>(xc));
-                if ((q & 15) == 0) {
-                    const int kb = (q - xm[p] * row_chunks) >> 4;
-                    xsum[kb * 16 + xm[p]] = s;
-                }
+                // row of chunk q: a float estimate (q < 2^22, off by at most one) corrected exactly
+                int m = (int)((float)q * inv_row_chunks);
+                m -= m * row_chunks > q ? 1 : 0;
+                m += (m + 1) * row_chunks <= q ? 1 : 0;
+                const float s = row16_sum(sum8<kBF16>(reinterpret_cast<const uint4*>(xs)[q]));
+                if ((q & 15) == 0) xsum[((q - m * row_chunks) >> 4) * 16 + m] = s;
             }
         }
         __syncthreads();
@@ -334,7 +327,7 @@ GemvPlan plan_gemv_with(int64_t M, int64_t K, int64_t N, int cols_per_wg) {
     p.waves = p.waves_k * cols_per_wg;
     const int64_t threads = 64 * p.waves;
     const size_t partial_bytes = p.waves_k > 1 ? (size_t)p.waves * 64 * 16 : 0;
-    const size_t staged_bytes = (size_t)M * K * 2 + (size_t)KB * 16 * 4 + partial_bytes;
+    const size_t staged_bytes = (size_t)staged_x_bytes(M * K / 8) + (size_t)KB * 16 * 4 + partial_bytes;
     p.chunks_per_thread = (int)((M * K / 8 + threads - 1) / threads);
     p.staged = staged_bytes <= kStagedLdsLimit && p.chunks_per_thread <= kMaxStagedChunksPerThread;
     p.lds_bytes = p.staged ? staged_bytes : partial_bytes;
