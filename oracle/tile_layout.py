@@ -6,8 +6,8 @@ must produce exactly these bytes; nothing here is shared with it.
 The pages describe a one-time reorder after loading (vLLM note "Carga de capas
 cuantizadas", "Responsabilidades" and "Flujo de datos": process_weights_after_loading
 rewrites qweight into the layout the kernel expects) but the layout is the
-kernel's own. This library's layout, version 1, for a K x N weight with group
-size G (G = K for group_size = -1; G a multiple of 128 dividing K):
+kernel's own. This library's layout, version 2, for a K x N weight with group
+size G (G = K for group_size = -1; G = 32, 64, or a multiple of 128 dividing K):
 
   KB = K / 128 row blocks; Np = N rounded up to a multiple of 16, NB = Np / 16
   column blocks. N must be a multiple of 8, the pack factor of the checkpoint
@@ -26,17 +26,19 @@ size G (G = K for group_size = -1; G a multiple of 128 dividing K):
     (bits 4s .. 4s+3) holds the code of row e = TILE_ORDER[s].
     TILE_ORDER = (0, 2, 4, 6, 1, 3, 5, 7): slots t and t+4 hold rows 2t and 2t+1.
 
-  Metadata plane, bytes [K*Np/2, K*Np/2 + 4*Np*KBP), KBP = KB rounded up to a
-  multiple of 4:
-    uint32 number n * KBP + kb describes column n over row block kb (so one
-    column's words for all row blocks are contiguous), whose group is
-    g = (128 kb) div G:
+  Metadata plane, bytes [K*Np/2, K*Np/2 + 4*Np*UW): one word per metadata unit
+  of Gu = min(G, 128) rows (a 128-row block, or 1/2 or 1/4 of one for G = 64 or
+  32); U = K / Gu units, UW = U rounded up to a multiple of 4:
+    uint32 number n * UW + b describes column n over unit b (rows b Gu ..
+    b Gu + Gu - 1; so one column's words are contiguous), whose group is
+    g = (b Gu) div G:
       bits 0..15  = the 16-bit pattern of S[g, n] (the scale, fp16 or bf16),
       bits 16..19 = Z[g, n] (the zero point, 0..15),
       bits 20..31 = 0;
-    words kb = KB .. KBP-1 of every column are 0 (padding).
+    words b = U .. UW-1 of every column are 0 (padding).
+  For G >= 128 a unit is a row block (UW = KB rounded up to 4).
 
-  Total size: K*Np/2 + 4*Np*KBP bytes.
+  Total size: K*Np/2 + 4*Np*UW bytes.
 
 Column blocks are independent (as the n-blocks of the CPU layout are in the
 vllm-omni commit "cpu_int4: repack weights in n-blocks, to bound the load-time
@@ -62,8 +64,8 @@ def check_shape(K, N, group_size):
     if N % 8 != 0:
         raise ValueError("N must be a multiple of 8")
     G = K if group_size == -1 else int(group_size)
-    if G <= 0 or G % ROWS_PER_BLOCK != 0 or K % G != 0:
-        raise ValueError("group size must be -1 or a multiple of 128 dividing K")
+    if G <= 0 or K % G != 0 or (G % ROWS_PER_BLOCK != 0 and G not in (32, 64)):
+        raise ValueError("group size must be -1, 32, 64 or a multiple of 128 dividing K")
     return G
 
 
@@ -72,14 +74,25 @@ def padded_row_blocks(K):
     return (KB + 3) // 4 * 4
 
 
+def unit_rows(G):
+    """Rows described by one metadata word: min(G, 128)."""
+    return min(G, ROWS_PER_BLOCK)
+
+
+def padded_units(K, G):
+    """Metadata words per column: K / unit_rows(G) rounded up to a multiple of 4."""
+    U = K // unit_rows(G)
+    return (U + 3) // 4 * 4
+
+
 def padded_cols(N):
     return (N + COLS_PER_BLOCK - 1) // COLS_PER_BLOCK * COLS_PER_BLOCK
 
 
 def packed_bytes(K, N, group_size):
-    check_shape(K, N, group_size)
+    G = check_shape(K, N, group_size)
     Np = padded_cols(N)
-    return K * Np // 2 + 4 * Np * padded_row_blocks(K)
+    return K * Np // 2 + 4 * Np * padded_units(K, G)
 
 
 def repack(Q, Z, scale_bits, group_size):
@@ -108,11 +121,13 @@ def repack(Q, Z, scale_bits, group_size):
     # lane L = 16 h + c, so [h, c] flattens to L in order
     weight_plane = words.reshape(NB, KB, 64, 4)
 
-    group_of_block = (np.arange(KB) * ROWS_PER_BLOCK) // G             # [kb]
-    s_blk = scale_bits[group_of_block].astype(np.uint32)               # [kb, N]
-    z_blk = Z[group_of_block].astype(np.uint32)                        # [kb, N]
-    meta = np.zeros((N, padded_row_blocks(K)), dtype=np.uint32)        # [n, kb], padding 0
-    meta[:, :KB] = (s_blk | (z_blk << np.uint32(16))).T
+    Gu = unit_rows(G)
+    U = K // Gu
+    group_of_unit = (np.arange(U) * Gu) // G                           # [b]
+    s_u = scale_bits[group_of_unit].astype(np.uint32)                  # [b, N]
+    z_u = Z[group_of_unit].astype(np.uint32)                           # [b, N]
+    meta = np.zeros((N, padded_units(K, G)), dtype=np.uint32)          # [n, b], padding 0
+    meta[:, :U] = (s_u | (z_u << np.uint32(16))).T
 
     out = np.concatenate([
         np.ascontiguousarray(weight_plane).astype("<u4").view(np.uint8).reshape(-1),
@@ -147,12 +162,13 @@ def repack_loops(Q, Z, scale_bits, group_size):
                     off = base + 16 * lane + 4 * i
                     out[off:off + 4] = word.to_bytes(4, "little")
     meta_base = K * Np // 2
-    KBP = padded_row_blocks(K)
+    Gu = min(G, 128)
+    UW = padded_units(K, G)
     for n in range(N):                 # padding columns' words stay 0
-        for kb in range(KB):           # words kb >= KB stay 0
-            g = (128 * kb) // G
+        for b in range(K // Gu):       # words b >= K / Gu stay 0
+            g = (Gu * b) // G
             word = int(scale_bits[g, n]) | (int(Z[g, n]) << 16)
-            off = meta_base + 4 * (n * KBP + kb)
+            off = meta_base + 4 * (n * UW + b)
             out[off:off + 4] = word.to_bytes(4, "little")
     return np.frombuffer(bytes(out), dtype=np.uint8)
 
@@ -175,16 +191,17 @@ def decode(packed, K, N, group_size):
         q[:, :, :, TILE_ORDER[s], :, :] = codes.transpose(1, 4, 2, 0, 3)
     Q = q.reshape(K, N)
 
-    meta_all = packed[wbytes:].view("<u4").reshape(N, padded_row_blocks(K))
-    if np.any(meta_all[:, KB:]):
+    U = K // unit_rows(G)
+    meta_all = packed[wbytes:].view("<u4").reshape(N, padded_units(K, G))
+    if np.any(meta_all[:, U:]):
         raise ValueError("metadata padding is not zero")
-    meta = meta_all[:, :KB].T                                          # [kb, n]
+    meta = meta_all[:, :U].T                                           # [b, n]
     if np.any(meta >> np.uint32(20)):
         raise ValueError("reserved metadata bits are not zero")
-    blocks_per_group = G // ROWS_PER_BLOCK
-    meta_g = meta.reshape(K // G, blocks_per_group, N)
+    units_per_group = G // unit_rows(G)
+    meta_g = meta.reshape(K // G, units_per_group, N)
     if np.any(meta_g != meta_g[:, :1, :]):
-        raise ValueError("row blocks of one group carry different metadata")
+        raise ValueError("units of one group carry different metadata")
     first = meta_g[:, 0, :]
     S = (first & np.uint32(0xFFFF)).astype(np.uint16)
     Z = ((first >> np.uint32(16)) & np.uint32(0xF)).astype(np.uint8)

@@ -304,6 +304,31 @@ def pin_layout_half_block(tile_layout):
     return True
 
 
+def pin_layout_small_groups(tile_layout, G, K=384, N=16):
+    """G = 32 or 64: scale bits of group g, column n = (g << 8) | n, zero point
+    (3 g) mod 16. Closed form: K / G words per column (a word per G rows), word b
+    of column n = ((b << 8) | n) | ((3 b mod 16) << 16), padded with zero words to a
+    multiple of 4, the plane after the K*N/2 code bytes; the codes are untouched."""
+    U = K // G
+    UW = (U + 3) // 4 * 4
+    g = np.arange(U)
+    S = ((g[:, None] << 8) | np.arange(N)[None, :]).astype(np.uint16)
+    Z = np.repeat(((3 * g) % 16).astype(np.uint8)[:, None], N, axis=1)
+    Q = (np.arange(K)[:, None] % 16 + np.zeros((1, N), dtype=np.int64)).astype(np.uint8)
+    out = tile_layout.repack(Q, Z, S, G)
+    if out.size != K * N // 2 + 4 * N * UW:
+        return False
+    ref128 = tile_layout.repack(Q, np.zeros((K // 128, N), np.uint8), np.zeros((K // 128, N), np.uint16), 128)
+    if not np.array_equal(out[:K * N // 2], ref128[:K * N // 2]):
+        return False
+    meta = out[K * N // 2:].view("<u4").reshape(N, UW)
+    for n in range(N):
+        want = [((b << 8) | n) | (((3 * b) % 16) << 16) for b in range(U)] + [0] * (UW - U)
+        if meta[n].tolist() != want:
+            return False
+    return True
+
+
 # ---------------------------------------------------------------- tied embedding
 
 def _bf16_bits_of(v):

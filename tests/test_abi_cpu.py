@@ -52,16 +52,17 @@ def test_layout_version_and_sizes(w):
     from oracle import tile_layout
     assert w.w4a16_layout_version() == tile_layout.LAYOUT_VERSION
     for K, N, G in [(512, 512, 128), (2048, 13312, 128), (6656, 2048, 128), (2048, 131072, 128),
-                    (1024, 48, 256), (1024, 48, -1), (256, 24, 128), (2048, 13288, 128)]:
+                    (1024, 48, 256), (1024, 48, -1), (256, 24, 128), (2048, 13288, 128), (384, 40, 64),
+                    (384, 40, 32), (6656, 2048, 32)]:
         assert w.w4a16_packed_bytes(K, N, G) == tile_layout.packed_bytes(K, N, G)
-    for K, N, G in [(100, 16, 128), (256, 20, 128), (256, 16, 64), (384, 16, 256), (0, 16, 128), (128, 0, 128)]:
+    for K, N, G in [(100, 16, 128), (256, 20, 128), (256, 16, 96), (384, 16, 256), (0, 16, 128), (128, 0, 128)]:
         assert w.w4a16_packed_bytes(K, N, G) == 0
     # K split over workgroups only when the output has too few tiles for the GPU
     assert w.w4a16_workspace_bytes(512, 2048, 131072, 128) == 0
     assert w.w4a16_workspace_bytes(512, 2048, 13312, 128) == 0
     ws = w.w4a16_workspace_bytes(16, 6656, 2048, 128)
     assert ws > 16 * 2048 * 4 and ws % 4 == 0
-    assert w.w4a16_workspace_bytes(16, 6656, 2048, 64) == 0          # invalid group size
+    assert w.w4a16_workspace_bytes(16, 6656, 2048, 96) == 0          # invalid group size
     # sized for the MFMA GEMM, which any M may be sent to; the GEMV needs none
     assert w.w4a16_workspace_bytes(1, 2048, 131072, 128) == 0
     assert w.w4a16_workspace_bytes(0, 6656, 2048, 128) == 0
@@ -95,7 +96,7 @@ def test_gemm_validation_before_any_device_call(w):
     assert gemm(w, N=(1 << 28) + 16) == 2
     assert gemm(w, K=1 << 20, N=1 << 18) == 2
     assert gemm(w, M=1 << 13, K=1 << 20) == 2
-    assert gemm(w, G=64) == 3
+    assert gemm(w, G=96) == 3
     assert gemm(w, G=384) == 3
     assert gemm(w, dtype=2) == 4
     assert gemm(w, x=None) == 1
@@ -126,7 +127,7 @@ def test_repack_validation_before_any_device_call(w):
         return w.lib.w4a16_repack(qw, qz, sc, dtype, K, N, G, packed, pbytes, None)
     assert repack(K=100) == 2
     assert repack(N=12) == 2
-    assert repack(G=32) == 3
+    assert repack(G=96) == 3
     assert repack(dtype=-1) == 4
     assert repack(qw=None) == 1
     assert repack(qz=None) == 1
@@ -160,7 +161,7 @@ def test_repack_gptq_validation_before_any_device_call(w):
         return w.lib.w4a16_repack_gptq(qw, qz, sc, dtype, K, N, G, packed, pbytes, None)
     assert repack(K=100) == 2
     assert repack(N=12) == 2
-    assert repack(G=32) == 3
+    assert repack(G=96) == 3
     assert repack(dtype=-1) == 4
     assert repack(qw=None) == 1
     assert repack(qz=None) == 1
@@ -178,7 +179,7 @@ def test_embedding_validation_before_any_device_call(w):
         return w.lib.w4a16_embedding(ids, T, packed, pbytes, dtype, K, N, G, out, None)
     assert emb(K=100) == 2
     assert emb(N=12) == 2
-    assert emb(G=32) == 3
+    assert emb(G=96) == 3
     assert emb(dtype=2) == 4
     assert emb(T=-1) == 2
     assert emb(T=1 << 31) == 2

@@ -201,7 +201,7 @@ def test_gemm_rejects_bad_calls(w):
         w.w4a16_gemm_ex(xbig, packed, 32, 128, path="gemv")
     assert e.value.status == "W4A16_ERR_PATH"
     with pytest.raises(w.W4A16Error) as e:
-        w.w4a16_gemm(x, packed, 32, 64)
+        w.w4a16_gemm(x, packed, 32, 96)
     assert e.value.status == "W4A16_ERR_GROUP"
 
 

@@ -193,7 +193,9 @@ def test_layout_sizes_and_rejections():
     assert tile_layout.packed_bytes(6656, 2048, 128) == 6656 * 2048 // 2 + 4 * 52 * 2048
     assert tile_layout.packed_bytes(384, 16, 128) == 384 * 16 // 2 + 4 * 4 * 16      # 3 row blocks padded to 4
     assert tile_layout.packed_bytes(256, 24, 128) == 256 * 32 // 2 + 4 * 4 * 32      # half block padded to 16
-    for K, N, G in [(100, 16, 128), (256, 20, 128), (256, 16, 64), (384, 16, 256)]:
+    assert tile_layout.packed_bytes(384, 16, 64) == 384 * 16 // 2 + 4 * 8 * 16       # 6 units of 64 rows -> 8
+    assert tile_layout.packed_bytes(384, 16, 32) == 384 * 16 // 2 + 4 * 12 * 16      # 12 units of 32 rows
+    for K, N, G in [(100, 16, 128), (256, 20, 128), (256, 16, 96), (256, 16, 16), (384, 16, 256)]:
         with pytest.raises(ValueError):
             tile_layout.packed_bytes(K, N, G)
 
@@ -442,6 +444,44 @@ def test_planted_half_block_mistakes_are_caught(desc, old, new):
     try:
         mut = _mutant("tile_layout", old, new)
         ok = pins.pin_layout_half_block(mut)
+    except (ValueError, AssertionError, IndexError):
+        ok = False
+    assert not ok
+
+
+# ---------------------------------------------------------------- group sizes 32 and 64
+
+@pytest.mark.parametrize("G", [32, 64])
+def test_layout_small_group_metadata(G):
+    assert pins.pin_layout_small_groups(tile_layout, G)
+
+
+@pytest.mark.parametrize("G", [32, 64])
+def test_layout_small_group_roundtrip(G):
+    rng = np.random.default_rng(G)
+    K, N = 384, 40
+    Q = rng.integers(0, 16, (K, N), dtype=np.uint8)
+    Z = rng.integers(0, 16, (K // G, N), dtype=np.uint8)
+    S = rng.integers(0, 2**16, (K // G, N), dtype=np.uint16)
+    out = tile_layout.repack(Q, Z, S, G)
+    assert np.array_equal(out, tile_layout.repack_loops(Q, Z, S, G))
+    Q2, Z2, S2 = tile_layout.decode(out, K, N, G)
+    assert np.array_equal(Q2, Q) and np.array_equal(Z2, Z) and np.array_equal(S2, S)
+
+
+SMALL_GROUP_MUTANTS = [
+    ("one word per row block", "    return min(G, ROWS_PER_BLOCK)", "    return ROWS_PER_BLOCK"),
+    ("unit groups from 128-row blocks", "group_of_unit = (np.arange(U) * Gu) // G",
+     "group_of_unit = (np.arange(U) * ROWS_PER_BLOCK) // G % (K // G)"),
+    ("units unpadded", "    return (U + 3) // 4 * 4", "    return U"),
+]
+
+
+@pytest.mark.parametrize("desc,old,new", SMALL_GROUP_MUTANTS, ids=[m[0] for m in SMALL_GROUP_MUTANTS])
+def test_planted_small_group_mistakes_are_caught(desc, old, new):
+    try:
+        mut = _mutant("tile_layout", old, new)
+        ok = pins.pin_layout_small_groups(mut, 32) and pins.pin_layout_small_groups(mut, 64)
     except (ValueError, AssertionError, IndexError):
         ok = False
     assert not ok

@@ -7,6 +7,7 @@
 #include <atomic>
 
 #include "../../include/w4a16.h"
+#include "device_common.h"
 #include "launch.h"
 
 namespace {
@@ -27,17 +28,17 @@ w4a16_status check_shape(int64_t K, int64_t N, int64_t group_size, int64_t* G_ou
     if (K <= 0 || N <= 0 || K % 128 != 0 || N % 8 != 0) return W4A16_ERR_SHAPE;
     if (K > kMaxK || N > kMaxN || K * N > kMaxKN) return W4A16_ERR_SHAPE;
     const int64_t G = group_size == -1 ? K : group_size;
-    if (G <= 0 || G % 128 != 0 || K % G != 0) return W4A16_ERR_GROUP;
+    if (G <= 0 || K % G != 0 || (G % 128 != 0 && G != 32 && G != 64)) return W4A16_ERR_GROUP;
     *G_out = G;
     return W4A16_OK;
 }
 
 // K x Np codes (Np = N rounded up to 16 columns) + one 32-bit word per column per
-// 128-row block, the row-block count rounded up to 4
-size_t packed_size(int64_t K, int64_t N) {
-    const size_t kbp = (size_t)((K / 128 + 3) / 4 * 4);
-    const size_t np = (size_t)((N + 15) / 16 * 16);
-    return (size_t)K * np / 2 + (size_t)4 * kbp * np;
+// unit of min(G, 128) rows, the unit count rounded up to 4 (G resolved)
+size_t packed_size(int64_t K, int64_t N, int64_t G) {
+    const size_t uw = (size_t)w4a16::padded_units(K, G);
+    const size_t np = (size_t)w4a16::padded_cols(N);
+    return (size_t)K * np / 2 + (size_t)4 * uw * np;
 }
 
 // 0 = unknown, 1 = gfx950, 2 = other; cached per device ordinal.
@@ -74,9 +75,9 @@ w4a16_status gemm_impl(const void* x, const void* packed, size_t packed_bytes, w
     if (!x || !packed || !y) return W4A16_ERR_NULL;
     if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(y, 16) || (bias && !aligned(bias, 2)))
         return W4A16_ERR_ALIGN;
-    if (packed_bytes < packed_size(K, N)) return W4A16_ERR_BUFFER_SIZE;
+    if (packed_bytes < packed_size(K, N, G)) return W4A16_ERR_BUFFER_SIZE;
     const bool use_gemv = path == W4A16_PATH_GEMV || (path == W4A16_PATH_AUTO && M <= gemv_max_m);
-    const size_t need = use_gemv ? 0 : w4a16::plan_gemm(M, K, N).workspace_bytes;
+    const size_t need = use_gemv ? 0 : w4a16::plan_gemm(M, K, N, G).workspace_bytes;
     if (need > 0) {
         if (!workspace) return W4A16_ERR_NULL;
         if (!aligned(workspace, 16)) return W4A16_ERR_ALIGN;
@@ -91,8 +92,8 @@ w4a16_status gemm_impl(const void* x, const void* packed, size_t packed_bytes, w
     const auto* bp = static_cast<const uint16_t*>(bias);
     auto* yp = static_cast<uint16_t*>(y);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const hipError_t err = use_gemv ? w4a16::launch_gemv(xp, wp, bp, yp, M, K, N, bf16, s)
-                                    : w4a16::launch_gemm(xp, wp, bp, yp, M, K, N, bf16, workspace, s);
+    const hipError_t err = use_gemv ? w4a16::launch_gemv(xp, wp, bp, yp, M, K, N, G, bf16, s)
+                                    : w4a16::launch_gemm(xp, wp, bp, yp, M, K, N, G, bf16, workspace, s);
     return err == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
 }
 
@@ -111,7 +112,7 @@ w4a16_status repack_impl(bool gptq, const int32_t* qweight, const int32_t* qzero
     if (!qweight || !qzeros || !scales || !packed) return W4A16_ERR_NULL;
     if (!aligned(qweight, 4) || !aligned(qzeros, 4) || !aligned(scales, 2) || !aligned(packed, 16))
         return W4A16_ERR_ALIGN;
-    if (packed_bytes < packed_size(K, N)) return W4A16_ERR_BUFFER_SIZE;
+    if (packed_bytes < packed_size(K, N, G)) return W4A16_ERR_BUFFER_SIZE;
     st = check_device();
     if (st != W4A16_OK) return st;
     const auto* sc = static_cast<const uint16_t*>(scales);
@@ -131,7 +132,7 @@ int w4a16_layout_version(void) { return kLayoutVersion; }
 size_t w4a16_packed_bytes(int64_t K, int64_t N, int64_t group_size) {
     int64_t G = 0;
     if (check_shape(K, N, group_size, &G) != W4A16_OK) return 0;
-    return packed_size(K, N);
+    return packed_size(K, N, G);
 }
 
 w4a16_status w4a16_repack(const int32_t* qweight, const int32_t* qzeros, const void* scales, w4a16_dtype dtype,
@@ -165,7 +166,7 @@ size_t w4a16_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t group_size
     if (M <= 0 || check_shape(K, N, group_size, &G) != W4A16_OK) return 0;
     if (M >= (int64_t(1) << 31) || M * K > kMaxMK) return 0;
     // only the MFMA GEMM uses one (when it splits K over workgroups); the GEMV needs none
-    return w4a16::plan_gemm(M, K, N).workspace_bytes;
+    return w4a16::plan_gemm(M, K, N, G).workspace_bytes;
 }
 
 w4a16_status w4a16_gemm(const void* x, const void* packed, size_t packed_bytes, w4a16_dtype dtype, void* y,
@@ -192,11 +193,11 @@ w4a16_status w4a16_embedding(const int32_t* ids, int64_t T, const void* packed, 
     if (T == 0) return W4A16_OK;
     if (!ids || !packed || !out) return W4A16_ERR_NULL;
     if (!aligned(ids, 4) || !aligned(packed, 16) || !aligned(out, 16)) return W4A16_ERR_ALIGN;
-    if (packed_bytes < packed_size(K, N)) return W4A16_ERR_BUFFER_SIZE;
+    if (packed_bytes < packed_size(K, N, G)) return W4A16_ERR_BUFFER_SIZE;
     st = check_device();
     if (st != W4A16_OK) return st;
     const hipError_t err = w4a16::launch_embedding(ids, T, static_cast<const uint8_t*>(packed),
-                                                   static_cast<uint16_t*>(out), K, N, dtype == W4A16_BF16,
+                                                   static_cast<uint16_t*>(out), K, N, G, dtype == W4A16_BF16,
                                                    static_cast<hipStream_t>(stream));
     return err == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
 }
@@ -224,7 +225,7 @@ w4a16_status w4a16_packed_header(int64_t K, int64_t N, int64_t group_size, w4a16
     if (header_bytes < W4A16_PACKED_HEADER_BYTES) return W4A16_ERR_BUFFER_SIZE;
     uint8_t h[W4A16_PACKED_HEADER_BYTES] = {};
     const uint32_t version = kLayoutVersion, dt = (uint32_t)dtype;
-    const uint64_t nbytes = packed_size(K, N);
+    const uint64_t nbytes = packed_size(K, N, G);
     memcpy(h, kHeaderMagic, 8);
     memcpy(h + 8, &version, 4);
     memcpy(h + 12, &dt, 4);
@@ -259,7 +260,7 @@ w4a16_status w4a16_parse_packed_header(const void* header, size_t header_bytes, 
     if (version != (uint32_t)kLayoutVersion) return W4A16_ERR_LAYOUT;
     int64_t G = 0;
     if (check_shape(k, n, g, &G) != W4A16_OK || (dt != W4A16_FP16 && dt != W4A16_BF16) ||
-        nbytes != packed_size(k, n))
+        nbytes != packed_size(k, n, G))
         return W4A16_ERR_LAYOUT;
     *K = k;
     *N = n;

@@ -27,6 +27,12 @@ constexpr int kBlockBytes = 1024;
 __host__ __device__ constexpr int64_t padded_row_blocks(int64_t K) { return ((K / kRowsPerBlock) + 3) / 4 * 4; }
 // Columns of the packed layout: N rounded up to whole 16-column blocks (N % 8 == 0;
 // a last block of 8 real columns carries 8 zero columns, code 0 and metadata 0).
+// Metadata words: one per unit of min(G, 128) rows, i.e. 128 / G per 128-row block
+// for group sizes 32 and 64 (1 otherwise); per column, K / unit rows rounded up to 4.
+__host__ __device__ constexpr int units_per_block(int64_t G) { return G < kRowsPerBlock ? (int)(kRowsPerBlock / G) : 1; }
+__host__ __device__ constexpr int64_t padded_units(int64_t K, int64_t G) {
+    return ((K / kRowsPerBlock) * units_per_block(G) + 3) / 4 * 4;
+}
 __host__ __device__ constexpr int64_t padded_cols(int64_t N) { return (N + kColsPerBlock - 1) / kColsPerBlock * kColsPerBlock; }
 
 // Row e held by nibble slot s of a tile word: 0,2,4,6,1,3,5,7. Slots t and t+4

@@ -49,19 +49,19 @@ __device__ __forceinline__ uint32_t pick(const uint4 v, int i) {
 // One stage of the LDS ring: the activation tile of one 128-row block of K, the
 // workgroup's blocks of packed codes (W waves x CBW) and its metadata words (64 per
 // wave, of which the first 16 * CBW are used).
-template <int BM, int CBW, int W>
+template <int BM, int CBW, int W, int kSub>
 struct Stage {
     // [BM rows][16 chunks of 16 bytes], chunk j of row r stored at chunk j ^ (r % 16)
     uint4 x[BM * 16];
     uint4 w[W * CBW * 64];                  // 1 KiB per block, as in global memory
-    uint32_t meta[W * 64];
+    uint32_t meta[kSub * W * 64];           // [unit of the k block][wave][lane]
 };
 
 // Workgroup tile: 16*MR rows x 64*CBW columns, 4 waves side by side along N, each
 // owning CBW column blocks and all rows. `splits` > 1 splits the K range over
 // workgroups; their fp32 partial tiles meet in `workspace` and the last workgroup of
 // a tile to finish adds them in split order (deterministic) and writes y.
-template <bool kBF16, int MR, int CBW, int kWaves>
+template <bool kBF16, int MR, int CBW, int kWaves, int kSub>
 __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed, const uint16_t* __restrict__ bias,
     uint16_t* __restrict__ y, int M, int K, int N, int tiles_m, int tiles_n, int splits,
@@ -69,9 +69,9 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(
     constexpr int BM = 16 * MR;
     constexpr int kSlabsPerWave = BM / 4 / kWaves;      // 1 KiB slabs (4 rows) of the x tile per wave
     static_assert(kSlabsPerWave * 4 * kWaves == BM, "x tile must split over the waves");
-    constexpr int kDmaPerStage = kSlabsPerWave + CBW + 1;   // copies per wave per stage
+    constexpr int kDmaPerStage = kSlabsPerWave + CBW + kSub;   // copies per wave per stage
     constexpr int kStages = 3;
-    using StageT = Stage<BM, CBW, kWaves>;
+    using StageT = Stage<BM, CBW, kWaves, kSub>;
     __shared__ StageT ring[kStages];
     __shared__ int last_split;
 
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(
     if (n_tile >= tiles_n) return;
 
     const int KB = K / kRowsPerBlock;
-    const int KBP = (int)padded_row_blocks(K);
+    const int UW = (int)padded_units(K, kRowsPerBlock / kSub);     // metadata words per column
     const int Np = (int)padded_cols(N);                         // columns of the packed layout
     const int NB = Np / kColsPerBlock;
     const int kb_begin = (int)((int64_t)KB * split / splits);
@@ -127,8 +127,8 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(
     // metadata: column words of this wave's columns (lanes past 16 * CBW repeat one)
     const int col0 = nbw * kColsPerBlock < Np ? nbw * kColsPerBlock : Np - kColsPerBlock;
     const int ncol = nbw * kColsPerBlock + (lane < 16 * CBW ? lane : 0);
-    const uint8_t* mbase = uniform_ptr(packed + (size_t)K * Np / 2 + (size_t)col0 * KBP * 4);
-    const uint32_t moff = (uint32_t)((ncol < Np ? ncol : Np - 1) - col0) * (uint32_t)KBP * 4u;
+    const uint8_t* mbase = uniform_ptr(packed + (size_t)K * Np / 2 + (size_t)col0 * UW * 4);
+    const uint32_t moff = (uint32_t)((ncol < Np ? ncol : Np - 1) - col0) * (uint32_t)UW * 4u;
     const uint32_t ring_base = lds_addr(&ring[0]);
 
     // copy q (0 .. kDmaPerStage-1) of k block kb into ring slot `slot`
@@ -141,7 +141,8 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(
             dma16(wbase + (size_t)kb * kBlockBytes, woff[q - kSlabsPerWave],
                   st + (uint32_t)offsetof(StageT, w) + (uint32_t)(w * CBW + q - kSlabsPerWave) * 1024u);
         else
-            dma4(mbase + (size_t)kb * 4, moff, st + (uint32_t)offsetof(StageT, meta) + (uint32_t)w * 256u);
+            dma4(mbase + ((size_t)kb * kSub + (q - kSlabsPerWave - CBW)) * 4, moff,
+                 st + (uint32_t)offsetof(StageT, meta) + (uint32_t)((q - kSlabsPerWave - CBW) * kWaves + w) * 256u);
     };
     auto issue = [&](int slot, int kb) {
 #pragma unroll
@@ -169,11 +170,12 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(
         if (t + 2 < nkb) issue((t + 2) % kStages, kb_begin + t + 2);
 
         const StageT& st = ring[t % kStages];
-        Dequant<kBF16> dq[CBW];
+        Dequant<kBF16> dq[CBW][kSub];           // per column block and metadata unit
         uint4 wq[CBW];
 #pragma unroll
         for (int j = 0; j < CBW; ++j) {
-            dq[j] = Dequant<kBF16>(st.meta[w * 64 + 16 * j + c]);
+#pragma unroll
+            for (int v = 0; v < kSub; ++v) dq[j][v] = Dequant<kBF16>(st.meta[(v * kWaves + w) * 64 + 16 * j + c]);
             wq[j] = st.w[(w * CBW + j) * 64 + lane];
         }
         if constexpr (kBF16) {
@@ -187,7 +189,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(
             uint4 a[MR];
 #pragma unroll
             for (int r = 0; r < MR; ++r) a[r] = st.x[(16 * r + c) * 16 + (h ^ c)];
-            uint4 b = dq[0](pick(wq[0], 0));
+            uint4 b = dq[0][0](pick(wq[0], 0));
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -197,7 +199,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(
                     const int jn = j + 1 < CBW ? j + 1 : 0;
                     const int in = j + 1 < CBW ? i : i + 1;
                     const uint32_t dn = has_next ? pick(wq[jn], in & 3) : 0u;
-                    const float sn = dq[jn].s, zn = dq[jn].nzs;
+                    const float sn = dq[jn][((in & 3) * kSub) / 4].s, zn = dq[jn][((in & 3) * kSub) / 4].nzs;
                     uint32_t lo = 0u, hi = 0u;
                     float cv[8], fv[8];
                     uint32_t o[4] = {0u, 0u, 0u, 0u};
@@ -251,7 +253,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(
                 for (int r = 0; r < MR; ++r) a[r] = st.x[(16 * r + c) * 16 + chunk];
 #pragma unroll
                 for (int j = 0; j < CBW; ++j) {
-                    const uint4 b = dq[j](pick(wq[j], i));
+                    const uint4 b = dq[j][(i * kSub) / 4](pick(wq[j], i));
 #pragma unroll
                     for (int r = 0; r < MR; ++r) acc[r][j] = mfma16x16x32<kBF16>(b, a[r], acc[r][j]);
                 }
@@ -364,18 +366,27 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(
 
 constexpr int kTargetWorkgroups = 256;   // one per CU
 
-template <bool kBF16, int MR, int CBW, int W>
+template <bool kBF16, int MR, int CBW, int W, int kSub = 1>
 void launch_cfg(const GemmPlan& p, const uint16_t* x, const uint8_t* packed, const uint16_t* bias, uint16_t* y,
                 int M, int K, int N, uint32_t* counters, float* partials, hipStream_t stream) {
     const int tiles_n_pad = (p.tiles_n + kXcds - 1) / kXcds * kXcds;
     const dim3 grid((unsigned)(p.tiles_m * p.splits * tiles_n_pad));
-    hipLaunchKernelGGL((gemm_kernel<kBF16, MR, CBW, W>), grid, dim3(64 * W), 0, stream, x, packed, bias, y, M, K, N,
-                       p.tiles_m, p.tiles_n, p.splits, counters, partials);
+    hipLaunchKernelGGL((gemm_kernel<kBF16, MR, CBW, W, kSub>), grid, dim3(64 * W), 0, stream, x, packed, bias, y, M,
+                       K, N, p.tiles_m, p.tiles_n, p.splits, counters, partials);
 }
 
 template <bool kBF16, int MR>
 void launch_mr(const GemmPlan& p, const uint16_t* x, const uint8_t* packed, const uint16_t* bias, uint16_t* y,
                int M, int K, int N, uint32_t* counters, float* partials, hipStream_t stream) {
+    // group sizes 32 and 64: one tile shape, 4 waves of one column block
+    if (p.sub == 4) {
+        launch_cfg<kBF16, MR, 1, 4, 4>(p, x, packed, bias, y, M, K, N, counters, partials, stream);
+        return;
+    }
+    if (p.sub == 2) {
+        launch_cfg<kBF16, MR, 1, 4, 2>(p, x, packed, bias, y, M, K, N, counters, partials, stream);
+        return;
+    }
     if constexpr (MR >= 2) {
         if (p.waves == 8) {
             launch_cfg<kBF16, MR, 2, 8>(p, x, packed, bias, y, M, K, N, counters, partials, stream);
@@ -398,15 +409,18 @@ void launch_typed(const GemmPlan& p, const uint16_t* x, const uint8_t* packed, c
 
 }  // namespace
 
-GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N) {
+GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G) {
     GemmPlan p;
+    p.sub = units_per_block(G);
     const int64_t NB = padded_cols(N) / kColsPerBlock;
     const int64_t KB = K / kRowsPerBlock;
     p.mr = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
     p.tiles_m = (int)((M + 16 * p.mr - 1) / (16 * p.mr));
     p.waves = 4;
     p.cbw = 1;
-    if (p.mr >= 4) {
+    if (p.sub > 1) {
+        // group sizes 32 and 64: 4 waves of one column block, the tile's rows by M
+    } else if (p.mr >= 4) {
         // Tile shape from a cost model: rounds of tiles over the CUs (one workgroup per
         // CU) x tile area / throughput of that shape. Throughputs are relative output
         // elements per unit time, per k block, measured with one tile per CU on MI355X:
@@ -472,8 +486,9 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N) {
 }
 
 hipError_t launch_gemm(const uint16_t* x, const uint8_t* packed, const uint16_t* bias, uint16_t* y,
-                       int64_t M, int64_t K, int64_t N, bool bf16, void* workspace, hipStream_t stream) {
-    const GemmPlan p = plan_gemm(M, K, N);
+                       int64_t M, int64_t K, int64_t N, int64_t G, bool bf16, void* workspace,
+                       hipStream_t stream) {
+    const GemmPlan p = plan_gemm(M, K, N, G);
     uint32_t* counters = static_cast<uint32_t*>(workspace);
     float* partials = nullptr;
     if (p.splits > 1) {

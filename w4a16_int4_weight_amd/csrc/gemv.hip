@@ -89,13 +89,18 @@ __device__ __forceinline__ float sum8(const uint4 v) {
     return s;
 }
 
-// Sum over each row of 16 lanes, result in all 16 lanes (DPP: swap neighbours,
-// swap pairs, mirror half rows, mirror rows). Fixed order, so deterministic.
-__device__ __forceinline__ float row16_sum(float v) {
+// Sum over aligned groups of kLanes (4, 8 or 16) lanes within rows of 16, result in
+// every lane of the group (DPP: swap neighbours, swap pairs, mirror half rows, mirror
+// rows). Fixed order, so deterministic.
+template <int kLanes>
+__device__ __forceinline__ float group_sum(float v) {
+    static_assert(kLanes == 4 || kLanes == 8 || kLanes == 16, "group of 4, 8 or 16 lanes");
     v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
     v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
-    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));  // row_half_mirror
-    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));  // row_mirror
+    if constexpr (kLanes >= 8)
+        v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));  // row_half_mirror
+    if constexpr (kLanes >= 16)
+        v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));  // row_mirror
     return v;
 }
 
@@ -109,14 +114,20 @@ struct GemvArgs {
     int waves_k;            // waves per column block (they split K)
 };
 
-template <bool kBF16, bool kStaged, int kChunks>
-__global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(const GemvArgs a) {
+// kSub: metadata units per 128-row block (1; 2 or 4 for group sizes 64 or 32): each
+// unit has its own scale, zero point, MFMA accumulator and activation sum.
+// Group size 32 (kSub = 4) holds 4x the accumulators: at most 8 waves per workgroup,
+// so that the register budget doubles instead of spilling.
+constexpr int max_waves(int sub) { return sub == 4 ? kMaxWaves / 2 : kMaxWaves; }
+
+template <bool kBF16, bool kStaged, int kChunks, int kSub>
+__global__ __launch_bounds__(64 * max_waves(kSub)) void gemv_kernel(const GemvArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     using Mg = Magic<kBF16>;
 
     const int M = a.M, K = a.K, N = a.N;
     const int KB = K / kRowsPerBlock;
-    const int KBP = (int)padded_row_blocks(K);
+    const int UW = (int)padded_units(K, kRowsPerBlock / kSub);    // metadata words per column
     const int waves = blockDim.x >> 6;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);     // wave-uniform
     const int cbl = w / a.waves_k;                                       // column block in the workgroup
@@ -134,12 +145,12 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(const GemvArgs a) 
     const int kb_end = kb_begin + a.kb_per_wave < KB ? kb_begin + a.kb_per_wave : KB;
     const int xr = c < M ? c : 0;    // activation row this lane feeds to the MFMA
 
-    // LDS: [staged x, M x K 16-bit, in whole 1 KiB wave copies][row-block sums X,
-    // KB x 16 fp32][wave partials]
+    // LDS: [staged x, M x K 16-bit, in whole 1 KiB wave copies][unit sums X,
+    // KB x kSub x 16 fp32][wave partials]
     const int row_chunks = K / 8;
     const int chunks = M * row_chunks;                            // 16-byte activation chunks
     const int xs_bytes = kStaged ? (int)staged_x_bytes(chunks) : 0;
-    const int xsum_bytes = kStaged ? KB * 16 * 4 : 0;
+    const int xsum_bytes = kStaged ? KB * kSub * 16 * 4 : 0;
     uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
     float* xsum = reinterpret_cast<float*>(smem + xs_bytes);
     f32x4* partial = reinterpret_cast<f32x4*>(smem + xs_bytes + xsum_bytes);
@@ -168,16 +179,22 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(const GemvArgs a) 
     // 2. codes and metadata of this wave's first run (clamped into the column block;
     //    row blocks past kb_end are loaded but weighted by zero)
     const uint4* wcol = reinterpret_cast<const uint4*>(a.packed) + (size_t)nb * KB * 64 + lane;
-    const uint4* mcol = reinterpret_cast<const uint4*>(a.packed + (size_t)K * padded_cols(N) / 2) + ((size_t)(nb * kColsPerBlock + c) * KBP) / 4;
-    auto load_run = [&](int kb0, uint4 (&wq)[kRun], uint4& md) {
-        md = load_once(mcol + (kb0 < KB ? kb0 : KB - 1) / 4);
+    const uint4* mcol = reinterpret_cast<const uint4*>(a.packed + (size_t)K * padded_cols(N) / 2) + ((size_t)(nb * kColsPerBlock + c) * UW) / 4;
+    // a run's metadata: the kRun x kSub words of row blocks kb0 .. kb0 + 3 (kb0 a
+    // multiple of 4), clamped to the column's words (the entries past KB weigh zero)
+    auto load_run = [&](int kb0, uint4 (&wq)[kRun], uint4 (&md)[kSub]) {
+#pragma unroll
+        for (int s4 = 0; s4 < kSub; ++s4) {
+            const int idx = ((kb0 < KB ? kb0 : KB - 1) / 4) * kSub + s4;
+            md[s4] = load_once(mcol + (idx < UW / 4 ? idx : UW / 4 - 1));
+        }
 #pragma unroll
         for (int u = 0; u < kRun; ++u) {
             const int kb = kb0 + u < KB ? kb0 + u : KB - 1;
             wq[u] = load_once(wcol + (size_t)kb * 64);
         }
     };
-    uint4 wq[kRun], md;
+    uint4 wq[kRun], md[kSub];
     load_run(kb_begin, wq, md);
 
     // 3. staged variant: the row-block sums X of the staged activations (rows < M; the
@@ -186,21 +203,23 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(const GemvArgs a) 
         // this wave's copies are done (its run's loads may still be in flight); each
         // lane sums the chunk its own copy wrote, so no barrier is needed before the
         // sums, only after them
-        wait_vmcnt<kRun + 1>();
+        wait_vmcnt<kRun + kSub>();
         asm volatile("" : : : "memory");
         const float inv_row_chunks = 1.0f / (float)row_chunks;
 #pragma unroll
         for (int p = 0; p < kChunks; ++p) {
             const int q = threadIdx.x + p * blockDim.x;
-            // chunks of one (row, row block) are 16 consecutive q: one row of 16 lanes,
-            // all valid or all past the end together (row_chunks is a multiple of 16)
+            // chunks of one (row, metadata unit) are 16 / kSub consecutive q within one
+            // row of 16 lanes, all valid or all past the end together (row_chunks is a
+            // multiple of 16)
             if (q < chunks) {
                 // row of chunk q: a float estimate (q < 2^22, off by at most one) corrected exactly
                 int m = (int)((float)q * inv_row_chunks);
                 m -= m * row_chunks > q ? 1 : 0;
                 m += (m + 1) * row_chunks <= q ? 1 : 0;
-                const float s = row16_sum(sum8<kBF16>(reinterpret_cast<const uint4*>(xs)[q]));
-                if ((q & 15) == 0) xsum[((q - m * row_chunks) >> 4) * 16 + m] = s;
+                const float s = group_sum<16 / kSub>(sum8<kBF16>(reinterpret_cast<const uint4*>(xs)[q]));
+                // chunk (q - m row_chunks) is unit (q - m row_chunks) / (16 / kSub)
+                if ((q & (16 / kSub - 1)) == 0) xsum[((q - m * row_chunks) / (16 / kSub)) * 16 + m] = s;
             }
         }
         __syncthreads();
@@ -209,25 +228,31 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(const GemvArgs a) 
     // 4. runs of row blocks, the next run's loads in flight during the current one
     const uint32_t mask = pair_mask_vgpr();
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    auto compute_run = [&](const int kb0, const uint4 (&wr)[kRun], const uint4 mr) {
+    auto compute_run = [&](const int kb0, const uint4 (&wr)[kRun], const uint4 (&mr)[kSub]) {
         // row block of each run entry (entries past kb_end read block 0's activations:
-        // finite values, weighted by zero)
+        // finite values, weighted by zero); unit v of entry u is word u kSub + v
         int kbl[kRun];
-        float s[kRun];
-        uint32_t z[kRun];
+        float s[kRun][kSub];
+        uint32_t z[kRun][kSub];
 #pragma unroll
         for (int u = 0; u < kRun; ++u) {
             const bool valid = kb0 + u < kb_end;
             kbl[u] = valid ? kb0 + u : 0;
-            const uint32_t mdv = pick(mr, u);             // kb0 is a multiple of 4
-            s[u] = valid ? half_bits_to_f32<kBF16>(mdv & 0xFFFFu) : 0.f;
-            z[u] = (mdv >> 16) & 0xFu;
-        }
-        f32x4 t[kRun];
 #pragma unroll
-        for (int u = 0; u < kRun; ++u) t[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int v = 0; v < kSub; ++v) {
+                const uint32_t mdv = pick(mr[(u * kSub + v) / 4], (u * kSub + v) % 4);
+                s[u][v] = valid ? half_bits_to_f32<kBF16>(mdv & 0xFFFFu) : 0.f;
+                z[u][v] = (mdv >> 16) & 0xFu;
+            }
+        }
+        f32x4 t[kRun][kSub];
+#pragma unroll
+        for (int u = 0; u < kRun; ++u)
+#pragma unroll
+            for (int v = 0; v < kSub; ++v) t[u][v] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
+            const int v = i * kSub / 4;                 // unit of 32-row step i
 #pragma unroll
             for (int u = 0; u < kRun; ++u) {
                 uint4 xa;
@@ -235,11 +260,11 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(const GemvArgs a) 
                     xa = *reinterpret_cast<const uint4*>(xs + xr * K + kbl[u] * kRowsPerBlock + 32 * i + 8 * h);
                 else
                     xa = *reinterpret_cast<const uint4*>(a.x + (size_t)xr * K + kbl[u] * kRowsPerBlock + 32 * i + 8 * h);
-                t[u] = mfma16x16x32<kBF16>(xa, magic_operand<kBF16>(pick(wr[u], i), mask), t[u]);
+                t[u][v] = mfma16x16x32<kBF16>(xa, magic_operand<kBF16>(pick(wr[u], i), mask), t[u][v]);
                 if constexpr (!kStaged) {
-                    const uint32_t nz = Mg::kNegBase | z[u];            // -(base + z), exact
+                    const uint32_t nz = Mg::kNegBase | z[u][v];         // -(base + z), exact
                     const uint32_t nz2 = nz | (nz << 16);
-                    t[u] = mfma16x16x32<kBF16>(xa, make_uint4(nz2, nz2, nz2, nz2), t[u]);
+                    t[u][v] = mfma16x16x32<kBF16>(xa, make_uint4(nz2, nz2, nz2, nz2), t[u][v]);
                 }
             }
         }
@@ -247,28 +272,35 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(const GemvArgs a) 
             if (M == 1) {      // only register 0 of lanes 0..15 holds a kept result
 #pragma unroll
                 for (int u = 0; u < kRun; ++u)
-                    acc[0] += s[u] * (t[u][0] - (Mg::kBase + (float)z[u]) * xsum[kbl[u] * 16]);
+#pragma unroll
+                    for (int v = 0; v < kSub; ++v)
+                        acc[0] += s[u][v] * (t[u][v][0] - (Mg::kBase + (float)z[u][v]) * xsum[(kbl[u] * kSub + v) * 16]);
             } else {
 #pragma unroll
-                for (int u = 0; u < kRun; ++u) {
-                    const f32x4 xsv = *reinterpret_cast<const f32x4*>(xsum + kbl[u] * 16 + 4 * h);
-                    acc += s[u] * (t[u] - (Mg::kBase + (float)z[u]) * xsv);
-                }
+                for (int u = 0; u < kRun; ++u)
+#pragma unroll
+                    for (int v = 0; v < kSub; ++v) {
+                        const f32x4 xsv = *reinterpret_cast<const f32x4*>(xsum + (kbl[u] * kSub + v) * 16 + 4 * h);
+                        acc += s[u][v] * (t[u][v] - (Mg::kBase + (float)z[u][v]) * xsv);
+                    }
             }
         } else {
 #pragma unroll
-            for (int u = 0; u < kRun; ++u) acc += s[u] * t[u];
+            for (int u = 0; u < kRun; ++u)
+#pragma unroll
+                for (int v = 0; v < kSub; ++v) acc += s[u][v] * t[u][v];
         }
     };
     const int runs = a.kb_per_wave / kRun;
     int kb0 = kb_begin;
     for (int r = 1; r < runs; ++r, kb0 += kRun) {
-        uint4 wqn[kRun], mdn;
+        uint4 wqn[kRun], mdn[kSub];
         load_run(kb0 + kRun, wqn, mdn);
         compute_run(kb0, wq, md);
 #pragma unroll
         for (int u = 0; u < kRun; ++u) wq[u] = wqn[u];
-        md = mdn;
+#pragma unroll
+        for (int v = 0; v < kSub; ++v) md[v] = mdn[v];
     }
     compute_run(kb0, wq, md);
 
@@ -295,39 +327,48 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(const GemvArgs a) 
     }
 }
 
-template <bool kBF16>
-void launch_typed(const GemvPlan& p, const GemvArgs& args, hipStream_t s) {
+template <bool kBF16, int kSub>
+void launch_sub(const GemvPlan& p, const GemvArgs& args, hipStream_t s) {
     const int cols_per_wg = p.waves / p.waves_k;
     const dim3 grid((unsigned)((padded_cols(args.N) / kColsPerBlock + cols_per_wg - 1) / cols_per_wg));
     const dim3 block((unsigned)(64 * p.waves));
     if (!p.staged)
-        hipLaunchKernelGGL((gemv_kernel<kBF16, false, 1>), grid, block, p.lds_bytes, s, args);
+        hipLaunchKernelGGL((gemv_kernel<kBF16, false, 1, kSub>), grid, block, p.lds_bytes, s, args);
     else if (p.chunks_per_thread <= 1)
-        hipLaunchKernelGGL((gemv_kernel<kBF16, true, 1>), grid, block, p.lds_bytes, s, args);
+        hipLaunchKernelGGL((gemv_kernel<kBF16, true, 1, kSub>), grid, block, p.lds_bytes, s, args);
     else if (p.chunks_per_thread <= 2)
-        hipLaunchKernelGGL((gemv_kernel<kBF16, true, 2>), grid, block, p.lds_bytes, s, args);
+        hipLaunchKernelGGL((gemv_kernel<kBF16, true, 2, kSub>), grid, block, p.lds_bytes, s, args);
     else if (p.chunks_per_thread <= 4)
-        hipLaunchKernelGGL((gemv_kernel<kBF16, true, 4>), grid, block, p.lds_bytes, s, args);
+        hipLaunchKernelGGL((gemv_kernel<kBF16, true, 4, kSub>), grid, block, p.lds_bytes, s, args);
     else
-        hipLaunchKernelGGL((gemv_kernel<kBF16, true, 8>), grid, block, p.lds_bytes, s, args);
+        hipLaunchKernelGGL((gemv_kernel<kBF16, true, 8, kSub>), grid, block, p.lds_bytes, s, args);
+}
+
+template <bool kBF16>
+void launch_typed(const GemvPlan& p, const GemvArgs& args, hipStream_t s) {
+    if (p.sub == 4) launch_sub<kBF16, 4>(p, args, s);
+    else if (p.sub == 2) launch_sub<kBF16, 2>(p, args, s);
+    else launch_sub<kBF16, 1>(p, args, s);
 }
 
 }  // namespace
 
-GemvPlan plan_gemv_with(int64_t M, int64_t K, int64_t N, int cols_per_wg) {
+GemvPlan plan_gemv_with(int64_t M, int64_t K, int64_t N, int64_t G, int cols_per_wg) {
     (void)N;
     GemvPlan p;
+    p.sub = units_per_block(G);
     const int64_t KB = K / kRowsPerBlock;
-    // runs of 4 row blocks per wave, at most 16 waves per column block
+    // runs of 4 row blocks per wave, at most 16 waves (8 for group size 32) per workgroup
+    const int wmax = max_waves(p.sub);
     int64_t kpw = kRun;
-    while ((KB + kpw - 1) / kpw > kMaxWaves) kpw += kRun;
+    while ((KB + kpw - 1) / kpw > wmax) kpw += kRun;
     p.kb_per_wave = (int)kpw;
     p.waves_k = (int)((KB + kpw - 1) / kpw);
-    if (cols_per_wg < 1 || cols_per_wg * p.waves_k > kMaxWaves) cols_per_wg = 1;
+    if (cols_per_wg < 1 || cols_per_wg * p.waves_k > wmax) cols_per_wg = 1;
     p.waves = p.waves_k * cols_per_wg;
     const int64_t threads = 64 * p.waves;
     const size_t partial_bytes = p.waves_k > 1 ? (size_t)p.waves * 64 * 16 : 0;
-    const size_t staged_bytes = (size_t)staged_x_bytes(M * K / 8) + (size_t)KB * 16 * 4 + partial_bytes;
+    const size_t staged_bytes = (size_t)staged_x_bytes(M * K / 8) + (size_t)KB * p.sub * 16 * 4 + partial_bytes;
     p.chunks_per_thread = (int)((M * K / 8 + threads - 1) / threads);
     p.staged = staged_bytes <= kStagedLdsLimit && p.chunks_per_thread <= kMaxStagedChunksPerThread;
     p.lds_bytes = p.staged ? staged_bytes : partial_bytes;
@@ -338,16 +379,16 @@ GemvPlan plan_gemv_with(int64_t M, int64_t K, int64_t N, int cols_per_wg) {
 // 400): fewer, larger workgroups per compute unit share one copy of the activations.
 // Measured on the 2048 x 13312 decode shape: M = 8 -9%, M = 4 -4%, M = 1 even; four
 // blocks per workgroup, or two for N = 131072 or N = 3072, measured slower.
-GemvPlan plan_gemv(int64_t M, int64_t K, int64_t N) {
+GemvPlan plan_gemv(int64_t M, int64_t K, int64_t N, int64_t G) {
     const int64_t NB = padded_cols(N) / kColsPerBlock;
-    const GemvPlan one = plan_gemv_with(M, K, N, 1);
-    if (NB <= 1024 && NB / 2 >= 200 && 2 * one.waves_k <= kMaxWaves) return plan_gemv_with(M, K, N, 2);
+    const GemvPlan one = plan_gemv_with(M, K, N, G, 1);
+    if (NB <= 1024 && NB / 2 >= 200 && 2 * one.waves_k <= max_waves(one.sub)) return plan_gemv_with(M, K, N, G, 2);
     return one;
 }
 
 hipError_t launch_gemv(const uint16_t* x, const uint8_t* packed, const uint16_t* bias, uint16_t* y,
-                       int64_t M, int64_t K, int64_t N, bool bf16, hipStream_t stream) {
-    const GemvPlan p = plan_gemv(M, K, N);
+                       int64_t M, int64_t K, int64_t N, int64_t G, bool bf16, hipStream_t stream) {
+    const GemvPlan p = plan_gemv(M, K, N, G);
     GemvArgs args;
     args.x = x;
     args.packed = packed;

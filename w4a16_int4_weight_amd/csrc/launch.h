@@ -26,17 +26,18 @@ struct GemvPlan {
     int waves_k;           // waves splitting K for one 16-column block
     bool staged;           // activations staged in LDS
     int chunks_per_thread; // 16-byte activation chunks each thread stages
+    int sub;               // metadata units per 128-row block (128 / G for G = 32, 64; else 1)
     size_t lds_bytes;
 };
-GemvPlan plan_gemv(int64_t M, int64_t K, int64_t N);
+GemvPlan plan_gemv(int64_t M, int64_t K, int64_t N, int64_t G);
 
 hipError_t launch_gemv(const uint16_t* x, const uint8_t* packed, const uint16_t* bias, uint16_t* y,
-                       int64_t M, int64_t K, int64_t N, bool bf16, hipStream_t stream);
+                       int64_t M, int64_t K, int64_t N, int64_t G, bool bf16, hipStream_t stream);
 
 // Tied-embedding gather: out[t, :] = dequantised column ids[t] of the packed [K, N]
 // weight (zeros for ids outside [0, N)).
 hipError_t launch_embedding(const int32_t* ids, int64_t T, const uint8_t* packed, uint16_t* out, int64_t K,
-                            int64_t N, bool bf16, hipStream_t stream);
+                            int64_t N, int64_t G, bool bf16, hipStream_t stream);
 
 // LDS-staged dequantise -> MFMA GEMM for any M >= 1: tile shape and K split chosen
 // from the shape; workspace_bytes > 0 when K is split over workgroups.
@@ -46,13 +47,15 @@ struct GemmPlan {
     int waves;         // waves per workgroup, side by side along N (4 or 8)
     int tiles_m, tiles_n;
     int splits;        // workgroups per tile along K
+    int sub;           // metadata units per 128-row block (128 / G for G = 32, 64; else 1)
     size_t workspace_bytes;   // [tile counters, 256-byte aligned][splits x M x N fp32 partials]
 };
-GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N);
+GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G);
 
-// `workspace` must hold plan_gemm(M, K, N).workspace_bytes bytes whose counter part is
+// `workspace` must hold plan_gemm(M, K, N, G).workspace_bytes bytes whose counter part is
 // zero; the kernel leaves it zero.
 hipError_t launch_gemm(const uint16_t* x, const uint8_t* packed, const uint16_t* bias, uint16_t* y,
-                       int64_t M, int64_t K, int64_t N, bool bf16, void* workspace, hipStream_t stream);
+                       int64_t M, int64_t K, int64_t N, int64_t G, bool bf16, void* workspace,
+                       hipStream_t stream);
 
 }  // namespace w4a16

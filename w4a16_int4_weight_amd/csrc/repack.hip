@@ -106,25 +106,27 @@ __global__ __launch_bounds__(kRepackThreads) void repack_kernel(
     }
 
     // 4. metadata: the workgroups of row block 0 write, for each column of their tile's
-    //    blocks, its whole row of KBP words (scale bits | zero << 16 per row block, then
-    //    zero padding; all zero for the padding columns of a last half block), 16 bytes
-    //    at a time
+    //    blocks, its whole row of UW words (scale bits | zero << 16 per metadata unit of
+    //    min(G, 128) rows, then zero padding; all zero for the padding columns of a last
+    //    half block), 16 bytes at a time
     if (kb != 0) return;
-    const int64_t KBP = padded_row_blocks(K);
+    const int64_t UW = padded_units(K, G);
+    const int64_t U = KB * units_per_block(G);
+    const int64_t Gu = kRowsPerBlock / units_per_block(G);      // rows per unit
     uint32_t* meta = reinterpret_cast<uint32_t*>(packed + K * padded_cols(Nt) / 2);
     for (int q = tid; q < nblk * kColsPerBlock; q += kRepackThreads) {
         const int64_t n = j0 * 8 + q;                 // column of the input tensors
         const bool real = n < N;
         const int zshift = 4 * awq_slot_of_column((int)(n & 7));
-        uint4* row = reinterpret_cast<uint4*>(meta + (n0 + n) * KBP);
-        for (int64_t p0 = 0; p0 < KBP; p0 += 4) {
+        uint4* row = reinterpret_cast<uint4*>(meta + (n0 + n) * UW);
+        for (int64_t p0 = 0; p0 < UW; p0 += 4) {
             uint32_t word[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int64_t b = p0 + e;
                 word[e] = 0u;
-                if (real && b < KB) {
-                    const int64_t g = (b * kRowsPerBlock) / G;
+                if (real && b < U) {
+                    const int64_t g = (b * Gu) / G;
                     const uint32_t z = (qzeros[g * words_per_row + (n >> 3)] >> zshift) & 0xFu;
                     word[e] = (uint32_t)scales[g * N + n] | (z << 16);
                 }
@@ -181,17 +183,20 @@ __global__ __launch_bounds__(kGptqColumns) void repack_gptq_kernel(
         blk[c + 16 * h] = make_uint4(t[0], t[1], t[2], t[3]);
     }
     if (kb != 0) return;
-    // metadata row of column n: scale bits | zero << 16 per row block, zero padding
-    const int64_t KBP = padded_row_blocks(K);
-    uint4* row = reinterpret_cast<uint4*>(packed + K * padded_cols(Nt) / 2 + (n0 + n) * KBP * 4);
-    for (int64_t p0 = 0; p0 < KBP; p0 += 4) {
+    // metadata row of column n: scale bits | zero << 16 per unit of min(G, 128) rows,
+    // zero padding
+    const int64_t UW = padded_units(K, G);
+    const int64_t U = KB * units_per_block(G);
+    const int64_t Gu = kRowsPerBlock / units_per_block(G);
+    uint4* row = reinterpret_cast<uint4*>(packed + K * padded_cols(Nt) / 2 + (n0 + n) * UW * 4);
+    for (int64_t p0 = 0; p0 < UW; p0 += 4) {
         uint32_t word[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int64_t b = p0 + e;
             word[e] = 0u;
-            if (real && b < KB) {
-                const int64_t g = (b * kRowsPerBlock) / G;
+            if (real && b < U) {
+                const int64_t g = (b * Gu) / G;
                 const uint32_t z = (qzeros[g * (N / 8) + n / 8] >> (4 * (n % 8))) & 0xFu;
                 word[e] = (uint32_t)scales[g * N + n] | (z << 16);
             }
