@@ -4,7 +4,8 @@
  * AWQ-packed weights into this library's GPU tile layout.
  *
  *   y[m, n] = sum_k x[m, k] * W[k, n],   W[k, n] = (q[k, n] - z[g, n]) * s[g, n],
- *   g = k div G  (G = group size, 128 in the common case; -1 means G = K).
+ *   g = k div G  (G = group size: 128 in the common case, also 32, 64 or any
+ *   multiple of 128 dividing K; -1 means G = K).
  *
  * Lifecycle, after the three phases of a quantised linear layer in the vLLM
  * note "Carga de capas cuantizadas: AWQ / GPTQ / Marlin / fp8" (section
@@ -46,7 +47,7 @@ typedef enum {
     W4A16_ERR_NULL = 1,         /* a required pointer is NULL                       */
     W4A16_ERR_SHAPE = 2,        /* M < 0, K or N <= 0, K % 128 != 0, N % 8 != 0,
                                    K > 2^20, N > 2^28, K*N > 2^37 or M*K > 2^32       */
-    W4A16_ERR_GROUP = 3,        /* group size not -1 and not a multiple of 128 dividing K */
+    W4A16_ERR_GROUP = 3,        /* group size not -1, 32, 64 or a multiple of 128 dividing K */
     W4A16_ERR_DTYPE = 4,        /* dtype is neither W4A16_FP16 nor W4A16_BF16        */
     W4A16_ERR_ALIGN = 5,        /* a pointer is not aligned as documented            */
     W4A16_ERR_BUFFER_SIZE = 6,  /* a caller buffer is smaller than required          */
@@ -72,9 +73,9 @@ typedef enum {
 int w4a16_layout_version(void);
 
 /* Bytes of the packed buffer for a K x N weight with group size `group_size`:
- * K*Np/2 (4-bit codes) + 4*KBP*Np (one 32-bit scale/zero word per column per
- * 128-row block), Np = N rounded up to a multiple of 16 and KBP = K/128 rounded up
- * to a multiple of 4. N must be a multiple of 8 (the AWQ and GPTQ pack factor); with
+ * K*Np/2 (4-bit codes) + 4*UW*Np (one 32-bit scale/zero word per column per unit
+ * of min(G, 128) rows), Np = N rounded up to a multiple of 16 and UW = K/min(G, 128)
+ * rounded up to a multiple of 4. N must be a multiple of 8 (the AWQ and GPTQ pack factor); with
  * N % 16 == 8 the last 16-column block carries 8 zero columns that no entry point
  * reads into a result.
  * Returns 0 if the shape or group size is not supported. */
