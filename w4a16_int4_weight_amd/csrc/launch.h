@@ -9,7 +9,7 @@ namespace w4a16 {
 
 // AWQ tensors of columns [n0, n0 + N) of a K x Nt weight -> those columns of the
 // packed tile layout of the K x Nt weight (n0 % 16 == 0; N % 16 == 0 unless
-// n0 + N == Nt). G: resolved group size (multiple of 128, divides K).
+// n0 + N == Nt). G: resolved group size (32, 64, or a multiple of 128 dividing K).
 hipError_t launch_repack(const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
                          uint8_t* packed, int64_t K, int64_t N, int64_t G, int64_t n0, int64_t Nt,
                          hipStream_t stream);
