@@ -30,6 +30,8 @@ Modules:
   tile_layout  repack / decode: the GPU tile layout, written from its spec
   gemm         dequant / gemm / tolerance check
   embedding    tied-embedding gather: dequantised columns of the head weight
+  w4a8         fp8 (E4M3) activations: the format, per-row quantisation, the
+               activation operand order, the W4A8 product
 """
 
-from . import numerics, awq, gptq, tile_layout, gemm, embedding  # noqa: F401
+from . import numerics, awq, gptq, tile_layout, gemm, embedding, w4a8  # noqa: F401

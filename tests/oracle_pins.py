@@ -471,3 +471,230 @@ def pin_gptq_row_moves_one_nibble(gptq):
 def run_gptq_pins(gptq):
     return {"golden": pin_gptq_golden(gptq), "roundtrips": pin_gptq_roundtrips(gptq),
             "one nibble": pin_gptq_row_moves_one_nibble(gptq)}
+
+
+# ---------------------------------------------------------------- W4A8 (fp8 activations)
+# Facts fixed by the E4M3 format (OCP 8-bit floating point, "fn" variant): bias 7,
+# 3 mantissa bits, subnormals m * 2^-9, largest finite 448, S.1111.111 NaN.
+E4M3_SPEC = [
+    (0.0, 0x00), (2.0 ** -9, 0x01), (7 * 2.0 ** -9, 0x07), (2.0 ** -6, 0x08), (0.5, 0x30),
+    (1.0, 0x38), (1.125, 0x39), (2.0, 0x40), (-2.0, 0xC0), (240.0, 0x77), (256.0, 0x78),
+    (448.0, 0x7E), (-448.0, 0xFE),
+]
+# ties go to the even mantissa; values past 448 below the midpoint 464 round to 448
+E4M3_TIES = [
+    (1.0625, 0x38), (1.1875, 0x3A), (0.5 * 2.0 ** -9, 0x00), (1.5 * 2.0 ** -9, 0x02),
+    (2.5 * 2.0 ** -9, 0x02), (7.5 * 2.0 ** -9, 0x08), (456.0, 0x7E), (-1.0625, 0xB8),
+]
+
+
+def pin_e4m3_spec(w):
+    for v, c in E4M3_SPEC:
+        if int(w.e4m3_encode_rne(np.array([v]))[0]) != c or float(w.e4m3_decode(np.array([c]))[0]) != v:
+            return False
+    for v, c in E4M3_TIES:
+        if int(w.e4m3_encode_rne(np.array([v]))[0]) != c:
+            return False
+    if int(w.e4m3_encode_rne(np.array([-0.0]))[0]) != 0x80:
+        return False
+    d = w.e4m3_decode(np.arange(256, dtype=np.uint8))
+    if not (np.isnan(d[0x7F]) and np.isnan(d[0xFF]) and np.sum(np.isnan(d)) == 2):
+        return False
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    return bool(np.array_equal(w.e4m3_encode_rne(w.e4m3_decode(finite)), finite))
+
+
+def _all_bf16_within(limit):
+    with np.errstate(invalid="ignore"):       # NaN patterns among the 65536
+        v = (np.arange(65536, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
+    return v[np.isfinite(v) & (np.abs(v) <= limit)]
+
+
+def pin_e4m3_against_torch(w):
+    """Decode of all 256 codes and encode of every bf16 value in [-448, 448] agree
+    with torch's float8_e4m3fn conversions (an independent implementation)."""
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = w.e4m3_decode(codes)
+    if not np.array_equal(np.isnan(ref), np.isnan(got)) or not np.array_equal(ref[~np.isnan(ref)], got[~np.isnan(got)]):
+        return False
+    v = _all_bf16_within(448.0)
+    ref = torch.from_numpy(v.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return bool(np.array_equal(w.e4m3_encode_rne(v), ref))
+
+
+def _nearest_even_bruteforce(v):
+    """Nearest finite E4M3 code by exhaustive search, ties to the even code."""
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.int64)
+    vals = np.empty(codes.shape)
+    for t, c in enumerate(codes):            # decode written out again, field by field
+        s = -1.0 if c & 0x80 else 1.0
+        e, m = (c >> 3) & 15, c & 7
+        vals[t] = s * (m / 512.0 if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 7))
+    out = np.empty(v.shape, dtype=np.int64)
+    for a in range(0, v.size, 4096):
+        x = v[a:a + 4096, None]
+        # codes of the value's own sign (so -0.0 and small negatives go to 0x80)
+        same_sign = (codes[None, :] >= 128) == np.signbit(x)
+        dist = np.where(same_sign, np.abs(vals[None, :] - x), np.inf)
+        cand = dist == dist.min(axis=1, keepdims=True)
+        # of equally near codes, the even one (mantissa bit 0 clear)
+        pick = np.where(cand & (codes[None, :] % 2 == 0), codes[None, :], 1 << 20).min(axis=1)
+        pick = np.where(pick == 1 << 20, np.where(cand, codes[None, :], 1 << 20).min(axis=1), pick)
+        out[a:a + 4096] = pick
+    return out
+
+
+def pin_e4m3_bruteforce(w):
+    v = _all_bf16_within(460.0)
+    v = np.concatenate([v, np.array([E4M3_TIES[i][0] for i in range(len(E4M3_TIES))])])
+    return bool(np.array_equal(w.e4m3_encode_rne(v).astype(np.int64), _nearest_even_bruteforce(v)))
+
+
+def pin_nibble_reading(w):
+    """A code q in the low nibble of an E4M3 byte reads q * 2^-9: the factor 512."""
+    return bool(np.array_equal(w.e4m3_decode(np.arange(16, dtype=np.uint8)), np.arange(16) / 512.0))
+
+
+def pin_quantize_rows(w, seed=3):
+    rng = np.random.default_rng(seed)
+    M, K = 6, 256
+    X = rng.standard_normal((M, K)).astype(np.float32)
+    X[1] = 0.0                                    # a row of zeros
+    X[2] = 0.0
+    X[2, 17] = -3.5                               # one non-zero
+    X[3] *= 1e-3                                  # small values (subnormal codes)
+    bits = (X.view(np.uint32) >> 16).astype(np.uint16)      # truncate to bf16 bit patterns
+    codes, scale = w.quantize_rows(bits, "bf16")
+    Xb = (bits.astype(np.uint32) << 16).view(np.float32)
+    amax = np.abs(Xb).max(axis=1)
+    want_scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    if not np.array_equal(scale, want_scale):
+        return False
+    if np.any(codes[1] != 0) or scale[1] != 1.0:
+        return False
+    # the largest magnitude of each non-zero row lands on +-448
+    for m in (0, 2, 3, 4, 5):
+        k = int(np.argmax(np.abs(Xb[m])))
+        if codes[m, k] & 0x7F != 0x7E:
+            return False
+    # every code is the nearest-even E4M3 value of the float32 quotient
+    q = (Xb / scale[:, None]).astype(np.float32).astype(np.float64)
+    if not np.array_equal(codes.reshape(-1).astype(np.int64), _nearest_even_bruteforce(q.reshape(-1))):
+        return False
+    # on-grid rows come back unchanged: x = dec(c) / 8 with a +-448 / 8 entry
+    c = rng.integers(0, 0x7F, size=(2, 128)).astype(np.uint8) | (rng.integers(0, 2, size=(2, 128)) << 7).astype(np.uint8)
+    c[c == 0xFF] = 0xFE
+    c[:, 5] = 0x7E
+    vals = (w.e4m3_decode(c) / 8.0).astype(np.float32)
+    g_bits = (vals.view(np.uint32) >> 16).astype(np.uint16)
+    gc, gs = w.quantize_rows(g_bits, "bf16")
+    return bool(np.array_equal(gc, c) and np.all(gs == np.float32(1.0 / 8.0)))
+
+
+def pin_operand_order(w, tile_layout, seed=4):
+    """The operand order pairs each activation byte with the weight code of the
+    same row: for every lane (c, h) of a weight block, byte 8 i + j of the lane's
+    expanded codes (word i, byte j of (word & 0x0F0F0F0F) for j < 4, of
+    ((word >> 4) & 0x0F0F0F0F) for j >= 4) meets activation byte 32 h + 8 i + j,
+    and the products summed over the block's lanes give sum_k a[k] * Q[k, c]."""
+    rng = np.random.default_rng(seed)
+    K, N = 256, 16
+    a = rng.integers(0, 256, size=(3, K)).astype(np.uint8)
+    if not np.array_equal(w.element_order(w.operand_order(a)), a):
+        return False
+    Q = rng.integers(0, 16, size=(K, N)).astype(np.uint8)
+    packed = tile_layout.repack(Q, np.zeros((K // 128, N), np.uint8), np.zeros((K // 128, N), np.uint16), 128)
+    words = packed[:K * N // 2].view(np.uint32).reshape(K // 128, 64, 4)    # one column block: [kb, lane, i]
+    ops = w.operand_order(a).astype(np.int64)
+    want = a.astype(np.int64) @ Q.astype(np.int64)
+    got = np.zeros_like(want)
+    for kb in range(K // 128):
+        for lane in range(64):
+            c, h = lane % 16, lane // 16
+            for i in range(4):
+                wd = int(words[kb, lane, i])
+                for j in range(8):
+                    code = (wd >> (8 * j)) & 0xF if j < 4 else (wd >> (8 * (j - 4) + 4)) & 0xF
+                    got[:, c] += ops[:, kb * 128 + 32 * h + 8 * i + j] * code
+    return bool(np.array_equal(got, want))
+
+
+def _bf16_bits_rne(v):
+    """float array -> bf16 bit patterns, nearest even (finite values)."""
+    b = np.asarray(v, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def pin_w4a8_bruteforce(w, awq, seed=8):
+    """Tiny layer in exact rationals: y = a[m] * sum_k dec(e) (q - z) s (+ bias)."""
+    rng = np.random.default_rng(seed)
+    M, K, N, G = 2, 256, 8, 128
+    Q = rng.integers(0, 16, size=(K, N)).astype(np.uint8)
+    Z = rng.integers(0, 16, size=(K // G, N)).astype(np.uint8)
+    S = _bf16_bits_rne(rng.uniform(0.005, 0.02, size=(K // G, N)))
+    e = rng.integers(0, 0x7F, size=(M, K)).astype(np.uint8) | (rng.integers(0, 2, size=(M, K)) << 7).astype(np.uint8)
+    scale = np.array([0.0078125, 0.013], dtype=np.float32)
+    bias = _bf16_bits_rne(np.array([0.25, -1.5, 0, 0, 3.0, 0, 0, 0.125]))
+    y = w.w4a8_reference(e, scale, Q, Z, S, "bf16", G, bias)
+
+    def frac_e4m3(c):
+        c = int(c)
+        s = -1 if c & 0x80 else 1
+        ex, m = (c >> 3) & 15, c & 7
+        return s * (Fraction(m, 512) if ex == 0 else Fraction(8 + m, 8) * Fraction(2) ** (ex - 7))
+
+    def frac_bf16(b):
+        return Fraction(float((np.array([b], np.uint32) << 16).view(np.float32)[0]))
+
+    for m in range(M):
+        for n in range(N):
+            acc = Fraction(0)
+            for k in range(K):
+                acc += frac_e4m3(e[m, k]) * (int(Q[k, n]) - int(Z[k // G, n])) * frac_bf16(S[k // G, n])
+            ref = Fraction(float(scale[m])) * acc + frac_bf16(bias[n])
+            if abs(float(ref) - y[m, n]) > 1e-12 * max(1.0, abs(float(ref))):
+                return False
+    return True
+
+
+def pin_w4a8_on_grid_equals_w4a16(w, gemm_mod, awq, seed=9):
+    """Activations already on the E4M3 grid of their row scale quantise without
+    error, so the W4A8 layer equals the (separately pinned) W4A16 layer."""
+    rng = np.random.default_rng(seed)
+    M, K, N, G = 3, 512, 16, 128
+    c = rng.integers(0, 0x7F, size=(M, K)).astype(np.uint8) | (rng.integers(0, 2, size=(M, K)) << 7).astype(np.uint8)
+    c[:, 0] = 0x7E
+    x = (w.e4m3_decode(c) * 2.0 ** -5).astype(np.float32)
+    x_bits = (x.view(np.uint32) >> 16).astype(np.uint16)
+    Q = rng.integers(0, 16, size=(K, N)).astype(np.uint8)
+    Z = rng.integers(0, 16, size=(K // G, N)).astype(np.uint8)
+    S = _bf16_bits_rne(rng.uniform(0.005, 0.02, size=(K // G, N)))
+    qw, qz = awq.pack_awq(Q), awq.pack_awq(Z)
+    y8 = w.w4a8_layer(x_bits, qw, qz, S, "bf16", G)
+    y16 = gemm_mod.w4a16_reference(x_bits, qw, qz, S, "bf16", G)
+    return bool(np.max(np.abs(y8 - y16)) <= 1e-12 * np.max(np.abs(y16)))
+
+
+def pin_w4a8_block_sums(w, seed=10):
+    rng = np.random.default_rng(seed)
+    e = rng.integers(0, 0x7F, size=(2, 384)).astype(np.uint8)
+    s = w.block_sums(e)
+    want = np.array([[sum(float(w.e4m3_decode(np.array([e[m, k]]))[0]) for k in range(128 * b, 128 * b + 128))
+                      for b in range(3)] for m in range(2)])
+    return s.shape == (2, 3) and bool(np.array_equal(s, want))
+
+
+def run_w4a8_pins(w, gemm_mod, awq, tile_layout):
+    return {
+        "spec": pin_e4m3_spec(w),
+        "torch": pin_e4m3_against_torch(w),
+        "bruteforce": pin_e4m3_bruteforce(w),
+        "nibble": pin_nibble_reading(w),
+        "quantize": pin_quantize_rows(w),
+        "operand_order": pin_operand_order(w, tile_layout),
+        "gemm_bruteforce": pin_w4a8_bruteforce(w, awq),
+        "on_grid": pin_w4a8_on_grid_equals_w4a16(w, gemm_mod, awq),
+        "block_sums": pin_w4a8_block_sums(w),
+    }
