@@ -229,6 +229,59 @@ w4a16_status w4a16_embedding(const int32_t* ids, int64_t T, const void* packed, 
                              w4a16_dtype dtype, int64_t K, int64_t N, int64_t group_size, void* out,
                              void* stream);
 
+/* ---------------------------------------------------------------- W4A8
+ * The same packed int4 weights against fp8 (E4M3) activations. The vLLM note
+ * "Carga de capas cuantizadas: AWQ / GPTQ / Marlin / fp8" (section "Límites y
+ * fallos") describes the int4 Marlin kernel taking float8_e4m3fn activations, with
+ * the scales multiplied by 512: a 4-bit code in the low nibble of an E4M3 byte reads
+ * as code * 2^-9, and 512 restores the scale. Here the factor is applied as each
+ * scale is read, so the buffer w4a16_repack wrote serves W4A16 and W4A8 alike.
+ *
+ * Two calls: w4a8_quantize turns 16-bit activations into the W4A8 activation
+ * buffer, w4a8_gemm multiplies it by the packed weight. The product is
+ *   y[m, n] = a[m] * sum_k e[m, k] * (q[k, n] - z[g, n]) * s[g, n]  (+ bias[n]),
+ * a[m] the row scale and e the E4M3 code values, accumulated in fp32 and rounded
+ * once to the output dtype (nearest even). */
+
+/* Bytes of the W4A8 activation buffer for M rows of K (K % 128 == 0); 0 for an
+ * invalid shape or M = 0. Layout, each part starting on a 256-byte boundary:
+ *   codes      M*K bytes, E4M3 (OCP, no infinities, largest finite 448), row-major;
+ *              within each 128-element block of a row, byte 32 h + 8 i + j holds
+ *              element 32 i + 8 h + (0, 4, 1, 5, 2, 6, 3, 7)[j] (h, i = 0..3, j = 0..7):
+ *              the order in which the fp8 matrix-core operands pair each activation
+ *              with its weight code in the packed tiles;
+ *   row scales M fp32, a[m];
+ *   block sums M * K/128 fp32, row-major: the sum of the decoded codes of each
+ *              128-element block (used for the zero points). */
+size_t w4a8_activation_bytes(int64_t M, int64_t K);
+
+/* Per-row dynamic quantisation: a[m] = max_k |x[m, k]| / 448 (fp32; 1 for a row of
+ * zeros), codes e = RNE_E4M3(x[m, k] / a[m]) with the quotient in fp32 (correctly
+ * rounded division), written with the row scales and block sums into `act`.
+ *   x    [M, K] row-major, `dtype`, finite values. 16-byte aligned.
+ *   act  at least w4a8_activation_bytes(M, K) bytes, 16-byte aligned, written in full
+ *        (its padding excepted). Must not overlap x.
+ * Bit-for-bit deterministic. M = 0 is a valid no-op. */
+w4a16_status w4a8_quantize(const void* x, w4a16_dtype dtype, int64_t M, int64_t K, void* act, size_t act_bytes,
+                           void* stream);
+
+/* Workspace bytes w4a8_gemm needs for this shape (0 when it splits no K range, or for
+ * an invalid shape), under the contract of w4a16_workspace_bytes: zero-filled before
+ * first use, left zero by every call, not shared by calls that may overlap. */
+size_t w4a8_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t group_size);
+
+/* y = (W4A8 product above), from an activation buffer written by w4a8_quantize for
+ * these M, K and a weight buffer written by w4a16_repack (any front end).
+ *   act      `act_bytes` >= w4a8_activation_bytes(M, K). 16-byte aligned.
+ *   packed   as for w4a16_gemm; group_size -1 or a multiple of 128 (one fp8 MFMA
+ *            covers a 128-row block; 32 and 64 give W4A16_ERR_GROUP).
+ *   dtype    the dtype of the scales the buffer holds, of bias and of y.
+ *   y, bias, workspace: as for w4a16_gemm.
+ * Bit-for-bit reproducible for fixed inputs and shape. M = 0 is a valid no-op. */
+w4a16_status w4a8_gemm(const void* act, size_t act_bytes, const void* packed, size_t packed_bytes,
+                       w4a16_dtype dtype, void* y, int64_t M, int64_t K, int64_t N, int64_t group_size,
+                       const void* bias, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, NUL-terminated description of a status code ("unknown status" otherwise). */
 const char* w4a16_status_str(w4a16_status status);
 

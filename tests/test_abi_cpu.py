@@ -14,7 +14,7 @@ HEADER = os.path.join(ROOT, "include", "w4a16.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(w4a16_[a-z_0-9]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(w4a(?:16|8)_[a-z_0-9]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -27,7 +27,8 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "w4a16_embedding", "w4a16_gemm", "w4a16_gemm_ex", "w4a16_layout_version", "w4a16_packed_bytes",
         "w4a16_packed_header", "w4a16_parse_packed_header", "w4a16_repack", "w4a16_repack_columns",
-        "w4a16_repack_gptq", "w4a16_repack_gptq_columns", "w4a16_status_str", "w4a16_workspace_bytes"])
+        "w4a16_repack_gptq", "w4a16_repack_gptq_columns", "w4a16_status_str", "w4a16_workspace_bytes",
+        "w4a8_activation_bytes", "w4a8_gemm", "w4a8_quantize", "w4a8_workspace_bytes"])
 
 
 def test_library_exports_every_declared_symbol(w):
@@ -272,3 +273,57 @@ def test_save_and_load_packed_file_on_host(w, tmp_path):
     path.write_bytes(raw[:-1])                      # truncated payload
     with pytest.raises(w.W4A16Error):
         w.load_packed(str(path), device="cpu")
+
+
+def test_w4a8_sizes(w):
+    # codes, row scales and block sums, each from a 256-byte boundary
+    for M, K in [(1, 2048), (512, 2048), (3, 384), (8, 6656)]:
+        want = (M * K + 255) // 256 * 256 + (4 * M + 255) // 256 * 256 + 4 * M * (K // 128)
+        assert w.w4a8_activation_bytes(M, K) == want
+    for M, K in [(0, 2048), (-1, 2048), (4, 100), (4, 0)]:
+        assert w.w4a8_activation_bytes(M, K) == 0
+    # the same tiles and K split as the 16-bit MFMA GEMM; 32- and 64-row groups are not taken
+    for M, K, N in [(16, 6656, 2048), (512, 2048, 131072), (1, 2048, 3072)]:
+        assert w.w4a8_workspace_bytes(M, K, N, 128) == w.w4a16_workspace_bytes(M, K, N, 128)
+    assert w.w4a8_workspace_bytes(16, 6656, 2048, 64) == 0
+
+
+def test_w4a8_quantize_validation_before_any_device_call(w):
+    def q(x=P(256), dtype=1, M=4, K=512, act=P(4096), abytes=1 << 30):
+        return w.lib.w4a8_quantize(x, dtype, M, K, act, abytes, None)
+    assert q(M=-1) == 2
+    assert q(K=100) == 2
+    assert q(K=(1 << 20) + 128) == 2
+    assert q(dtype=2) == 4
+    assert q(x=None) == 1
+    assert q(act=None) == 1
+    assert q(x=P(258)) == 5
+    assert q(act=P(4100)) == 5
+    assert q(abytes=4 * 512) == 6
+    assert q(M=0, x=None, act=None) == 0
+    assert q() == 7
+
+
+def test_w4a8_gemm_validation_before_any_device_call(w):
+    def g(act=P(256), abytes=1 << 30, packed=P(512), pbytes=1 << 40, dtype=1, y=P(1024), M=4, K=512, N=512,
+          G=128, bias=None, ws=None, wsb=0):
+        return w.lib.w4a8_gemm(act, abytes, packed, pbytes, dtype, y, M, K, N, G, bias, ws, wsb, None)
+    assert g(M=-1) == 2
+    assert g(K=500) == 2
+    assert g(N=20) == 2
+    assert g(G=96) == 3
+    assert g(G=64) == 3
+    assert g(G=32) == 3
+    assert g(dtype=2) == 4
+    assert g(act=None) == 1
+    assert g(packed=None) == 1
+    assert g(y=None) == 1
+    assert g(act=P(264)) == 5
+    assert g(bias=P(1025)) == 5
+    assert g(abytes=512 * 4) == 6
+    assert g(pbytes=512 * 512 // 2) == 6
+    assert g(M=16, K=6656, N=2048) == 1                                 # K split: workspace needed
+    assert g(M=16, K=6656, N=2048, ws=P(4096), wsb=64) == 6
+    assert g(M=0, act=None, packed=None, y=None) == 0
+    assert g(G=-1) == 7
+    assert g() == 7

@@ -102,6 +102,14 @@ def _load():
     h.w4a16_gemm_ex.restype = _int
     h.w4a16_embedding.argtypes = [_vp, _i64, _vp, _sz, _int, _i64, _i64, _i64, _vp, _vp]
     h.w4a16_embedding.restype = _int
+    h.w4a8_activation_bytes.argtypes = [_i64, _i64]
+    h.w4a8_activation_bytes.restype = _sz
+    h.w4a8_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64]
+    h.w4a8_workspace_bytes.restype = _sz
+    h.w4a8_quantize.argtypes = [_vp, _int, _i64, _i64, _vp, _sz, _vp]
+    h.w4a8_quantize.restype = _int
+    h.w4a8_gemm.argtypes = [_vp, _sz, _vp, _sz, _int, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _sz, _vp]
+    h.w4a8_gemm.restype = _int
     h.w4a16_status_str.argtypes = [_int]
     h.w4a16_status_str.restype = ctypes.c_char_p
     _lib = h
@@ -372,3 +380,68 @@ def w4a16_embedding(ids, packed, K, N, group_size=128, dtype=torch.bfloat16, out
                                    _dtype_code(dtype), K, N, group_size, _ptr(out), _stream(stream, ids.device))
     _check(code, "w4a16_embedding")
     return out
+
+
+# ---------------------------------------------------------------- W4A8
+
+def w4a8_activation_bytes(M, K):
+    return int(_load().w4a8_activation_bytes(M, K))
+
+
+def w4a8_workspace_bytes(M, K, N, group_size):
+    return int(_load().w4a8_workspace_bytes(M, K, N, group_size))
+
+
+def w4a8_act_parts(act, M, K):
+    """Views of a W4A8 activation buffer: (codes uint8 [M, K] in operand order,
+    row scales float32 [M], block sums float32 [M, K / 128])."""
+    off_s = (M * K + 255) // 256 * 256
+    off_b = off_s + (M * 4 + 255) // 256 * 256
+    codes = act[:M * K].view(M, K)
+    scale = act[off_s:off_s + 4 * M].view(torch.float32)
+    sums = act[off_b:off_b + 4 * M * (K // 128)].view(torch.float32).view(M, K // 128)
+    return codes, scale, sums
+
+
+def w4a8_quantize(x, act=None, stream=None):
+    """x [M, K] (fp16/bf16) -> W4A8 activation buffer (uint8 tensor of
+    w4a8_activation_bytes(M, K) bytes; see w4a8_act_parts for its parts)."""
+    if x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [M, K] tensor")
+    M, K = x.shape
+    need = w4a8_activation_bytes(M, K) if M > 0 else 0
+    if act is None:
+        act = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    code = _load().w4a8_quantize(_ptr(x), _dtype_code(x.dtype), M, K, _ptr(act), act.numel() * act.element_size(),
+                                 _stream(stream, x.device))
+    _check(code, "w4a8_quantize")
+    return act
+
+
+def w4a8_gemm(act, packed, M, K, N, group_size=128, dtype=torch.bfloat16, bias=None, y=None, workspace=None,
+              stream=None):
+    """W4A8 activation buffer (from w4a8_quantize) times the packed weight (+ bias)
+    -> y [M, N] of `dtype` (the dtype of the weight's scales)."""
+    if workspace is None and M > 0:
+        need = w4a8_workspace_bytes(M, K, N, group_size)
+        if need > 0:
+            workspace = _default_workspace(act.device, need)
+    if y is None:
+        y = torch.empty((M, N), dtype=dtype, device=act.device)
+    if tuple(y.shape) != (M, N) or y.dtype != dtype or not y.is_contiguous():
+        raise ValueError("y must be a contiguous [M, N] tensor of `dtype`")
+    if bias is not None and (bias.dtype != dtype or tuple(bias.shape) != (N,) or not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous [N] tensor of `dtype`")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    code = _load().w4a8_gemm(_ptr(act), act.numel() * act.element_size(), _ptr(packed),
+                             packed.numel() * packed.element_size(), _dtype_code(dtype), _ptr(y), M, K, N, group_size,
+                             _ptr(bias), _ptr(workspace), ws_bytes, _stream(stream, act.device))
+    _check(code, "w4a8_gemm")
+    return y
+
+
+def w4a8_linear(x, packed, N, group_size=128, bias=None, y=None, act=None, workspace=None, stream=None):
+    """x [M, K] (fp16/bf16): quantise to fp8 per row, then the W4A8 product -> y [M, N]."""
+    M, K = x.shape
+    act = w4a8_quantize(x, act=act, stream=stream)
+    return w4a8_gemm(act, packed, M, K, N, group_size, x.dtype, bias, y, workspace, stream)

@@ -41,6 +41,23 @@ size_t packed_size(int64_t K, int64_t N, int64_t G) {
     return (size_t)K * np / 2 + (size_t)4 * uw * np;
 }
 
+// W4A8 activation buffer: codes (M*K bytes), row scales (M fp32), block sums
+// (M*K/128 fp32), each part starting on a 256-byte boundary.
+size_t round256(size_t v) { return (v + 255) / 256 * 256; }
+size_t act_scale_offset(int64_t M, int64_t K) { return round256((size_t)M * (size_t)K); }
+size_t act_sum_offset(int64_t M, int64_t K) { return act_scale_offset(M, K) + round256((size_t)M * 4); }
+size_t act_size(int64_t M, int64_t K) { return act_sum_offset(M, K) + (size_t)M * (size_t)(K / 128) * 4; }
+w4a16_status check_act_shape(int64_t M, int64_t K) {
+    if (M < 0 || M >= (int64_t(1) << 31) || K <= 0 || K % 128 != 0 || K > kMaxK || M * K > kMaxMK)
+        return W4A16_ERR_SHAPE;
+    return W4A16_OK;
+}
+w4a16::W4A8Act act_parts(void* act, int64_t M, int64_t K) {
+    uint8_t* base = static_cast<uint8_t*>(act);
+    return w4a16::W4A8Act{base, reinterpret_cast<float*>(base + act_scale_offset(M, K)),
+                          reinterpret_cast<float*>(base + act_sum_offset(M, K))};
+}
+
 // 0 = unknown, 1 = gfx950, 2 = other; cached per device ordinal.
 std::atomic<int> g_device_kind[kMaxDevices];
 
@@ -202,6 +219,66 @@ w4a16_status w4a16_embedding(const int32_t* ids, int64_t T, const void* packed, 
     return err == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
 }
 
+size_t w4a8_activation_bytes(int64_t M, int64_t K) {
+    if (M <= 0 || check_act_shape(M, K) != W4A16_OK) return 0;
+    return act_size(M, K);
+}
+
+size_t w4a8_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t group_size) {
+    int64_t G = 0;
+    if (M <= 0 || check_shape(K, N, group_size, &G) != W4A16_OK || G < 128) return 0;
+    if (check_act_shape(M, K) != W4A16_OK) return 0;
+    return w4a16::plan_gemm(M, K, N, G).workspace_bytes;
+}
+
+w4a16_status w4a8_quantize(const void* x, w4a16_dtype dtype, int64_t M, int64_t K, void* act, size_t act_bytes,
+                           void* stream) {
+    w4a16_status st = check_act_shape(M, K);
+    if (st != W4A16_OK) return st;
+    if (dtype != W4A16_FP16 && dtype != W4A16_BF16) return W4A16_ERR_DTYPE;
+    if (M == 0) return W4A16_OK;
+    if (!x || !act) return W4A16_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(act, 16)) return W4A16_ERR_ALIGN;
+    if (act_bytes < act_size(M, K)) return W4A16_ERR_BUFFER_SIZE;
+    st = check_device();
+    if (st != W4A16_OK) return st;
+    const hipError_t err = w4a16::launch_w4a8_quantize(static_cast<const uint16_t*>(x), M, K, dtype == W4A16_BF16,
+                                                       act_parts(act, M, K), static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
+w4a16_status w4a8_gemm(const void* act, size_t act_bytes, const void* packed, size_t packed_bytes,
+                       w4a16_dtype dtype, void* y, int64_t M, int64_t K, int64_t N, int64_t group_size,
+                       const void* bias, void* workspace, size_t workspace_bytes, void* stream) {
+    int64_t G = 0;
+    w4a16_status st = check_shape(K, N, group_size, &G);
+    if (st != W4A16_OK) return st;
+    if (G < 128) return W4A16_ERR_GROUP;     // one fp8 MFMA spans a 128-row block
+    st = check_act_shape(M, K);
+    if (st != W4A16_OK) return st;
+    if (dtype != W4A16_FP16 && dtype != W4A16_BF16) return W4A16_ERR_DTYPE;
+    if (M == 0) return W4A16_OK;
+    if (!act || !packed || !y) return W4A16_ERR_NULL;
+    if (!aligned(act, 16) || !aligned(packed, 16) || !aligned(y, 16) || (bias && !aligned(bias, 2)))
+        return W4A16_ERR_ALIGN;
+    if (act_bytes < act_size(M, K) || packed_bytes < packed_size(K, N, G)) return W4A16_ERR_BUFFER_SIZE;
+    const size_t need = w4a16::plan_gemm(M, K, N, G).workspace_bytes;
+    if (need > 0) {
+        if (!workspace) return W4A16_ERR_NULL;
+        if (!aligned(workspace, 16)) return W4A16_ERR_ALIGN;
+        if (workspace_bytes < need) return W4A16_ERR_BUFFER_SIZE;
+    }
+    st = check_device();
+    if (st != W4A16_OK) return st;
+    // the kernel reads the activation parts through const pointers
+    const hipError_t err = w4a16::launch_w4a8_gemm(act_parts(const_cast<void*>(act), M, K),
+                                                   static_cast<const uint8_t*>(packed),
+                                                   static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), M,
+                                                   K, N, G, dtype == W4A16_BF16, workspace,
+                                                   static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
 // Packed-buffer header: magic, layout version, dtype, K, N, group size, buffer bytes,
 // an FNV-1a checksum of those 48 bytes, 8 reserved zero bytes.
 constexpr char kHeaderMagic[8] = {'W', '4', 'A', '1', '6', 'P', 'K', 0};
@@ -275,7 +352,8 @@ const char* w4a16_status_str(w4a16_status status) {
         case W4A16_OK: return "ok";
         case W4A16_ERR_NULL: return "a required pointer is NULL";
         case W4A16_ERR_SHAPE: return "unsupported shape (need M >= 0, K % 128 == 0, N % 8 == 0)";
-        case W4A16_ERR_GROUP: return "unsupported group size (need -1 or a multiple of 128 dividing K)";
+        case W4A16_ERR_GROUP:
+            return "unsupported group size (need -1, 32, 64 or a multiple of 128 dividing K; W4A8: not 32 or 64)";
         case W4A16_ERR_DTYPE: return "unsupported dtype (need fp16 or bf16)";
         case W4A16_ERR_ALIGN: return "misaligned pointer";
         case W4A16_ERR_BUFFER_SIZE: return "caller buffer too small";

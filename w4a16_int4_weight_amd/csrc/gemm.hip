@@ -35,6 +35,7 @@
 
 #include "device_common.h"
 #include "launch.h"
+#include "split_k.h"
 
 namespace w4a16 {
 namespace {
@@ -73,7 +74,6 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(
     constexpr int kStages = 3;
     using StageT = Stage<BM, CBW, kWaves, kSub>;
     __shared__ StageT ring[kStages];
-    __shared__ int last_split;
 
     // XCD-aware order: ids id, id+8, id+16, ... share an XCD; they take the M tiles and
     // the K splits of one N tile. Ids past the last N tile (grid padding) exit.
@@ -262,84 +262,8 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(
     }
 
     // transposed tiles: lane (c, h), register e -> row 16 r + c, column 16 j + 4 h + e
-    if (splits > 1) {
-        // Publish this split's partial tile with agent-scope stores (coherent across the
-        // XCDs' L2s without writing back a whole L2), wait until they have completed,
-        // then count the tile's finished splits; the last split to arrive reads the
-        // other splits' partials back (agent-scope loads), adds them in split order and
-        // writes y. Partials are kept per (tile, split, wave, fragment) in the lanes'
-        // own order, 1 KiB per fragment: every store and load instruction covers 512
-        // contiguous bytes (whole cache lines), the low and high halves of the lanes'
-        // 16 bytes in two such runs.
-        const int tile = m_tile * tiles_n + n_tile;
-        auto part = [&](int sp, int f) {
-            const size_t slot = (((size_t)tile * splits + sp) * kWaves + w) * (MR * CBW) + f;
-            return reinterpret_cast<uint64_t*>(reinterpret_cast<uint8_t*>(partials) + slot * 1024) + lane;
-        };
-#pragma unroll
-        for (int j = 0; j < CBW; ++j) {
-#pragma unroll
-            for (int r = 0; r < MR; ++r) {
-                uint64_t* q = part(split, r * CBW + j);
-                const f32x4 v = acc[r][j];
-                __hip_atomic_store(q, __builtin_bit_cast(uint64_t, f32x2{v[0], v[1]}), __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(q + 64, __builtin_bit_cast(uint64_t, f32x2{v[2], v[3]}), __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-            }
-        }
-        __builtin_amdgcn_s_waitcnt(0);          // this thread's partial stores have completed
-        __syncthreads();
-        if (tid == 0)
-            last_split = __hip_atomic_fetch_add(&counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                         (uint32_t)(splits - 1);
-        __syncthreads();
-        if (!last_split) return;
-        // Sum in split order; this workgroup's own split comes from its registers. The
-        // loads of a batch of splits are all issued before the first is used: kBatch
-        // splits x MR x CBW fragments in flight (one memory round trip per batch).
-        constexpr int kBatch = MR * CBW >= 16 ? 1 : 16 / (MR * CBW);
-        f32x4 sum[MR][CBW];
-#pragma unroll
-        for (int j = 0; j < CBW; ++j)
-#pragma unroll
-            for (int r = 0; r < MR; ++r) sum[r][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int sp0 = 0; sp0 < splits; sp0 += kBatch) {
-            f32x4 got[kBatch][MR][CBW];
-#pragma unroll
-            for (int b = 0; b < kBatch; ++b) {
-                const int sp = sp0 + b;
-#pragma unroll
-                for (int j = 0; j < CBW; ++j) {
-#pragma unroll
-                    for (int r = 0; r < MR; ++r) {
-                        got[b][r][j] = acc[r][j];
-                        if (sp < splits && sp != split) {
-                            const uint64_t* q = part(sp, r * CBW + j);
-                            const f32x2 lo = __builtin_bit_cast(f32x2, __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-                            const f32x2 hi = __builtin_bit_cast(f32x2, __hip_atomic_load(q + 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-                            got[b][r][j] = f32x4{lo[0], lo[1], hi[0], hi[1]};
-                        }
-                    }
-                }
-            }
-#pragma unroll
-            for (int b = 0; b < kBatch; ++b) {
-                if (sp0 + b < splits) {
-#pragma unroll
-                    for (int j = 0; j < CBW; ++j)
-#pragma unroll
-                        for (int r = 0; r < MR; ++r) sum[r][j] += got[b][r][j];
-                }
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < CBW; ++j)
-#pragma unroll
-            for (int r = 0; r < MR; ++r) acc[r][j] = sum[r][j];
-        if (tid == 0)      // leave the counter at zero for the next call
-            __hip_atomic_store(&counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    if (splits > 1 && !reduce_splits<MR, CBW, kWaves>(acc, counters, partials, m_tile * tiles_n + n_tile, split, splits))
+        return;
 
 #pragma unroll
     for (int j = 0; j < CBW; ++j) {

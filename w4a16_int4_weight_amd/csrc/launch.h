@@ -58,4 +58,18 @@ hipError_t launch_gemm(const uint16_t* x, const uint8_t* packed, const uint16_t*
                        int64_t M, int64_t K, int64_t N, int64_t G, bool bf16, void* workspace,
                        hipStream_t stream);
 
+// W4A8 activations after quantisation (one caller buffer, see w4a8_activation_bytes):
+// codes [M x K] E4M3 bytes in operand order, row_scale [M] fp32, block_sum [M x K/128]
+// fp32 (sum of each 128-element block's decoded codes).
+struct W4A8Act {
+    uint8_t* codes;
+    float* row_scale;
+    float* block_sum;
+};
+hipError_t launch_w4a8_quantize(const uint16_t* x, int64_t M, int64_t K, bool bf16, const W4A8Act& a,
+                                hipStream_t stream);
+// Same tiles, K split and workspace as launch_gemm (plan_gemm with G >= 128).
+hipError_t launch_w4a8_gemm(const W4A8Act& a, const uint8_t* packed, const uint16_t* bias, uint16_t* y, int64_t M,
+                            int64_t K, int64_t N, int64_t G, bool bf16, void* workspace, hipStream_t stream);
+
 }  // namespace w4a16

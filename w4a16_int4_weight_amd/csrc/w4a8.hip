@@ -1,0 +1,371 @@
+// W4A8: the packed int4 weights of the W4A16 layer against fp8 (E4M3) activations,
+// on the fp8 matrix cores.
+//
+// The vLLM note "Carga de capas cuantizadas: AWQ / GPTQ / Marlin / fp8" (section
+// "Límites y fallos") describes the int4 Marlin kernel taking float8_e4m3fn
+// activations: the weights get a one-time fp8 pre-processing and the scales are
+// multiplied by 512. The factor has a plain reason on any hardware: a 4-bit code q
+// in the low nibble of an E4M3 byte (exponent field 0 or 1, mantissa the low three
+// bits) reads as q * 2^-9 exactly, so the packed codes become fp8 operands with two
+// instructions per 8 codes (mask, shift-and-mask), and 2^9 restores the scale. Here
+// the factor is applied to each scale as it is read, so one packed buffer (the W4A16
+// layout, unchanged) serves both activation types.
+//
+// Activations are quantised per row: a = max |x| / 448, codes RNE(x / a), with the
+// codes written in the order the MFMA operands take them and each 128-element block's
+// code sum written beside them (quantize_kernel). The product is
+//
+//   y[m, n] = a[m] * sum_g ( 512 s[g, n] * D[g] - s[g, n] z[g, n] * X[m, g] ) + bias[n],
+//   D[g] = sum_{k in block g} e[m, k] * (q[k, n] * 2^-9),  X[m, g] = sum_{k in g} e[m, k],
+//
+// one 16x16x128 fp8 MFMA per 16x16 output fragment and 128-row block giving D
+// exactly (products of two E4M3 values are exact, the sum is fp32); 512 s scales it
+// into the fp32 accumulators. The zero-point term, a [M x K/128] by [K/128 x N]
+// product, runs after the loop on the fp32 matrix cores (16x16x4).
+//
+// Tiling, the three-stage ring of direct global -> LDS copies, the XCD-aware
+// workgroup order and the K split are those of the 16-bit GEMM; the activation
+// tile is half the size (one byte per element).
+#include <stddef.h>
+
+#include "device_common.h"
+#include "launch.h"
+#include "split_k.h"
+
+namespace w4a16 {
+namespace {
+
+constexpr int kXcds = 8;
+constexpr float kE4M3Max = 448.0f;
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// ---------------------------------------------------------------- quantisation
+
+constexpr int kQuantThreads = 256;
+
+// One workgroup per row. Pass 1: max |x|; pass 2: codes, in operand order (within each
+// 128-element block, byte 32 h + 8 i + j holds element 32 i + 8 h + (0,4,1,5,2,6,3,7)[j]),
+// and the block sums of the decoded codes.
+template <bool kBF16>
+__global__ __launch_bounds__(kQuantThreads) void quantize_kernel(const uint16_t* __restrict__ x,
+                                                                  uint8_t* __restrict__ codes,
+                                                                  float* __restrict__ row_scale,
+                                                                  float* __restrict__ block_sum, int K) {
+    __shared__ float wave_max[kQuantThreads / 64];
+    const int m = blockIdx.x;
+    const uint16_t* xr = x + (size_t)m * K;
+    const int chunks = K / 8;                  // 8 elements (16 bytes) each
+    float amax = 0.f;
+    for (int c = threadIdx.x; c < chunks; c += kQuantThreads) {
+        const uint4 v = *reinterpret_cast<const uint4*>(xr + 8 * c);
+        const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            amax = fmaxf(amax, fabsf(half_bits_to_f32<kBF16>(wd[t] & 0xFFFFu)));
+            amax = fmaxf(amax, fabsf(half_bits_to_f32<kBF16>(wd[t] >> 16)));
+        }
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) amax = fmaxf(amax, __shfl_xor(amax, d));
+    if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = amax;
+    __syncthreads();
+    amax = wave_max[0];
+#pragma unroll
+    for (int i = 1; i < kQuantThreads / 64; ++i) amax = fmaxf(amax, wave_max[i]);
+    const float scale = amax > 0.f ? amax / kE4M3Max : 1.f;     // IEEE division, as are the quotients
+    if (threadIdx.x == 0) row_scale[m] = scale;
+
+    uint8_t* cr = codes + (size_t)m * K;
+    const int KB = K / kRowsPerBlock;
+    for (int c = threadIdx.x; c < chunks; c += kQuantThreads) {
+        // chunk c: block c / 16, rows 8 (c % 16) .. +7 of it = step i, lane group h
+        const int kb = c >> 4, i = (c & 15) >> 2, h = c & 3;
+        const uint4 v = *reinterpret_cast<const uint4*>(xr + 8 * c);
+        const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+        float q[8];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            q[2 * t] = half_bits_to_f32<kBF16>(wd[t] & 0xFFFFu) / scale;
+            q[2 * t + 1] = half_bits_to_f32<kBF16>(wd[t] >> 16) / scale;
+        }
+        // bytes 0..3 = rows 0, 4, 1, 5; bytes 4..7 = rows 2, 6, 3, 7 (RNE, OCP E4M3)
+        int lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[4], 0, false);
+        lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[1], q[5], lo, true);
+        int hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[6], 0, false);
+        hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[3], q[7], hi, true);
+        *reinterpret_cast<uint2*>(cr + (size_t)kb * kRowsPerBlock + 32 * h + 8 * i) = make_uint2((uint32_t)lo, (uint32_t)hi);
+        float s = __builtin_amdgcn_cvt_f32_fp8(lo, 0) + __builtin_amdgcn_cvt_f32_fp8(lo, 1);
+        s += __builtin_amdgcn_cvt_f32_fp8(lo, 2) + __builtin_amdgcn_cvt_f32_fp8(lo, 3);
+        s += __builtin_amdgcn_cvt_f32_fp8(hi, 0) + __builtin_amdgcn_cvt_f32_fp8(hi, 1);
+        s += __builtin_amdgcn_cvt_f32_fp8(hi, 2) + __builtin_amdgcn_cvt_f32_fp8(hi, 3);
+        // the 16 chunks of a block sit in 16 consecutive lanes (K / 8 is a multiple of 16)
+#pragma unroll
+        for (int d = 8; d >= 1; d >>= 1) s += __shfl_xor(s, d, 16);
+        if ((c & 15) == 0) block_sum[(size_t)m * KB + kb] = s;
+    }
+}
+
+// ---------------------------------------------------------------- GEMM
+
+// One stage of the LDS ring: the fp8 activation tile of one 128-row block of K
+// (16-byte chunk j of row r stored at chunk j ^ (r % 8)), the workgroup's blocks of
+// packed codes and its metadata words (64 per wave, the first 16 * CBW used).
+template <int BM, int CBW, int W>
+struct StageA8 {
+    uint4 x[BM * 8];
+    uint4 w[W * CBW * 64];
+    uint32_t meta[W * 64];
+};
+
+__device__ __forceinline__ f32x4 mfma_fp8(const i32x8& a, const i32x8& b) {
+    // format 0 (E4M3) for both operands, no block scales: the plain 16x16x128 fp8 MFMA
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+}
+
+// Workgroup tile 16*MR rows x 16*CBW*kWaves columns, waves side by side along N as in
+// the 16-bit GEMM. MFMA operands: weights first, activations second, so each lane
+// holds 4 adjacent output columns of one row (lane (c, h), register e -> row 16 r + c,
+// column 16 j + 4 h + e).
+template <bool kBF16, int MR, int CBW, int kWaves>
+__global__ __launch_bounds__(64 * kWaves) void w4a8_gemm_kernel(
+    const uint8_t* __restrict__ act, const float* __restrict__ row_scale, const float* __restrict__ block_sum,
+    const uint8_t* __restrict__ packed, const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int M, int K,
+    int N, int tiles_m, int tiles_n, int splits, uint32_t* __restrict__ counters, float* __restrict__ partials) {
+    constexpr int BM = 16 * MR;
+    constexpr int kXBytes = BM * kRowsPerBlock;
+    // 1 KiB copies (8 rows) when every wave gets at least one, else 256-byte ones (2 rows)
+    constexpr bool kXSlabs = kXBytes >= kWaves * 1024;
+    constexpr int kXCopyBytes = kXSlabs ? 1024 : 256;
+    constexpr int kXPerWave = kXBytes / kXCopyBytes / kWaves;
+    static_assert(kXPerWave >= 1 && kXPerWave * kXCopyBytes * kWaves == kXBytes, "x tile must split over the waves");
+    constexpr int kDmaPerStage = kXPerWave + CBW + 1;
+    constexpr int kStages = 3;
+    using StageT = StageA8<BM, CBW, kWaves>;
+    __shared__ StageT ring[kStages];
+
+    const int id = blockIdx.x;
+    const int local = id / kXcds;
+    const int m_tile = local % tiles_m;
+    const int rest = local / tiles_m;
+    const int split = rest % splits;
+    const int n_tile = (rest / splits) * kXcds + id % kXcds;
+    if (n_tile >= tiles_n) return;
+
+    const int KB = K / kRowsPerBlock;
+    const int UW = (int)padded_units(K, kRowsPerBlock);
+    const int Np = (int)padded_cols(N);
+    const int NB = Np / kColsPerBlock;
+    const int kb_begin = (int)((int64_t)KB * split / splits);
+    const int kb_end = (int)((int64_t)KB * (split + 1) / splits);
+    const int nkb = kb_end - kb_begin;
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int c = lane & 15;
+    const int h = lane >> 4;
+    const int m0 = m_tile * BM;
+    const int nbw = (n_tile * kWaves + w) * CBW;
+
+    // activation copies: copy p of this wave covers tile rows (8 or 2 per copy);
+    // rows past M read row M-1 (their outputs are not written)
+    const uint8_t* xbase = uniform_ptr(act + (size_t)m0 * K);
+    uint32_t xoff[kXPerWave];
+#pragma unroll
+    for (int t = 0; t < kXPerWave; ++t) {
+        const int piece = w * kXPerWave + t;
+        const int row = kXSlabs ? 8 * piece + (lane >> 3) : 2 * piece + (lane >> 5);
+        const int chunk = kXSlabs ? (lane & 7) : ((lane & 31) >> 2);
+        const int sub = kXSlabs ? 0 : 4 * (lane & 3);
+        const int m = m0 + row < M ? m0 + row : M - 1;
+        xoff[t] = (uint32_t)(m - m0) * (uint32_t)K + 16u * (uint32_t)(chunk ^ (row & 7)) + (uint32_t)sub;
+    }
+    const int nbw0 = nbw < NB ? nbw : NB - 1;
+    const uint8_t* wbase = uniform_ptr(packed + (size_t)nbw0 * KB * kBlockBytes);
+    uint32_t woff[CBW];
+#pragma unroll
+    for (int j = 0; j < CBW; ++j) {
+        const int nbj = nbw + j < NB ? nbw + j : NB - 1;
+        woff[j] = (uint32_t)(nbj - nbw0) * (uint32_t)KB * kBlockBytes + 16u * (uint32_t)lane;
+    }
+    const uint32_t* meta_plane = reinterpret_cast<const uint32_t*>(packed + (size_t)K * Np / 2);
+    const int col0 = nbw * kColsPerBlock < Np ? nbw * kColsPerBlock : Np - kColsPerBlock;
+    const int ncol = nbw * kColsPerBlock + (lane < 16 * CBW ? lane : 0);
+    const uint8_t* mbase = uniform_ptr(meta_plane + (size_t)col0 * UW);
+    const uint32_t moff = (uint32_t)((ncol < Np ? ncol : Np - 1) - col0) * (uint32_t)UW * 4u;
+    const uint32_t ring_base = lds_addr(&ring[0]);
+
+    auto issue = [&](int slot, int kb) {
+        const uint32_t st = ring_base + (uint32_t)slot * (uint32_t)sizeof(StageT);
+#pragma unroll
+        for (int t = 0; t < kXPerWave; ++t) {
+            const uint32_t dst = st + (uint32_t)offsetof(StageT, x) + (uint32_t)((w * kXPerWave + t) * kXCopyBytes);
+            if constexpr (kXSlabs) dma16(xbase + (size_t)kb * kRowsPerBlock, xoff[t], dst);
+            else dma4(xbase + (size_t)kb * kRowsPerBlock, xoff[t], dst);
+        }
+#pragma unroll
+        for (int j = 0; j < CBW; ++j)
+            dma16(wbase + (size_t)kb * kBlockBytes, woff[j],
+                  st + (uint32_t)offsetof(StageT, w) + (uint32_t)(w * CBW + j) * 1024u);
+        dma4(mbase + (size_t)kb * 4, moff, st + (uint32_t)offsetof(StageT, meta) + (uint32_t)w * 256u);
+    };
+
+    f32x4 acc[MR][CBW];
+#pragma unroll
+    for (int r = 0; r < MR; ++r)
+#pragma unroll
+        for (int j = 0; j < CBW; ++j) acc[r][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    if (nkb > 0) issue(0, kb_begin);
+    if (nkb > 1) issue(1, kb_begin + 1);
+    for (int t = 0; t < nkb; ++t) {
+        if (t + 1 < nkb) wait_vmcnt<kDmaPerStage>();
+        else wait_vmcnt<0>();
+        lds_barrier();
+        if (t + 2 < nkb) issue((t + 2) % kStages, kb_begin + t + 2);
+
+        const StageT& st = ring[t % kStages];
+        // 512 s for this lane's 4 columns of each column block
+        float sc[CBW][4];
+        i32x8 b[CBW];
+#pragma unroll
+        for (int j = 0; j < CBW; ++j) {
+            const uint4 md = *reinterpret_cast<const uint4*>(&st.meta[w * 64 + 16 * j + 4 * h]);
+            sc[j][0] = 512.f * half_bits_to_f32<kBF16>(md.x & 0xFFFFu);
+            sc[j][1] = 512.f * half_bits_to_f32<kBF16>(md.y & 0xFFFFu);
+            sc[j][2] = 512.f * half_bits_to_f32<kBF16>(md.z & 0xFFFFu);
+            sc[j][3] = 512.f * half_bits_to_f32<kBF16>(md.w & 0xFFFFu);
+            // codes -> E4M3 bytes q * 2^-9: word i gives bytes 8 i .. 8 i + 7 (rows 0,4,1,5 | 2,6,3,7)
+            const uint4 wq = st.w[(w * CBW + j) * 64 + lane];
+            b[j] = i32x8{(int)(wq.x & 0x0F0F0F0Fu), (int)((wq.x >> 4) & 0x0F0F0F0Fu),
+                         (int)(wq.y & 0x0F0F0F0Fu), (int)((wq.y >> 4) & 0x0F0F0F0Fu),
+                         (int)(wq.z & 0x0F0F0F0Fu), (int)((wq.z >> 4) & 0x0F0F0F0Fu),
+                         (int)(wq.w & 0x0F0F0F0Fu), (int)((wq.w >> 4) & 0x0F0F0F0Fu)};
+        }
+#pragma unroll
+        for (int r = 0; r < MR; ++r) {
+            // row 16 r + c, bytes 32 h .. 32 h + 31 of the block: stored chunks 2h, 2h+1 (swizzled)
+            const int row = 16 * r + c;
+            const uint4 a0 = st.x[row * 8 + ((2 * h) ^ (c & 7))];
+            const uint4 a1 = st.x[row * 8 + ((2 * h + 1) ^ (c & 7))];
+            const i32x8 a = i32x8{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
+                                  (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+#pragma unroll
+            for (int j = 0; j < CBW; ++j) {
+                const f32x4 d = mfma_fp8(b[j], a);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[r][j][e] = fmaf(sc[j][e], d[e], acc[r][j][e]);
+            }
+        }
+    }
+
+    // zero-point term over this split's blocks: acc -= sum_kb (s z)[kb, n] * X[m, kb],
+    // as 16x16x4 fp32 MFMAs over groups of 4 blocks (lane group h takes block 4 t + h;
+    // blocks past the split's end contribute 0)
+    for (int t0 = kb_begin; t0 < kb_end; t0 += 4) {
+        const int kb = t0 + h;
+        const bool valid = kb < kb_end;
+        const int kbc = valid ? kb : kb_begin;
+        float zs[CBW];
+#pragma unroll
+        for (int j = 0; j < CBW; ++j) {
+            int n = (nbw + j) * kColsPerBlock + c;
+            n = n < Np ? n : Np - 1;
+            const uint32_t md = meta_plane[(size_t)n * UW + kbc];
+            zs[j] = valid ? -half_bits_to_f32<kBF16>(md & 0xFFFFu) * (float)((md >> 16) & 0xFu) : 0.f;
+        }
+#pragma unroll
+        for (int r = 0; r < MR; ++r) {
+            const int m = m0 + 16 * r + c < M ? m0 + 16 * r + c : M - 1;
+            const float xs = valid ? block_sum[(size_t)m * KB + kbc] : 0.f;
+#pragma unroll
+            for (int j = 0; j < CBW; ++j) acc[r][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(zs[j], xs, acc[r][j], 0, 0, 0);
+        }
+    }
+
+    if (splits > 1 && !reduce_splits<MR, CBW, kWaves>(acc, counters, partials, m_tile * tiles_n + n_tile, split, splits))
+        return;
+
+#pragma unroll
+    for (int j = 0; j < CBW; ++j) {
+        if (nbw + j >= NB) continue;
+        const int n = (nbw + j) * kColsPerBlock + 4 * h;
+        if (n >= N) continue;                  // zero padding of a last half block
+        float bv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (bias) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) bv[e] = half_bits_to_f32<kBF16>(bias[n + e]);
+        }
+#pragma unroll
+        for (int r = 0; r < MR; ++r) {
+            const int m = m0 + 16 * r + c;
+            if (m < M) {
+                const float a = row_scale[m];
+                const f32x4 v = acc[r][j];
+                const uint2 o = make_uint2(pack2_rne<kBF16>(fmaf(a, v[0], bv[0]), fmaf(a, v[1], bv[1])),
+                                           pack2_rne<kBF16>(fmaf(a, v[2], bv[2]), fmaf(a, v[3], bv[3])));
+                *reinterpret_cast<uint2*>(y + (size_t)m * N + n) = o;
+            }
+        }
+    }
+}
+
+template <bool kBF16, int MR, int CBW, int W>
+void launch_cfg(const GemmPlan& p, const W4A8Act& a, const uint8_t* packed, const uint16_t* bias, uint16_t* y,
+                int M, int K, int N, uint32_t* counters, float* partials, hipStream_t stream) {
+    const int tiles_n_pad = (p.tiles_n + kXcds - 1) / kXcds * kXcds;
+    const dim3 grid((unsigned)(p.tiles_m * p.splits * tiles_n_pad));
+    hipLaunchKernelGGL((w4a8_gemm_kernel<kBF16, MR, CBW, W>), grid, dim3(64 * W), 0, stream, a.codes, a.row_scale,
+                       a.block_sum, packed, bias, y, M, K, N, p.tiles_m, p.tiles_n, p.splits, counters, partials);
+}
+
+template <bool kBF16, int MR>
+void launch_mr(const GemmPlan& p, const W4A8Act& a, const uint8_t* packed, const uint16_t* bias, uint16_t* y,
+               int M, int K, int N, uint32_t* counters, float* partials, hipStream_t stream) {
+    if constexpr (MR >= 2) {
+        if (p.waves == 8) {
+            launch_cfg<kBF16, MR, 2, 8>(p, a, packed, bias, y, M, K, N, counters, partials, stream);
+            return;
+        }
+    }
+    if (p.cbw == 4) launch_cfg<kBF16, MR, 4, 4>(p, a, packed, bias, y, M, K, N, counters, partials, stream);
+    else if (p.cbw == 2) launch_cfg<kBF16, MR, 2, 4>(p, a, packed, bias, y, M, K, N, counters, partials, stream);
+    else launch_cfg<kBF16, MR, 1, 4>(p, a, packed, bias, y, M, K, N, counters, partials, stream);
+}
+
+template <bool kBF16>
+void launch_typed(const GemmPlan& p, const W4A8Act& a, const uint8_t* packed, const uint16_t* bias, uint16_t* y,
+                  int M, int K, int N, uint32_t* counters, float* partials, hipStream_t stream) {
+    if (p.mr == 1) launch_mr<kBF16, 1>(p, a, packed, bias, y, M, K, N, counters, partials, stream);
+    else if (p.mr == 2) launch_mr<kBF16, 2>(p, a, packed, bias, y, M, K, N, counters, partials, stream);
+    else if (p.mr == 4) launch_mr<kBF16, 4>(p, a, packed, bias, y, M, K, N, counters, partials, stream);
+    else launch_mr<kBF16, 8>(p, a, packed, bias, y, M, K, N, counters, partials, stream);
+}
+
+}  // namespace
+
+hipError_t launch_w4a8_quantize(const uint16_t* x, int64_t M, int64_t K, bool bf16, const W4A8Act& a,
+                                hipStream_t stream) {
+    const dim3 grid((unsigned)M), block(kQuantThreads);
+    if (bf16)
+        hipLaunchKernelGGL(quantize_kernel<true>, grid, block, 0, stream, x, a.codes, a.row_scale, a.block_sum, (int)K);
+    else
+        hipLaunchKernelGGL(quantize_kernel<false>, grid, block, 0, stream, x, a.codes, a.row_scale, a.block_sum, (int)K);
+    return hipGetLastError();
+}
+
+hipError_t launch_w4a8_gemm(const W4A8Act& a, const uint8_t* packed, const uint16_t* bias, uint16_t* y, int64_t M,
+                            int64_t K, int64_t N, int64_t G, bool bf16, void* workspace, hipStream_t stream) {
+    const GemmPlan p = plan_gemm(M, K, N, G);
+    uint32_t* counters = static_cast<uint32_t*>(workspace);
+    float* partials = nullptr;
+    if (p.splits > 1) {
+        const size_t counter_bytes = ((size_t)p.tiles_m * p.tiles_n * 4 + 255) / 256 * 256;
+        partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + counter_bytes);
+    }
+    if (bf16) launch_typed<true>(p, a, packed, bias, y, (int)M, (int)K, (int)N, counters, partials, stream);
+    else launch_typed<false>(p, a, packed, bias, y, (int)M, (int)K, (int)N, counters, partials, stream);
+    return hipGetLastError();
+}
+
+}  // namespace w4a16
