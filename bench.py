@@ -45,6 +45,7 @@ sys.path.insert(0, ROOT)
 METRIC = "W4A16 GEMM GB/s (M=1) & TFLOP/s (M=512) vs roofline; repack GB/s"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+MFMA_FP8_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 MFMA, published
 ROTATE_BYTES = 1 << 30
 MAX_COPIES = 128
 
@@ -124,6 +125,38 @@ def measure_gemm(w, workload, M, steps, warmup, dev, path="auto"):
                 GBps=nbytes / per_launch_s / 1e9, TFLOPs=flops / per_launch_s / 1e12)
 
 
+def measure_w4a8(w, workload, M, steps, warmup, dev):
+    """W4A8 on a 16-bit workload: the product alone from quantised activations (the
+    kernel the roofline is for), and the whole step, quantisation included."""
+    import torch
+    import synth
+    ws = synth.make(workload, Ms=(M,))
+    K, N, G = ws.K, ws.N, ws.group_size
+    qw = torch.from_numpy(ws.qweight).to(dev)
+    qz = torch.from_numpy(ws.qzeros).to(dev)
+    sc = to_dev_bits(ws.scale_bits, ws.dtype, dev)
+    packed0 = w.w4a16_repack(qw, qz, sc, G)
+    del qw, qz, sc
+    copies = max(1, min(MAX_COPIES, math.ceil(ROTATE_BYTES / packed0.numel())))
+    packs = [packed0] + [packed0.clone() for _ in range(copies - 1)]
+    x = to_dev_bits(ws.x_bits[M], ws.dtype, dev)
+    act = w.w4a8_quantize(x)
+    y = torch.empty((M, N), dtype=x.dtype, device=dev)
+    gemm_calls = [(lambda p=packs[i % copies]: w.w4a8_gemm(act, p, M, K, N, G, x.dtype, y=y)) for i in range(steps)]
+    ms, n = time_graph(gemm_calls, warmup)
+    gemm_s = ms / 1e3 / n
+    step_calls = [(lambda p=packs[i % copies]: w.w4a8_linear(x, p, N, G, y=y, act=act)) for i in range(steps)]
+    ms, n = time_graph(step_calls, warmup)
+    step_s = ms / 1e3 / n
+    flops = 2 * M * N * K
+    del packs, packed0
+    torch.cuda.empty_cache()
+    return dict(workload=workload, M=M, K=K, N=N, group_size=G, dtype=ws.dtype, activations="fp8 e4m3",
+                kernel="w4a8_gemm_mfma", weight_copies=copies, launches=n, us_per_launch=gemm_s * 1e6,
+                us_per_step_with_quantize=step_s * 1e6, flops=flops, TFLOPs=flops / gemm_s / 1e12,
+                TFLOPs_step=flops / step_s / 1e12)
+
+
 def measure_repack(w, workload, steps, warmup, dev, fmt="awq"):
     """fmt "awq": w4a16_repack from AWQ tensors; "gptq": w4a16_repack_gptq from
     GPTQ-standard tensors of the same shape (same recipe, same byte count)."""
@@ -198,9 +231,10 @@ def roofline_hbm(entry, traffic=None):
             "frac": round(entry["GBps"] / HBM_PEAK_GBS, 4), "traffic": traffic}
 
 
-def roofline_mfma(entry):
-    return {"bound": "mfma", "achieved": round(entry["TFLOPs"], 1), "peak": MFMA_BF16_PEAK_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(entry["TFLOPs"] / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
+def roofline_mfma(entry, peak=None):
+    peak = MFMA_BF16_PEAK_TFLOPS if peak is None else peak
+    return {"bound": "mfma", "achieved": round(entry["TFLOPs"], 1), "peak": peak,
+            "unit": "TFLOP/s", "frac": round(entry["TFLOPs"] / peak, 4), "traffic": None}
 
 
 CALIBRATION_COPY_BYTES = 256 << 20
@@ -267,7 +301,13 @@ def pmc_probe(dev):
     for _ in range(3):
         w.w4a16_gemm(x, packed, ws.N, ws.group_size, y=y)
     torch.cuda.synchronize()
-    log("pmc probe done: 3 x 256 MiB copy, 10 x gate_up_decode GEMV, 3 x lm_head M=512 GEMM")
+    # the W4A8 GEMM on the same weights, three launches from one quantised activation buffer
+    act = w.w4a8_quantize(x)
+    for _ in range(3):
+        w.w4a8_gemm(act, packed, 512, ws.K, ws.N, ws.group_size, x.dtype, y=y)
+    torch.cuda.synchronize()
+    log("pmc probe done: 3 x 256 MiB copy, 10 x gate_up_decode GEMV, 3 x lm_head M=512 GEMM, "
+        "3 x lm_head M=512 W4A8 GEMM")
 
 
 def cpu_baseline(workload, M, budget_s=15.0):
@@ -347,6 +387,12 @@ def main():
         r["roofline"] = roofline_hbm(r)
         log(f"lm_head repack from GPTQ: {r['us_per_launch']:.1f} us, {r['GBps']:.0f} GB/s")
         secondary.append(r)
+        for wl in ("qkv_prefill", "gate_up_prefill", "lm_head"):
+            e = measure_w4a8(w, wl, 512, max(20, args.steps // 4), min(args.warmup, 10), dev)
+            e["roofline"] = roofline_mfma(e, MFMA_FP8_PEAK_TFLOPS)
+            log(f"{wl} W4A8 M=512: {e['us_per_launch']:.2f} us, {e['TFLOPs']:.1f} TFLOP/s (with quantisation "
+                f"{e['us_per_step_with_quantize']:.2f} us)")
+            secondary.append(e)
         e = measure_embedding(w, "lm_head", 512, args.steps, min(args.warmup, 10), dev)
         e["roofline"] = roofline_hbm(e)
         log(f"lm_head tied-embedding gather T=512: {e['us_per_launch']:.2f} us, {e['GBps']:.0f} GB/s")

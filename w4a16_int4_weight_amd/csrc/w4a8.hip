@@ -109,14 +109,23 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(const uint16_t*
 // ---------------------------------------------------------------- GEMM
 
 // One stage of the LDS ring: the fp8 activation tile of one 128-row block of K
-// (16-byte chunk j of row r stored at chunk j ^ (r % 8)), the workgroup's blocks of
-// packed codes and its metadata words (64 per wave, the first 16 * CBW used).
+// (16-byte chunk j of row r stored at chunk j ^ row_swizzle(r)), the workgroup's
+// blocks of packed codes and its metadata words (64 per wave, the first 16 * CBW used).
 template <int BM, int CBW, int W>
 struct StageA8 {
     uint4 x[BM * 8];
     uint4 w[W * CBW * 64];
     uint32_t meta[W * 64];
 };
+
+// XOR applied to the chunk index of row r of the activation tile. A fragment read
+// (16 rows, chunks 2h and 2h+1 of each) then meets no bank twice, whether the LDS
+// serves 16 lanes per cycle from 64 banks or 32 lanes from 128: bits 1..3 of the row
+// go to the chunk bits in the order (2, 1, 3), so rows 4 apart (one 512-byte bank
+// span) and rows 2 apart (one 256-byte span) differ in chunk bits that the lane
+// groups h do not use. (XOR with r % 8 measured one bank-conflict cycle per read
+// cycle on gfx950.)
+__device__ __forceinline__ int row_swizzle(int r) { return ((r >> 2) & 1) | (r & 2) | (((r >> 3) & 1) << 2); }
 
 __device__ __forceinline__ f32x4 mfma_fp8(const i32x8& a, const i32x8& b) {
     // format 0 (E4M3) for both operands, no block scales: the plain 16x16x128 fp8 MFMA
@@ -178,7 +187,7 @@ __global__ __launch_bounds__(64 * kWaves) void w4a8_gemm_kernel(
         const int chunk = kXSlabs ? (lane & 7) : ((lane & 31) >> 2);
         const int sub = kXSlabs ? 0 : 4 * (lane & 3);
         const int m = m0 + row < M ? m0 + row : M - 1;
-        xoff[t] = (uint32_t)(m - m0) * (uint32_t)K + 16u * (uint32_t)(chunk ^ (row & 7)) + (uint32_t)sub;
+        xoff[t] = (uint32_t)(m - m0) * (uint32_t)K + 16u * (uint32_t)(chunk ^ row_swizzle(row)) + (uint32_t)sub;
     }
     const int nbw0 = nbw < NB ? nbw : NB - 1;
     const uint8_t* wbase = uniform_ptr(packed + (size_t)nbw0 * KB * kBlockBytes);
@@ -244,10 +253,11 @@ __global__ __launch_bounds__(64 * kWaves) void w4a8_gemm_kernel(
         }
 #pragma unroll
         for (int r = 0; r < MR; ++r) {
-            // row 16 r + c, bytes 32 h .. 32 h + 31 of the block: stored chunks 2h, 2h+1 (swizzled)
+            // row 16 r + c, bytes 32 h .. 32 h + 31 of the block: chunks 2h, 2h+1
+            // (row_swizzle(16 r + c) = row_swizzle(c))
             const int row = 16 * r + c;
-            const uint4 a0 = st.x[row * 8 + ((2 * h) ^ (c & 7))];
-            const uint4 a1 = st.x[row * 8 + ((2 * h + 1) ^ (c & 7))];
+            const uint4 a0 = st.x[row * 8 + ((2 * h) ^ row_swizzle(c))];
+            const uint4 a1 = st.x[row * 8 + ((2 * h + 1) ^ row_swizzle(c))];
             const i32x8 a = i32x8{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
                                   (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
 #pragma unroll
