@@ -112,6 +112,9 @@ W4A8_CASES = [
     (40, 384, 40, 128, "bf16"), (100, 2048, 1040, -1, "fp16"), (300, 512, 520, 256, "bf16"),
     (512, 2048, 3072, 128, "bf16"), (512, 2048, 13312, 128, "bf16"), (129, 1024, 13288, 128, "bf16"),
     (33, 6656, 2048, 128, "bf16"),
+    # 256 x 256 tiles (outputs of at least two rounds of them): ragged M, a half last
+    # column block, fp16 with one group per column
+    (257, 256, 65544, 128, "bf16"), (512, 384, 65536, -1, "fp16"),
 ]
 
 

@@ -68,7 +68,8 @@ struct W4A8Act {
 };
 hipError_t launch_w4a8_quantize(const uint16_t* x, int64_t M, int64_t K, bool bf16, const W4A8Act& a,
                                 hipStream_t stream);
-// Same tiles, K split and workspace as launch_gemm (plan_gemm with G >= 128).
+// Tiles of launch_gemm (plan_gemm, G >= 128), plus a 256 x 256 tile for outputs of at
+// least two rounds of it; the workspace never exceeds plan_gemm's.
 hipError_t launch_w4a8_gemm(const W4A8Act& a, const uint8_t* packed, const uint16_t* bias, uint16_t* y, int64_t M,
                             int64_t K, int64_t N, int64_t G, bool bf16, void* workspace, hipStream_t stream);
 

@@ -36,6 +36,7 @@ namespace w4a16 {
 namespace {
 
 constexpr int kXcds = 8;
+constexpr int kTilesPerRound = 256;       // one workgroup of the widest tile per CU
 constexpr float kE4M3Max = 448.0f;
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -293,8 +294,13 @@ __global__ __launch_bounds__(64 * kWaves) void w4a8_gemm_kernel(
         }
     }
 
-    if (splits > 1 && !reduce_splits<MR, CBW, kWaves>(acc, counters, partials, m_tile * tiles_n + n_tile, split, splits))
-        return;
+    // (tiles of more than 16 fragments per wave are only planned for outputs that need no
+    // K split: their reduction would not fit in registers)
+    if constexpr (MR * CBW <= 16) {
+        if (splits > 1 && !reduce_splits<MR, CBW, kWaves>(acc, counters, partials, m_tile * tiles_n + n_tile, split,
+                                                           splits))
+            return;
+    }
 
 #pragma unroll
     for (int j = 0; j < CBW; ++j) {
@@ -332,15 +338,19 @@ void launch_cfg(const GemmPlan& p, const W4A8Act& a, const uint8_t* packed, cons
 template <bool kBF16, int MR>
 void launch_mr(const GemmPlan& p, const W4A8Act& a, const uint8_t* packed, const uint16_t* bias, uint16_t* y,
                int M, int K, int N, uint32_t* counters, float* partials, hipStream_t stream) {
-    if constexpr (MR >= 2) {
-        if (p.waves == 8) {
-            launch_cfg<kBF16, MR, 2, 8>(p, a, packed, bias, y, M, K, N, counters, partials, stream);
-            return;
+    if constexpr (MR == 16) {
+        launch_cfg<kBF16, 16, 2, 8>(p, a, packed, bias, y, M, K, N, counters, partials, stream);
+    } else {
+        if constexpr (MR >= 2) {
+            if (p.waves == 8) {
+                launch_cfg<kBF16, MR, 2, 8>(p, a, packed, bias, y, M, K, N, counters, partials, stream);
+                return;
+            }
         }
+        if (p.cbw == 4) launch_cfg<kBF16, MR, 4, 4>(p, a, packed, bias, y, M, K, N, counters, partials, stream);
+        else if (p.cbw == 2) launch_cfg<kBF16, MR, 2, 4>(p, a, packed, bias, y, M, K, N, counters, partials, stream);
+        else launch_cfg<kBF16, MR, 1, 4>(p, a, packed, bias, y, M, K, N, counters, partials, stream);
     }
-    if (p.cbw == 4) launch_cfg<kBF16, MR, 4, 4>(p, a, packed, bias, y, M, K, N, counters, partials, stream);
-    else if (p.cbw == 2) launch_cfg<kBF16, MR, 2, 4>(p, a, packed, bias, y, M, K, N, counters, partials, stream);
-    else launch_cfg<kBF16, MR, 1, 4>(p, a, packed, bias, y, M, K, N, counters, partials, stream);
 }
 
 template <bool kBF16>
@@ -349,7 +359,29 @@ void launch_typed(const GemmPlan& p, const W4A8Act& a, const uint8_t* packed, co
     if (p.mr == 1) launch_mr<kBF16, 1>(p, a, packed, bias, y, M, K, N, counters, partials, stream);
     else if (p.mr == 2) launch_mr<kBF16, 2>(p, a, packed, bias, y, M, K, N, counters, partials, stream);
     else if (p.mr == 4) launch_mr<kBF16, 4>(p, a, packed, bias, y, M, K, N, counters, partials, stream);
-    else launch_mr<kBF16, 8>(p, a, packed, bias, y, M, K, N, counters, partials, stream);
+    else if (p.mr == 8) launch_mr<kBF16, 8>(p, a, packed, bias, y, M, K, N, counters, partials, stream);
+    else launch_mr<kBF16, 16>(p, a, packed, bias, y, M, K, N, counters, partials, stream);
+}
+
+// The 16-bit GEMM's plan, except that outputs with at least two rounds of 256 x 256
+// tiles over the CUs take that tile (8 waves of 16 fragments each): the activation
+// and weight copies per output element, which bound this kernel (a run without the
+// MFMA work takes ~85% of the full time on the LM head), drop by a quarter.
+// Such outputs never split K.
+GemmPlan plan_w4a8(int64_t M, int64_t K, int64_t N, int64_t G) {
+    GemmPlan p = plan_gemm(M, K, N, G);
+    const int64_t NB = padded_cols(N) / kColsPerBlock;
+    const int64_t tm = (M + 255) / 256, tn = (NB + 15) / 16;
+    if (tm * tn >= 2 * kTilesPerRound) {
+        p.mr = 16;
+        p.cbw = 2;
+        p.waves = 8;
+        p.tiles_m = (int)tm;
+        p.tiles_n = (int)tn;
+        p.splits = 1;
+        p.workspace_bytes = 0;
+    }
+    return p;
 }
 
 }  // namespace
@@ -366,7 +398,7 @@ hipError_t launch_w4a8_quantize(const uint16_t* x, int64_t M, int64_t K, bool bf
 
 hipError_t launch_w4a8_gemm(const W4A8Act& a, const uint8_t* packed, const uint16_t* bias, uint16_t* y, int64_t M,
                             int64_t K, int64_t N, int64_t G, bool bf16, void* workspace, hipStream_t stream) {
-    const GemmPlan p = plan_gemm(M, K, N, G);
+    const GemmPlan p = plan_w4a8(M, K, N, G);
     uint32_t* counters = static_cast<uint32_t*>(workspace);
     float* partials = nullptr;
     if (p.splits > 1) {
