@@ -21,8 +21,8 @@
 // (word j, lane group h) transposes rows 32 i + 8 h + 0..7 for i = 0..3 and places,
 // for each of its 8 columns, the 16-byte chunk of lane (column % 16) + 16 h in LDS;
 // the workgroup then writes its 32 blocks whole. Wave h reads 64 consecutive words
-// (256 bytes) of one row per load instruction. The workgroups of row block 0 also
-// write the metadata rows of their 512 columns (one column's row is contiguous).
+// (256 bytes) of one row per load instruction. The tile's metadata rows are dealt
+// to its row-block workgroups and written whole (1 KiB per wave store).
 #include "device_common.h"
 #include "launch.h"
 
@@ -56,6 +56,54 @@ __device__ __forceinline__ void transpose8x8_nibbles(uint32_t (&v)[8]) {
     }
 }
 
+// XOR applied to a chunk's lane index in the LDS staging of block b (b < 32, so the
+// result stays in 0..63): the 32 blocks one store instruction touches then map a lane
+// to 32 different 16-byte slots of a 512-byte bank span, two lanes per slot.
+__device__ __forceinline__ int stage_swizzle(int b) { return b & 31; }
+
+// Metadata rows of columns [c0, c0 + cols) of the input tensors (padding columns of
+// a last half block included), written whole: the columns are dealt to the KB
+// workgroups of row blocks kb = 0 .. KB-1 of one column tile, and a thread writes one
+// 16-byte chunk (4 consecutive unit words: scale bits | zero << 16 per unit of
+// min(G, 128) rows, zero past the last unit and for padding columns) of one column's
+// row, so a wave stores 1 KiB of consecutive rows. (Rows written in 4- or 16-byte
+// pieces strided over many lines left partial lines to HBM: ~12 us on the LM head.)
+// kAwq: qzeros in AWQ slot order, else in standard order, both packed along N.
+template <bool kAwq>
+__device__ __forceinline__ void write_metadata_rows(const uint32_t* __restrict__ qzeros,
+                                                    const uint16_t* __restrict__ scales, uint8_t* __restrict__ packed,
+                                                    int64_t K, int64_t N, int64_t G, int64_t n0, int64_t Nt,
+                                                    int64_t c0, int cols, int64_t kb, int tid, int nthreads) {
+    const int64_t KB = K / kRowsPerBlock;
+    const int sub = units_per_block(G);
+    const int64_t Gu = kRowsPerBlock / sub;                       // rows per unit
+    const int64_t U = KB * sub;
+    const int cpr = (int)(padded_units(K, G) / 4);                // 16-byte chunks per row
+    const int cpw = (int)((cols + KB - 1) / KB);                  // columns per workgroup
+    const int c_begin = kb * cpw < cols ? (int)(kb * cpw) : cols;
+    const int c_end = c_begin + cpw < cols ? c_begin + cpw : cols;
+    uint4* meta4 = reinterpret_cast<uint4*>(packed + K * padded_cols(Nt) / 2);
+    for (int q = tid; q < (c_end - c_begin) * cpr; q += nthreads) {
+        const int r = q / cpr;
+        const int p4 = q - r * cpr;
+        const int64_t n = c0 + c_begin + r;                       // column of the input tensors
+        const bool real = n < N;
+        const int zshift = 4 * (kAwq ? awq_slot_of_column((int)(n & 7)) : (int)(n & 7));
+        uint32_t word[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int64_t b = 4 * p4 + e;
+            word[e] = 0u;
+            if (real && b < U) {
+                const int64_t g = (b * Gu) / G;
+                const uint32_t z = (qzeros[g * (N / 8) + (n >> 3)] >> zshift) & 0xFu;
+                word[e] = (uint32_t)scales[g * N + n] | (z << 16);
+            }
+        }
+        meta4[(n0 + n) * cpr + p4] = make_uint4(word[0], word[1], word[2], word[3]);
+    }
+}
+
 // Input tensors hold columns [n0, n0 + N) of a K x Nt weight (the whole weight when
 // n0 = 0 and N = Nt): qweight [K, N/8], qzeros [K/G, N/8], scales [K/G, N]. Output:
 // those columns' blocks and metadata rows in the packed layout of the K x Nt weight.
@@ -74,6 +122,9 @@ __global__ __launch_bounds__(kRepackThreads) void repack_kernel(
     const bool active = j < words_per_row;
     const int64_t jc = active ? j : words_per_row - 1;            // clamped: loads stay in bounds
 
+    const int64_t tile_words = words_per_row - j0 < kWordsPerTile ? words_per_row - j0 : kWordsPerTile;
+    const int nblk = (int)((tile_words + 1) / 2);                 // a last half block included
+
     // 1. rows 128 kb + 32 i + 8 h + e of word column jc, fed in tile slot order
     uint32_t t[4][8];
 #pragma unroll
@@ -90,50 +141,30 @@ __global__ __launch_bounds__(kRepackThreads) void repack_kernel(
     //    The tile's 32 blocks are assembled in LDS and written out whole, each wave
     //    storing contiguous 1 KiB blocks.
     //    With N % 16 == 8 the last block has one word: its other 8 columns are zero.
+    //    In LDS, chunk `lane` of block b sits at b * 64 + (lane ^ stage_swizzle(b)): the
+    //    64 threads of one store instruction write one chunk into each of 32 blocks,
+    //    1 KiB apart, which unswizzled would all fall on the same banks (32-way
+    //    conflicts measured); the XOR spreads them over 32 different 16-byte bank
+    //    groups, and each block stays a permutation of its own 64 chunks.
     __shared__ uint4 stage[kWordsPerTile / 2 * 64];
 #pragma unroll
     for (int c8 = 0; c8 < 8; ++c8) {
         const int s = awq_slot_of_column(c8);
+        const int b = jl >> 1;
         const int lane = 8 * (jl & 1) + c8 + 16 * h;
-        stage[(jl >> 1) * 64 + lane] = active ? make_uint4(t[0][s], t[1][s], t[2][s], t[3][s]) : make_uint4(0, 0, 0, 0);
+        stage[b * 64 + (lane ^ stage_swizzle(b))] =
+            active ? make_uint4(t[0][s], t[1][s], t[2][s], t[3][s]) : make_uint4(0, 0, 0, 0);
     }
     __syncthreads();
-    const int64_t tile_words = words_per_row - j0 < kWordsPerTile ? words_per_row - j0 : kWordsPerTile;
-    const int nblk = (int)((tile_words + 1) / 2);                 // a last half block included
     for (int q = tid; q < nblk * 64; q += kRepackThreads) {
-        const int64_t nb = n0 / kColsPerBlock + (j0 >> 1) + (q >> 6);
-        reinterpret_cast<uint4*>(packed + (nb * KB + kb) * kBlockBytes)[q & 63] = stage[q];
+        const int b = q >> 6;
+        const int64_t nb = n0 / kColsPerBlock + (j0 >> 1) + b;
+        reinterpret_cast<uint4*>(packed + (nb * KB + kb) * kBlockBytes)[q & 63] = stage[b * 64 + ((q & 63) ^ stage_swizzle(b))];
     }
 
-    // 4. metadata: the workgroups of row block 0 write, for each column of their tile's
-    //    blocks, its whole row of UW words (scale bits | zero << 16 per metadata unit of
-    //    min(G, 128) rows, then zero padding; all zero for the padding columns of a last
-    //    half block), 16 bytes at a time
-    if (kb != 0) return;
-    const int64_t UW = padded_units(K, G);
-    const int64_t U = KB * units_per_block(G);
-    const int64_t Gu = kRowsPerBlock / units_per_block(G);      // rows per unit
-    uint32_t* meta = reinterpret_cast<uint32_t*>(packed + K * padded_cols(Nt) / 2);
-    for (int q = tid; q < nblk * kColsPerBlock; q += kRepackThreads) {
-        const int64_t n = j0 * 8 + q;                 // column of the input tensors
-        const bool real = n < N;
-        const int zshift = 4 * awq_slot_of_column((int)(n & 7));
-        uint4* row = reinterpret_cast<uint4*>(meta + (n0 + n) * UW);
-        for (int64_t p0 = 0; p0 < UW; p0 += 4) {
-            uint32_t word[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int64_t b = p0 + e;
-                word[e] = 0u;
-                if (real && b < U) {
-                    const int64_t g = (b * Gu) / G;
-                    const uint32_t z = (qzeros[g * words_per_row + (n >> 3)] >> zshift) & 0xFu;
-                    word[e] = (uint32_t)scales[g * N + n] | (z << 16);
-                }
-            }
-            row[p0 / 4] = make_uint4(word[0], word[1], word[2], word[3]);
-        }
-    }
+    // 4. the tile's metadata rows, dealt to its row-block workgroups
+    write_metadata_rows<true>(qzeros, scales, packed, K, N, G, n0, Nt, j0 * 8, nblk * kColsPerBlock, kb, tid,
+                              kRepackThreads);
 }
 
 // ---- GPTQ-standard input: codes packed along K ----
@@ -168,41 +199,27 @@ __global__ __launch_bounds__(kGptqColumns) void repack_gptq_kernel(
     int64_t K, int64_t N, int64_t G, int64_t n0, int64_t Nt) {
     const int64_t KB = K / kRowsPerBlock;
     const int64_t kb = blockIdx.y;
-    const int64_t n = (int64_t)blockIdx.x * kGptqColumns + threadIdx.x;
-    if (n >= padded_cols(N)) return;
-    const bool real = n < N;          // else a zero padding column of a last half block
-    const int64_t nb = (n0 + n) / kColsPerBlock;
-    const int c = (int)(n % kColsPerBlock);
-    uint4* blk = reinterpret_cast<uint4*>(packed + (nb * KB + kb) * kBlockBytes);
-    // GPTQ word row i = 16 kb + 4 w + h: lane group h, word w of the tile
+    const int64_t c0 = (int64_t)blockIdx.x * kGptqColumns;
+    const int64_t n = c0 + threadIdx.x;
+    const int64_t Np = padded_cols(N);
+    if (n < Np) {
+        const bool real = n < N;      // else a zero padding column of a last half block
+        const int64_t nb = (n0 + n) / kColsPerBlock;
+        const int c = (int)(n % kColsPerBlock);
+        uint4* blk = reinterpret_cast<uint4*>(packed + (nb * KB + kb) * kBlockBytes);
+        // GPTQ word row i = 16 kb + 4 w + h: lane group h, word w of the tile
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-        uint32_t t[4];
+        for (int h = 0; h < 4; ++h) {
+            uint32_t t[4];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) t[w] = real ? unzip_nibbles(qweight[(16 * kb + 4 * w + h) * N + n]) : 0u;
-        blk[c + 16 * h] = make_uint4(t[0], t[1], t[2], t[3]);
-    }
-    if (kb != 0) return;
-    // metadata row of column n: scale bits | zero << 16 per unit of min(G, 128) rows,
-    // zero padding
-    const int64_t UW = padded_units(K, G);
-    const int64_t U = KB * units_per_block(G);
-    const int64_t Gu = kRowsPerBlock / units_per_block(G);
-    uint4* row = reinterpret_cast<uint4*>(packed + K * padded_cols(Nt) / 2 + (n0 + n) * UW * 4);
-    for (int64_t p0 = 0; p0 < UW; p0 += 4) {
-        uint32_t word[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int64_t b = p0 + e;
-            word[e] = 0u;
-            if (real && b < U) {
-                const int64_t g = (b * Gu) / G;
-                const uint32_t z = (qzeros[g * (N / 8) + n / 8] >> (4 * (n % 8))) & 0xFu;
-                word[e] = (uint32_t)scales[g * N + n] | (z << 16);
-            }
+            for (int w = 0; w < 4; ++w) t[w] = real ? unzip_nibbles(qweight[(16 * kb + 4 * w + h) * N + n]) : 0u;
+            blk[c + 16 * h] = make_uint4(t[0], t[1], t[2], t[3]);
         }
-        row[p0 / 4] = make_uint4(word[0], word[1], word[2], word[3]);
     }
+    // the metadata rows of the workgroup's columns, dealt to its row-block workgroups
+    const int cols = (int)(Np - c0 < kGptqColumns ? Np - c0 : kGptqColumns);
+    write_metadata_rows<false>(qzeros, scales, packed, K, N, G, n0, Nt, c0, cols, kb, (int)threadIdx.x,
+                               kGptqColumns);
 }
 
 }  // namespace
