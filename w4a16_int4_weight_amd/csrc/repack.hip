@@ -113,8 +113,10 @@ __global__ __launch_bounds__(kRepackThreads) void repack_kernel(
     int64_t K, int64_t N, int64_t G, int64_t n0, int64_t Nt) {
     const int64_t KB = K / kRowsPerBlock;
     const int64_t words_per_row = N / 8;
-    const int64_t kb = blockIdx.y;
-    const int64_t j0 = (int64_t)blockIdx.x * kWordsPerTile;     // first AWQ word of the tile
+    // row blocks vary fastest over the grid: the workgroups running together write
+    // whole column blocks (each column block's K range is contiguous in the layout)
+    const int64_t kb = blockIdx.x % KB;
+    const int64_t j0 = (int64_t)(blockIdx.x / KB) * kWordsPerTile;     // first AWQ word of the tile
     const int tid = threadIdx.x;
     const int jl = tid & (kWordsPerTile - 1);
     const int h = tid / kWordsPerTile;                            // lane group (wave) 0..3
@@ -198,8 +200,11 @@ __global__ __launch_bounds__(kGptqColumns) void repack_gptq_kernel(
     const uint16_t* __restrict__ scales, uint8_t* __restrict__ packed,
     int64_t K, int64_t N, int64_t G, int64_t n0, int64_t Nt) {
     const int64_t KB = K / kRowsPerBlock;
-    const int64_t kb = blockIdx.y;
-    const int64_t c0 = (int64_t)blockIdx.x * kGptqColumns;
+    // column tiles vary fastest over the grid: the workgroups running together read
+    // long stretches of the same GPTQ rows (the other order measured ~2% slower here)
+    const int64_t tiles = (padded_cols(N) + kGptqColumns - 1) / kGptqColumns;
+    const int64_t kb = blockIdx.x / tiles;
+    const int64_t c0 = (int64_t)(blockIdx.x % tiles) * kGptqColumns;
     const int64_t n = c0 + threadIdx.x;
     const int64_t Np = padded_cols(N);
     if (n < Np) {
@@ -227,7 +232,9 @@ __global__ __launch_bounds__(kGptqColumns) void repack_gptq_kernel(
 hipError_t launch_repack_gptq(const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
                               uint8_t* packed, int64_t K, int64_t N, int64_t G, int64_t n0, int64_t Nt,
                               hipStream_t stream) {
-    const dim3 grid((unsigned)((padded_cols(N) + kGptqColumns - 1) / kGptqColumns), (unsigned)(K / kRowsPerBlock));
+    // one workgroup per (256-column tile, row block), tiles fastest: at most
+    // K N / 2^15 <= 2^22 workgroups
+    const dim3 grid((unsigned)(K / kRowsPerBlock * ((padded_cols(N) + kGptqColumns - 1) / kGptqColumns)));
     hipLaunchKernelGGL(repack_gptq_kernel, grid, dim3(kGptqColumns), 0, stream,
                        reinterpret_cast<const uint32_t*>(qweight), reinterpret_cast<const uint32_t*>(qzeros),
                        scales, packed, K, N, G, n0, Nt);
@@ -239,7 +246,9 @@ hipError_t launch_repack(const int32_t* qweight, const int32_t* qzeros, const ui
                          hipStream_t stream) {
     const int64_t KB = K / kRowsPerBlock;
     const int64_t words = N / 8;
-    dim3 grid((unsigned)((words + kWordsPerTile - 1) / kWordsPerTile), (unsigned)KB);
+    // one workgroup per (row block, 64-word tile), row blocks fastest: at most
+    // K N / 2^16 <= 2^21 workgroups
+    const dim3 grid((unsigned)(KB * ((words + kWordsPerTile - 1) / kWordsPerTile)));
     hipLaunchKernelGGL(repack_kernel, grid, dim3(kRepackThreads), 0, stream,
                        reinterpret_cast<const uint32_t*>(qweight), reinterpret_cast<const uint32_t*>(qzeros),
                        scales, packed, K, N, G, n0, Nt);
