@@ -172,11 +172,18 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(const void* p) {
     const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
     return reinterpret_cast<const uint8_t*>((hi << 32) | lo);
 }
+// M0 is written as an output operand bound to that register ("={m0}"), not listed as a
+// clobber: the compiler then knows the statement defines M0 and keeps nothing of its
+// own there across it (a clobber of a reserved register is not honoured).
 __device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(base), "s"(lds) : "memory", "m0");
+    uint32_t m0v;
+    asm volatile("s_mov_b32 %0, %3\n\tglobal_load_lds_dwordx4 %1, %2" : "={m0}"(m0v) : "v"(voff), "s"(base), "s"(lds)
+                 : "memory");
 }
 __device__ __forceinline__ void dma4(const uint8_t* base, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" : : "v"(voff), "s"(base), "s"(lds) : "memory", "m0");
+    uint32_t m0v;
+    asm volatile("s_mov_b32 %0, %3\n\tglobal_load_lds_dword %1, %2" : "={m0}"(m0v) : "v"(voff), "s"(base), "s"(lds)
+                 : "memory");
 }
 
 // Workgroup barrier that is also a compiler barrier for memory operations, without
