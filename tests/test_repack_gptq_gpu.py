@@ -31,7 +31,8 @@ def oracle_gptq_repack(gs):
 
 
 SHAPES = [(2048, 13312, 128, "bf16"), (6656, 2048, 128, "bf16"), (2048, 3072, 128, "bf16"),
-          (512, 512, 128, "fp16"), (128, 16, 128, "bf16"), (384, 272, -1, "fp16"), (1024, 48, 256, "bf16")]
+          (512, 512, 128, "fp16"), (128, 16, 128, "bf16"), (384, 272, -1, "fp16"), (1024, 48, 256, "bf16"),
+          (8192, 40, 128, "bf16")]
 
 
 @pytest.mark.parametrize("K,N,G,dtype", SHAPES)

@@ -40,7 +40,10 @@ def test_repack_bit_exact_on_workloads(w, name):
 
 
 @pytest.mark.parametrize("K,N,G,dtype", [(128, 16, 128, "bf16"), (256, 272, 128, "bf16"), (512, 48, 256, "fp16"),
-                                         (384, 4112, -1, "bf16"), (1024, 64, 512, "fp16"), (2048, 2048, 128, "bf16")])
+                                         (384, 4112, -1, "bf16"), (1024, 64, 512, "fp16"), (2048, 2048, 128, "bf16"),
+                                         # more row blocks (65) than the tile has columns (24): the
+                                         # metadata rows are dealt to the first row blocks only
+                                         (8320, 24, 128, "bf16")])
 def test_repack_bit_exact_shapes_and_groups(w, K, N, G, dtype):
     print(f"repack K={K} N={N} G={G} {dtype}", flush=True)
     ws = synth.make_custom(1000 + K + N, 1, K, N, dtype, G)
