@@ -11,8 +11,8 @@
 //
 // Workgroup: 4 or 8 waves side by side along N, each owning CBW column blocks (16 CBW
 // columns) and all 16*MR rows of the tile; the 256-column tile runs as 8 waves of
-// 2 blocks, two per SIMD, so that one computes while the other waits on its copies
-// or the barrier. Per 128-row block of K:
+// 2 blocks and the 64 x 128 tile as 8 waves of one, two per SIMD, so that one
+// computes while the other waits on its copies or the barrier. Per 128-row block of K:
 //   * a 3-stage LDS ring holds, per k block, the activation tile [16*MR x 128]
 //     (16-byte chunks XOR-swizzled by row, so the fragment reads of a wave spread
 //     over all banks), the workgroup's blocks of packed codes and its metadata;
@@ -311,6 +311,12 @@ void launch_mr(const GemmPlan& p, const uint16_t* x, const uint8_t* packed, cons
         launch_cfg<kBF16, MR, 1, 4, 2>(p, x, packed, bias, y, M, K, N, counters, partials, stream);
         return;
     }
+    if constexpr (MR >= 4) {
+        if (p.waves == 8 && p.cbw == 1) {
+            launch_cfg<kBF16, MR, 1, 8>(p, x, packed, bias, y, M, K, N, counters, partials, stream);
+            return;
+        }
+    }
     if constexpr (MR >= 2) {
         if (p.waves == 8) {
             launch_cfg<kBF16, MR, 2, 8>(p, x, packed, bias, y, M, K, N, counters, partials, stream);
@@ -356,6 +362,7 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G) {
             {8, 2, 4, 10.4},   // 128 x 128
             {8, 1, 4, 7.2},    // 128 x 64
             {4, 2, 8, 10.8},   // 64 x 256
+            {4, 1, 8, 8.0},    // 64 x 128 as 8 waves of one block (qkv prefill: 18.4 -> 16.9 us)
             {4, 2, 4, 7.4},    // 64 x 128
             {4, 1, 4, 5.4},    // 64 x 64
         };

@@ -370,6 +370,13 @@ void launch_typed(const GemmPlan& p, const W4A8Act& a, const uint8_t* packed, co
 // Such outputs never split K.
 GemmPlan plan_w4a8(int64_t M, int64_t K, int64_t N, int64_t G) {
     GemmPlan p = plan_gemm(M, K, N, G);
+    // the same column tile as 4 waves of 2 blocks where the 16-bit plan runs it as 8
+    // waves of one (a shape this kernel is not built for); tiles, splits and workspace
+    // depend on the tile's width only, so they stand
+    if (p.waves == 8 && p.cbw == 1) {
+        p.waves = 4;
+        p.cbw = 2;
+    }
     const int64_t NB = padded_cols(N) / kColsPerBlock;
     const int64_t tm = (M + 255) / 256, tn = (NB + 15) / 16;
     if (tm * tn >= 2 * kTilesPerRound) {
