@@ -112,6 +112,8 @@ W4A8_CASES = [
     (40, 384, 40, 128, "bf16"), (100, 2048, 1040, -1, "fp16"), (300, 512, 520, 256, "bf16"),
     (512, 2048, 3072, 128, "bf16"), (512, 2048, 13312, 128, "bf16"), (129, 1024, 13288, 128, "bf16"),
     (33, 6656, 2048, 128, "bf16"),
+    # 64 x 128 tiles as 8 waves of one column block: ragged M, a half last column block
+    (480, 512, 3080, 128, "fp16"),
     # 256 x 256 tiles (outputs of at least two rounds of them): ragged M, a half last
     # column block, fp16 with one group per column
     (257, 256, 65544, 128, "bf16"), (512, 384, 65536, -1, "fp16"),

@@ -341,6 +341,12 @@ void launch_mr(const GemmPlan& p, const W4A8Act& a, const uint8_t* packed, const
     if constexpr (MR == 16) {
         launch_cfg<kBF16, 16, 2, 8>(p, a, packed, bias, y, M, K, N, counters, partials, stream);
     } else {
+        if constexpr (MR >= 4) {
+            if (p.waves == 8 && p.cbw == 1) {
+                launch_cfg<kBF16, MR, 1, 8>(p, a, packed, bias, y, M, K, N, counters, partials, stream);
+                return;
+            }
+        }
         if constexpr (MR >= 2) {
             if (p.waves == 8) {
                 launch_cfg<kBF16, MR, 2, 8>(p, a, packed, bias, y, M, K, N, counters, partials, stream);
@@ -370,13 +376,6 @@ void launch_typed(const GemmPlan& p, const W4A8Act& a, const uint8_t* packed, co
 // Such outputs never split K.
 GemmPlan plan_w4a8(int64_t M, int64_t K, int64_t N, int64_t G) {
     GemmPlan p = plan_gemm(M, K, N, G);
-    // the same column tile as 4 waves of 2 blocks where the 16-bit plan runs it as 8
-    // waves of one (a shape this kernel is not built for); tiles, splits and workspace
-    // depend on the tile's width only, so they stand
-    if (p.waves == 8 && p.cbw == 1) {
-        p.waves = 4;
-        p.cbw = 2;
-    }
     const int64_t NB = padded_cols(N) / kColsPerBlock;
     const int64_t tm = (M + 255) / 256, tn = (NB + 15) / 16;
     if (tm * tn >= 2 * kTilesPerRound) {
