@@ -300,15 +300,17 @@ def test_gemm_wide_n(w, M):
 
 @pytest.mark.parametrize("M,N,dtype", [(500, 13264, "bf16"), (500, 13264, "fp16"), (250, 13264, "bf16"),
                                        (3000, 2608, "bf16"), (20, 131072, "bf16"), (480, 3080, "bf16"),
-                                       (480, 3080, "fp16")])
+                                       (480, 3080, "fp16"), (1000, 2600, "bf16"), (1000, 2600, "fp16"),
+                                       (48, 65528, "bf16")])
 def test_gemm_tile_shapes(w, M, N, dtype):
     # 256-column tiles run as 8 waves of 2 column blocks: N = 13264 (829 blocks) leaves
     # a last tile whose last wave lies wholly past N, M = 500 a ragged last row tile
-    # (128-row tiles); M = 250 takes 64-row tiles of that width; M = 3000, N = 2608 takes
-    # 128 x 128 tiles (4 waves of 2 blocks, the last tile 3 blocks wide); M = 20 is the
-    # shortest 8-wave tile (32 rows: one activation copy per wave); M = 480, N = 3080
-    # takes 64 x 128 tiles as 8 waves of one block (a ragged last row tile, a last half
-    # column block). Wide N on sampled column blocks.
+    # (128-row tiles); M = 48, N = 65528 takes 64 x 256 tiles (a ragged row tile, a
+    # half last block); M = 20 is the shortest 8-wave tile (32 rows: one activation copy
+    # per wave). 128 x 128 tiles as 8 waves of one block: M = 250 and M = 3000 (N = 2608,
+    # the last tile 3 blocks wide), M = 1000, N = 2600 (ragged rows, a half last block).
+    # 64 x 128 tiles as 8 waves of one block: M = 480, N = 3080 (ragged rows, a half
+    # last block). Wide N on sampled column blocks.
     ws = synth.make_custom(900 + M % 97, M, 256, N, dtype, 128)
     packed = pack_on_gpu(w, ws)
     got = y_to_f64(run(w, ws, packed, ws.x_bits[M], path="mfma"), dtype)
