@@ -7,7 +7,8 @@ batch; the weights were repacked once before timing. Secondary entries in the sa
 JSON line measure the other rows of the path on their own workloads: the LM-head
 repack from AWQ and from GPTQ-standard tensors (GB/s), the MFMA GEMM at M=512
 (TFLOP/s), the GEMV on the other shapes and the tied-embedding gather of 512 tokens
-from the packed LM head (GB/s).
+from the packed LM head (GB/s). As context, not as the metric, it also times the same
+products with dense bf16 weights through torch.matmul (the vendor GEMM library).
 
 Timing: warm-up calls, then K calls captured in one HIP graph and replayed once
 between two events on the launch stream, with a device synchronisation on both
@@ -226,6 +227,48 @@ def measure_embedding(w, workload, T, steps, warmup, dev):
                 algorithmic_bytes=nbytes, GBps=nbytes / per_launch_s / 1e9)
 
 
+def measure_dense_reference(workload, M, steps, warmup, dev):
+    """Context, not the metric: the same product with dense bf16 weights through
+    torch.matmul (the vendor GEMM library), weights rotated through >= 1 GiB of copies
+    and timed like the W4A16 entries. Algorithmic bytes: K*N*2 weights + M*K*2 + M*N*2."""
+    import torch
+    import synth
+    shape = synth.WORKLOADS[workload]
+    K, N = shape.K, shape.N
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    w0 = (torch.randn((K, N), device=dev, generator=g) * 0.05).to(torch.bfloat16)
+    copies = max(1, min(MAX_COPIES, math.ceil(ROTATE_BYTES / (K * N * 2))))
+    ws = [w0] + [w0.clone() for _ in range(copies - 1)]
+    x = torch.randn((M, K), device=dev, generator=g).to(torch.bfloat16)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    calls = [(lambda wt=ws[i % copies]: torch.matmul(x, wt, out=y)) for i in range(steps)]
+    try:
+        ms, n = time_graph(calls, warmup)
+        how = "HIP graph of K calls, events"
+    except Exception as exc:  # a library call that cannot be captured: time it eagerly
+        torch.cuda.synchronize()
+        log(f"dense reference not capturable ({type(exc).__name__}); timed eagerly")
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record()
+        for fn in calls:
+            fn()
+        end.record()
+        torch.cuda.synchronize()
+        ms, n = start.elapsed_time(end), len(calls)
+        how = "eager launches, events"
+    per_launch_s = ms / 1e3 / n
+    nbytes = K * N * 2 + M * K * 2 + M * N * 2
+    flops = 2 * M * N * K
+    del ws, w0
+    torch.cuda.empty_cache()
+    return dict(workload=workload, M=M, K=K, N=N, dtype="bf16", kind="dense bf16 weights, torch.matmul",
+                weight_copies=copies, launches=n, timing=how, us_per_launch=per_launch_s * 1e6,
+                algorithmic_bytes=nbytes, flops=flops, GBps=nbytes / per_launch_s / 1e9,
+                TFLOPs=flops / per_launch_s / 1e12)
+
+
 def roofline_hbm(entry, traffic=None):
     return {"bound": "hbm", "achieved": round(entry["GBps"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(entry["GBps"] / HBM_PEAK_GBS, 4), "traffic": traffic}
@@ -398,6 +441,21 @@ def main():
         log(f"lm_head tied-embedding gather T=512: {e['us_per_launch']:.2f} us, {e['GBps']:.0f} GB/s")
         secondary.append(e)
 
+    dense = []
+    if not args.quick:
+        # context: the same products with dense bf16 weights (4x the weight bytes)
+        w4 = {(head["workload"], 1): head}
+        w4.update({(e["workload"], e["M"]): e for e in secondary if "M" in e and "activations" not in e})
+        for wl, M in [("gate_up_decode", 1), ("down_proj", 1), ("lm_head", 1), ("qkv_prefill", 512),
+                      ("gate_up_prefill", 512), ("lm_head", 512)]:
+            steps = args.steps if M <= 16 else max(20, args.steps // 4)
+            d = measure_dense_reference(wl, M, steps, min(args.warmup, 10), dev)
+            if (wl, M) in w4:
+                d["w4a16_speedup"] = round(d["us_per_launch"] / w4[(wl, M)]["us_per_launch"], 3)
+            log(f"dense bf16 reference {wl} M={M}: {d['us_per_launch']:.2f} us, {d['GBps']:.0f} GB/s, "
+                f"{d['TFLOPs']:.1f} TFLOP/s")
+            dense.append(d)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
@@ -423,6 +481,7 @@ def main():
         "roofline": roofline_hbm(head, counter_traffic()),
         "cpu_baseline": cpu,
         "secondary": secondary,
+        "dense_bf16_reference": dense,
     }
     print(json.dumps(line), flush=True)
 
