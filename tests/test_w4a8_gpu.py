@@ -46,7 +46,9 @@ def oracle_w4a8_y(ws, x_bits, cols=None, bias_bits=None):
 
 
 @pytest.mark.parametrize("M,K,dtype", [(1, 2048, "bf16"), (5, 384, "fp16"), (512, 2048, "bf16"), (8, 6656, "bf16"),
-                                       (300, 128, "fp16")])
+                                       (300, 128, "fp16"),
+                                       # long rows: several 16-byte chunks per thread in both passes
+                                       (3, 16384, "bf16"), (2, 10240, "fp16")])
 def test_quantize_matches_oracle(w, M, K, dtype):
     print(f"w4a8 quantize M={M} K={K} {dtype}", flush=True)
     rng = np.random.default_rng(600 + M)
