@@ -234,6 +234,32 @@ def test_split_k_workspace_is_reused_and_left_zero(w):
     assert int(work[:tiles_bytes].count_nonzero()) == 0
 
 
+def test_split_k_default_workspace_per_stream(w):
+    # split-K calls on two streams with no workspace passed: the binding gives each
+    # stream its own zeroed workspace, so calls queued on both at once do not meet in
+    # each other's tile counters; every result matches the one-stream result bit for bit
+    ws = synth.make_custom(113, 16, 6656, 2048, "bf16", 128)
+    assert w.w4a16_workspace_bytes(16, 6656, 2048, 128) > 0
+    packed = pack_on_gpu(w, ws)
+    x = bits_to_device(ws.x_bits[16], "bf16")
+    want = device_to_bits(w.w4a16_gemm_ex(x, packed, 2048, 128, path="mfma"))
+    torch.cuda.synchronize()
+    assert ogemm.max_rel_error(numerics.half_bits_to_f64(want, "bf16"), oracle_y(ws, ws.x_bits[16])) <= TOL
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    ys = []
+    for i in range(8):
+        s = streams[i % 2]
+        with torch.cuda.stream(s):
+            ys.append(w.w4a16_gemm_ex(x, packed, 2048, 128, path="mfma", stream=s))
+    torch.cuda.synchronize()
+    for y in ys:
+        assert np.array_equal(device_to_bits(y), want)
+    keys = {k for k in w._workspaces if k[0] == torch.device(DEV).index}
+    assert {(torch.device(DEV).index, s.cuda_stream) for s in streams} <= keys
+
+
 def test_split_k_rejects_small_workspace(w):
     ws = synth.make_custom(112, 16, 6656, 2048, "bf16", 128)
     packed = pack_on_gpu(w, ws)

@@ -317,14 +317,19 @@ def load_packed(path, device="cuda:0"):
 _workspaces = {}
 
 
-def _default_workspace(device, nbytes):
-    """A zero-filled workspace per device, grown on demand. The kernels leave its
-    counters at zero, so it is reused by consecutive calls; calls overlapping on
-    different streams must pass their own `workspace`."""
-    key = torch.device(device).index
+def _default_workspace(device, nbytes, stream=None):
+    """A zero-filled workspace per (device, stream), grown on demand. The kernels leave
+    its counters at zero, so consecutive calls on one stream reuse it; calls on other
+    streams get their own. It is allocated and zeroed on that stream, so the memory of
+    a buffer replaced by a larger one is only handed out again behind the calls already
+    queued there."""
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    key = (torch.device(device).index, stream.cuda_stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        with torch.cuda.stream(stream):
+            ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
 
@@ -336,7 +341,7 @@ def _gemm_args(x, packed, N, group_size, bias, y, workspace, stream):
     if workspace is None and M > 0:
         need = w4a16_workspace_bytes(M, K, N, group_size)
         if need > 0:
-            workspace = _default_workspace(x.device, need)
+            workspace = _default_workspace(x.device, need, stream)
     if y is None:
         y = torch.empty((M, N), dtype=x.dtype, device=x.device)
     if tuple(y.shape) != (M, N) or y.dtype != x.dtype or not y.is_contiguous():
@@ -425,7 +430,7 @@ def w4a8_gemm(act, packed, M, K, N, group_size=128, dtype=torch.bfloat16, bias=N
     if workspace is None and M > 0:
         need = w4a8_workspace_bytes(M, K, N, group_size)
         if need > 0:
-            workspace = _default_workspace(act.device, need)
+            workspace = _default_workspace(act.device, need, stream)
     if y is None:
         y = torch.empty((M, N), dtype=dtype, device=act.device)
     if tuple(y.shape) != (M, N) or y.dtype != dtype or not y.is_contiguous():
