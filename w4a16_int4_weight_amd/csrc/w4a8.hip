@@ -272,25 +272,38 @@ __global__ __launch_bounds__(64 * kWaves) void w4a8_gemm_kernel(
 
     // zero-point term over this split's blocks: acc -= sum_kb (s z)[kb, n] * X[m, kb],
     // as 16x16x4 fp32 MFMAs over groups of 4 blocks (lane group h takes block 4 t + h;
-    // blocks past the split's end contribute 0)
-    for (int t0 = kb_begin; t0 < kb_end; t0 += 4) {
-        const int kb = t0 + h;
-        const bool valid = kb < kb_end;
-        const int kbc = valid ? kb : kb_begin;
-        float zs[CBW];
+    // blocks past the split's end contribute 0). The operands of kZeroBatch groups are
+    // loaded before any of their MFMAs, so the loads of a batch share one memory round
+    // trip (loaded group by group, each group waited for its own)
+    constexpr int kZeroBatch = 4;
+    for (int t0 = kb_begin; t0 < kb_end; t0 += 4 * kZeroBatch) {
+        float zs[kZeroBatch][CBW], xs[kZeroBatch][MR];
 #pragma unroll
-        for (int j = 0; j < CBW; ++j) {
-            int n = (nbw + j) * kColsPerBlock + c;
-            n = n < Np ? n : Np - 1;
-            const uint32_t md = meta_plane[(size_t)n * UW + kbc];
-            zs[j] = valid ? -half_bits_to_f32<kBF16>(md & 0xFFFFu) * (float)((md >> 16) & 0xFu) : 0.f;
+        for (int u = 0; u < kZeroBatch; ++u) {
+            const int kb = t0 + 4 * u + h;
+            const bool valid = kb < kb_end;
+            const int kbc = valid ? kb : kb_begin;
+#pragma unroll
+            for (int j = 0; j < CBW; ++j) {
+                int n = (nbw + j) * kColsPerBlock + c;
+                n = n < Np ? n : Np - 1;
+                const uint32_t md = valid ? meta_plane[(size_t)n * UW + kbc] : 0u;
+                zs[u][j] = valid ? -half_bits_to_f32<kBF16>(md & 0xFFFFu) * (float)((md >> 16) & 0xFu) : 0.f;
+            }
+#pragma unroll
+            for (int r = 0; r < MR; ++r) {
+                const int m = m0 + 16 * r + c < M ? m0 + 16 * r + c : M - 1;
+                xs[u][r] = valid ? block_sum[(size_t)m * KB + kbc] : 0.f;
+            }
         }
 #pragma unroll
-        for (int r = 0; r < MR; ++r) {
-            const int m = m0 + 16 * r + c < M ? m0 + 16 * r + c : M - 1;
-            const float xs = valid ? block_sum[(size_t)m * KB + kbc] : 0.f;
+        for (int u = 0; u < kZeroBatch; ++u) {
+            if (t0 + 4 * u >= kb_end) break;          // a group wholly past the end adds nothing
 #pragma unroll
-            for (int j = 0; j < CBW; ++j) acc[r][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(zs[j], xs, acc[r][j], 0, 0, 0);
+            for (int r = 0; r < MR; ++r)
+#pragma unroll
+                for (int j = 0; j < CBW; ++j)
+                    acc[r][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(zs[u][j], xs[u][r], acc[r][j], 0, 0, 0);
         }
     }
 
@@ -302,6 +315,11 @@ __global__ __launch_bounds__(64 * kWaves) void w4a8_gemm_kernel(
             return;
     }
 
+    // the row scales of this lane's rows, loaded before the first store (loaded next to
+    // each store, a load could wait behind the stores issued before it)
+    float rs[MR];
+#pragma unroll
+    for (int r = 0; r < MR; ++r) rs[r] = m0 + 16 * r + c < M ? row_scale[m0 + 16 * r + c] : 0.f;
 #pragma unroll
     for (int j = 0; j < CBW; ++j) {
         if (nbw + j >= NB) continue;
@@ -316,7 +334,7 @@ __global__ __launch_bounds__(64 * kWaves) void w4a8_gemm_kernel(
         for (int r = 0; r < MR; ++r) {
             const int m = m0 + 16 * r + c;
             if (m < M) {
-                const float a = row_scale[m];
+                const float a = rs[r];
                 const f32x4 v = acc[r][j];
                 const uint2 o = make_uint2(pack2_rne<kBF16>(fmaf(a, v[0], bv[0]), fmaf(a, v[1], bv[1])),
                                            pack2_rne<kBF16>(fmaf(a, v[2], bv[2]), fmaf(a, v[3], bv[3])));
