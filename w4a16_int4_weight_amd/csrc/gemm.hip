@@ -265,26 +265,43 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(
     if (splits > 1 && !reduce_splits<MR, CBW, kWaves>(acc, counters, partials, m_tile * tiles_n + n_tile, split, splits))
         return;
 
+    // Epilogue through LDS: the lanes write their rounded outputs into the free ring as
+    // a row-major [BM][BN] tile (rows padded by 16 bytes against bank conflicts), and the
+    // waves store whole rows, 16 bytes per lane and 1 KiB per instruction, instead of
+    // each wave writing half of every 128-byte line it touches.
+    constexpr int BN = 16 * CBW * kWaves;
+    constexpr int kRowBytes = BN * 2 + 16;
+    static_assert((size_t)BM * kRowBytes <= kStages * sizeof(StageT), "the output tile fits in the ring");
+    uint8_t* otile = reinterpret_cast<uint8_t*>(&ring[0]);
+    lds_barrier();                           // every wave is done with the ring's operands
 #pragma unroll
     for (int j = 0; j < CBW; ++j) {
-        if (nbw + j >= NB) continue;
-        const int n = (nbw + j) * kColsPerBlock + 4 * h;
-        if (n >= N) continue;                  // zero padding of a last half block (N % 8 == 0)
+        const int col = 16 * (w * CBW + j) + 4 * h;        // in the tile
+        const int n = (nbw + j) * kColsPerBlock + 4 * h;   // in y
         float bv[4] = {0.f, 0.f, 0.f, 0.f};
-        if (bias) {
+        if (bias && n < N) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) bv[e] = half_bits_to_f32<kBF16>(bias[n + e]);
         }
 #pragma unroll
         for (int r = 0; r < MR; ++r) {
-            const int m = m0 + 16 * r + c;
-            if (m < M) {
-                const f32x4 v = acc[r][j];
-                const uint2 o = make_uint2(pack2_rne<kBF16>(v[0] + bv[0], v[1] + bv[1]),
-                                           pack2_rne<kBF16>(v[2] + bv[2], v[3] + bv[3]));
-                *reinterpret_cast<uint2*>(y + (size_t)m * N + n) = o;
-            }
+            const f32x4 v = acc[r][j];
+            const uint2 o = make_uint2(pack2_rne<kBF16>(v[0] + bv[0], v[1] + bv[1]),
+                                       pack2_rne<kBF16>(v[2] + bv[2], v[3] + bv[3]));
+            *reinterpret_cast<uint2*>(otile + (16 * r + c) * kRowBytes + 2 * col) = o;
         }
+    }
+    __syncthreads();
+    // rows past M and columns past N (the zero padding of a last half block, whole
+    // column blocks past the last) are not stored; N % 8 == 0, so a 16-byte chunk of 8
+    // columns lies wholly inside or outside
+    const int n0 = n_tile * BN;
+    for (int q = tid; q < BM * (BN / 8); q += 64 * kWaves) {
+        const int row = q / (BN / 8);
+        const int ch = q - row * (BN / 8);
+        const int m = m0 + row, n = n0 + 8 * ch;
+        if (m < M && n < N)
+            *reinterpret_cast<uint4*>(y + (size_t)m * N + n) = *reinterpret_cast<const uint4*>(otile + row * kRowBytes + 16 * ch);
     }
 }
 

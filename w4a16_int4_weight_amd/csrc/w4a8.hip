@@ -315,32 +315,51 @@ __global__ __launch_bounds__(64 * kWaves) void w4a8_gemm_kernel(
             return;
     }
 
-    // the row scales of this lane's rows, loaded before the first store (loaded next to
-    // each store, a load could wait behind the stores issued before it)
+    // Epilogue through LDS: the lanes write their rounded outputs (4 adjacent columns
+    // of one row each) into the free ring as a row-major [BM][BN] tile, rows padded by
+    // 16 bytes (16 rows of a fragment then fall on different banks), and the waves then
+    // store whole rows, 16 bytes per lane and 1 KiB per instruction. (Stored straight
+    // from the fragments, each wave wrote half of every 128-byte line it touched, and
+    // lines evicted between the two halves were written twice: 1.49x the output
+    // bytes on the LM head.)
+    constexpr int BN = 16 * CBW * kWaves;
+    constexpr int kRowBytes = BN * 2 + 16;
+    static_assert((size_t)BM * kRowBytes <= kStages * sizeof(StageT), "the output tile fits in the ring");
+    uint8_t* otile = reinterpret_cast<uint8_t*>(&ring[0]);
+    lds_barrier();                           // every wave is done with the ring's operands
+    // the row scales of this lane's rows
     float rs[MR];
 #pragma unroll
     for (int r = 0; r < MR; ++r) rs[r] = m0 + 16 * r + c < M ? row_scale[m0 + 16 * r + c] : 0.f;
 #pragma unroll
     for (int j = 0; j < CBW; ++j) {
-        if (nbw + j >= NB) continue;
-        const int n = (nbw + j) * kColsPerBlock + 4 * h;
-        if (n >= N) continue;                  // zero padding of a last half block
+        const int col = 16 * (w * CBW + j) + 4 * h;        // in the tile
+        const int n = (nbw + j) * kColsPerBlock + 4 * h;   // in y
         float bv[4] = {0.f, 0.f, 0.f, 0.f};
-        if (bias) {
+        if (bias && n < N) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) bv[e] = half_bits_to_f32<kBF16>(bias[n + e]);
         }
 #pragma unroll
         for (int r = 0; r < MR; ++r) {
-            const int m = m0 + 16 * r + c;
-            if (m < M) {
-                const float a = rs[r];
-                const f32x4 v = acc[r][j];
-                const uint2 o = make_uint2(pack2_rne<kBF16>(fmaf(a, v[0], bv[0]), fmaf(a, v[1], bv[1])),
-                                           pack2_rne<kBF16>(fmaf(a, v[2], bv[2]), fmaf(a, v[3], bv[3])));
-                *reinterpret_cast<uint2*>(y + (size_t)m * N + n) = o;
-            }
+            const float a = rs[r];
+            const f32x4 v = acc[r][j];
+            const uint2 o = make_uint2(pack2_rne<kBF16>(fmaf(a, v[0], bv[0]), fmaf(a, v[1], bv[1])),
+                                       pack2_rne<kBF16>(fmaf(a, v[2], bv[2]), fmaf(a, v[3], bv[3])));
+            *reinterpret_cast<uint2*>(otile + (16 * r + c) * kRowBytes + 2 * col) = o;
         }
+    }
+    __syncthreads();
+    // rows past M and columns past N (the zero padding of a last half block, whole
+    // column blocks past the last) are not stored; N % 8 == 0, so a 16-byte chunk of 8
+    // columns lies wholly inside or outside
+    const int n0 = n_tile * BN;
+    for (int q = tid; q < BM * (BN / 8); q += 64 * kWaves) {
+        const int row = q / (BN / 8);
+        const int ch = q - row * (BN / 8);
+        const int m = m0 + row, n = n0 + 8 * ch;
+        if (m < M && n < N)
+            *reinterpret_cast<uint4*>(y + (size_t)m * N + n) = *reinterpret_cast<const uint4*>(otile + row * kRowBytes + 16 * ch);
     }
 }
 
