@@ -271,40 +271,49 @@ __global__ __launch_bounds__(64 * kWaves) void w4a8_gemm_kernel(
     }
 
     // zero-point term over this split's blocks: acc -= sum_kb (s z)[kb, n] * X[m, kb],
-    // as 16x16x4 fp32 MFMAs over groups of 4 blocks (lane group h takes block 4 t + h;
-    // blocks past the split's end contribute 0). The operands of kZeroBatch groups are
-    // loaded before any of their MFMAs, so the loads of a batch share one memory round
-    // trip (loaded group by group, each group waited for its own)
-    constexpr int kZeroBatch = 4;
-    for (int t0 = kb_begin; t0 < kb_end; t0 += 4 * kZeroBatch) {
-        float zs[kZeroBatch][CBW], xs[kZeroBatch][MR];
+    // as 16x16x4 fp32 MFMAs, in batches of 16 blocks: in batch t0, MFMA u takes block
+    // t0 + 4 h + u in lane group h (blocks past the split's end contribute 0). A lane's
+    // four blocks are consecutive, so where they are 16-byte aligned its four block sums
+    // of a row and four metadata words of a column come in one load each (18 loads per
+    // batch instead of 72 4-byte ones), all issued before the batch's MFMAs.
+    for (int t0 = kb_begin; t0 < kb_end; t0 += 16) {
+        const int kb4 = t0 + 4 * h;
+        const bool vec = ((KB | kb4) & 3) == 0 && kb4 + 3 < kb_end;    // UW % 4 == 0 always
+        float zs[4][CBW], xs[4][MR];
 #pragma unroll
-        for (int u = 0; u < kZeroBatch; ++u) {
-            const int kb = t0 + 4 * u + h;
-            const bool valid = kb < kb_end;
-            const int kbc = valid ? kb : kb_begin;
+        for (int j = 0; j < CBW; ++j) {
+            int n = (nbw + j) * kColsPerBlock + c;
+            n = n < Np ? n : Np - 1;
+            uint32_t md[4];
+            if (vec) {
+                const uint4 v = *reinterpret_cast<const uint4*>(meta_plane + (size_t)n * UW + kb4);
+                md[0] = v.x; md[1] = v.y; md[2] = v.z; md[3] = v.w;
+            } else {
 #pragma unroll
-            for (int j = 0; j < CBW; ++j) {
-                int n = (nbw + j) * kColsPerBlock + c;
-                n = n < Np ? n : Np - 1;
-                const uint32_t md = valid ? meta_plane[(size_t)n * UW + kbc] : 0u;
-                zs[u][j] = valid ? -half_bits_to_f32<kBF16>(md & 0xFFFFu) * (float)((md >> 16) & 0xFu) : 0.f;
+                for (int u = 0; u < 4; ++u) md[u] = kb4 + u < kb_end ? meta_plane[(size_t)n * UW + kb4 + u] : 0u;
             }
 #pragma unroll
-            for (int r = 0; r < MR; ++r) {
-                const int m = m0 + 16 * r + c < M ? m0 + 16 * r + c : M - 1;
-                xs[u][r] = valid ? block_sum[(size_t)m * KB + kbc] : 0.f;
+            for (int u = 0; u < 4; ++u)
+                zs[u][j] = kb4 + u < kb_end ? -half_bits_to_f32<kBF16>(md[u] & 0xFFFFu) * (float)((md[u] >> 16) & 0xFu) : 0.f;
+        }
+#pragma unroll
+        for (int r = 0; r < MR; ++r) {
+            const int m = m0 + 16 * r + c < M ? m0 + 16 * r + c : M - 1;
+            if (vec) {
+                const float4 v = *reinterpret_cast<const float4*>(block_sum + (size_t)m * KB + kb4);
+                xs[0][r] = v.x; xs[1][r] = v.y; xs[2][r] = v.z; xs[3][r] = v.w;
+            } else {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) xs[u][r] = kb4 + u < kb_end ? block_sum[(size_t)m * KB + kb4 + u] : 0.f;
             }
         }
 #pragma unroll
-        for (int u = 0; u < kZeroBatch; ++u) {
-            if (t0 + 4 * u >= kb_end) break;          // a group wholly past the end adds nothing
+        for (int u = 0; u < 4; ++u)
 #pragma unroll
             for (int r = 0; r < MR; ++r)
 #pragma unroll
                 for (int j = 0; j < CBW; ++j)
                     acc[r][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(zs[u][j], xs[u][r], acc[r][j], 0, 0, 0);
-        }
     }
 
     // (tiles of more than 16 fragments per wave are only planned for outputs that need no
