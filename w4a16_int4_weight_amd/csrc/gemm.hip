@@ -47,15 +47,24 @@ __device__ __forceinline__ uint32_t pick(const uint4 v, int i) {
 }
 
 
-// One stage of the LDS ring: the activation tile of one 128-row block of K, the
-// workgroup's blocks of packed codes (W waves x CBW) and its metadata words (64 per
-// wave, of which the first 16 * CBW are used).
+// One stage of the LDS ring: the activation tile of one 128-row block of K and the
+// workgroup's blocks of packed codes (W waves x CBW).
 template <int BM, int CBW, int W, int kSub>
 struct Stage {
     // [BM rows][16 chunks of 16 bytes], chunk j of row r stored at chunk j ^ (r % 16)
     uint4 x[BM * 16];
     uint4 w[W * CBW * 64];                  // 1 KiB per block, as in global memory
-    uint32_t meta[kSub * W * 64];           // [unit of the k block][wave][lane]
+};
+
+// Metadata of 4 consecutive k blocks ("a group") for the 16 CBW columns of one wave:
+// per column its 4 kSub unit words, which are contiguous in the packed layout, so the
+// group is copied with CBW kSub 4-byte copies whose lanes cover 16 columns each (16
+// cache lines per copy). (One copy per k block, each lane reading one word of its own
+// column, touched 32 lines per copy for 256 useful bytes: dropping those copies alone
+// made the LM-head GEMM ~8% faster.)
+template <int CBW, int kSub>
+struct MetaGroup {
+    uint32_t words[16 * CBW * 4 * kSub];    // [column of the wave][unit of the group]
 };
 
 // Workgroup tile: 16*MR rows x 64*CBW columns, 4 waves side by side along N, each
@@ -70,10 +79,14 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(
     constexpr int BM = 16 * MR;
     constexpr int kSlabsPerWave = BM / 4 / kWaves;      // 1 KiB slabs (4 rows) of the x tile per wave
     static_assert(kSlabsPerWave * 4 * kWaves == BM, "x tile must split over the waves");
-    constexpr int kDmaPerStage = kSlabsPerWave + CBW + kSub;   // copies per wave per stage
+    constexpr int kDmaPerStage = kSlabsPerWave + CBW;          // copies per wave per stage
+    constexpr int kMetaDma = CBW * kSub;                        // + these in a group's first stage
     constexpr int kStages = 3;
     using StageT = Stage<BM, CBW, kWaves, kSub>;
+    using MetaT = MetaGroup<CBW, kSub>;
+    static_assert(sizeof(MetaT) == (size_t)kMetaDma * 256, "a group is whole 4-byte copies");
     __shared__ StageT ring[kStages];
+    __shared__ MetaT mring[2][kWaves];       // group g of this split in slot g % 2
 
     // XCD-aware order: ids id, id+8, id+16, ... share an XCD; they take the M tiles and
     // the K splits of one N tile. Ids past the last N tile (grid padding) exit.
@@ -124,12 +137,14 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(
         const int nbj = nbw + j < NB ? nbw + j : NB - 1;
         woff[j] = (uint32_t)(nbj - nbw0) * (uint32_t)KB * kBlockBytes + 16u * (uint32_t)lane;
     }
-    // metadata: column words of this wave's columns (lanes past 16 * CBW repeat one)
+    // metadata: word 64 i + lane of a group's copy i is column (64 i + lane) / (4 kSub)
+    // of the wave and unit (64 i + lane) % (4 kSub) of the group, columns past the last
+    // reading the last, units past the column's last word reading that word (they feed
+    // only outputs or k blocks that do not count)
     const int col0 = nbw * kColsPerBlock < Np ? nbw * kColsPerBlock : Np - kColsPerBlock;
-    const int ncol = nbw * kColsPerBlock + (lane < 16 * CBW ? lane : 0);
     const uint8_t* mbase = uniform_ptr(packed + (size_t)K * Np / 2 + (size_t)col0 * UW * 4);
-    const uint32_t moff = (uint32_t)((ncol < Np ? ncol : Np - 1) - col0) * (uint32_t)UW * 4u;
     const uint32_t ring_base = lds_addr(&ring[0]);
+    const uint32_t mring_base = lds_addr(&mring[0][w]);
 
     // copy q (0 .. kDmaPerStage-1) of k block kb into ring slot `slot`
     auto issue_one = [&](int slot, int kb, int q) {
@@ -140,13 +155,24 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(
         else if (q < kSlabsPerWave + CBW)
             dma16(wbase + (size_t)kb * kBlockBytes, woff[q - kSlabsPerWave],
                   st + (uint32_t)offsetof(StageT, w) + (uint32_t)(w * CBW + q - kSlabsPerWave) * 1024u);
-        else
-            dma4(mbase + ((size_t)kb * kSub + (q - kSlabsPerWave - CBW)) * 4, moff,
-                 st + (uint32_t)offsetof(StageT, meta) + (uint32_t)((q - kSlabsPerWave - CBW) * kWaves + w) * 256u);
     };
-    auto issue = [&](int slot, int kb) {
+    // stage t (k block kb_begin + t); a group's first stage also copies the group's
+    // metadata into slot (t / 4) % 2
+    auto issue = [&](int slot, int t) {
+        const int kb = kb_begin + t;
 #pragma unroll
         for (int q = 0; q < kDmaPerStage; ++q) issue_one(slot, kb, q);
+        if ((t & 3) == 0) {
+            const uint32_t dst = mring_base + (uint32_t)((t >> 2) & 1) * (uint32_t)(kWaves * sizeof(MetaT));
+#pragma unroll
+            for (int i = 0; i < kMetaDma; ++i) {
+                const int wi = 64 * i + lane;
+                const int cl = wi / (4 * kSub), u = wi % (4 * kSub);
+                const int n = nbw * kColsPerBlock + cl < Np ? nbw * kColsPerBlock + cl : Np - 1;
+                const int ua = kb * kSub + u < UW ? kb * kSub + u : UW - 1;
+                dma4(mbase, ((uint32_t)(n - col0) * (uint32_t)UW + (uint32_t)ua) * 4u, dst + (uint32_t)i * 256u);
+            }
+        }
     };
 
     f32x4 acc[MR][CBW];
@@ -155,19 +181,22 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(
 #pragma unroll
         for (int j = 0; j < CBW; ++j) acc[r][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    issue(0, kb_begin);
-    if (nkb > 1) issue(1, kb_begin + 1);
+    issue(0, 0);
+    if (nkb > 1) issue(1, 1);
     for (int t = 0; t < nkb; ++t) {
-        // this wave's copies of step t are done (step t+1's may be in flight); the
-        // barrier makes every wave's copies visible and retires the reads of step
-        // t-1, whose slot is then refilled with step t+2
-        if (t + 1 < nkb) wait_vmcnt<kDmaPerStage>();
-        else wait_vmcnt<0>();
+        // this wave's copies of step t are done (step t+1's may be in flight: one more
+        // per metadata copy when t+1 starts a group); the barrier makes every wave's
+        // copies visible and retires the reads of step t-1, whose slot is then refilled
+        // with step t+2 (a group's metadata slot is refilled at step 4g + 6, after every
+        // wave has passed the group's last step 4g + 3)
+        if (t + 1 >= nkb) wait_vmcnt<0>();
+        else if (((t + 1) & 3) == 0) wait_vmcnt<kDmaPerStage + kMetaDma>();
+        else wait_vmcnt<kDmaPerStage>();
         lds_barrier();
         // The copies queue at the CU's address unit (about 16 cycles per 1 KiB copy, the
         // 4 waves' together) and each wave waits until its own are accepted: about a
         // sixth of the loop. Spreading them between the MFMAs measured slower.
-        if (t + 2 < nkb) issue((t + 2) % kStages, kb_begin + t + 2);
+        if (t + 2 < nkb) issue((t + 2) % kStages, t + 2);
 
         const StageT& st = ring[t % kStages];
         Dequant<kBF16> dq[CBW][kSub];           // per column block and metadata unit
@@ -175,7 +204,8 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(
 #pragma unroll
         for (int j = 0; j < CBW; ++j) {
 #pragma unroll
-            for (int v = 0; v < kSub; ++v) dq[j][v] = Dequant<kBF16>(st.meta[(v * kWaves + w) * 64 + 16 * j + c]);
+            for (int v = 0; v < kSub; ++v)
+                dq[j][v] = Dequant<kBF16>(mring[(t >> 2) & 1][w].words[(16 * j + c) * 4 * kSub + (t & 3) * kSub + v]);
             wq[j] = st.w[(w * CBW + j) * 64 + lane];
         }
         if constexpr (kBF16) {
