@@ -110,13 +110,21 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(const uint16_t*
 // ---------------------------------------------------------------- GEMM
 
 // One stage of the LDS ring: the fp8 activation tile of one 128-row block of K
-// (16-byte chunk j of row r stored at chunk j ^ row_swizzle(r)), the workgroup's
-// blocks of packed codes and its metadata words (64 per wave, the first 16 * CBW used).
-template <int BM, int CBW, int W>
+// (16-byte chunk j of row r stored at chunk j ^ row_swizzle(r)) and the workgroup's
+// blocks of packed codes.
+template <int BM, int CBW, int W, bool kGroupMeta>
 struct StageA8 {
     uint4 x[BM * 8];
     uint4 w[W * CBW * 64];
-    uint32_t meta[W * 64];
+    uint32_t meta[kGroupMeta ? 1 : W * 64];  // per-stage metadata of small tiles (64 per wave)
+};
+
+// Metadata of 4 consecutive k blocks for the 16 CBW columns of one wave, per column its
+// 4 words (contiguous in the packed layout): CBW 4-byte copies of 16 columns each, with
+// the group's first stage, instead of one copy per k block touching a line per lane.
+template <int CBW>
+struct MetaGroupA8 {
+    uint32_t words[16 * CBW * 4];           // [column of the wave][k block of the group]
 };
 
 // XOR applied to the chunk index of row r of the activation tile. A fragment read
@@ -149,10 +157,18 @@ __global__ __launch_bounds__(64 * kWaves) void w4a8_gemm_kernel(
     constexpr int kXCopyBytes = kXSlabs ? 1024 : 256;
     constexpr int kXPerWave = kXBytes / kXCopyBytes / kWaves;
     static_assert(kXPerWave >= 1 && kXPerWave * kXCopyBytes * kWaves == kXBytes, "x tile must split over the waves");
-    constexpr int kDmaPerStage = kXPerWave + CBW + 1;
+    // tiles of 8 or more fragments per wave copy their metadata 4 k blocks at a time
+    // (LM head 182 -> 175-177 us); smaller ones one k block at a time (qkv 12.4 us
+    // against 13.3-13.7 us grouped)
+    constexpr bool kGroupMeta = MR * CBW >= 8;
+    constexpr int kDmaPerStage = kXPerWave + CBW + (kGroupMeta ? 0 : 1);   // + kMetaDma in a group's first stage
+    constexpr int kMetaDma = kGroupMeta ? CBW : 0;
     constexpr int kStages = 3;
-    using StageT = StageA8<BM, CBW, kWaves>;
+    using StageT = StageA8<BM, CBW, kWaves, kGroupMeta>;
     __shared__ StageT ring[kStages];
+    using MetaT = MetaGroupA8<CBW>;
+    static_assert(!kGroupMeta || sizeof(MetaT) == (size_t)kMetaDma * 256, "a group is whole 4-byte copies");
+    __shared__ MetaT mring[kGroupMeta ? 2 : 1][kGroupMeta ? kWaves : 1];  // group g in slot g % 2
 
     const int id = blockIdx.x;
     const int local = id / kXcds;
@@ -199,13 +215,22 @@ __global__ __launch_bounds__(64 * kWaves) void w4a8_gemm_kernel(
         woff[j] = (uint32_t)(nbj - nbw0) * (uint32_t)KB * kBlockBytes + 16u * (uint32_t)lane;
     }
     const uint32_t* meta_plane = reinterpret_cast<const uint32_t*>(packed + (size_t)K * Np / 2);
+    // metadata copies: word 64 i + lane of copy i is column (64 i + lane) / 4 of the
+    // wave and k block (64 i + lane) % 4 of the group (16 columns, so 16 cache lines, per
+    // copy; ordered k block first it would be 32 lines per copy with two column blocks
+    // per wave, measured slower); columns past the last read the last, blocks past the
+    // column's last word read that word
     const int col0 = nbw * kColsPerBlock < Np ? nbw * kColsPerBlock : Np - kColsPerBlock;
-    const int ncol = nbw * kColsPerBlock + (lane < 16 * CBW ? lane : 0);
     const uint8_t* mbase = uniform_ptr(meta_plane + (size_t)col0 * UW);
-    const uint32_t moff = (uint32_t)((ncol < Np ? ncol : Np - 1) - col0) * (uint32_t)UW * 4u;
     const uint32_t ring_base = lds_addr(&ring[0]);
+    const uint32_t mring_base = lds_addr(&mring[0][kGroupMeta ? w : 0]);
+    const int ncol = nbw * kColsPerBlock + (lane < 16 * CBW ? lane : 0);   // per-stage copies
+    const uint32_t moff = (uint32_t)((ncol < Np ? ncol : Np - 1) - col0) * (uint32_t)UW * 4u;
 
-    auto issue = [&](int slot, int kb) {
+    // stage t (k block kb_begin + t); a group's first stage also copies the group's
+    // metadata into slot (t / 4) % 2
+    auto issue = [&](int slot, int t) {
+        const int kb = kb_begin + t;
         const uint32_t st = ring_base + (uint32_t)slot * (uint32_t)sizeof(StageT);
 #pragma unroll
         for (int t = 0; t < kXPerWave; ++t) {
@@ -217,7 +242,19 @@ __global__ __launch_bounds__(64 * kWaves) void w4a8_gemm_kernel(
         for (int j = 0; j < CBW; ++j)
             dma16(wbase + (size_t)kb * kBlockBytes, woff[j],
                   st + (uint32_t)offsetof(StageT, w) + (uint32_t)(w * CBW + j) * 1024u);
-        dma4(mbase + (size_t)kb * 4, moff, st + (uint32_t)offsetof(StageT, meta) + (uint32_t)w * 256u);
+        if constexpr (!kGroupMeta)
+            dma4(mbase + (size_t)kb * 4, moff, st + (uint32_t)offsetof(StageT, meta) + (uint32_t)w * 256u);
+        if (kGroupMeta && (t & 3) == 0) {
+            const uint32_t dst = mring_base + (uint32_t)((t >> 2) & 1) * (uint32_t)(kWaves * sizeof(MetaT));
+#pragma unroll
+            for (int i = 0; i < kMetaDma; ++i) {
+                const int wi = 64 * i + lane;
+                const int cl = wi >> 2, u = wi & 3;
+                const int n = nbw * kColsPerBlock + cl < Np ? nbw * kColsPerBlock + cl : Np - 1;
+                const int ua = kb + u < UW ? kb + u : UW - 1;
+                dma4(mbase, ((uint32_t)(n - col0) * (uint32_t)UW + (uint32_t)ua) * 4u, dst + (uint32_t)i * 256u);
+            }
+        }
     };
 
     f32x4 acc[MR][CBW];
@@ -226,13 +263,17 @@ __global__ __launch_bounds__(64 * kWaves) void w4a8_gemm_kernel(
 #pragma unroll
         for (int j = 0; j < CBW; ++j) acc[r][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    if (nkb > 0) issue(0, kb_begin);
-    if (nkb > 1) issue(1, kb_begin + 1);
+    if (nkb > 0) issue(0, 0);
+    if (nkb > 1) issue(1, 1);
     for (int t = 0; t < nkb; ++t) {
-        if (t + 1 < nkb) wait_vmcnt<kDmaPerStage>();
-        else wait_vmcnt<0>();
+        // leave step t+1's copies in flight (its metadata copies too when it starts a
+        // group); a group's metadata slot is refilled at step 4g + 6, after every wave
+        // has passed the group's last step 4g + 3
+        if (t + 1 >= nkb) wait_vmcnt<0>();
+        else if (((t + 1) & 3) == 0) wait_vmcnt<kDmaPerStage + kMetaDma>();
+        else wait_vmcnt<kDmaPerStage>();
         lds_barrier();
-        if (t + 2 < nkb) issue((t + 2) % kStages, kb_begin + t + 2);
+        if (t + 2 < nkb) issue((t + 2) % kStages, t + 2);
 
         const StageT& st = ring[t % kStages];
         // 512 s for this lane's 4 columns of each column block
@@ -240,11 +281,17 @@ __global__ __launch_bounds__(64 * kWaves) void w4a8_gemm_kernel(
         i32x8 b[CBW];
 #pragma unroll
         for (int j = 0; j < CBW; ++j) {
-            const uint4 md = *reinterpret_cast<const uint4*>(&st.meta[w * 64 + 16 * j + 4 * h]);
-            sc[j][0] = 512.f * half_bits_to_f32<kBF16>(md.x & 0xFFFFu);
-            sc[j][1] = 512.f * half_bits_to_f32<kBF16>(md.y & 0xFFFFu);
-            sc[j][2] = 512.f * half_bits_to_f32<kBF16>(md.z & 0xFFFFu);
-            sc[j][3] = 512.f * half_bits_to_f32<kBF16>(md.w & 0xFFFFu);
+            if constexpr (kGroupMeta) {
+                const uint32_t* mw = &mring[(t >> 2) & 1][w].words[(16 * j + 4 * h) * 4 + (t & 3)];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sc[j][e] = 512.f * half_bits_to_f32<kBF16>(mw[4 * e] & 0xFFFFu);
+            } else {
+                const uint4 md = *reinterpret_cast<const uint4*>(&st.meta[w * 64 + 16 * j + 4 * h]);
+                sc[j][0] = 512.f * half_bits_to_f32<kBF16>(md.x & 0xFFFFu);
+                sc[j][1] = 512.f * half_bits_to_f32<kBF16>(md.y & 0xFFFFu);
+                sc[j][2] = 512.f * half_bits_to_f32<kBF16>(md.z & 0xFFFFu);
+                sc[j][3] = 512.f * half_bits_to_f32<kBF16>(md.w & 0xFFFFu);
+            }
             // codes -> E4M3 bytes q * 2^-9: word i gives bytes 8 i .. 8 i + 7 (rows 0,4,1,5 | 2,6,3,7)
             const uint4 wq = st.w[(w * CBW + j) * 64 + lane];
             b[j] = i32x8{(int)(wq.x & 0x0F0F0F0Fu), (int)((wq.x >> 4) & 0x0F0F0F0Fu),
