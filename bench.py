@@ -97,6 +97,40 @@ def time_graph(fn_list, warmup):
     return start.elapsed_time(end), len(fn_list)
 
 
+def time_graphs_alternating(fn_lists, warmup, rounds=3):
+    """Captures one graph per call list, replays each once untimed, then times
+    `rounds` replays of each in alternation (a, b, a, b, ...) so that the entries
+    compared see the same clock and power state. Returns the median ms of each."""
+    import statistics
+    import torch
+    graphs = []
+    for fns in fn_lists:
+        for i in range(warmup):
+            fns[i % len(fns)]()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for fn in fns:
+                fn()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        graphs.append(g)
+    stream = torch.cuda.current_stream()
+    times = [[] for _ in graphs]
+    for _ in range(rounds):
+        for j, g in enumerate(graphs):
+            start = torch.cuda.Event(enable_timing=True)
+            end = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            start.record(stream)
+            g.replay()
+            end.record(stream)
+            torch.cuda.synchronize()
+            times[j].append(start.elapsed_time(end))
+    return [statistics.median(t) for t in times]
+
+
 def measure_gemm(w, workload, M, steps, warmup, dev, path="auto"):
     import torch
     import synth
@@ -144,11 +178,11 @@ def measure_w4a8(w, workload, M, steps, warmup, dev):
     act = w.w4a8_quantize(x)
     y = torch.empty((M, N), dtype=x.dtype, device=dev)
     gemm_calls = [(lambda p=packs[i % copies]: w.w4a8_gemm(act, p, M, K, N, G, x.dtype, y=y)) for i in range(steps)]
-    ms, n = time_graph(gemm_calls, warmup)
-    gemm_s = ms / 1e3 / n
     step_calls = [(lambda p=packs[i % copies]: w.w4a8_linear(x, p, N, G, y=y, act=act)) for i in range(steps)]
-    ms, n = time_graph(step_calls, warmup)
-    step_s = ms / 1e3 / n
+    gemm_ms, step_ms = time_graphs_alternating([gemm_calls, step_calls], warmup)
+    n = steps
+    gemm_s = gemm_ms / 1e3 / n
+    step_s = step_ms / 1e3 / n
     flops = 2 * M * N * K
     del packs, packed0
     torch.cuda.empty_cache()
