@@ -168,10 +168,14 @@ w4a16_status w4a16_parse_packed_header(const void* header, size_t header_bytes, 
  * (fp32) and one counter per output tile live there. Independent of the path that
  * w4a16_gemm_ex would choose: the value suffices for every path.
  *
+ * Layout: its first 512 bytes hold the tile counters for every shape (a split plan
+ * has fewer than 128 output tiles), the partial sums follow.
+ *
  * Contract: the workspace must be zero-filled before its first use and is left
- * zero-filled (in its counter part) by every call, so one zeroed allocation can be
- * reused by consecutive calls on one stream. Calls that overlap in time (different
- * streams) need different workspaces. 16-byte alignment. */
+ * zero-filled (in its counter part) by every call, so one zeroed allocation as large
+ * as the largest requirement can be reused by consecutive calls of any shapes on one
+ * stream, W4A8 calls included. Calls that overlap in time (different streams) need
+ * different workspaces. 16-byte alignment. */
 size_t w4a16_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t group_size);
 
 /* y = x . dequant(W) (+ bias), from a buffer written by w4a16_repack

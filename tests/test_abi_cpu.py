@@ -63,6 +63,12 @@ def test_layout_version_and_sizes(w):
     assert w.w4a16_workspace_bytes(512, 2048, 13312, 128) == 0
     ws = w.w4a16_workspace_bytes(16, 6656, 2048, 128)
     assert ws > 16 * 2048 * 4 and ws % 4 == 0
+    # a split plan's workspace: 128 tile counters (512 bytes) whatever its tile count,
+    # then fp32 partial tiles of 16 x 64 per tile and split (32 tiles x 8 splits here;
+    # 96 tiles x 3 splits at N = 6144, K = 2048), so no shape's partials overlap
+    # another shape's counters
+    assert ws == 512 + 8 * 32 * 16 * 64 * 4
+    assert w.w4a16_workspace_bytes(16, 2048, 6144, 128) == 512 + 3 * 96 * 16 * 64 * 4
     assert w.w4a16_workspace_bytes(16, 6656, 2048, 96) == 0          # invalid group size
     # sized for the MFMA GEMM, which any M may be sent to; the GEMV needs none
     assert w.w4a16_workspace_bytes(1, 2048, 131072, 128) == 0

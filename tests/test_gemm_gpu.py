@@ -229,9 +229,49 @@ def test_split_k_workspace_is_reused_and_left_zero(w):
     y2 = w.w4a16_gemm_ex(bits_to_device(ws2.x_bits[40], "bf16"), packed2, 96, 128, workspace=work, path="mfma")
     torch.cuda.synchronize()
     assert ogemm.max_rel_error(y_to_f64(y2, "bf16"), oracle_y(ws2, ws2.x_bits[40])) <= TOL
-    # the counter part of the workspace is zero again
-    tiles_bytes = 256
-    assert int(work[:tiles_bytes].count_nonzero()) == 0
+    # the counter part of the workspace (one fixed 512-byte region) is zero again
+    assert int(work[:512].count_nonzero()) == 0
+
+
+def test_split_k_workspace_shared_across_growing_shapes(w):
+    # one zeroed workspace serves split-K calls of different shapes in any order: a
+    # call with 32 output tiles (K split 8 ways) leaves fp32 partials behind its
+    # counters, and a later call with 96 tiles (split 3 ways) and the W4A8 GEMM on
+    # that shape must still find all of their counters at zero. Each result agrees
+    # bit for bit with the same call on a fresh workspace.
+    shapes = [(16, 6656, 2048), (16, 2048, 6144)]
+    needs = [w.w4a16_workspace_bytes(M, K, N, 128) for M, K, N in shapes]
+    assert all(n > 0 for n in needs)
+    assert w.w4a8_workspace_bytes(16, 2048, 6144, 128) == needs[1]
+    cases = []
+    for seed, (M, K, N) in zip((120, 121), shapes):
+        ws = synth.make_custom(seed, M, K, N, "bf16", 128)
+        cases.append((ws, pack_on_gpu(w, ws), bits_to_device(ws.x_bits[M], "bf16")))
+
+    def w4a16(i, work):
+        ws, packed, x = cases[i]
+        return device_to_bits(w.w4a16_gemm_ex(x, packed, ws.N, 128, workspace=work, path="mfma"))
+
+    def w4a8(i, work):
+        ws, packed, x = cases[i]
+        M, K, N = shapes[i]
+        act = w.w4a8_quantize(x)
+        return device_to_bits(w.w4a8_gemm(act, packed, M, K, N, 128, torch.bfloat16, workspace=work))
+
+    fresh = lambda n: torch.zeros(n, dtype=torch.uint8, device=DEV)
+    want = [w4a16(0, fresh(needs[0])), w4a16(1, fresh(needs[1])), w4a8(1, fresh(needs[1]))]
+    torch.cuda.synchronize()
+    for i in (0, 1):
+        ws = cases[i][0]
+        got = numerics.half_bits_to_f64(want[i], "bf16")
+        assert ogemm.max_rel_error(got, oracle_y(ws, ws.x_bits[shapes[i][0]])) <= TOL
+    shared = fresh(max(needs))
+    order = [("w4a16", 0), ("w4a16", 1), ("w4a8", 1), ("w4a16", 0), ("w4a8", 1), ("w4a16", 1)]
+    for kind, i in order:
+        got = w4a16(i, shared) if kind == "w4a16" else w4a8(i, shared)
+        torch.cuda.synchronize()
+        assert np.array_equal(got, want[i] if kind == "w4a16" else want[2]), (kind, shapes[i])
+    assert int(shared[:512].count_nonzero()) == 0
 
 
 def test_split_k_default_workspace_per_stream(w):

@@ -450,6 +450,7 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G) {
     const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
     // too few tiles for the chip: split K, at least 4 row blocks per split
     p.splits = 1;
+    static_assert(kTargetWorkgroups / 2 <= kMaxSplitTiles, "split tiles must fit the counter region");
     if (tiles < kTargetWorkgroups / 2 && KB >= 8) {
         const int64_t want = (kTargetWorkgroups + tiles - 1) / tiles;
         const int64_t most = KB / 4;
@@ -457,9 +458,8 @@ GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G) {
     }
     p.workspace_bytes = 0;
     if (p.splits > 1) {
-        const size_t counters = ((size_t)tiles * 4 + 255) / 256 * 256;
         // fp32 partial tiles: splits x tiles x (16 mr) x (16 waves cbw)
-        p.workspace_bytes = counters + (size_t)p.splits * (size_t)tiles * (size_t)(16 * p.mr) *
+        p.workspace_bytes = kSplitCounterBytes + (size_t)p.splits * (size_t)tiles * (size_t)(16 * p.mr) *
                                            (size_t)(16 * p.waves * p.cbw) * 4;
     }
     return p;
@@ -472,8 +472,7 @@ hipError_t launch_gemm(const uint16_t* x, const uint8_t* packed, const uint16_t*
     uint32_t* counters = static_cast<uint32_t*>(workspace);
     float* partials = nullptr;
     if (p.splits > 1) {
-        const size_t counter_bytes = ((size_t)p.tiles_m * p.tiles_n * 4 + 255) / 256 * 256;
-        partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + counter_bytes);
+        partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + kSplitCounterBytes);
     }
     if (bf16) launch_typed<true>(p, x, packed, bias, y, (int)M, (int)K, (int)N, counters, partials, stream);
     else launch_typed<false>(p, x, packed, bias, y, (int)M, (int)K, (int)N, counters, partials, stream);

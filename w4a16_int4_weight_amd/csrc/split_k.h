@@ -6,6 +6,14 @@
 
 namespace w4a16 {
 
+// Workspace of a K split: kMaxSplitTiles 32-bit counters, then the fp32 partial
+// tiles. Plans split K only when the output has fewer than kMaxSplitTiles tiles, and
+// the counter region has this one size for every shape, so no call's partials land
+// where another call keeps its counters: one zeroed workspace serves consecutive
+// calls of any shape (the counters are zero again when a call ends).
+constexpr int kMaxSplitTiles = 128;
+constexpr size_t kSplitCounterBytes = (size_t)kMaxSplitTiles * sizeof(uint32_t);
+
 // acc: this workgroup's partial tile, MR x CBW fragments per wave in the lanes' own
 // order. Returns true in the one workgroup that then holds the tile's full sum in
 // acc (the others return false and must exit); the sum is taken in split order, so

@@ -501,8 +501,7 @@ hipError_t launch_w4a8_gemm(const W4A8Act& a, const uint8_t* packed, const uint1
     uint32_t* counters = static_cast<uint32_t*>(workspace);
     float* partials = nullptr;
     if (p.splits > 1) {
-        const size_t counter_bytes = ((size_t)p.tiles_m * p.tiles_n * 4 + 255) / 256 * 256;
-        partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + counter_bytes);
+        partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + kSplitCounterBytes);
     }
     if (bf16) launch_typed<true>(p, a, packed, bias, y, (int)M, (int)K, (int)N, counters, partials, stream);
     else launch_typed<false>(p, a, packed, bias, y, (int)M, (int)K, (int)N, counters, partials, stream);
