@@ -205,6 +205,27 @@ def test_gemm_rejects_bad_calls(w):
     assert e.value.status == "W4A16_ERR_GROUP"
 
 
+@pytest.mark.parametrize("M,K,N,path", [
+    (8, 2048, 20480, "gemv"),      # M <= 8: the GEMV at every size
+    (9, 2048, 20480, "mfma"),      # 20 MiB of codes: the MFMA GEMM from M = 9
+    (12, 2048, 13312, "gemv"),     # 13 MiB: the GEMV through M = 12
+    (13, 2048, 13312, "mfma"),
+    (15, 2048, 3072, "gemv"),      # 3 MiB: the GEMV through M = 15
+    (16, 2048, 3072, "mfma"),      # M >= 16: the MFMA GEMM at every size
+])
+def test_default_dispatch_follows_weight_size(w, M, K, N, path):
+    ws = synth.make_custom(130 + M, M, K, N, "bf16", 128)
+    packed = pack_on_gpu(w, ws)
+    x = bits_to_device(ws.x_bits[M], "bf16")
+    auto = device_to_bits(w.w4a16_gemm(x, packed, N, 128))
+    forced = device_to_bits(w.w4a16_gemm_ex(x, packed, N, 128, path=path))
+    torch.cuda.synchronize()
+    assert np.array_equal(auto, forced), (M, K, N, path)
+    if N == 3072:
+        ref = oracle_y(ws, ws.x_bits[M])
+        assert ogemm.max_rel_error(numerics.half_bits_to_f64(auto, "bf16"), ref) <= TOL
+
+
 def test_split_k_workspace_is_reused_and_left_zero(w):
     # a skinny shape whose MFMA GEMM splits K over workgroups: three calls on one
     # zeroed workspace must agree bit for bit (the tile counters are reset each call),

@@ -15,6 +15,19 @@ namespace {
 constexpr int kLayoutVersion = 2;
 constexpr int64_t kGemvMaxRows = 16;      // rows one GEMV A operand holds
 constexpr int64_t kDefaultGemvMaxM = 8;
+
+// Default split between the GEMV and the MFMA GEMM. M <= 8 takes the GEMV and M >= 16
+// the MFMA GEMM at every shape; in between, the GEMV stays ahead the longer the
+// smaller the weight is (MI355X, G = 128, bf16: through M = 15 at K x N = 2048 x 3072,
+// through 13 at 2048 x 13312, through 12 at 6656 x 2048, and behind already at M = 8
+// at 2048 x 131072), so the last GEMV row count follows the size of the codes.
+int64_t default_gemv_max_m(int64_t K, int64_t N, int64_t G) {
+    if (G % 128 != 0) return kDefaultGemvMaxM;        // group sizes 32, 64: not measured
+    const int64_t code_bytes = K * N / 2;
+    if (code_bytes <= (int64_t(4) << 20)) return 15;
+    if (code_bytes <= (int64_t(16) << 20)) return 12;
+    return kDefaultGemvMaxM;
+}
 constexpr int kMaxDevices = 64;
 constexpr int64_t kMaxK = int64_t(1) << 20;   // kernels index rows and columns with 32-bit integers
 constexpr int64_t kMaxN = int64_t(1) << 28;
@@ -84,7 +97,7 @@ w4a16_status gemm_impl(const void* x, const void* packed, size_t packed_bytes, w
     if (st != W4A16_OK) return st;
     if (dtype != W4A16_FP16 && dtype != W4A16_BF16) return W4A16_ERR_DTYPE;
     if (path != W4A16_PATH_AUTO && path != W4A16_PATH_GEMV && path != W4A16_PATH_MFMA) return W4A16_ERR_PATH;
-    if (gemv_max_m < 0) gemv_max_m = kDefaultGemvMaxM;
+    if (gemv_max_m < 0) gemv_max_m = default_gemv_max_m(K, N, G);
     if (gemv_max_m > kGemvMaxRows) return W4A16_ERR_PATH;
     if (path == W4A16_PATH_GEMV && M > kGemvMaxRows) return W4A16_ERR_PATH;
     if (M >= (int64_t(1) << 31) || M * K > kMaxMK) return W4A16_ERR_SHAPE;
@@ -190,7 +203,7 @@ w4a16_status w4a16_gemm(const void* x, const void* packed, size_t packed_bytes, 
                         int64_t M, int64_t K, int64_t N, int64_t group_size, const void* bias, void* workspace,
                         size_t workspace_bytes, void* stream) {
     return gemm_impl(x, packed, packed_bytes, dtype, y, M, K, N, group_size, bias, workspace, workspace_bytes,
-                     stream, W4A16_PATH_AUTO, kDefaultGemvMaxM);
+                     stream, W4A16_PATH_AUTO, -1);
 }
 
 w4a16_status w4a16_gemm_ex(const void* x, const void* packed, size_t packed_bytes, w4a16_dtype dtype, void* y,
