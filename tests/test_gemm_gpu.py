@@ -352,14 +352,16 @@ def test_gemv_needs_no_workspace(w):
     assert ogemm.max_rel_error(y_to_f64(y, "bf16"), oracle_y(ws, ws.x_bits[8])) <= TOL
 
 
-@pytest.mark.parametrize("K,M,dtype", [(2048, 1, "bf16"), (2048, 8, "bf16"), (2048, 3, "fp16"),
-                                       (512, 2, "bf16"), (1024, 5, "bf16")])
-def test_gemv_several_column_blocks_per_workgroup(w, K, M, dtype):
-    # N = 13296 (831 column blocks) runs 2 blocks per workgroup: the last workgroup has
-    # a block past N, which repeats the last block and must store nothing. K = 512 has
-    # one wave per block (no K split), K = 1024 two.
-    print(f"gemv 2 blocks per workgroup K={K} M={M} {dtype}", flush=True)
-    N = 13296
+@pytest.mark.parametrize("K,M,N,dtype", [(2048, 1, 13296, "bf16"), (2048, 8, 13296, "bf16"),
+                                         (2048, 3, 13296, "fp16"), (512, 2, 13296, "bf16"),
+                                         (1024, 5, 13296, "bf16"), (1024, 4, 16400, "bf16"),
+                                         (1024, 8, 16400, "fp16")])
+def test_gemv_several_column_blocks_per_workgroup(w, K, M, N, dtype):
+    # N = 13296 (831 column blocks) runs 2 blocks per workgroup at every M, N = 16400
+    # (1025 blocks) from M = 4: the last workgroup has a block past N, which repeats
+    # the last block and must store nothing. K = 512 has one wave per block (no K
+    # split), K = 1024 two.
+    print(f"gemv 2 blocks per workgroup K={K} M={M} N={N} {dtype}", flush=True)
     ws = synth.make_custom(1000 + K // 128 + M, M, K, N, dtype, 128)
     packed = pack_on_gpu(w, ws)
     x = bits_to_device(ws.x_bits[M], dtype)

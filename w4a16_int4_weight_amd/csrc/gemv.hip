@@ -379,14 +379,17 @@ GemvPlan plan_gemv_with(int64_t M, int64_t K, int64_t N, int64_t G, int cols_per
     return p;
 }
 
-// Two column blocks per workgroup when N is mid-sized (at most 1024 blocks, at least
-// 400): fewer, larger workgroups per compute unit share one copy of the activations.
-// Measured on the 2048 x 13312 decode shape: M = 8 -9%, M = 4 -4%, M = 1 even; four
-// blocks per workgroup, or two for N = 131072 or N = 3072, measured slower.
+// Two column blocks per workgroup when there are at least 400 blocks and either N is
+// mid-sized (at most 1024 blocks) or M >= 4: the workgroups' copies of the
+// activations (M x K each) then serve twice the columns. Measured on the 2048 x 13312
+// decode shape: M = 8 -9%, M = 4 -4%, M = 1 even; on 2048 x 131072: M = 8 -18%
+// (45.5 -> 37.2 us), M = 12 -11%, M = 4 -5%, M = 1 and 2 even. Four blocks per
+// workgroup measured slower everywhere, and two on 2048 x 3072 (192 blocks).
 GemvPlan plan_gemv(int64_t M, int64_t K, int64_t N, int64_t G) {
     const int64_t NB = padded_cols(N) / kColsPerBlock;
     const GemvPlan one = plan_gemv_with(M, K, N, G, 1);
-    if (NB <= 1024 && NB / 2 >= 200 && 2 * one.waves_k <= max_waves(one.sub)) return plan_gemv_with(M, K, N, G, 2);
+    if ((NB <= 1024 || M >= 4) && NB / 2 >= 200 && 2 * one.waves_k <= max_waves(one.sub))
+        return plan_gemv_with(M, K, N, G, 2);
     return one;
 }
 
