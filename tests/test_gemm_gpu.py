@@ -205,22 +205,23 @@ def test_gemm_rejects_bad_calls(w):
     assert e.value.status == "W4A16_ERR_GROUP"
 
 
-@pytest.mark.parametrize("M,K,N,path", [
-    (8, 2048, 20480, "gemv"),      # M <= 8: the GEMV at every size
-    (9, 2048, 20480, "mfma"),      # 20 MiB of codes: the MFMA GEMM from M = 9
-    (12, 2048, 13312, "gemv"),     # 13 MiB: the GEMV through M = 12
-    (13, 2048, 13312, "mfma"),
-    (15, 2048, 3072, "gemv"),      # 3 MiB: the GEMV through M = 15
-    (16, 2048, 3072, "mfma"),      # M >= 16: the MFMA GEMM at every size
+@pytest.mark.parametrize("M,K,N,path,G", [
+    (8, 2048, 20480, "gemv", 128),     # M <= 8: the GEMV at every size
+    (9, 2048, 20480, "mfma", 128),     # 20 MiB of codes: the MFMA GEMM from M = 9
+    (12, 2048, 13312, "gemv", 128),    # 13 MiB: the GEMV through M = 12
+    (13, 2048, 13312, "mfma", 128),
+    (15, 2048, 3072, "gemv", 128),     # 3 MiB: the GEMV through M = 15
+    (16, 2048, 3072, "mfma", 128),     # M >= 16: the MFMA GEMM at every size
+    (9, 2048, 3072, "mfma", 64),       # groups of 64 rows keep the stated M <= 8
 ])
-def test_default_dispatch_follows_weight_size(w, M, K, N, path):
-    ws = synth.make_custom(130 + M, M, K, N, "bf16", 128)
+def test_default_dispatch_follows_weight_size(w, M, K, N, path, G):
+    ws = synth.make_custom(130 + M, M, K, N, "bf16", G)
     packed = pack_on_gpu(w, ws)
     x = bits_to_device(ws.x_bits[M], "bf16")
-    auto = device_to_bits(w.w4a16_gemm(x, packed, N, 128))
-    forced = device_to_bits(w.w4a16_gemm_ex(x, packed, N, 128, path=path))
+    auto = device_to_bits(w.w4a16_gemm(x, packed, N, G))
+    forced = device_to_bits(w.w4a16_gemm_ex(x, packed, N, G, path=path))
     torch.cuda.synchronize()
-    assert np.array_equal(auto, forced), (M, K, N, path)
+    assert np.array_equal(auto, forced), (M, K, N, path, G)
     if N == 3072:
         ref = oracle_y(ws, ws.x_bits[M])
         assert ogemm.max_rel_error(numerics.half_bits_to_f64(auto, "bf16"), ref) <= TOL
