@@ -344,6 +344,43 @@ def test_gemv_long_k(w, K, M):
     assert ogemm.max_rel_error(got, oracle_y(ws, ws.x_bits[M])) <= TOL
 
 
+@pytest.mark.parametrize("M,K,N,dtype", [(8, 6656, 2048, "bf16"), (12, 6656, 2048, "fp16"),
+                                         (16, 6656, 2048, "bf16"), (8, 4096, 1000, "bf16"),
+                                         (9, 2048, 1024, "fp16"), (1, 6656, 2048, "bf16")])
+def test_gemv_k_split_over_workgroups(w, M, K, N, dtype):
+    # narrow outputs (at most 128 column blocks) split each block's K range over 2-4
+    # workgroups from M = 8 when the workspace holds their partials (N = 1000 and
+    # K = 4096: 4 ways; M = 1 keeps one workgroup per block): parity with the oracle, the
+    # same result on a second call, the counters left at zero, nothing written
+    # outside y (N = 1000: a ragged last block); without a workspace one workgroup
+    # per block gives a result within the same tolerance
+    print(f"gemv K split over workgroups M={M} K={K} N={N} {dtype}", flush=True)
+    ws = synth.make_custom(150 + M, M, K, N, dtype, 128)
+    packed = pack_on_gpu(w, ws)
+    x = bits_to_device(ws.x_bits[M], dtype)
+    ref = oracle_y(ws, ws.x_bits[M])
+    need = w.w4a16_workspace_bytes(M, K, N, 128)
+    assert need > 0
+    work = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    pad = 4096
+    outs = []
+    for _ in range(2):
+        buf = torch.full((M * N + 2 * pad,), -7.0, dtype=TORCH_DTYPE[dtype], device=DEV)
+        y = buf[pad:pad + M * N].view(M, N)
+        w.w4a16_gemm_ex(x, packed, N, 128, y=y, workspace=work, path="gemv")
+        torch.cuda.synchronize()
+        b = buf.cpu()
+        assert torch.all(b[:pad] == -7.0) and torch.all(b[-pad:] == -7.0), "write outside y"
+        outs.append(device_to_bits(y))
+    assert np.array_equal(outs[0], outs[1])
+    assert int(work[:512].count_nonzero()) == 0
+    assert ogemm.max_rel_error(numerics.half_bits_to_f64(outs[0], dtype), ref) <= TOL
+    none = torch.empty(0, dtype=torch.uint8, device=DEV)
+    y1 = w.w4a16_gemm_ex(x, packed, N, 128, workspace=none, path="gemv")
+    torch.cuda.synchronize()
+    assert ogemm.max_rel_error(y_to_f64(y1, dtype), ref) <= TOL
+
+
 def test_gemv_needs_no_workspace(w):
     ws = synth.make_custom(140, 8, 6656, 2048, "bf16", 128)
     packed = pack_on_gpu(w, ws)

@@ -122,7 +122,10 @@ w4a16_status gemm_impl(const void* x, const void* packed, size_t packed_bytes, w
     const auto* bp = static_cast<const uint16_t*>(bias);
     auto* yp = static_cast<uint16_t*>(y);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const hipError_t err = use_gemv ? w4a16::launch_gemv(xp, wp, bp, yp, M, K, N, G, bf16, s)
+    // the GEMV splits K over workgroups only if the workspace is large enough for it
+    void* gemv_ws = workspace && aligned(workspace, 16) ? workspace : nullptr;
+    const hipError_t err = use_gemv ? w4a16::launch_gemv(xp, wp, bp, yp, M, K, N, G, bf16, gemv_ws,
+                                                         gemv_ws ? workspace_bytes : 0, s)
                                     : w4a16::launch_gemm(xp, wp, bp, yp, M, K, N, G, bf16, workspace, s);
     return err == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
 }

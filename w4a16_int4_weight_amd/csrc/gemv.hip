@@ -37,6 +37,7 @@
 //           to -(base + z) in every entry.
 #include "device_common.h"
 #include "launch.h"
+#include "split_k.h"
 
 namespace w4a16 {
 namespace {
@@ -116,6 +117,10 @@ struct GemvArgs {
     int M, K, N;
     int kb_per_wave;        // row blocks per wave (multiple of kRun)
     int waves_k;            // waves per column block (they split K)
+    int splits;             // workgroups per column block (they split K), 1..4
+    int kb_per_split;       // row blocks per such workgroup (KB when splits = 1)
+    uint32_t* counters;     // splits > 1: one per column block, zero on entry and exit
+    float* partials;        // splits > 1: [block][split] 1 KiB fp32 partials
 };
 
 // kSub: metadata units per 128-row block (1; 2 or 4 for group sizes 64 or 32): each
@@ -124,7 +129,9 @@ struct GemvArgs {
 // so that the register budget doubles instead of spilling.
 constexpr int max_waves(int sub) { return sub == 4 ? kMaxWaves / 2 : kMaxWaves; }
 
-template <bool kBF16, bool kStaged, int kChunks, int kSub>
+// kSplit: several workgroups per column block split K and meet in the workspace
+// (a separate instantiation, so that the single-workgroup kernel carries none of it)
+template <bool kBF16, bool kStaged, int kChunks, int kSub, bool kSplit>
 __global__ __launch_bounds__(64 * max_waves(kSub)) void gemv_kernel(const GemvArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     using Mg = Magic<kBF16>;
@@ -136,7 +143,9 @@ __global__ __launch_bounds__(64 * max_waves(kSub)) void gemv_kernel(const GemvAr
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);     // wave-uniform
     const int cbl = w / a.waves_k;                                       // column block in the workgroup
     const int wk = w - cbl * a.waves_k;                                  // K slice of this wave
-    const int nb_raw = blockIdx.x * (waves / a.waves_k) + cbl;
+    const int split = kSplit ? (int)(blockIdx.x % (unsigned)a.splits) : 0;     // K range of this workgroup
+    const int group = kSplit ? (int)(blockIdx.x / (unsigned)a.splits) : (int)blockIdx.x;
+    const int nb_raw = group * (waves / a.waves_k) + cbl;
     const int NB = (int)(padded_cols(N) / kColsPerBlock);
     const bool nb_valid = nb_raw < NB;
     const int nb = nb_valid ? nb_raw : NB - 1;                           // a ragged last workgroup
@@ -144,9 +153,11 @@ __global__ __launch_bounds__(64 * max_waves(kSub)) void gemv_kernel(const GemvAr
     const int lane = threadIdx.x & 63;
     const int c = lane & 15;         // column in the block, and activation row of the A operand
     const int h = lane >> 4;         // which 8 of every 32 rows
-    // row blocks of this wave [kb_begin, kb_end)
-    const int kb_begin = wk * a.kb_per_wave;
-    const int kb_end = kb_begin + a.kb_per_wave < KB ? kb_begin + a.kb_per_wave : KB;
+    // row blocks of this workgroup [kb_lo, kb_hi) and of this wave [kb_begin, kb_end)
+    const int kb_lo = kSplit ? split * a.kb_per_split : 0;
+    const int kb_hi = kSplit && kb_lo + a.kb_per_split < KB ? kb_lo + a.kb_per_split : KB;
+    const int kb_begin = kb_lo + wk * a.kb_per_wave;
+    const int kb_end = kb_begin + a.kb_per_wave < kb_hi ? kb_begin + a.kb_per_wave : kb_hi;
     const int xr = c < M ? c : 0;    // activation row this lane feeds to the MFMA
 
     // LDS: [staged x, M x K 16-bit, in whole 1 KiB wave copies][unit sums X,
@@ -319,6 +330,42 @@ __global__ __launch_bounds__(64 * max_waves(kSub)) void gemv_kernel(const GemvAr
     }
     if (!nb_valid) return;
 
+    // 6. K split over workgroups: publish this workgroup's partial with agent-scope
+    //    stores (lane's 4 rows in two 512-byte runs of the block's 1 KiB slot), wait
+    //    for them, count the block's finished splits; the last to arrive adds every
+    //    split's partial in split order (its own from registers) and stores y
+    if constexpr (kSplit) {
+        auto slot = [&](int sp) {
+            return reinterpret_cast<uint64_t*>(reinterpret_cast<uint8_t*>(a.partials) +
+                                               ((size_t)nb * a.splits + sp) * 1024) + lane;
+        };
+        uint64_t* q = slot(split);
+        __hip_atomic_store(q, __builtin_bit_cast(uint64_t, f32x2{acc[0], acc[1]}), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(q + 64, __builtin_bit_cast(uint64_t, f32x2{acc[2], acc[3]}), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0);          // this wave's partial stores have completed
+        uint32_t arrived = 0;
+        if (lane == 0)
+            arrived = __hip_atomic_fetch_add(&a.counters[nb], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        arrived = __builtin_amdgcn_readfirstlane(arrived);
+        if (arrived != (uint32_t)(a.splits - 1)) return;
+        f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+        for (int sp = 0; sp < a.splits; ++sp) {
+            f32x4 v = acc;
+            if (sp != split) {
+                const uint64_t* r = slot(sp);
+                const f32x2 lo = __builtin_bit_cast(f32x2, __hip_atomic_load(r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+                const f32x2 hi = __builtin_bit_cast(f32x2, __hip_atomic_load(r + 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+                v = f32x4{lo[0], lo[1], hi[0], hi[1]};
+            }
+            sum += v;
+        }
+        acc = sum;
+        if (lane == 0)      // leave the counter at zero for the next call
+            __hip_atomic_store(&a.counters[nb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+
     // lane (c, h), register r -> row 4h + r, column 16 nb + c (columns past N: the
     // zero padding of a last half block, not stored)
     const int n = nb * kColsPerBlock + c;
@@ -331,21 +378,27 @@ __global__ __launch_bounds__(64 * max_waves(kSub)) void gemv_kernel(const GemvAr
     }
 }
 
-template <bool kBF16, int kSub>
-void launch_sub(const GemvPlan& p, const GemvArgs& args, hipStream_t s) {
+template <bool kBF16, int kSub, bool kSplit>
+void launch_var(const GemvPlan& p, const GemvArgs& args, hipStream_t s) {
     const int cols_per_wg = p.waves / p.waves_k;
-    const dim3 grid((unsigned)((padded_cols(args.N) / kColsPerBlock + cols_per_wg - 1) / cols_per_wg));
+    const dim3 grid((unsigned)((padded_cols(args.N) / kColsPerBlock + cols_per_wg - 1) / cols_per_wg * p.splits));
     const dim3 block((unsigned)(64 * p.waves));
     if (!p.staged)
-        hipLaunchKernelGGL((gemv_kernel<kBF16, false, 1, kSub>), grid, block, p.lds_bytes, s, args);
+        hipLaunchKernelGGL((gemv_kernel<kBF16, false, 1, kSub, kSplit>), grid, block, p.lds_bytes, s, args);
     else if (p.chunks_per_thread <= 1)
-        hipLaunchKernelGGL((gemv_kernel<kBF16, true, 1, kSub>), grid, block, p.lds_bytes, s, args);
+        hipLaunchKernelGGL((gemv_kernel<kBF16, true, 1, kSub, kSplit>), grid, block, p.lds_bytes, s, args);
     else if (p.chunks_per_thread <= 2)
-        hipLaunchKernelGGL((gemv_kernel<kBF16, true, 2, kSub>), grid, block, p.lds_bytes, s, args);
+        hipLaunchKernelGGL((gemv_kernel<kBF16, true, 2, kSub, kSplit>), grid, block, p.lds_bytes, s, args);
     else if (p.chunks_per_thread <= 4)
-        hipLaunchKernelGGL((gemv_kernel<kBF16, true, 4, kSub>), grid, block, p.lds_bytes, s, args);
+        hipLaunchKernelGGL((gemv_kernel<kBF16, true, 4, kSub, kSplit>), grid, block, p.lds_bytes, s, args);
     else
-        hipLaunchKernelGGL((gemv_kernel<kBF16, true, 8, kSub>), grid, block, p.lds_bytes, s, args);
+        hipLaunchKernelGGL((gemv_kernel<kBF16, true, 8, kSub, kSplit>), grid, block, p.lds_bytes, s, args);
+}
+
+template <bool kBF16, int kSub>
+void launch_sub(const GemvPlan& p, const GemvArgs& args, hipStream_t s) {
+    if (p.splits > 1) launch_var<kBF16, kSub, true>(p, args, s);
+    else launch_var<kBF16, kSub, false>(p, args, s);
 }
 
 template <bool kBF16>
@@ -357,17 +410,22 @@ void launch_typed(const GemvPlan& p, const GemvArgs& args, hipStream_t s) {
 
 }  // namespace
 
-GemvPlan plan_gemv_with(int64_t M, int64_t K, int64_t N, int64_t G, int cols_per_wg) {
+GemvPlan plan_gemv_with(int64_t M, int64_t K, int64_t N, int64_t G, int cols_per_wg, int splits) {
     (void)N;
     GemvPlan p;
     p.sub = units_per_block(G);
     const int64_t KB = K / kRowsPerBlock;
+    p.splits = splits;
+    // a whole number of runs per split: a run's metadata is one 16-byte load of the
+    // words of 4 row blocks, the first a multiple of 4
+    p.kb_per_split = (int)(((KB + splits - 1) / splits + kRun - 1) / kRun * kRun);
+    p.workspace_bytes = 0;
     // runs of 4 row blocks per wave, at most 16 waves (8 for group size 32) per workgroup
     const int wmax = max_waves(p.sub);
     int64_t kpw = kRun;
-    while ((KB + kpw - 1) / kpw > wmax) kpw += kRun;
+    while ((p.kb_per_split + kpw - 1) / kpw > wmax) kpw += kRun;
     p.kb_per_wave = (int)kpw;
-    p.waves_k = (int)((KB + kpw - 1) / kpw);
+    p.waves_k = (int)((p.kb_per_split + kpw - 1) / kpw);
     if (cols_per_wg < 1 || cols_per_wg * p.waves_k > wmax) cols_per_wg = 1;
     p.waves = p.waves_k * cols_per_wg;
     const int64_t threads = 64 * p.waves;
@@ -385,17 +443,38 @@ GemvPlan plan_gemv_with(int64_t M, int64_t K, int64_t N, int64_t G, int cols_per
 // decode shape: M = 8 -9%, M = 4 -4%, M = 1 even; on 2048 x 131072: M = 8 -18%
 // (45.5 -> 37.2 us), M = 12 -11%, M = 4 -5%, M = 1 and 2 even. Four blocks per
 // workgroup measured slower everywhere, and two on 2048 x 3072 (192 blocks).
-GemvPlan plan_gemv(int64_t M, int64_t K, int64_t N, int64_t G) {
+//
+// Outputs of at most 128 column blocks leave CUs idle with one workgroup per block
+// (the down projection, N = 2048: 128 of 256); there, from M = 8 and given a
+// workspace for the partials, 2-4 workgroups split each block's K range (at least 8
+// row blocks each) so that the grid reaches 256 workgroups, meeting as the MFMA
+// GEMM's K splits do. Measured on 6656 x 2048: M = 8 7.63 -> 7.2 us, M = 12 8.7 ->
+// 7.8 us, M = 16 9.9 -> 8.4 us; at M = 1, 2, 4 the meeting's round trip cost more
+// than the idle CUs (5.6 -> 5.8, 5.85 -> 6.3, 6.55 -> 7.3 us).
+GemvPlan plan_gemv(int64_t M, int64_t K, int64_t N, int64_t G, size_t workspace_bytes) {
     const int64_t NB = padded_cols(N) / kColsPerBlock;
-    const GemvPlan one = plan_gemv_with(M, K, N, G, 1);
+    const int64_t KB = K / kRowsPerBlock;
+    const GemvPlan one = plan_gemv_with(M, K, N, G, 1, 1);
     if ((NB <= 1024 || M >= 4) && NB / 2 >= 200 && 2 * one.waves_k <= max_waves(one.sub))
-        return plan_gemv_with(M, K, N, G, 2);
+        return plan_gemv_with(M, K, N, G, 2, 1);
+    if (M >= 8 && NB <= kMaxSplitTiles && KB >= 16) {
+        int64_t splits = 256 / NB;
+        if (splits > KB / 8) splits = KB / 8;
+        if (splits > 4) splits = 4;
+        const size_t need = kSplitCounterBytes + (size_t)splits * (size_t)NB * 1024;
+        if (splits >= 2 && workspace_bytes >= need) {
+            GemvPlan p = plan_gemv_with(M, K, N, G, 1, (int)splits);
+            p.workspace_bytes = need;
+            return p;
+        }
+    }
     return one;
 }
 
 hipError_t launch_gemv(const uint16_t* x, const uint8_t* packed, const uint16_t* bias, uint16_t* y,
-                       int64_t M, int64_t K, int64_t N, int64_t G, bool bf16, hipStream_t stream) {
-    const GemvPlan p = plan_gemv(M, K, N, G);
+                       int64_t M, int64_t K, int64_t N, int64_t G, bool bf16, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+    const GemvPlan p = plan_gemv(M, K, N, G, workspace ? workspace_bytes : 0);
     GemvArgs args;
     args.x = x;
     args.packed = packed;
@@ -406,6 +485,11 @@ hipError_t launch_gemv(const uint16_t* x, const uint8_t* packed, const uint16_t*
     args.N = (int)N;
     args.kb_per_wave = p.kb_per_wave;
     args.waves_k = p.waves_k;
+    args.splits = p.splits;
+    args.kb_per_split = p.kb_per_split;
+    args.counters = static_cast<uint32_t*>(workspace);
+    args.partials = p.splits > 1 ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + kSplitCounterBytes)
+                                 : nullptr;
     if (bf16) launch_typed<true>(p, args, stream);
     else launch_typed<false>(p, args, stream);
     return hipGetLastError();

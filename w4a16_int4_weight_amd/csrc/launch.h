@@ -18,8 +18,9 @@ hipError_t launch_repack_gptq(const int32_t* qweight, const int32_t* qzeros, con
                               uint8_t* packed, int64_t K, int64_t N, int64_t G, int64_t n0, int64_t Nt,
                               hipStream_t stream);
 
-// Weight-streaming split-K GEMV for 1 <= M <= 16 (K split over the waves of a
-// workgroup; no workspace).
+// Weight-streaming split-K GEMV for 1 <= M <= 16: K split over the waves of a
+// workgroup, and for outputs of at most 128 column blocks also over 2-4 workgroups
+// per block when the caller's workspace holds their partials (else one workgroup).
 struct GemvPlan {
     int kb_per_wave;       // row blocks per wave (multiple of 4)
     int waves;             // waves per workgroup (waves_k per column block)
@@ -28,11 +29,18 @@ struct GemvPlan {
     int chunks_per_thread; // 16-byte activation chunks each thread stages
     int sub;               // metadata units per 128-row block (128 / G for G = 32, 64; else 1)
     size_t lds_bytes;
+    int splits;            // workgroups per column block along K
+    int kb_per_split;      // row blocks per such workgroup
+    size_t workspace_bytes;   // [counters][splits x blocks x 1 KiB fp32 partials] when splits > 1
 };
-GemvPlan plan_gemv(int64_t M, int64_t K, int64_t N, int64_t G);
+GemvPlan plan_gemv(int64_t M, int64_t K, int64_t N, int64_t G, size_t workspace_bytes);
 
+// `workspace` (or NULL) holds `workspace_bytes` bytes whose counter part is zero; the
+// kernel uses it only if plan_gemv splits K over workgroups with that many bytes, and
+// leaves the counters zero.
 hipError_t launch_gemv(const uint16_t* x, const uint8_t* packed, const uint16_t* bias, uint16_t* y,
-                       int64_t M, int64_t K, int64_t N, int64_t G, bool bf16, hipStream_t stream);
+                       int64_t M, int64_t K, int64_t N, int64_t G, bool bf16, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream);
 
 // Tied-embedding gather: out[t, :] = dequantised column ids[t] of the packed [K, N]
 // weight (zeros for ids outside [0, N)).
@@ -48,7 +56,7 @@ struct GemmPlan {
     int tiles_m, tiles_n;
     int splits;        // workgroups per tile along K
     int sub;           // metadata units per 128-row block (128 / G for G = 32, 64; else 1)
-    size_t workspace_bytes;   // [tile counters, 256-byte aligned][splits x M x N fp32 partials]
+    size_t workspace_bytes;   // [kSplitCounterBytes of tile counters][splits x M x N fp32 partials]
 };
 GemmPlan plan_gemm(int64_t M, int64_t K, int64_t N, int64_t G);
 
