@@ -213,6 +213,8 @@ def test_gemm_rejects_bad_calls(w):
     (15, 2048, 3072, "gemv", 128),     # 3 MiB: the GEMV through M = 15
     (16, 2048, 3072, "mfma", 128),     # M >= 16: the MFMA GEMM at every size
     (9, 2048, 3072, "mfma", 64),       # groups of 64 rows keep the stated M <= 8
+    (15, 6656, 2048, "gemv", 128),     # N <= 2048: the GEMV (K split) through M = 15
+    (16, 6656, 2048, "mfma", 128),
 ])
 def test_default_dispatch_follows_weight_size(w, M, K, N, path, G):
     ws = synth.make_custom(130 + M, M, K, N, "bf16", G)
