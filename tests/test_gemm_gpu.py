@@ -384,10 +384,13 @@ def test_gemv_k_split_over_workgroups(w, M, K, N, dtype):
 
 
 def test_gemv_needs_no_workspace(w):
+    # a NULL workspace (an empty buffer; None would get the binding's default) on a
+    # shape whose GEMV would split K over workgroups given one: one workgroup per block
     ws = synth.make_custom(140, 8, 6656, 2048, "bf16", 128)
     packed = pack_on_gpu(w, ws)
     x = bits_to_device(ws.x_bits[8], "bf16")
-    y = w.w4a16_gemm_ex(x, packed, 2048, 128, workspace=None, path="gemv")
+    none = torch.empty(0, dtype=torch.uint8, device=DEV)
+    y = w.w4a16_gemm_ex(x, packed, 2048, 128, workspace=none, path="gemv")
     torch.cuda.synchronize()
     assert ogemm.max_rel_error(y_to_f64(y, "bf16"), oracle_y(ws, ws.x_bits[8])) <= TOL
 
