@@ -206,7 +206,7 @@ w4a16_status w4a16_gemm(const void* x, const void* packed, size_t packed_bytes, 
  * W4A16_PATH_AUTO, M <= gemv_max_m takes the GEMV (gemv_max_m in 0..16; a
  * negative value selects the default, which w4a16_gemm uses: 8, raised to 12 when
  * the codes (K*N/2 bytes) take at most 16 MiB and to 15 at most 4 MiB or when
- * N <= 2048, for groups of 128 rows or more, where the GEMV was measured faster up
+ * N <= 2048 and K >= 2048, for groups of 128 rows or more, where the GEMV was measured faster up
  * to those row counts).
  * W4A16_PATH_GEMV requires M <= 16. Both paths read the same packed buffer. */
 w4a16_status w4a16_gemm_ex(const void* x, const void* packed, size_t packed_bytes, w4a16_dtype dtype,
