@@ -167,9 +167,10 @@ w4a16_status w4a16_parse_packed_header(const void* header, size_t header_bytes, 
  * too few tiles to fill the GPU (small N and M, long K); the split partial sums
  * (fp32) and one counter per output tile live there. Independent of the path that
  * w4a16_gemm_ex would choose: the value suffices for every path. The GEMV uses the
- * workspace too when one this large is passed, from M = 8 on outputs of at most 128
- * column blocks (N <= 2048), to split K over workgroups; with NULL it runs one
- * workgroup per column block (same result within the tolerance, not bit for bit).
+ * workspace too when one this large is passed, from M = 6 on outputs of at most 128
+ * column blocks (N <= 2048) with K >= 6144, to split K over workgroups; with NULL it
+ * runs one workgroup per column block (same result within the tolerance, not bit
+ * for bit).
  *
  * Layout: its first 512 bytes hold the tile counters for every shape (a split plan
  * has fewer than 128 output tiles), the partial sums follow.

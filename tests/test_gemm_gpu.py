@@ -347,12 +347,14 @@ def test_gemv_long_k(w, K, M):
 
 
 @pytest.mark.parametrize("M,K,N,dtype", [(8, 6656, 2048, "bf16"), (12, 6656, 2048, "fp16"),
-                                         (16, 6656, 2048, "bf16"), (8, 4096, 1000, "bf16"),
-                                         (9, 2048, 1024, "fp16"), (1, 6656, 2048, "bf16")])
+                                         (16, 6656, 2048, "bf16"), (6, 8192, 1000, "bf16"),
+                                         (9, 6656, 1280, "fp16"), (1, 6656, 2048, "bf16"),
+                                         (8, 2048, 2048, "bf16")])
 def test_gemv_k_split_over_workgroups(w, M, K, N, dtype):
-    # narrow outputs (at most 128 column blocks) split each block's K range over 2-4
-    # workgroups from M = 8 when the workspace holds their partials (N = 1000 and
-    # K = 4096: 4 ways; M = 1 keeps one workgroup per block): parity with the oracle, the
+    # narrow outputs (at most 128 column blocks) with K >= 6144 split each block's K
+    # range over 2-4 workgroups from M = 6 when the workspace holds their partials
+    # (N = 2048: 2 ways, N = 1280: 3, N = 1000: 4; M = 1 and K = 2048 keep one
+    # workgroup per block): parity with the oracle, the
     # same result on a second call, the counters left at zero, nothing written
     # outside y (N = 1000: a ragged last block); without a workspace one workgroup
     # per block gives a result within the same tolerance

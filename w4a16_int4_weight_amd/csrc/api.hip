@@ -21,9 +21,9 @@ constexpr int64_t kDefaultGemvMaxM = 8;
 // smaller the weight is (MI355X, G = 128, bf16: through M = 15 at K x N = 2048 x 3072,
 // through 13 at 2048 x 13312, through 12 at 6656 x 2048, and behind already at M = 8
 // at 2048 x 131072), so the last GEMV row count follows the size of the codes. Outputs
-// of at most 128 column blocks (N <= 2048) and K >= 2048, where the GEMV splits K
-// over workgroups from M = 8, keep it through M = 15 (2048 .. 8192 x 1024 .. 2048:
-// 6-30% ahead of the MFMA GEMM at M = 12 .. 16).
+// of at most 128 column blocks (N <= 2048) and K >= 2048 keep it through M = 15
+// (2048 .. 8192 x 1024 .. 2048: 6-30% ahead of the MFMA GEMM at M = 12 .. 16, with
+// the GEMV's K split over workgroups where K >= 6144).
 int64_t default_gemv_max_m(int64_t K, int64_t N, int64_t G) {
     if (G % 128 != 0) return kDefaultGemvMaxM;        // group sizes 32, 64: not measured
     if ((N + 15) / 16 <= 128 && K >= 2048) return 15;

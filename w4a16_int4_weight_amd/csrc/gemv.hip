@@ -445,19 +445,20 @@ GemvPlan plan_gemv_with(int64_t M, int64_t K, int64_t N, int64_t G, int cols_per
 // workgroup measured slower everywhere, and two on 2048 x 3072 (192 blocks).
 //
 // Outputs of at most 128 column blocks leave CUs idle with one workgroup per block
-// (the down projection, N = 2048: 128 of 256); there, from M = 8 and given a
-// workspace for the partials, 2-4 workgroups split each block's K range (at least 8
-// row blocks each) so that the grid reaches 256 workgroups, meeting as the MFMA
-// GEMM's K splits do. Measured on 6656 x 2048: M = 8 7.63 -> 7.2 us, M = 12 8.7 ->
-// 7.8 us, M = 16 9.9 -> 8.4 us; at M = 1, 2, 4 the meeting's round trip cost more
-// than the idle CUs (5.6 -> 5.8, 5.85 -> 6.3, 6.55 -> 7.3 us).
+// (the down projection, N = 2048: 128 of 256); there, for K >= 6144 from M = 6 and
+// given a workspace for the partials, 2-4 workgroups split each block's K range so
+// that the grid reaches 256 workgroups, meeting as the MFMA GEMM's K splits do.
+// Measured on 6656 x 2048: M = 6 7.27 -> 7.02 us, M = 8 7.63 -> 7.2 us, M = 12 8.7
+// -> 7.8 us, M = 16 9.9 -> 8.4 us; at M = 1 .. 4, and at any M up to 8 for K = 2048
+// and 4096 (each workgroup then keeps 16 row blocks or fewer), the meeting's round
+// trip cost more than the idle CUs (2048 x 2048, M = 8: 4.43 -> 4.95 us).
 GemvPlan plan_gemv(int64_t M, int64_t K, int64_t N, int64_t G, size_t workspace_bytes) {
     const int64_t NB = padded_cols(N) / kColsPerBlock;
     const int64_t KB = K / kRowsPerBlock;
     const GemvPlan one = plan_gemv_with(M, K, N, G, 1, 1);
     if ((NB <= 1024 || M >= 4) && NB / 2 >= 200 && 2 * one.waves_k <= max_waves(one.sub))
         return plan_gemv_with(M, K, N, G, 2, 1);
-    if (M >= 8 && NB <= kMaxSplitTiles && KB >= 16) {
+    if (M >= 6 && NB <= kMaxSplitTiles && KB >= 48) {
         int64_t splits = 256 / NB;
         if (splits > KB / 8) splits = KB / 8;
         if (splits > 4) splits = 4;

@@ -19,8 +19,8 @@ hipError_t launch_repack_gptq(const int32_t* qweight, const int32_t* qzeros, con
                               hipStream_t stream);
 
 // Weight-streaming split-K GEMV for 1 <= M <= 16: K split over the waves of a
-// workgroup, and for outputs of at most 128 column blocks also over 2-4 workgroups
-// per block when the caller's workspace holds their partials (else one workgroup).
+// workgroup, and for outputs of at most 128 column blocks (K >= 6144, M >= 6) also
+// over 2-4 workgroups per block when the caller's workspace holds their partials.
 struct GemvPlan {
     int kb_per_wave;       // row blocks per wave (multiple of 4)
     int waves;             // waves per workgroup (waves_k per column block)
