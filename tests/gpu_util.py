@@ -1,6 +1,8 @@
 """Helpers shared by the GPU tests: move seeded inputs to the device, read results
 back as 16-bit bit patterns, compute oracle references."""
 
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
 
@@ -51,8 +53,24 @@ def y_to_f64(y, dtype):
     return numerics.half_bits_to_f64(device_to_bits(y), dtype)
 
 
-def sample_column_blocks(N, count, seed):
-    rng = np.random.default_rng(seed)
-    nb = N // 16
-    pick = np.unique(np.concatenate([rng.choice(nb, size=min(count, nb), replace=False), [0, nb - 1]]))
-    return (pick[:, None] * 16 + np.arange(16)[None, :]).reshape(-1)
+def whole_output_error(got, ref_cols, chunk=8192, workers=8):
+    """max |got - ref| / max |ref| over the whole [M, N] output, the reference computed
+    in column chunks of `chunk` (a multiple of 16) by ref_cols(cols) -> float64
+    [M, len(cols)], `workers` chunks at a time (NumPy releases the interpreter lock in
+    its array work). Returns (error, max |ref|): the same measure as
+    oracle.gemm.max_rel_error on the whole tensor, with one max over all chunks."""
+    N = got.shape[1]
+    assert chunk % 16 == 0
+
+    def one(n0):
+        cols = np.arange(n0, min(n0 + chunk, N))
+        ref = ref_cols(cols)
+        return float(np.max(np.abs(got[:, cols] - ref))), float(np.max(np.abs(ref)))
+
+    with ThreadPoolExecutor(max_workers=workers) as pool:
+        parts = list(pool.map(one, range(0, N, chunk)))
+    num = max(p[0] for p in parts)
+    den = max(p[1] for p in parts)
+    if den == 0.0:
+        return (0.0 if num == 0.0 else np.inf), den
+    return num / den, den

@@ -217,10 +217,14 @@ def test_layout_decode_rejects_reserved_bits():
 # ---------------------------------------------------------------- planted mistakes
 
 def _mutant(modname, old, new):
+    """A copy of oracle/<modname>.py with `old` replaced by `new`. A target string
+    that is no longer in the source fails the test outright (pytest.fail is not an
+    AssertionError, so no caller's except clause can count it as a caught mistake)."""
     path = os.path.join(ORACLE_DIR, modname + ".py")
     with open(path) as f:
         src = f.read()
-    assert old in src, (modname, old)
+    if old not in src or old == new:
+        pytest.fail(f"planted mistake is stale: {old!r} is not in oracle/{modname}.py")
     mod = types.ModuleType(f"oracle.{modname}_mutant")
     mod.__package__ = "oracle"
     exec(compile(src.replace(old, new), path, "exec"), mod.__dict__)
@@ -284,18 +288,18 @@ LAYOUT_MUTANTS = [
      "codes = codes.transpose(3, 0, 4, 2, 1)"),
     ("blocks kb-major", "words = np.zeros((NB, KB, 4, 16, 4), dtype=np.uint32)   # [nb, kb, h, c, i]",
      "words = np.zeros((KB, NB, 4, 16, 4), dtype=np.uint32)"),
-    ("metadata zero in bits 12..15", "(z_blk << np.uint32(16))", "(z_blk << np.uint32(12))"),
-    ("metadata row-block-major", "meta[:, :KB] = (s_blk | (z_blk << np.uint32(16))).T",
-     "meta[:, :KB] = (s_blk | (z_blk << np.uint32(16))).reshape(N, KB)"),
-    ("metadata unpadded", "meta = np.zeros((N, padded_row_blocks(K)), dtype=np.uint32)",
-     "meta = np.zeros((N, KB), dtype=np.uint32)"),
+    ("metadata zero in bits 12..15", "(s_u | (z_u << np.uint32(16))).T", "(s_u | (z_u << np.uint32(12))).T"),
+    ("metadata row-block-major", "meta[:, :U] = (s_u | (z_u << np.uint32(16))).T",
+     "meta[:, :U] = (s_u | (z_u << np.uint32(16))).reshape(N, U)"),
+    ("metadata unpadded", "meta = np.zeros((N, padded_units(K, G)), dtype=np.uint32)          # [n, b], padding 0",
+     "meta = np.zeros((N, U), dtype=np.uint32)"),
 ]
 
 
 @pytest.mark.parametrize("desc,old,new", LAYOUT_MUTANTS, ids=[m[0] for m in LAYOUT_MUTANTS])
 def test_planted_layout_mistakes_are_caught(desc, old, new):
+    mut = _mutant("tile_layout", old, new)
     try:
-        mut = _mutant("tile_layout", old, new)
         ok = pins.pin_layout_index_patterns(mut) and pins.pin_layout_metadata(mut)
     except (ValueError, AssertionError):
         ok = False    # a mutant that breaks the layout's own size check is caught too
@@ -340,8 +344,8 @@ EMBEDDING_MUTANTS = [
 
 @pytest.mark.parametrize("desc,old,new", EMBEDDING_MUTANTS, ids=[m[0] for m in EMBEDDING_MUTANTS])
 def test_planted_embedding_mistakes_are_caught(desc, old, new):
+    mut = _mutant("embedding", old, new)
     try:
-        mut = _mutant("embedding", old, new)
         results = pins.run_embedding_pins(mut, gemm)
         ok = all(results.values())
     except (ValueError, IndexError):
@@ -434,15 +438,20 @@ HALF_BLOCK_MUTANTS = [
     ("padding metadata repeats the last column",
      "Q, Z, scale_bits = np.pad(Q, pad), np.pad(Z, pad), np.pad(scale_bits, pad)",
      "Q, Z, scale_bits = np.pad(Q, pad), np.pad(Z, pad), np.pad(scale_bits, pad, mode='edge')"),
-    ("metadata plane placed after K*N/2", "meta = np.zeros((N, padded_row_blocks(K)), dtype=np.uint32)",
-     "meta = np.zeros((N_real, padded_row_blocks(K)), dtype=np.uint32)"),
+    ("metadata plane placed after K*N/2 (padding codes moved to the end, same size)",
+     "reshape(-1),\n        np.ascontiguousarray(meta).astype(\"<u4\").view(np.uint8).reshape(-1),\n    ])",
+     "reshape(-1)[:K * N_real // 2],\n        np.ascontiguousarray(meta).astype(\"<u4\").view(np.uint8).reshape(-1),\n"
+     "        np.zeros(K * (N - N_real) // 2, dtype=np.uint8),\n    ])"),
+    ("metadata rows only for the real columns",
+     "meta = np.zeros((N, padded_units(K, G)), dtype=np.uint32)          # [n, b], padding 0",
+     "meta = np.zeros((N_real, padded_units(K, G)), dtype=np.uint32)"),
 ]
 
 
 @pytest.mark.parametrize("desc,old,new", HALF_BLOCK_MUTANTS, ids=[m[0] for m in HALF_BLOCK_MUTANTS])
 def test_planted_half_block_mistakes_are_caught(desc, old, new):
+    mut = _mutant("tile_layout", old, new)
     try:
-        mut = _mutant("tile_layout", old, new)
         ok = pins.pin_layout_half_block(mut)
     except (ValueError, AssertionError, IndexError):
         ok = False
@@ -479,8 +488,8 @@ SMALL_GROUP_MUTANTS = [
 
 @pytest.mark.parametrize("desc,old,new", SMALL_GROUP_MUTANTS, ids=[m[0] for m in SMALL_GROUP_MUTANTS])
 def test_planted_small_group_mistakes_are_caught(desc, old, new):
+    mut = _mutant("tile_layout", old, new)
     try:
-        mut = _mutant("tile_layout", old, new)
         ok = pins.pin_layout_small_groups(mut, 32) and pins.pin_layout_small_groups(mut, 64)
     except (ValueError, AssertionError, IndexError):
         ok = False

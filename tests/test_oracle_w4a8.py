@@ -73,7 +73,8 @@ def test_quantisation_error_is_bounded():
 def _mutant(old, new):
     path = os.path.join(ORACLE_DIR, "w4a8.py")
     src = open(path).read()
-    assert old in src, old
+    if old not in src or old == new:
+        pytest.fail(f"planted mistake is stale: {old!r} is not in oracle/w4a8.py")
     mod = types.ModuleType("oracle.w4a8_mutant")
     mod.__package__ = "oracle"
     exec(compile(src.replace(old, new, 1), path, "exec"), mod.__dict__)
