@@ -29,7 +29,8 @@
  *   - Every argument is validated on the host before anything is launched; an
  *     invalid call returns its status and touches no memory.
  *   - Calls on different streams touch only the buffers they are given, so
- *     they may run concurrently when their outputs do not overlap.
+ *     they may run concurrently when their outputs do not overlap (except
+ *     w4a16_gemm_noalloc, whose calls share one library-owned array per GPU).
  *   - Status codes are returned; nothing is thrown across the ABI.
  */
 #ifndef W4A16_H
@@ -214,6 +215,31 @@ w4a16_status w4a16_gemm_ex(const void* x, const void* packed, size_t packed_byte
                            void* y, int64_t M, int64_t K, int64_t N, int64_t group_size,
                            const void* bias, void* workspace, size_t workspace_bytes, void* stream,
                            w4a16_path path, int64_t gemv_max_m);
+
+/* w4a16_gemm for callers that cannot allocate: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc. It takes no workspace: the K-split
+ * partial sums and tile counters that w4a16_gemm keeps in the caller's workspace live
+ * in a device array of W4A16_NOALLOC_SCRATCH_BYTES owned by the library (one copy per
+ * GPU, held until the process ends). The call allocates nothing, on the host or the
+ * device, and returns exactly what w4a16_gemm returns for the same arguments with a
+ * large enough workspace (same plan, same kernels: bit-for-bit the same y).
+ *
+ *   Arguments, alignment, path choice and errors as for w4a16_gemm, plus:
+ *   W4A16_ERR_BUFFER_SIZE when w4a16_workspace_bytes(M, K, N, group_size) exceeds
+ *   W4A16_NOALLOC_SCRATCH_BYTES (4 MiB); nothing is launched then. Every call with
+ *   M <= 32 fits (decode and the GEMV); larger M are rejected only when the output
+ *   has too few tiles for the GPU and the MFMA GEMM splits a long K (e.g. M = 33,
+ *   K = 16384, N = 512): such callers use w4a16_gemm with a workspace.
+ *
+ * Every call on one GPU shares that GPU's array: calls that may overlap in time on one
+ * GPU (different streams, or different host threads without ordering) race on it and
+ * must not be issued; calls queued on one stream are safe. The array's counters start
+ * at zero (cleared by a small kernel on the first call on each device) and every call
+ * leaves them at zero. */
+#define W4A16_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+w4a16_status w4a16_gemm_noalloc(const void* x, const void* packed, size_t packed_bytes, w4a16_dtype dtype,
+                                void* y, int64_t M, int64_t K, int64_t N, int64_t group_size, const void* bias,
+                                void* stream);
 
 /* Tied-embedding gather from the packed head weight: a model whose input embedding
  * is tied to its output head keeps one quantised matrix for both (vllm-omni commit

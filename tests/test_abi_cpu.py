@@ -25,7 +25,8 @@ def w():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
-        "w4a16_embedding", "w4a16_gemm", "w4a16_gemm_ex", "w4a16_layout_version", "w4a16_packed_bytes",
+        "w4a16_embedding", "w4a16_gemm", "w4a16_gemm_ex", "w4a16_gemm_noalloc", "w4a16_layout_version",
+        "w4a16_packed_bytes",
         "w4a16_packed_header", "w4a16_parse_packed_header", "w4a16_repack", "w4a16_repack_columns",
         "w4a16_repack_gptq", "w4a16_repack_gptq_columns", "w4a16_status_str", "w4a16_workspace_bytes",
         "w4a8_activation_bytes", "w4a8_gemm", "w4a8_quantize", "w4a8_workspace_bytes"])
@@ -127,6 +128,40 @@ def test_gemm_validation_before_any_device_call(w):
     assert gemm(w, M=0, x=None, y=None, packed=None) == 0
     # a fully valid call on this GPU-less host stops at the device check
     assert gemm(w) == 7
+
+
+def test_gemm_noalloc_validation_before_any_device_call(w):
+    def noalloc(x=P(256), packed=P(512), pbytes=1 << 40, dtype=1, y=P(1024), M=4, K=512, N=512, G=128, bias=None):
+        return w.lib.w4a16_gemm_noalloc(x, packed, pbytes, dtype, y, M, K, N, G, bias, None)
+    assert noalloc(M=-1) == 2
+    assert noalloc(K=500) == 2
+    assert noalloc(G=96) == 3
+    assert noalloc(dtype=2) == 4
+    assert noalloc(x=None) == 1
+    assert noalloc(y=P(1032)) == 5
+    assert noalloc(pbytes=512 * 512 // 2) == 6
+    assert noalloc(M=0, x=None, y=None, packed=None) == 0
+    # a split plan whose partials exceed the library's array: rejected before the device
+    big = dict(M=33, K=16384, N=512)
+    assert w.w4a16_workspace_bytes(33, 16384, 512, 128) > w.NOALLOC_SCRATCH_BYTES
+    assert noalloc(**big) == 6
+    # split plans within the array, and plans with no split, reach the device check
+    assert 0 < w.w4a16_workspace_bytes(16, 6656, 2048, 128) <= w.NOALLOC_SCRATCH_BYTES
+    assert noalloc(M=16, K=6656, N=2048) == 7
+    assert noalloc(M=8, K=6656, N=2048) == 7
+    assert noalloc() == 7
+    # every M <= 32 fits the array (the split plans' partials stay below it)
+    for M in (1, 8, 16, 17, 32):
+        for K in (2048, 6656, 65536, 1 << 20):
+            for N in (16, 512, 2048, 8192):
+                assert w.w4a16_workspace_bytes(M, K, N, 128) <= w.NOALLOC_SCRATCH_BYTES, (M, K, N)
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(os.path.join(ROOT, "include", "w4a16.h")).read()
+    m = re.search(r"#define W4A16_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    import w4a16_int4_weight_amd as mod
+    assert m and int(m.group(1)) << int(m.group(2)) == mod.NOALLOC_SCRATCH_BYTES
 
 
 def test_repack_validation_before_any_device_call(w):

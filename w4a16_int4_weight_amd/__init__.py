@@ -15,6 +15,8 @@ Functions keep the C names:
   w4a16_gemm(x, packed, N, group_size, bias=None, y=None, workspace=None, stream=None) -> y
       (workspace=None: a zero-filled per-device workspace is allocated on demand)
   w4a16_gemm_ex(..., path="auto"|"gemv"|"mfma", gemv_max_m=-1)            -> y
+  w4a16_gemm_noalloc(x, packed, N, group_size, bias=None, y=None, stream=None) -> y
+      (no workspace: the library's per-GPU scratch array; nothing is allocated when y is given)
   w4a16_embedding(ids, packed, K, N, group_size, dtype, out=None, stream=None) -> out [T, K]
   w4a16_status_str(code)                         -> str
 
@@ -41,7 +43,7 @@ __all__ = [
     "W4A16Error", "lib", "w4a16_layout_version", "w4a16_packed_bytes", "w4a16_workspace_bytes",
     "w4a16_repack", "w4a16_repack_gptq", "w4a16_repack_columns", "w4a16_repack_gptq_columns",
     "w4a16_packed_header", "w4a16_parse_packed_header", "repack_from_host", "save_packed", "load_packed",
-    "w4a16_gemm", "w4a16_gemm_ex", "w4a16_embedding", "w4a16_status_str", "STATUS", "PATHS",
+    "w4a16_gemm", "w4a16_gemm_ex", "w4a16_gemm_noalloc", "w4a16_embedding", "w4a16_status_str", "STATUS", "PATHS",
 ]
 
 STATUS = {
@@ -100,6 +102,8 @@ def _load():
     h.w4a16_gemm.restype = _int
     h.w4a16_gemm_ex.argtypes = h.w4a16_gemm.argtypes + [_int, _i64]
     h.w4a16_gemm_ex.restype = _int
+    h.w4a16_gemm_noalloc.argtypes = [_vp, _vp, _sz, _int, _vp, _i64, _i64, _i64, _i64, _vp, _vp]
+    h.w4a16_gemm_noalloc.restype = _int
     h.w4a16_embedding.argtypes = [_vp, _i64, _vp, _sz, _int, _i64, _i64, _i64, _vp, _vp]
     h.w4a16_embedding.restype = _int
     h.w4a8_activation_bytes.argtypes = [_i64, _i64]
@@ -371,6 +375,29 @@ def w4a16_gemm_ex(x, packed, N, group_size=128, bias=None, y=None, workspace=Non
     return y
 
 
+def w4a16_gemm_noalloc(x, packed, N, group_size=128, bias=None, y=None, stream=None):
+    """w4a16_gemm without a workspace: the library's own per-GPU scratch array holds
+    the K-split partials (calls that may overlap in time on one GPU must not be made).
+    y must be given by a caller that cannot allocate."""
+    if x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [M, K] tensor")
+    M, K = x.shape
+    if y is None:
+        y = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    if tuple(y.shape) != (M, N) or y.dtype != x.dtype or not y.is_contiguous():
+        raise ValueError("y must be a contiguous [M, N] tensor of x's dtype")
+    if bias is not None and (bias.dtype != x.dtype or tuple(bias.shape) != (N,) or not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous [N] tensor of x's dtype")
+    code = _load().w4a16_gemm_noalloc(_ptr(x), _ptr(packed), packed.numel() * packed.element_size(),
+                                      _dtype_code(x.dtype), _ptr(y), M, K, N, group_size, _ptr(bias),
+                                      _stream(stream, x.device))
+    _check(code, "w4a16_gemm_noalloc")
+    return y
+
+
+NOALLOC_SCRATCH_BYTES = 4 << 20      # W4A16_NOALLOC_SCRATCH_BYTES
+
+
 def w4a16_embedding(ids, packed, K, N, group_size=128, dtype=torch.bfloat16, out=None, stream=None):
     """Token ids int32 [T] -> out [T, K] of `dtype`: row i is column ids[i] of the
     dequantised head weight the packed buffer holds (zeros for ids outside [0, N))."""
@@ -450,3 +477,4 @@ def w4a8_linear(x, packed, N, group_size=128, bias=None, y=None, act=None, works
     M, K = x.shape
     act = w4a8_quantize(x, act=act, stream=stream)
     return w4a8_gemm(act, packed, M, K, N, group_size, x.dtype, bias, y, workspace, stream)
+

@@ -5,10 +5,12 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "../../include/w4a16.h"
 #include "device_common.h"
 #include "launch.h"
+#include "split_k.h"
 
 namespace {
 
@@ -92,9 +94,11 @@ w4a16_status check_device() {
     return kind == 1 ? W4A16_OK : W4A16_ERR_DEVICE;
 }
 
-w4a16_status gemm_impl(const void* x, const void* packed, size_t packed_bytes, w4a16_dtype dtype, void* y,
-                       int64_t M, int64_t K, int64_t N, int64_t group_size, const void* bias, void* workspace,
-                       size_t workspace_bytes, void* stream, w4a16_path path, int64_t gemv_max_m) {
+// Host-side checks of a GEMM call (everything but the workspace and the device).
+// On W4A16_OK with M > 0, *G_out is the resolved group size and *use_gemv the path.
+w4a16_status check_gemm(const void* x, const void* packed, size_t packed_bytes, w4a16_dtype dtype, const void* y,
+                        int64_t M, int64_t K, int64_t N, int64_t group_size, const void* bias, w4a16_path path,
+                        int64_t gemv_max_m, int64_t* G_out, bool* use_gemv) {
     if (M < 0) return W4A16_ERR_SHAPE;
     int64_t G = 0;
     w4a16_status st = check_shape(K, N, group_size, &G);
@@ -110,16 +114,15 @@ w4a16_status gemm_impl(const void* x, const void* packed, size_t packed_bytes, w
     if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(y, 16) || (bias && !aligned(bias, 2)))
         return W4A16_ERR_ALIGN;
     if (packed_bytes < packed_size(K, N, G)) return W4A16_ERR_BUFFER_SIZE;
-    const bool use_gemv = path == W4A16_PATH_GEMV || (path == W4A16_PATH_AUTO && M <= gemv_max_m);
-    const size_t need = use_gemv ? 0 : w4a16::plan_gemm(M, K, N, G).workspace_bytes;
-    if (need > 0) {
-        if (!workspace) return W4A16_ERR_NULL;
-        if (!aligned(workspace, 16)) return W4A16_ERR_ALIGN;
-        if (workspace_bytes < need) return W4A16_ERR_BUFFER_SIZE;
-    }
-    st = check_device();
-    if (st != W4A16_OK) return st;
+    *G_out = G;
+    *use_gemv = path == W4A16_PATH_GEMV || (path == W4A16_PATH_AUTO && M <= gemv_max_m);
+    return W4A16_OK;
+}
 
+// Launches a checked GEMM call on the current device.
+w4a16_status launch_checked_gemm(const void* x, const void* packed, w4a16_dtype dtype, void* y, int64_t M,
+                                 int64_t K, int64_t N, int64_t G, const void* bias, void* workspace,
+                                 size_t workspace_bytes, void* stream, bool use_gemv) {
     const bool bf16 = dtype == W4A16_BF16;
     const auto* xp = static_cast<const uint16_t*>(x);
     const auto* wp = static_cast<const uint8_t*>(packed);
@@ -132,6 +135,73 @@ w4a16_status gemm_impl(const void* x, const void* packed, size_t packed_bytes, w
                                                          gemv_ws ? workspace_bytes : 0, s)
                                     : w4a16::launch_gemm(xp, wp, bp, yp, M, K, N, G, bf16, workspace, s);
     return err == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
+w4a16_status gemm_impl(const void* x, const void* packed, size_t packed_bytes, w4a16_dtype dtype, void* y,
+                       int64_t M, int64_t K, int64_t N, int64_t group_size, const void* bias, void* workspace,
+                       size_t workspace_bytes, void* stream, w4a16_path path, int64_t gemv_max_m) {
+    int64_t G = 0;
+    bool use_gemv = false;
+    w4a16_status st = check_gemm(x, packed, packed_bytes, dtype, y, M, K, N, group_size, bias, path, gemv_max_m,
+                                 &G, &use_gemv);
+    if (st != W4A16_OK || M == 0) return st;
+    const size_t need = use_gemv ? 0 : w4a16::plan_gemm(M, K, N, G).workspace_bytes;
+    if (need > 0) {
+        if (!workspace) return W4A16_ERR_NULL;
+        if (!aligned(workspace, 16)) return W4A16_ERR_ALIGN;
+        if (workspace_bytes < need) return W4A16_ERR_BUFFER_SIZE;
+    }
+    st = check_device();
+    if (st != W4A16_OK) return st;
+    return launch_checked_gemm(x, packed, dtype, y, M, K, N, G, bias, workspace, workspace_bytes, stream, use_gemv);
+}
+
+// ---------------------------------------------------------------- allocation-free GEMM
+// w4a16_gemm_noalloc keeps the K-split partials and tile counters in this array
+// instead of a caller workspace. Each GPU the library runs on holds its own copy until
+// the process ends; the host reaches it only through the device address that
+// hipGetSymbolAddress returns (kept per device), never through the array's name.
+constexpr size_t kScratchBytes = W4A16_NOALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes % 256 == 0 && kScratchBytes >= w4a16::kSplitCounterBytes, "scratch size");
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+__global__ void clear_words_kernel(uint32_t* __restrict__ p, int n) {
+    const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+    if (i < n) p[i] = 0u;
+}
+
+struct ScratchSlot {
+    std::mutex mu;
+    void* ptr = nullptr;      // device address of `scratch` on this device
+    bool cleared = false;     // its counter region zeroed by an eager launch
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// The current device's copy of `scratch`, its counter region zeroed ahead of the
+// caller's kernels on `stream`. The clear is launched once per device outside stream
+// capture; a captured first call puts the clear into its graph and leaves it pending
+// for the next eager call. (The kernels leave the counters at zero after every call.)
+w4a16_status device_scratch(hipStream_t stream, void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return W4A16_ERR_DEVICE;
+    ScratchSlot& slot = g_scratch[dev];
+    std::lock_guard<std::mutex> lock(slot.mu);
+    if (!slot.ptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return W4A16_ERR_HIP;
+        slot.ptr = p;
+    }
+    if (!slot.cleared) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return W4A16_ERR_HIP;
+        constexpr int words = (int)(w4a16::kSplitCounterBytes / 4);
+        hipLaunchKernelGGL(clear_words_kernel, dim3((words + 255) / 256), dim3(256), 0, stream,
+                           static_cast<uint32_t*>(slot.ptr), words);
+        if (hipGetLastError() != hipSuccess) return W4A16_ERR_HIP;
+        if (cs == hipStreamCaptureStatusNone) slot.cleared = true;
+    }
+    *out = slot.ptr;
+    return W4A16_OK;
 }
 
 // One repack entry: AWQ (gptq = false) or GPTQ-standard tensors holding columns
@@ -218,6 +288,24 @@ w4a16_status w4a16_gemm_ex(const void* x, const void* packed, size_t packed_byte
                            size_t workspace_bytes, void* stream, w4a16_path path, int64_t gemv_max_m) {
     return gemm_impl(x, packed, packed_bytes, dtype, y, M, K, N, group_size, bias, workspace, workspace_bytes,
                      stream, path, gemv_max_m);
+}
+
+w4a16_status w4a16_gemm_noalloc(const void* x, const void* packed, size_t packed_bytes, w4a16_dtype dtype,
+                                void* y, int64_t M, int64_t K, int64_t N, int64_t group_size, const void* bias,
+                                void* stream) {
+    int64_t G = 0;
+    bool use_gemv = false;
+    w4a16_status st = check_gemm(x, packed, packed_bytes, dtype, y, M, K, N, group_size, bias, W4A16_PATH_AUTO, -1,
+                                 &G, &use_gemv);
+    if (st != W4A16_OK || M == 0) return st;
+    // the same requirement w4a16_workspace_bytes states, against the array's size
+    if (w4a16::plan_gemm(M, K, N, G).workspace_bytes > kScratchBytes) return W4A16_ERR_BUFFER_SIZE;
+    st = check_device();
+    if (st != W4A16_OK) return st;
+    void* ws = nullptr;
+    st = device_scratch(static_cast<hipStream_t>(stream), &ws);
+    if (st != W4A16_OK) return st;
+    return launch_checked_gemm(x, packed, dtype, y, M, K, N, G, bias, ws, kScratchBytes, stream, use_gemv);
 }
 
 w4a16_status w4a16_embedding(const int32_t* ids, int64_t T, const void* packed, size_t packed_bytes,
