@@ -4,31 +4,55 @@ Headline (the JSON `value`): decode GEMV M=1 over the gate_up layer shape, K=204
 N=13312, group size 128, bf16, in algorithmic GB/s. A step is one w4a16_gemm call
 (dispatch, split-K GEMV, in-kernel reduction and epilogue) on one activation
 batch; the weights were repacked once before timing. Secondary entries in the same
-JSON line measure the other rows of the path on their own workloads: the LM-head
-repack from AWQ and from GPTQ-standard tensors (GB/s), the MFMA GEMM at M=512
-(TFLOP/s), the GEMV on the other shapes and the tied-embedding gather of 512 tokens
-from the packed LM head (GB/s). As context, not as the metric, it also times the same
-products with dense bf16 weights through torch.matmul (the vendor GEMM library).
+JSON line measure the other rows of the path on their own workloads: the GEMV on the
+down-projection and LM-head shapes, the MFMA GEMM at M=512 (TFLOP/s), the W4A8 GEMM,
+the LM-head repack from AWQ and from GPTQ-standard tensors (GB/s) and the
+tied-embedding gather of 512 tokens from the packed LM head (GB/s).
 
-Timing: warm-up calls, then K calls captured in one HIP graph and replayed once
-between two events on the launch stream, with a device synchronisation on both
-sides. Each call reads a different copy of the packed weights, rotating through
-at least 1 GiB of copies (at least 8 for the LM head), so the 256 MiB Infinity Cache
-cannot serve repeats: the bytes come from HBM. (A rotation of only 4 x 139 MB ran
-the LM-head GEMV about 8% slower than 8 copies; more copies only remove reuse.)
+Timing of every entry:
+  * the weights (or repack inputs) exist in `copies` copies spanning >= 1 GiB, call i
+    reading copy i mod copies, so a copy is never read twice within 1 GiB of traffic;
+  * W warm-up calls run eagerly, then exactly K calls (--steps) are captured in one HIP
+    graph and replayed once untimed;
+  * REPLAYS timed replays follow, each preceded by a 512 MiB streaming read of another
+    buffer (the MALL scrub: the 256 MiB Infinity Cache then holds none of the copies)
+    and a device synchronisation, and bracketed by two events on the launch stream;
+  * per-launch time = replay time / K; the entry reports the median over replays (the
+    value used everywhere), p10 and p90, the copies one replay touches and their bytes.
+So with the default K every call reads its weights from HBM, and with any K the first
+read of every copy in a replay does.
+
+Achievable references beside each entry, timed the same way (context, not targets):
+  * HBM-bound entries: w4a16_stream_read over the entry's algorithmic byte count (a
+    plain 16-byte streaming read; for the repack, w4a16_stream_copy of half the bytes,
+    reading one half and writing the other), reported as `achievable` and
+    `frac_of_achievable` in the entry's roofline object;
+  * MFMA-bound entries: the same product with dense bf16 weights through torch.matmul
+    (the vendor GEMM library), reported in `dense_bf16_reference`.
+
+The LM-head GEMV, a 140 MB stream, runs faster for its first ~80 back-to-back
+launches than after (the chip's response to a sustained ~6 TB/s stream): its entry
+carries a `fresh` state (replays of 20 calls after the scrub) and a `sustained` state
+(the third of three back-to-back replays of 128 calls).
 
 Algorithmic bytes of a GEMM (AWQ-sized): K*N/2 codes + (K/G)*N/2 zeros
 + (K/G)*N*2 scales + M*K*2 activations + M*N*2 outputs; flops 2*M*N*K.
 Repack bytes: each AWQ byte read once and written once, 2*(K*N/2 + (K/G)*N/2 + (K/G)*N*2).
 Gather bytes, per token: K/2 codes + (K/G)*2.5 zero and scale bytes + 4 (id) + 2K outputs.
 
+cpu_baseline: the oracle as it stands (AWQ unpack, float64 dequant, float64 matmul) on
+whole steps of the headline workload, on the host's cores: once on a pool of one
+thread per allotted core (each thread the oracle on its own range of output columns,
+BLAS held to one thread each), once on one thread.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--quick]
        python bench.py --pmc-probe     (launches for hardware-counter runs, no timing)
 
 --pmc-probe runs, without graphs or timing, a 256 MiB device copy (the calibration
 kernel for the byte counters: it reads and writes exactly 256 MiB) three times, then
-the headline GEMV ten times on rotating weight copies and the LM-head M=512 GEMM three
-times, so that counter runs see one dispatch per launch.
+the headline GEMV ten times on rotating weight copies, the down-projection GEMV at M=1
+and M=8 ten times each and the LM-head M=512 GEMM three times, so that counter runs see
+one dispatch per launch.
 """
 
 import argparse
@@ -37,6 +61,7 @@ import json
 import math
 import os
 import re
+import statistics
 import sys
 import time
 
@@ -47,8 +72,13 @@ METRIC = "W4A16 GEMM GB/s (M=1) & TFLOP/s (M=512) vs roofline; repack GB/s"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 MFMA_FP8_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 MFMA, published
-ROTATE_BYTES = 1 << 30
+ROTATE_BYTES = 1 << 30          # weight copies per entry span at least this
+SCRUB_BYTES = 512 << 20         # streaming read between timed replays (2x the Infinity Cache)
 MAX_COPIES = 128
+REPLAYS = 7
+LM_HEAD_FRESH_CALLS = 20
+SUSTAINED_CALLS = 128
+CPU_THREADS_CAP = 16            # the host cores allotted to one GPU
 
 
 def log(msg):
@@ -65,6 +95,12 @@ def repack_bytes(K, N, G):
     return 2 * (K * N // 2 + KG * N // 2 + KG * N * 2)
 
 
+def embedding_bytes(T, K, G):
+    """Algorithmic bytes of a T-token gather: per token its K codes (K/2 bytes), its
+    K/G zeros and scales (2.5 bytes each), the id (4 bytes) and the K outputs (2K)."""
+    return T * (K // 2 + (K // G) * 5 // 2 + 4 + 2 * K)
+
+
 def to_dev_bits(bits, dtype, dev):
     import numpy as np
     import torch
@@ -72,133 +108,211 @@ def to_dev_bits(bits, dtype, dev):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(td).to(dev)
 
 
-def time_graph(fn_list, warmup):
-    """Runs warm-up calls eagerly, captures the timed calls in a graph and replays it
-    once between events. Returns (elapsed_ms, launches)."""
-    import torch
-    for i in range(warmup):
-        fn_list[i % len(fn_list)]()
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for fn in fn_list:
-            fn()
-    torch.cuda.synchronize()
-    g.replay()                       # one untimed replay: graph upload, first-use costs
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    g.replay()
-    end.record(stream)
-    torch.cuda.synchronize()
-    return start.elapsed_time(end), len(fn_list)
+def copies_for(nbytes, cap=MAX_COPIES):
+    return max(1, min(cap, math.ceil(ROTATE_BYTES / max(nbytes, 1))))
 
 
-def time_graphs_alternating(fn_lists, warmup, rounds=3):
-    """Captures one graph per call list, replays each once untimed, then times
-    `rounds` replays of each in alternation (a, b, a, b, ...) so that the entries
-    compared see the same clock and power state. Returns the median ms of each."""
-    import statistics
-    import torch
-    graphs = []
-    for fns in fn_lists:
-        for i in range(warmup):
-            fns[i % len(fns)]()
-        torch.cuda.synchronize()
+def pct(vals, q):
+    """q-th percentile (0..100) of a small sample, linear interpolation."""
+    s = sorted(vals)
+    if len(s) == 1:
+        return s[0]
+    pos = (len(s) - 1) * q / 100.0
+    lo = int(math.floor(pos))
+    hi = min(lo + 1, len(s) - 1)
+    return s[lo] + (s[hi] - s[lo]) * (pos - lo)
+
+
+class Timer:
+    """Graph capture, MALL scrub and event timing shared by every entry."""
+
+    def __init__(self, w, dev, steps, warmup, replays=REPLAYS):
+        import torch
+        self.w, self.dev, self.steps, self.warmup, self.replays = w, dev, steps, warmup, replays
+        self.scrub_buf = torch.empty(SCRUB_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        self.scrub_sink = torch.empty(w.w4a16_stream_sink_bytes(SCRUB_BYTES), dtype=torch.uint8, device=dev)
+
+    def scrub(self):
+        self.w.w4a16_stream_read(self.scrub_buf, sink=self.scrub_sink)
+
+    def capture(self, fns):
+        import torch
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for fn in fns:
                 fn()
         torch.cuda.synchronize()
-        g.replay()
+        g.replay()                   # untimed: graph upload, first-use costs
         torch.cuda.synchronize()
-        graphs.append(g)
-    stream = torch.cuda.current_stream()
-    times = [[] for _ in graphs]
-    for _ in range(rounds):
-        for j, g in enumerate(graphs):
-            start = torch.cuda.Event(enable_timing=True)
-            end = torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            start.record(stream)
-            g.replay()
-            end.record(stream)
-            torch.cuda.synchronize()
-            times[j].append(start.elapsed_time(end))
-    return [statistics.median(t) for t in times]
+        return g
+
+    def replay_ms(self, g, scrub=True):
+        import torch
+        if scrub:
+            self.scrub()
+        stream = torch.cuda.current_stream()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        g.replay()
+        end.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end)
+
+    def time(self, rotation, copies, bytes_per_copy, calls=None):
+        """rotation[i] is a call reading copy i mod copies. Runs the warm-up, captures
+        `calls` (default K) calls, times self.replays replays after scrubs. Returns the
+        per-launch statistics in microseconds."""
+        import torch
+        n = self.steps if calls is None else calls
+        for i in range(self.warmup):
+            rotation[(n + i) % len(rotation)]()
+        torch.cuda.synchronize()
+        g = self.capture([rotation[i % len(rotation)] for i in range(n)])
+        per = [self.replay_ms(g) * 1e3 / n for _ in range(self.replays)]
+        del g
+        touched = min(n, copies)
+        return {"us_per_launch": statistics.median(per), "us_p10": pct(per, 10), "us_p90": pct(per, 90),
+                "replays": self.replays, "calls_per_replay": n, "copies": copies, "copies_touched_per_replay": touched,
+                "footprint_bytes_per_replay": touched * bytes_per_copy, "mall_scrub_bytes": SCRUB_BYTES}
+
+    def time_sustained(self, rotation, calls=SUSTAINED_CALLS):
+        """Three back-to-back replays of `calls` launches (no scrub, no gap); the third
+        is timed. Returns microseconds per launch."""
+        import torch
+        g = self.capture([rotation[i % len(rotation)] for i in range(calls)])
+        stream = torch.cuda.current_stream()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        g.replay()
+        g.replay()
+        start.record(stream)
+        g.replay()
+        end.record(stream)
+        torch.cuda.synchronize()
+        del g
+        return start.elapsed_time(end) * 1e3 / calls
+
+    def stream_floor(self, nbytes, copy=False):
+        """The streaming reference over `nbytes` algorithmic bytes: a read of nbytes, or
+        (copy=True) a copy of nbytes / 2 (reading one half, writing the other)."""
+        import torch
+        w = self.w
+        part = (nbytes // 2 if copy else nbytes) // 16 * 16
+        per_copy = 2 * part if copy else part
+        copies = copies_for(per_copy)
+        srcs = [torch.empty(part, dtype=torch.uint8, device=self.dev).fill_(3) for _ in range(copies)]
+        if copy:
+            dsts = [torch.empty(part, dtype=torch.uint8, device=self.dev) for _ in range(copies)]
+            rotation = [(lambda s=srcs[i], d=dsts[i]: w.w4a16_stream_copy(s, d)) for i in range(copies)]
+        else:
+            sink = torch.empty(w.w4a16_stream_sink_bytes(part), dtype=torch.uint8, device=self.dev)
+            rotation = [(lambda s=srcs[i]: w.w4a16_stream_read(s, sink=sink)) for i in range(copies)]
+        t = self.time(rotation, copies, per_copy)
+        del srcs, rotation
+        if copy:
+            del dsts
+        torch.cuda.empty_cache()
+        return {"kernel": "w4a16_stream_copy" if copy else "w4a16_stream_read", "bytes": 2 * part if copy else part,
+                "us_per_launch": round(t["us_per_launch"], 3), "us_p10": round(t["us_p10"], 3),
+                "us_p90": round(t["us_p90"], 3), "GBps": round(nbytes / t["us_per_launch"] / 1e3, 1)}
 
 
-def measure_gemm(w, workload, M, steps, warmup, dev, path="auto"):
-    import torch
+_WEIGHT_SETS = {}
+
+
+def weight_set(workload):
+    """synth.make(workload) with every M of the workload, drawn once per process."""
     import synth
-    ws = synth.make(workload, Ms=(M,))
-    K, N, G = ws.K, ws.N, ws.group_size
+    if workload not in _WEIGHT_SETS:
+        _WEIGHT_SETS[workload] = synth.make(workload)
+    return _WEIGHT_SETS[workload]
+
+
+def packed_copies(w, ws, dev):
+    import torch
     qw = torch.from_numpy(ws.qweight).to(dev)
     qz = torch.from_numpy(ws.qzeros).to(dev)
     sc = to_dev_bits(ws.scale_bits, ws.dtype, dev)
-    packed0 = w.w4a16_repack(qw, qz, sc, G)
+    packed0 = w.w4a16_repack(qw, qz, sc, ws.group_size)
     del qw, qz, sc
-    pbytes = packed0.numel()
-    copies = max(1, min(MAX_COPIES, math.ceil(ROTATE_BYTES / pbytes)))
-    packs = [packed0] + [packed0.clone() for _ in range(copies - 1)]
+    copies = copies_for(packed0.numel())
+    return [packed0] + [packed0.clone() for _ in range(copies - 1)]
+
+
+def round_entry(e):
+    for k in ("us_per_launch", "us_p10", "us_p90"):
+        if k in e:
+            e[k] = round(e[k], 3)
+    return e
+
+
+def measure_gemm(T, w, workload, M, dev, path="auto", sustained=False):
+    import torch
+    ws = weight_set(workload)
+    K, N, G = ws.K, ws.N, ws.group_size
+    packs = packed_copies(w, ws, dev)
+    copies = len(packs)
     x = to_dev_bits(ws.x_bits[M], ws.dtype, dev)
     y = torch.empty((M, N), dtype=x.dtype, device=dev)
-    calls = [(lambda p=packs[i % copies]: w.w4a16_gemm_ex(x, p, N, G, y=y, path=path)) for i in range(steps)]
-    ms, n = time_graph(calls, warmup)
-    per_launch_s = ms / 1e3 / n
+    rotation = [(lambda p=packs[i]: w.w4a16_gemm_ex(x, p, N, G, y=y, path=path)) for i in range(copies)]
     nbytes = gemm_bytes(M, K, N, G)
     flops = 2 * M * N * K
-    del packs, packed0
+    e = dict(workload=workload, M=M, K=K, N=N, group_size=G, dtype=ws.dtype, path=path,
+             algorithmic_bytes=nbytes, flops=flops)
+    if sustained:
+        # fresh: replays of a few calls after the scrub; sustained: back-to-back launches
+        e.update(T.time(rotation, copies, packs[0].numel(), calls=LM_HEAD_FRESH_CALLS))
+        e["state"] = f"fresh: {LM_HEAD_FRESH_CALLS} calls per replay after the scrub"
+        us_s = T.time_sustained(rotation)
+        e["sustained"] = {"us_per_launch": round(us_s, 3), "GBps": round(nbytes / us_s / 1e3, 1),
+                          "calls": SUSTAINED_CALLS,
+                          "timing": f"third of three back-to-back replays of {SUSTAINED_CALLS} calls"}
+    else:
+        e.update(T.time(rotation, copies, packs[0].numel()))
+    del packs, rotation
     torch.cuda.empty_cache()
-    return dict(workload=workload, M=M, K=K, N=N, group_size=G, dtype=ws.dtype, path=path,
-                kernel="w4a16_gemv" if (path == "gemv" or (path == "auto" and M <= 8)) else "w4a16_gemm_mfma",
-                weight_copies=copies, launches=n, us_per_launch=per_launch_s * 1e6,
-                algorithmic_bytes=nbytes, flops=flops,
-                GBps=nbytes / per_launch_s / 1e9, TFLOPs=flops / per_launch_s / 1e12)
+    us = e["us_per_launch"]
+    e["GBps"] = nbytes / us / 1e3
+    e["TFLOPs"] = flops / us / 1e6
+    return round_entry(e)
 
 
-def measure_w4a8(w, workload, M, steps, warmup, dev):
+def measure_w4a8(T, w, workload, M, dev):
     """W4A8 on a 16-bit workload: the product alone from quantised activations (the
-    kernel the roofline is for), and the whole step, quantisation included."""
+    kernel the roofline is for), and the whole step with the activation quantisation."""
     import torch
-    import synth
-    ws = synth.make(workload, Ms=(M,))
+    ws = weight_set(workload)
     K, N, G = ws.K, ws.N, ws.group_size
-    qw = torch.from_numpy(ws.qweight).to(dev)
-    qz = torch.from_numpy(ws.qzeros).to(dev)
-    sc = to_dev_bits(ws.scale_bits, ws.dtype, dev)
-    packed0 = w.w4a16_repack(qw, qz, sc, G)
-    del qw, qz, sc
-    copies = max(1, min(MAX_COPIES, math.ceil(ROTATE_BYTES / packed0.numel())))
-    packs = [packed0] + [packed0.clone() for _ in range(copies - 1)]
+    packs = packed_copies(w, ws, dev)
+    copies = len(packs)
     x = to_dev_bits(ws.x_bits[M], ws.dtype, dev)
     act = w.w4a8_quantize(x)
     y = torch.empty((M, N), dtype=x.dtype, device=dev)
-    gemm_calls = [(lambda p=packs[i % copies]: w.w4a8_gemm(act, p, M, K, N, G, x.dtype, y=y)) for i in range(steps)]
-    step_calls = [(lambda p=packs[i % copies]: w.w4a8_linear(x, p, N, G, y=y, act=act)) for i in range(steps)]
-    gemm_ms, step_ms = time_graphs_alternating([gemm_calls, step_calls], warmup)
-    n = steps
-    gemm_s = gemm_ms / 1e3 / n
-    step_s = step_ms / 1e3 / n
+    gemm_rot = [(lambda p=packs[i]: w.w4a8_gemm(act, p, M, K, N, G, x.dtype, y=y)) for i in range(copies)]
+    step_rot = [(lambda p=packs[i]: w.w4a8_linear(x, p, N, G, y=y, act=act)) for i in range(copies)]
     flops = 2 * M * N * K
-    del packs, packed0
+    e = dict(workload=workload, M=M, K=K, N=N, group_size=G, dtype=ws.dtype, activations="fp8 e4m3",
+             kernel="w4a8_gemm_mfma", flops=flops)
+    e.update(T.time(gemm_rot, copies, packs[0].numel()))
+    step = T.time(step_rot, copies, packs[0].numel())
+    e["us_per_step_with_quantize"] = round(step["us_per_launch"], 3)
+    e["TFLOPs"] = flops / e["us_per_launch"] / 1e6
+    e["TFLOPs_step"] = flops / step["us_per_launch"] / 1e6
+    del packs, gemm_rot, step_rot
     torch.cuda.empty_cache()
-    return dict(workload=workload, M=M, K=K, N=N, group_size=G, dtype=ws.dtype, activations="fp8 e4m3",
-                kernel="w4a8_gemm_mfma", weight_copies=copies, launches=n, us_per_launch=gemm_s * 1e6,
-                us_per_step_with_quantize=step_s * 1e6, flops=flops, TFLOPs=flops / gemm_s / 1e12,
-                TFLOPs_step=flops / step_s / 1e12)
+    return round_entry(e)
 
 
-def measure_repack(w, workload, steps, warmup, dev, fmt="awq"):
+def measure_repack(T, w, workload, dev, fmt="awq"):
     """fmt "awq": w4a16_repack from AWQ tensors; "gptq": w4a16_repack_gptq from
     GPTQ-standard tensors of the same shape (same recipe, same byte count)."""
     import torch
     import synth
     if fmt == "awq":
-        ws = synth.make(workload, Ms=())
+        ws = weight_set(workload)
         fn = w.w4a16_repack
     else:
         wl = synth.WORKLOADS[workload]
@@ -210,61 +324,48 @@ def measure_repack(w, workload, steps, warmup, dev, fmt="awq"):
     sc = to_dev_bits(ws.scale_bits, ws.dtype, dev)
     pbytes = w.w4a16_packed_bytes(K, N, G)
     in_bytes = qw.numel() * 4 + qz.numel() * 4 + sc.numel() * 2
-    copies = max(1, min(16, math.ceil(ROTATE_BYTES / (in_bytes + pbytes))))
+    copies = copies_for(in_bytes + pbytes, cap=16)
     ins = [(qw, qz, sc)] + [(qw.clone(), qz.clone(), sc.clone()) for _ in range(copies - 1)]
     outs = [torch.empty(pbytes, dtype=torch.uint8, device=dev) for _ in range(copies)]
-    calls = [(lambda a=ins[i % copies], o=outs[i % copies]: fn(a[0], a[1], a[2], G, packed=o))
-             for i in range(steps)]
-    ms, n = time_graph(calls, warmup)
-    per_launch_s = ms / 1e3 / n
+    rotation = [(lambda a=ins[i], o=outs[i]: fn(a[0], a[1], a[2], G, packed=o)) for i in range(copies)]
     nbytes = repack_bytes(K, N, G)
-    del ins, outs
+    e = dict(workload=workload + (" repack" if fmt == "awq" else " repack from GPTQ"), K=K, N=N, group_size=G,
+             dtype=ws.dtype, kernel="w4a16_repack" if fmt == "awq" else "w4a16_repack_gptq",
+             algorithmic_bytes=nbytes)
+    e.update(T.time(rotation, copies, in_bytes + pbytes))
+    del ins, outs, rotation
     torch.cuda.empty_cache()
-    return dict(workload=workload + (" repack" if fmt == "awq" else " repack from GPTQ"), K=K, N=N, group_size=G,
-                dtype=ws.dtype, kernel="w4a16_repack" if fmt == "awq" else "w4a16_repack_gptq",
-                copies=copies, launches=n, us_per_launch=per_launch_s * 1e6, algorithmic_bytes=nbytes,
-                GBps=nbytes / per_launch_s / 1e9)
+    e["GBps"] = nbytes / e["us_per_launch"] / 1e3
+    return round_entry(e)
 
 
-def embedding_bytes(T, K, G):
-    """Algorithmic bytes of a T-token gather: per token its K codes (K/2 bytes), its
-    K/G zeros and scales (2.5 bytes each), the id (4 bytes) and the K outputs (2K)."""
-    return T * (K // 2 + (K // G) * 5 // 2 + 4 + 2 * K)
-
-
-def measure_embedding(w, workload, T, steps, warmup, dev):
-    import numpy as np
+def measure_embedding(T, w, workload, tokens, dev):
     import torch
     import synth
-    ws = synth.make(workload, Ms=())
+    ws = weight_set(workload)
     K, N, G = ws.K, ws.N, ws.group_size
-    qw = torch.from_numpy(ws.qweight).to(dev)
-    qz = torch.from_numpy(ws.qzeros).to(dev)
-    sc = to_dev_bits(ws.scale_bits, ws.dtype, dev)
-    packed0 = w.w4a16_repack(qw, qz, sc, G)
-    del qw, qz, sc
-    copies = max(1, min(MAX_COPIES, math.ceil(ROTATE_BYTES / packed0.numel())))
-    packs = [packed0] + [packed0.clone() for _ in range(copies - 1)]
-    # a different set of prompt tokens per call, so repeated calls do not re-read the
+    packs = packed_copies(w, ws, dev)
+    copies = len(packs)
+    # a different set of prompt tokens per copy, so repeated calls do not re-read the
     # same columns from the caches
-    ids = [torch.from_numpy(synth.draw_token_ids(7000 + i, T, N)).to(dev) for i in range(steps)]
-    out = torch.empty((T, K), dtype=torch.bfloat16 if ws.dtype == "bf16" else torch.float16, device=dev)
-    calls = [(lambda p=packs[i % copies], t=ids[i]: w.w4a16_embedding(t, p, K, N, G, out.dtype, out=out))
-             for i in range(steps)]
-    ms, n = time_graph(calls, warmup)
-    per_launch_s = ms / 1e3 / n
-    nbytes = embedding_bytes(T, K, G)
-    del packs, packed0, ids
+    ids = [torch.from_numpy(synth.draw_token_ids(7000 + i, tokens, N)).to(dev) for i in range(copies)]
+    out = torch.empty((tokens, K), dtype=torch.bfloat16 if ws.dtype == "bf16" else torch.float16, device=dev)
+    rotation = [(lambda p=packs[i], t=ids[i]: w.w4a16_embedding(t, p, K, N, G, out.dtype, out=out))
+                for i in range(copies)]
+    nbytes = embedding_bytes(tokens, K, G)
+    e = dict(workload=workload + " tied-embedding gather", T=tokens, K=K, N=N, group_size=G, dtype=ws.dtype,
+             kernel="w4a16_embedding", algorithmic_bytes=nbytes)
+    e.update(T.time(rotation, copies, packs[0].numel()))
+    del packs, ids, rotation
     torch.cuda.empty_cache()
-    return dict(workload=workload + " tied-embedding gather", T=T, K=K, N=N, group_size=G, dtype=ws.dtype,
-                kernel="w4a16_embedding", weight_copies=copies, launches=n, us_per_launch=per_launch_s * 1e6,
-                algorithmic_bytes=nbytes, GBps=nbytes / per_launch_s / 1e9)
+    e["GBps"] = nbytes / e["us_per_launch"] / 1e3
+    return round_entry(e)
 
 
-def measure_dense_reference(workload, M, steps, warmup, dev):
+def measure_dense_reference(T, workload, M, dev):
     """Context, not the metric: the same product with dense bf16 weights through
-    torch.matmul (the vendor GEMM library), weights rotated through >= 1 GiB of copies
-    and timed like the W4A16 entries. Algorithmic bytes: K*N*2 weights + M*K*2 + M*N*2."""
+    torch.matmul (the vendor GEMM library), weights rotated and timed like the W4A16
+    entries. Algorithmic bytes: K*N*2 weights + M*K*2 + M*N*2."""
     import torch
     import synth
     shape = synth.WORKLOADS[workload]
@@ -272,46 +373,41 @@ def measure_dense_reference(workload, M, steps, warmup, dev):
     g = torch.Generator(device=dev)
     g.manual_seed(7)
     w0 = (torch.randn((K, N), device=dev, generator=g) * 0.05).to(torch.bfloat16)
-    copies = max(1, min(MAX_COPIES, math.ceil(ROTATE_BYTES / (K * N * 2))))
-    ws = [w0] + [w0.clone() for _ in range(copies - 1)]
+    copies = copies_for(K * N * 2)
+    wts = [w0] + [w0.clone() for _ in range(copies - 1)]
     x = torch.randn((M, K), device=dev, generator=g).to(torch.bfloat16)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    calls = [(lambda wt=ws[i % copies]: torch.matmul(x, wt, out=y)) for i in range(steps)]
-    try:
-        ms, n = time_graph(calls, warmup)
-        how = "HIP graph of K calls, events"
-    except Exception as exc:  # a library call that cannot be captured: time it eagerly
-        torch.cuda.synchronize()
-        log(f"dense reference not capturable ({type(exc).__name__}); timed eagerly")
-        start = torch.cuda.Event(enable_timing=True)
-        end = torch.cuda.Event(enable_timing=True)
-        start.record()
-        for fn in calls:
-            fn()
-        end.record()
-        torch.cuda.synchronize()
-        ms, n = start.elapsed_time(end), len(calls)
-        how = "eager launches, events"
-    per_launch_s = ms / 1e3 / n
+    rotation = [(lambda wt=wts[i]: torch.matmul(x, wt, out=y)) for i in range(copies)]
     nbytes = K * N * 2 + M * K * 2 + M * N * 2
     flops = 2 * M * N * K
-    del ws, w0
+    e = dict(workload=workload, M=M, K=K, N=N, dtype="bf16", kind="dense bf16 weights, torch.matmul",
+             algorithmic_bytes=nbytes, flops=flops)
+    e.update(T.time(rotation, copies, K * N * 2))
+    del wts, w0, rotation
     torch.cuda.empty_cache()
-    return dict(workload=workload, M=M, K=K, N=N, dtype="bf16", kind="dense bf16 weights, torch.matmul",
-                weight_copies=copies, launches=n, timing=how, us_per_launch=per_launch_s * 1e6,
-                algorithmic_bytes=nbytes, flops=flops, GBps=nbytes / per_launch_s / 1e9,
-                TFLOPs=flops / per_launch_s / 1e12)
+    e["GBps"] = nbytes / e["us_per_launch"] / 1e3
+    e["TFLOPs"] = flops / e["us_per_launch"] / 1e6
+    return round_entry(e)
 
 
-def roofline_hbm(entry, traffic=None):
-    return {"bound": "hbm", "achieved": round(entry["GBps"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(entry["GBps"] / HBM_PEAK_GBS, 4), "traffic": traffic}
+def roofline_hbm(entry, floor=None, traffic=None):
+    r = {"bound": "hbm", "achieved": round(entry["GBps"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+         "frac": round(entry["GBps"] / HBM_PEAK_GBS, 4), "traffic": traffic}
+    if floor is not None:
+        r["achievable"] = floor["GBps"]
+        r["frac_of_achievable"] = round(entry["GBps"] / floor["GBps"], 4)
+        r["achievable_reference"] = floor
+    return r
 
 
-def roofline_mfma(entry, peak=None):
+def roofline_mfma(entry, peak=None, dense=None):
     peak = MFMA_BF16_PEAK_TFLOPS if peak is None else peak
-    return {"bound": "mfma", "achieved": round(entry["TFLOPs"], 1), "peak": peak,
-            "unit": "TFLOP/s", "frac": round(entry["TFLOPs"] / peak, 4), "traffic": None}
+    r = {"bound": "mfma", "achieved": round(entry["TFLOPs"], 1), "peak": peak,
+         "unit": "TFLOP/s", "frac": round(entry["TFLOPs"] / peak, 4), "traffic": None}
+    if dense is not None:
+        r["dense_bf16_TFLOPs"] = round(dense["TFLOPs"], 1)
+        r["speedup_vs_dense_bf16"] = round(dense["us_per_launch"] / entry["us_per_launch"], 3)
+    return r
 
 
 CALIBRATION_COPY_BYTES = 256 << 20
@@ -352,19 +448,16 @@ def pmc_probe(dev):
         dst.copy_(src)
     torch.cuda.synchronize()
     del src, dst
-    ws = synth.make("gate_up_decode", Ms=(1,))
-    qw = torch.from_numpy(ws.qweight).to(dev)
-    qz = torch.from_numpy(ws.qzeros).to(dev)
-    sc = to_dev_bits(ws.scale_bits, ws.dtype, dev)
-    packed0 = w.w4a16_repack(qw, qz, sc, ws.group_size)
-    packs = [packed0] + [packed0.clone() for _ in range(9)]
-    x = to_dev_bits(ws.x_bits[1], ws.dtype, dev)
-    y = torch.empty((1, ws.N), dtype=x.dtype, device=dev)
-    torch.cuda.synchronize()
-    for i in range(10):
-        w.w4a16_gemm(x, packs[i], ws.N, ws.group_size, y=y)
-    torch.cuda.synchronize()
-    del packs, packed0
+    for workload, M in (("gate_up_decode", 1), ("down_proj", 1), ("down_proj", 8)):
+        ws = synth.make(workload, Ms=(M,))
+        packs = packed_copies(w, ws, dev)[:10]
+        x = to_dev_bits(ws.x_bits[M], ws.dtype, dev)
+        y = torch.empty((M, ws.N), dtype=x.dtype, device=dev)
+        torch.cuda.synchronize()
+        for i in range(10):
+            w.w4a16_gemm(x, packs[i % len(packs)], ws.N, ws.group_size, y=y)
+        torch.cuda.synchronize()
+        del packs
     # the MFMA GEMM on the LM-head prefill (M=512), three launches on one weight copy
     ws = synth.make("lm_head", Ms=(512,))
     qw = torch.from_numpy(ws.qweight).to(dev)
@@ -383,40 +476,64 @@ def pmc_probe(dev):
     for _ in range(3):
         w.w4a8_gemm(act, packed, 512, ws.K, ws.N, ws.group_size, x.dtype, y=y)
     torch.cuda.synchronize()
-    log("pmc probe done: 3 x 256 MiB copy, 10 x gate_up_decode GEMV, 3 x lm_head M=512 GEMM, "
-        "3 x lm_head M=512 W4A8 GEMM")
+    log("pmc probe done: 3 x 256 MiB copy, 10 x gate_up_decode GEMV, 10 x down_proj GEMV M=1 and M=8, "
+        "3 x lm_head M=512 GEMM, 3 x lm_head M=512 W4A8 GEMM")
 
 
-def cpu_baseline(workload, M, budget_s=15.0):
-    """The oracle as it stands (unpack, float64 dequant, float64 matmul), BLAS held
-    to one thread, timed on whole steps of the same workload until ~budget_s."""
-    import numpy as np
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(workload, M, budget_s=16.0):
+    """The oracle as it stands (unpack, float64 dequant, float64 matmul) on whole steps
+    of the workload: first on a pool of one thread per allotted core, each thread the
+    oracle on its own range of output columns (whole AWQ words), then on one thread;
+    BLAS held to one thread per caller throughout. About budget_s in all."""
+    from concurrent.futures import ThreadPoolExecutor
     import synth
     from oracle import gemm as ogemm
-    try:
-        from threadpoolctl import threadpool_limits
-    except ImportError:  # pragma: no cover
-        threadpool_limits = None
+    from threadpoolctl import threadpool_limits
     ws = synth.make(workload, Ms=(M,))
-    ctx = threadpool_limits(limits=1) if threadpool_limits else None
-    if ctx:
-        ctx.__enter__()
-    try:
-        t0 = time.perf_counter()
-        n = 0
-        while True:
-            ogemm.w4a16_reference(ws.x_bits[M], ws.qweight, ws.qzeros, ws.scale_bits, ws.dtype, ws.group_size)
-            n += 1
-            if time.perf_counter() - t0 >= budget_s:
-                break
-        dt = (time.perf_counter() - t0) / n
-    finally:
-        if ctx:
-            ctx.__exit__(None, None, None)
+    J = ws.qweight.shape[1]
+    threads = max(1, min(len(os.sched_getaffinity(0)), CPU_THREADS_CAP))
+
+    def run(nthreads, seconds):
+        edges = [J * i // nthreads for i in range(nthreads + 1)]
+
+        def part(i):
+            j0, j1 = edges[i], edges[i + 1]
+            return ogemm.w4a16_reference(ws.x_bits[M], ws.qweight[:, j0:j1], ws.qzeros[:, j0:j1],
+                                         ws.scale_bits[:, 8 * j0:8 * j1], ws.dtype, ws.group_size)
+
+        with ThreadPoolExecutor(max_workers=nthreads) as pool:
+            list(pool.map(part, range(nthreads)))          # one untimed step
+            t0 = time.perf_counter()
+            n = 0
+            while True:
+                list(pool.map(part, range(nthreads)))
+                n += 1
+                if time.perf_counter() - t0 >= seconds:
+                    break
+            return (time.perf_counter() - t0) / n, n
+
     nbytes = gemm_bytes(M, ws.K, ws.N, ws.group_size)
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} whole steps of {workload} M={M} ({dt:.2f} s each): AWQ unpack, float64 dequant, "
-                      f"float64 matmul, BLAS limited to 1 thread, elementwise NumPy single-threaded"}
+    with threadpool_limits(limits=1):
+        dt_all, n_all = run(threads, budget_s / 2)
+        dt_one, n_one = run(1, budget_s / 2)
+    return {"value": round(nbytes / dt_all / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_all} whole steps of {workload} M={M} ({dt_all:.3f} s each) on {threads} threads, each the "
+                      f"oracle (AWQ unpack, float64 dequant, float64 matmul, BLAS 1 thread) on 1/{threads} of the "
+                      f"output columns",
+            "value_1_thread": round(nbytes / dt_one / 1e9, 4),
+            "sample_1_thread": f"{n_one} whole steps on 1 thread ({dt_one:.3f} s each)",
+            "cpu_model": cpu_model(), "host_cpus_visible": os.cpu_count()}
 
 
 def main():
@@ -445,56 +562,66 @@ def main():
         pmc_probe(dev)
         return
 
-    head = measure_gemm(w, "gate_up_decode", 1, args.steps, args.warmup, dev)
-    log(f"headline gate_up_decode M=1: {head['us_per_launch']:.2f} us, {head['GBps']:.0f} GB/s")
+    t_start = time.perf_counter()
+    T = Timer(w, dev, args.steps, args.warmup)
+    head = measure_gemm(T, w, "gate_up_decode", 1, dev)
+    head["kernel"] = "w4a16_gemv"
+    head_floor = T.stream_floor(head["algorithmic_bytes"])
+    log(f"headline gate_up_decode M=1: {head['us_per_launch']:.2f} us (p10 {head['us_p10']:.2f}, "
+        f"p90 {head['us_p90']:.2f}), {head['GBps']:.0f} GB/s; same-byte stream read "
+        f"{head_floor['us_per_launch']:.2f} us")
     secondary = []
+    dense = []
     if not args.quick:
-        for wl, M in [("lm_head", 1), ("down_proj", 1), ("down_proj", 8), ("down_proj", 16),
-                      ("qkv_prefill", 512), ("gate_up_prefill", 512), ("lm_head", 512)]:
-            steps = args.steps if M <= 16 else max(20, args.steps // 4)
-            e = measure_gemm(w, wl, M, steps, min(args.warmup, 10), dev)
-            e["roofline"] = roofline_hbm(e) if M <= 16 else roofline_mfma(e)
-            log(f"{wl} M={M}: {e['us_per_launch']:.2f} us, {e['GBps']:.0f} GB/s, {e['TFLOPs']:.1f} TFLOP/s")
+        for wl, M in [("lm_head", 1), ("down_proj", 1), ("down_proj", 8), ("down_proj", 16)]:
+            e = measure_gemm(T, w, wl, M, dev, sustained=(wl == "lm_head"))
+            e["kernel"] = "w4a16_gemv" if M <= 8 else "w4a16_gemm_mfma"
+            floor = T.stream_floor(e["algorithmic_bytes"])
+            e["roofline"] = roofline_hbm(e, floor)
+            log(f"{wl} M={M}: {e['us_per_launch']:.2f} us, {e['GBps']:.0f} GB/s (stream read "
+                f"{floor['us_per_launch']:.2f} us)" + (f"; sustained {e['sustained']['us_per_launch']:.2f} us"
+                                                        if "sustained" in e else ""))
             secondary.append(e)
-        r = measure_repack(w, "lm_head", max(10, args.steps // 10), 3, dev)
-        r["roofline"] = roofline_hbm(r)
-        log(f"lm_head repack: {r['us_per_launch']:.1f} us, {r['GBps']:.0f} GB/s")
-        secondary.append(r)
-        r = measure_repack(w, "lm_head", max(10, args.steps // 10), 3, dev, fmt="gptq")
-        r["roofline"] = roofline_hbm(r)
-        log(f"lm_head repack from GPTQ: {r['us_per_launch']:.1f} us, {r['GBps']:.0f} GB/s")
-        secondary.append(r)
         for wl in ("qkv_prefill", "gate_up_prefill", "lm_head"):
-            e = measure_w4a8(w, wl, 512, max(20, args.steps // 4), min(args.warmup, 10), dev)
+            e = measure_gemm(T, w, wl, 512, dev)
+            e["kernel"] = "w4a16_gemm_mfma"
+            d = measure_dense_reference(T, wl, 512, dev)
+            e["roofline"] = roofline_mfma(e, dense=d)
+            log(f"{wl} M=512: {e['us_per_launch']:.2f} us, {e['TFLOPs']:.1f} TFLOP/s (dense bf16 "
+                f"{d['us_per_launch']:.2f} us)")
+            secondary.append(e)
+            dense.append(d)
+        for wl in ("qkv_prefill", "gate_up_prefill", "lm_head"):
+            e = measure_w4a8(T, w, wl, 512, dev)
             e["roofline"] = roofline_mfma(e, MFMA_FP8_PEAK_TFLOPS)
             log(f"{wl} W4A8 M=512: {e['us_per_launch']:.2f} us, {e['TFLOPs']:.1f} TFLOP/s (with quantisation "
                 f"{e['us_per_step_with_quantize']:.2f} us)")
             secondary.append(e)
-        e = measure_embedding(w, "lm_head", 512, args.steps, min(args.warmup, 10), dev)
-        e["roofline"] = roofline_hbm(e)
+        for fmt in ("awq", "gptq"):
+            r = measure_repack(T, w, "lm_head", dev, fmt=fmt)
+            floor = T.stream_floor(r["algorithmic_bytes"], copy=True)
+            r["roofline"] = roofline_hbm(r, floor)
+            log(f"lm_head repack ({fmt}): {r['us_per_launch']:.1f} us, {r['GBps']:.0f} GB/s (stream copy "
+                f"{floor['us_per_launch']:.1f} us)")
+            secondary.append(r)
+        e = measure_embedding(T, w, "lm_head", 512, dev)
+        floor = T.stream_floor(e["algorithmic_bytes"])
+        e["roofline"] = roofline_hbm(e, floor)
         log(f"lm_head tied-embedding gather T=512: {e['us_per_launch']:.2f} us, {e['GBps']:.0f} GB/s")
         secondary.append(e)
-
-    dense = []
-    if not args.quick:
-        # context: the same products with dense bf16 weights (4x the weight bytes)
-        w4 = {(head["workload"], 1): head}
-        w4.update({(e["workload"], e["M"]): e for e in secondary if "M" in e and "activations" not in e})
-        for wl, M in [("gate_up_decode", 1), ("down_proj", 1), ("lm_head", 1), ("qkv_prefill", 512),
-                      ("gate_up_prefill", 512), ("lm_head", 512)]:
-            steps = args.steps if M <= 16 else max(20, args.steps // 4)
-            d = measure_dense_reference(wl, M, steps, min(args.warmup, 10), dev)
-            if (wl, M) in w4:
-                d["w4a16_speedup"] = round(d["us_per_launch"] / w4[(wl, M)]["us_per_launch"], 3)
-            log(f"dense bf16 reference {wl} M={M}: {d['us_per_launch']:.2f} us, {d['GBps']:.0f} GB/s, "
-                f"{d['TFLOPs']:.1f} TFLOP/s")
+        for wl, M in [("gate_up_decode", 1), ("down_proj", 1), ("lm_head", 1)]:
+            d = measure_dense_reference(T, wl, M, dev)
+            log(f"dense bf16 reference {wl} M={M}: {d['us_per_launch']:.2f} us, {d['GBps']:.0f} GB/s")
             dense.append(d)
+    gpu_s = time.perf_counter() - t_start
+    del T
+    torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         cpu = cpu_baseline("gate_up_decode", 1)
-        log(f"cpu baseline: {cpu['value']} GB/s")
+        log(f"cpu baseline: {cpu['value']} GB/s on {cpu['cores']} threads, {cpu['value_1_thread']} GB/s on 1")
 
     line = {
         "metric": METRIC,
@@ -511,11 +638,17 @@ def main():
         "data": "synthetic",
         "config": {"workload": "gate_up_decode: W4A16 GEMV M=1 K=2048 N=13312 group_size=128 bf16",
                    "M": 1, "K": 2048, "N": 13312, "group_size": 128,
-                   "weight_copies_rotated": head["weight_copies"], "timing": "HIP graph of K calls, events"},
-        "roofline": roofline_hbm(head, counter_traffic()),
+                   "weight_copies": head["copies"], "copies_touched_per_replay": head["copies_touched_per_replay"],
+                   "footprint_bytes_per_replay": head["footprint_bytes_per_replay"],
+                   "mall_scrub_bytes": SCRUB_BYTES, "replays": head["replays"],
+                   "us_per_launch_p10": head["us_p10"], "us_per_launch_p90": head["us_p90"],
+                   "timing": "HIP graph of K calls; median over timed replays, each after a 512 MiB streaming "
+                             "read and bracketed by events on the launch stream"},
+        "roofline": roofline_hbm(head, head_floor, counter_traffic()),
         "cpu_baseline": cpu,
         "secondary": secondary,
         "dense_bf16_reference": dense,
+        "gpu_timing_s": round(gpu_s, 1),
     }
     print(json.dumps(line), flush=True)
 

@@ -40,6 +40,44 @@ def test_library_exports_every_declared_symbol(w):
         assert callable(getattr(w, name)), name
 
 
+def measure_functions():
+    text = open(os.path.join(ROOT, "include", "w4a16_measure.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w4a16_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_measure_header_entry_points_are_exported_and_bound(w):
+    import subprocess
+    from w4a16_int4_weight_amd.build import LIB_PATH
+    assert measure_functions() == ["w4a16_stream_copy", "w4a16_stream_read", "w4a16_stream_sink_bytes"]
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in measure_functions():
+        assert name in exported and callable(getattr(w, name)), name
+
+
+def test_stream_validation_before_any_device_call(w):
+    assert w.w4a16_stream_sink_bytes(0) == 0
+    assert w.w4a16_stream_sink_bytes(24) == 0
+    assert w.w4a16_stream_sink_bytes(16) == 16                       # one chunk: one workgroup
+    assert w.w4a16_stream_sink_bytes(32768) == 512 * 16               # 512 .. 1024 shares up to 64 MiB
+    assert w.w4a16_stream_sink_bytes(14_194_688) == 866 * 16
+    assert w.w4a16_stream_sink_bytes(64 << 20) == 1024 * 16
+    assert w.w4a16_stream_sink_bytes((64 << 20) + 16) == ((64 << 20) // 16 + 1 + 2047) // 2048 * 16
+    lib = w.lib
+    assert lib.w4a16_stream_read(P(256), 24, P(512), 16, None) == 2
+    assert lib.w4a16_stream_read(None, 32, P(512), 16, None) == 1
+    assert lib.w4a16_stream_read(P(256), 32, None, 16, None) == 1
+    assert lib.w4a16_stream_read(P(260), 32, P(512), 16, None) == 5
+    assert lib.w4a16_stream_read(P(256), 32768 + 16, P(512), 16, None) == 6
+    assert lib.w4a16_stream_read(P(256), 32768, P(512), 512 * 16 - 1, None) == 6
+    assert lib.w4a16_stream_read(None, 0, None, 0, None) == 0
+    assert lib.w4a16_stream_copy(P(256), P(512), 40, None) == 2
+    assert lib.w4a16_stream_copy(P(256), None, 32, None) == 1
+    assert lib.w4a16_stream_copy(P(256), P(520), 32, None) == 5
+    assert lib.w4a16_stream_copy(None, None, 0, None) == 0
+
+
 def test_exports_are_c_symbols():
     # no C++ mangling on the entry points
     import subprocess

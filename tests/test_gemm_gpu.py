@@ -373,6 +373,10 @@ def test_gemv_k_split_over_workgroups(w, M, K, N, dtype):
         outs.append(device_to_bits(y))
     assert np.array_equal(outs[0], outs[1])
     assert int(work[:512].count_nonzero()) == 0
+    # the partials region shows whether the split ran: written by the split cases,
+    # untouched by M = 1 (the balanced M = 1 GEMV) and by K = 2048
+    splits = M >= 6 and K >= 6144
+    assert (int(work[512:].count_nonzero()) > 0) == splits, (M, K, N)
     assert ogemm.max_rel_error(numerics.half_bits_to_f64(outs[0], dtype), ref) <= TOL
     none = torch.empty(0, dtype=torch.uint8, device=DEV)
     y1 = w.w4a16_gemm_ex(x, packed, N, 128, workspace=none, path="gemv")
@@ -443,4 +447,40 @@ def test_gemm_tile_shapes(w, M, N, dtype):
     packed = pack_on_gpu(w, ws)
     got = y_to_f64(run(w, ws, packed, ws.x_bits[M], path="mfma"), dtype)
     err, _ = whole_output_error(got, lambda cols: oracle_y(ws, ws.x_bits[M], cols))
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("K,N,dtype,G,bias", [
+    (2048, 13312, "bf16", 128, False),   # 1664 half blocks on 256 workgroups: 6 or 7 each, 1 pair per group
+    (6656, 2048, "bf16", 128, True),     # one half block per workgroup, 4 pairs per group
+    (128, 8, "fp16", 128, False),        # one workgroup, one half block, 4 of 64 groups busy
+    (256, 24, "bf16", 128, True),        # a last half block (N % 16 == 8), 3 workgroups
+    (16384, 2056, "bf16", 128, False),   # 8 pairs per group, 257 half blocks: one workgroup takes 2
+    (4096, 4104, "fp16", 256, True),     # 2 pairs per group, 3 half blocks per workgroup, groups of 256
+    (1536, 1040, "bf16", -1, False),     # one group of all K rows
+    (1024, 40000, "bf16", 128, False),   # 20 half blocks per workgroup: beyond the balanced GEMV, the
+                                         # 16-column GEMV runs
+])
+def test_gemv_m1_balanced_half_blocks(w, K, N, dtype, G, bias):
+    print(f"gemv M=1 K={K} N={N} {dtype} G={G} bias={bias}", flush=True)
+    ws = synth.make_custom(1700 + K % 997 + N % 89, 1, K, N, dtype, G)
+    packed = pack_on_gpu(w, ws)
+    bias_bits = None
+    bt = None
+    if bias:
+        rng = np.random.default_rng(N)
+        bias_bits = synth.f32_to_half_bits(rng.standard_normal(N, dtype=np.float32), dtype)
+        bt = bits_to_device(bias_bits, dtype)
+    x = bits_to_device(ws.x_bits[1], dtype)
+    pad = 256
+    buf = torch.full((2 * pad + N,), -7.0, dtype=TORCH_DTYPE[dtype], device=DEV)
+    y = buf[pad:pad + N].view(1, N)
+    w.w4a16_gemm(x, packed, N, G, bias=bt, y=y)
+    y2 = w.w4a16_gemm(x, packed, N, G, bias=bt)
+    torch.cuda.synchronize()
+    b = buf.cpu()
+    assert torch.all(b[:pad] == -7.0) and torch.all(b[-pad:] == -7.0), "write outside y"
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), "not run-to-run deterministic"
+    err = ogemm.max_rel_error(y_to_f64(y, dtype), oracle_y(ws, ws.x_bits[1], bias_bits=bias_bits))
+    print(f"  max rel err {err:.3e}", flush=True)
     assert err <= TOL

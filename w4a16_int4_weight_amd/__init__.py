@@ -44,6 +44,7 @@ __all__ = [
     "w4a16_repack", "w4a16_repack_gptq", "w4a16_repack_columns", "w4a16_repack_gptq_columns",
     "w4a16_packed_header", "w4a16_parse_packed_header", "repack_from_host", "save_packed", "load_packed",
     "w4a16_gemm", "w4a16_gemm_ex", "w4a16_gemm_noalloc", "w4a16_embedding", "w4a16_status_str", "STATUS", "PATHS",
+    "w4a16_stream_sink_bytes", "w4a16_stream_read", "w4a16_stream_copy",
 ]
 
 STATUS = {
@@ -114,6 +115,12 @@ def _load():
     h.w4a8_quantize.restype = _int
     h.w4a8_gemm.argtypes = [_vp, _sz, _vp, _sz, _int, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _sz, _vp]
     h.w4a8_gemm.restype = _int
+    h.w4a16_stream_sink_bytes.argtypes = [_sz]
+    h.w4a16_stream_sink_bytes.restype = _sz
+    h.w4a16_stream_read.argtypes = [_vp, _sz, _vp, _sz, _vp]
+    h.w4a16_stream_read.restype = _int
+    h.w4a16_stream_copy.argtypes = [_vp, _vp, _sz, _vp]
+    h.w4a16_stream_copy.restype = _int
     h.w4a16_status_str.argtypes = [_int]
     h.w4a16_status_str.restype = ctypes.c_char_p
     _lib = h
@@ -478,3 +485,34 @@ def w4a8_linear(x, packed, N, group_size=128, bias=None, y=None, act=None, works
     act = w4a8_quantize(x, act=act, stream=stream)
     return w4a8_gemm(act, packed, M, K, N, group_size, x.dtype, bias, y, workspace, stream)
 
+
+# ---------------------------------------------------------------- streaming references
+# (include/w4a16_measure.h: the achievable-bandwidth floor beside the HBM-bound rows)
+
+def w4a16_stream_sink_bytes(nbytes):
+    return int(_load().w4a16_stream_sink_bytes(nbytes))
+
+
+def w4a16_stream_read(src, nbytes=None, sink=None, stream=None):
+    """Reads the first `nbytes` bytes of the device tensor `src` once; returns the sink
+    (uint8, 16 bytes per workgroup: each workgroup's XOR of what it read)."""
+    total = src.numel() * src.element_size()
+    nbytes = total if nbytes is None else nbytes
+    if nbytes > total:
+        raise ValueError("nbytes exceeds the tensor")
+    need = w4a16_stream_sink_bytes(nbytes) if nbytes else 0
+    if sink is None:
+        sink = torch.empty(max(need, 16), dtype=torch.uint8, device=src.device)
+    _check(_load().w4a16_stream_read(_ptr(src), nbytes, _ptr(sink), sink.numel() * sink.element_size(),
+                                     _stream(stream, src.device)), "w4a16_stream_read")
+    return sink
+
+
+def w4a16_stream_copy(src, dst, nbytes=None, stream=None):
+    """Copies the first `nbytes` bytes of `src` into `dst` (device tensors)."""
+    nbytes = src.numel() * src.element_size() if nbytes is None else nbytes
+    if nbytes > src.numel() * src.element_size() or nbytes > dst.numel() * dst.element_size():
+        raise ValueError("nbytes exceeds a tensor")
+    _check(_load().w4a16_stream_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream, src.device)),
+           "w4a16_stream_copy")
+    return dst

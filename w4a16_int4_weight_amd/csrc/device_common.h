@@ -202,6 +202,12 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// s_waitcnt with only lgkmcnt constrained, to zero: this wave's LDS accesses have
+// completed (vmcnt field at its maximum 63, expcnt 7).
+__device__ __forceinline__ void wait_lgkmcnt0() {
+    __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));
+}
+
 // D = A(16x32) * B(32x16) + C, fp32 accumulate. Operand layout for lane l:
 // A row l%16 / B column l%16, eight consecutive k starting at 8*(l/16);
 // C/D: rows 4*(l/16) + r (r = register 0..3), column l%16.

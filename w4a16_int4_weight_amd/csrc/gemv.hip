@@ -23,10 +23,17 @@
 //     the offset and the zero point leave in one correction, because
 //     sum_k x (base + q) - (base + z) sum_k x = sum_k x (q - z);
 //   * the waves' partial sums are added in wave order through LDS (deterministic),
-//     bias is added in fp32 and the result rounded once to the output dtype.
-//     (Splitting K over workgroups as well, with fp32 partials in a workspace and a
-//     last-arriver reduction, measured slower on every decode shape here, narrow N
-//     included: the extra pass costs more than the idle compute units.)
+//     bias is added in fp32 and the result rounded once to the output dtype;
+//   * on narrow outputs (at most 128 column blocks) with a long K (>= 6144), from
+//     M = 6 and given a workspace, 2-4 workgroups per column block split its K range
+//     and meet in the workspace (a separate instantiation): there the idle compute
+//     units cost more than the meeting's memory round trip. At smaller M, or K <= 4096,
+//     the meeting measured slower.
+//
+// One activation row (M = 1) takes the balanced GEMV of gemv_strip.hip instead when
+// the shape fits it (groups of 128 rows or more, K <= 8192, at most 16 of its code
+// loads per lane); this kernel runs the other M = 1 shapes (the LM head, K > 8192,
+// group sizes 32 and 64) and M = 2 .. 16.
 //
 // Two variants:
 //   staged  (the activations fit in LDS): the workgroup copies x to LDS and
@@ -475,6 +482,10 @@ GemvPlan plan_gemv(int64_t M, int64_t K, int64_t N, int64_t G, size_t workspace_
 hipError_t launch_gemv(const uint16_t* x, const uint8_t* packed, const uint16_t* bias, uint16_t* y,
                        int64_t M, int64_t K, int64_t N, int64_t G, bool bf16, void* workspace,
                        size_t workspace_bytes, hipStream_t stream) {
+    if (M == 1) {
+        const StripPlan sp = plan_gemv_strip(M, K, N, G);
+        if (sp.ok) return launch_gemv_strip(sp, x, packed, bias, y, K, N, G, bf16, stream);
+    }
     const GemvPlan p = plan_gemv(M, K, N, G, workspace ? workspace_bytes : 0);
     GemvArgs args;
     args.x = x;

@@ -42,6 +42,20 @@ hipError_t launch_gemv(const uint16_t* x, const uint8_t* packed, const uint16_t*
                        int64_t M, int64_t K, int64_t N, int64_t G, bool bf16, void* workspace,
                        size_t workspace_bytes, hipStream_t stream);
 
+// Decode GEMV for M = 1 over equal shares of 8-column half blocks, one workgroup per
+// compute unit (G >= 128). ok = false when the shape does not fit it (then the
+// GEMV above runs).
+struct StripPlan {
+    bool ok;
+    int grid;          // workgroups
+    int items;         // code loads in flight per lane
+    size_t lds_bytes;
+};
+StripPlan plan_gemv_strip(int64_t M, int64_t K, int64_t N, int64_t G);
+
+hipError_t launch_gemv_strip(const StripPlan& plan, const uint16_t* x, const uint8_t* packed, const uint16_t* bias,
+                             uint16_t* y, int64_t K, int64_t N, int64_t G, bool bf16, hipStream_t stream);
+
 // Tied-embedding gather: out[t, :] = dequantised column ids[t] of the packed [K, N]
 // weight (zeros for ids outside [0, N)).
 hipError_t launch_embedding(const int32_t* ids, int64_t T, const uint8_t* packed, uint16_t* out, int64_t K,

@@ -1,0 +1,141 @@
+// Streaming references for the HBM-bound rows: how fast this GPU reads (or copies)
+// a given number of bytes, measured beside each GEMV, repack and gather figure so
+// that a kernel's time can be read against the floor a bare stream of the same size
+// reaches (fixed launch cost included). Not a step of the method; the entry points
+// are declared in include/w4a16_measure.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/w4a16.h"
+#include "../../include/w4a16_measure.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int64_t kSmallBytes = (int64_t)64 << 20;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Launch shape, measured on MI355X over 7-140 MB (graph replays, buffers rotated
+// through 1 GiB, Infinity Cache scrubbed): up to 64 MiB, 512-1024 workgroups each
+// streaming one contiguous share with 4 loads per thread in flight (14.2 MB: 3.83 us,
+// against 4.43 us for one 32 KiB pass per workgroup); beyond, one 32 KiB pass per
+// workgroup with 8 loads per thread in flight (140 MB: 21.8 us, against 22.4 us).
+struct Shape {
+    int64_t blocks;
+    int unroll;
+};
+Shape shape_for(size_t bytes) {
+    const int64_t chunks = (int64_t)(bytes / 16);
+    if ((int64_t)bytes <= kSmallBytes) {
+        int64_t b = (int64_t)bytes / (16 << 10);
+        b = b < 512 ? 512 : b > 1024 ? 1024 : b;
+        return {b < chunks ? b : chunks, 4};
+    }
+    return {(chunks + kThreads * 8 - 1) / (kThreads * 8), 8};
+}
+
+// XOR over the 64 lanes of a wave, the same value in every lane: DPP within rows of
+// 16 lanes, then the four rows read back as scalars (a lane-shuffle tree through LDS
+// measured 0.2 us slower at the end of each 14 MB read).
+__device__ __forceinline__ unsigned xor_wave(unsigned v) {
+    v ^= (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);    // quad_perm 1,0,3,2
+    v ^= (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);    // quad_perm 2,3,0,1
+    v ^= (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false);   // row_half_mirror
+    v ^= (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false);   // row_mirror
+    return (unsigned)__builtin_amdgcn_readlane((int)v, 0) ^ (unsigned)__builtin_amdgcn_readlane((int)v, 16) ^
+           (unsigned)__builtin_amdgcn_readlane((int)v, 32) ^ (unsigned)__builtin_amdgcn_readlane((int)v, 48);
+}
+
+// Workgroup b of B streams chunks [b C / B, (b + 1) C / B) of 16 bytes (C chunks in
+// all), thread t reading chunks lo + t, lo + t + 256, ... with kUnroll loads issued
+// before the first is used (nontemporal). Read: the workgroup's XOR of everything it
+// read goes to sink[b]. Copy: each chunk is written to dst at the same offset.
+template <int kUnroll, bool kCopy>
+__global__ __launch_bounds__(kThreads) void stream_kernel(const u32x4* __restrict__ src, int64_t chunks,
+                                                          u32x4* __restrict__ out) {
+    __shared__ u32x4 part[kThreads / 64];
+    const int64_t nb = gridDim.x;
+    const int64_t lo = (int64_t)blockIdx.x * chunks / nb;
+    const int64_t hi = (int64_t)(blockIdx.x + 1) * chunks / nb;
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    for (int64_t base = lo + threadIdx.x; base < hi; base += (int64_t)kThreads * kUnroll) {
+        u32x4 v[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t i = base + (int64_t)u * kThreads;
+            v[u] = i < hi ? __builtin_nontemporal_load(src + i) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            if constexpr (kCopy) {
+                const int64_t i = base + (int64_t)u * kThreads;
+                if (i < hi) __builtin_nontemporal_store(v[u], out + i);
+            } else {
+                acc ^= v[u];
+            }
+        }
+    }
+    if constexpr (!kCopy) {
+        acc.x = xor_wave(acc.x);
+        acc.y = xor_wave(acc.y);
+        acc.z = xor_wave(acc.z);
+        acc.w = xor_wave(acc.w);
+        const int w = threadIdx.x >> 6;
+        if ((threadIdx.x & 63) == 0) part[w] = acc;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            u32x4 r = part[0];
+#pragma unroll
+            for (int i = 1; i < kThreads / 64; ++i) r ^= part[i];
+            out[blockIdx.x] = r;
+        }
+    }
+}
+
+template <bool kCopy>
+void launch_stream(const void* src, size_t bytes, void* out, hipStream_t stream) {
+    const Shape sh = shape_for(bytes);
+    const auto* s = static_cast<const u32x4*>(src);
+    auto* o = static_cast<u32x4*>(out);
+    if (sh.unroll == 4)
+        hipLaunchKernelGGL((stream_kernel<4, kCopy>), dim3((unsigned)sh.blocks), dim3(kThreads), 0, stream, s,
+                           (int64_t)(bytes / 16), o);
+    else
+        hipLaunchKernelGGL((stream_kernel<8, kCopy>), dim3((unsigned)sh.blocks), dim3(kThreads), 0, stream, s,
+                           (int64_t)(bytes / 16), o);
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr size_t kMaxBytes = (size_t)1 << 40;
+
+}  // namespace
+
+extern "C" {
+
+size_t w4a16_stream_sink_bytes(size_t bytes) {
+    if (bytes == 0 || bytes % 16 != 0 || bytes > kMaxBytes) return 0;
+    return (size_t)shape_for(bytes).blocks * 16;
+}
+
+w4a16_status w4a16_stream_read(const void* src, size_t bytes, void* sink, size_t sink_bytes, void* stream) {
+    if (bytes % 16 != 0 || bytes > kMaxBytes) return W4A16_ERR_SHAPE;
+    if (bytes == 0) return W4A16_OK;
+    if (!src || !sink) return W4A16_ERR_NULL;
+    if (!aligned16(src) || !aligned16(sink)) return W4A16_ERR_ALIGN;
+    if (sink_bytes < w4a16_stream_sink_bytes(bytes)) return W4A16_ERR_BUFFER_SIZE;
+    launch_stream<false>(src, bytes, sink, static_cast<hipStream_t>(stream));
+    return hipGetLastError() == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
+w4a16_status w4a16_stream_copy(const void* src, void* dst, size_t bytes, void* stream) {
+    if (bytes % 16 != 0 || bytes > kMaxBytes) return W4A16_ERR_SHAPE;
+    if (bytes == 0) return W4A16_OK;
+    if (!src || !dst) return W4A16_ERR_NULL;
+    if (!aligned16(src) || !aligned16(dst)) return W4A16_ERR_ALIGN;
+    launch_stream<true>(src, bytes, dst, static_cast<hipStream_t>(stream));
+    return hipGetLastError() == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
+}  // extern "C"
