@@ -51,8 +51,8 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [
 --pmc-probe runs, without graphs or timing, a 256 MiB device copy (the calibration
 kernel for the byte counters: it reads and writes exactly 256 MiB) three times, then
 the headline GEMV ten times on rotating weight copies, the down-projection GEMV at M=1
-and M=8 ten times each and the LM-head M=512 GEMM three times, so that counter runs see
-one dispatch per launch.
+and M=8 ten times each, the LM-head repack 1 + 3 times and the LM-head M=512 GEMM and
+W4A8 GEMM three times each, so that counter runs see one dispatch per launch.
 """
 
 import argparse
@@ -412,7 +412,9 @@ def roofline_mfma(entry, peak=None, dense=None):
 
 CALIBRATION_COPY_BYTES = 256 << 20
 COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "gemv_gate_up_decode_M1_counters.md")
-GEMV_SOURCES = ("w4a16_int4_weight_amd/csrc/gemv.hip", "w4a16_int4_weight_amd/csrc/device_common.h")
+# the headline launch runs the balanced M = 1 GEMV (gemv_strip.hip), dispatched from gemv.hip
+GEMV_SOURCES = ("w4a16_int4_weight_amd/csrc/gemv_strip.hip", "w4a16_int4_weight_amd/csrc/gemv.hip",
+                "w4a16_int4_weight_amd/csrc/device_common.h")
 
 
 def gemv_source_hash():
@@ -458,12 +460,17 @@ def pmc_probe(dev):
             w.w4a16_gemm(x, packs[i % len(packs)], ws.N, ws.group_size, y=y)
         torch.cuda.synchronize()
         del packs
-    # the MFMA GEMM on the LM-head prefill (M=512), three launches on one weight copy
+    # the LM-head repack three times, then the MFMA GEMM on the LM-head prefill (M=512),
+    # three launches on one weight copy
     ws = synth.make("lm_head", Ms=(512,))
     qw = torch.from_numpy(ws.qweight).to(dev)
     qz = torch.from_numpy(ws.qzeros).to(dev)
     sc = to_dev_bits(ws.scale_bits, ws.dtype, dev)
     packed = w.w4a16_repack(qw, qz, sc, ws.group_size)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        w.w4a16_repack(qw, qz, sc, ws.group_size, packed=packed)
+    torch.cuda.synchronize()
     del qw, qz, sc
     x = to_dev_bits(ws.x_bits[512], ws.dtype, dev)
     y = torch.empty((512, ws.N), dtype=x.dtype, device=dev)
@@ -477,7 +484,7 @@ def pmc_probe(dev):
         w.w4a8_gemm(act, packed, 512, ws.K, ws.N, ws.group_size, x.dtype, y=y)
     torch.cuda.synchronize()
     log("pmc probe done: 3 x 256 MiB copy, 10 x gate_up_decode GEMV, 10 x down_proj GEMV M=1 and M=8, "
-        "3 x lm_head M=512 GEMM, 3 x lm_head M=512 W4A8 GEMM")
+        "1 + 3 x lm_head repack, 3 x lm_head M=512 GEMM, 3 x lm_head M=512 W4A8 GEMM")
 
 
 def cpu_model():
@@ -648,7 +655,7 @@ def main():
         "cpu_baseline": cpu,
         "secondary": secondary,
         "dense_bf16_reference": dense,
-        "gpu_timing_s": round(gpu_s, 1),
+        "measure_wall_s": round(gpu_s, 1),
     }
     print(json.dumps(line), flush=True)
 
