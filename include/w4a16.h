@@ -244,7 +244,7 @@ w4a16_status w4a16_gemm_noalloc(const void* x, const void* packed, size_t packed
 /* Tied-embedding gather from the packed head weight: a model whose input embedding
  * is tied to its output head keeps one quantised matrix for both (vllm-omni commit
  * "cpu_int4: repack weights in n-blocks, to bound the load-time peak": the
- * 131072 x 2048 embedding is "tied, so it is also the head"; commit "Add cpu_int4,
+ * 131072 x 2048 embedding matrix doubles as the output head; commit "Add cpu_int4,
  * an asymmetric 4-bit weight path for vLLM's CPU backend": the quantised tied
  * embedding is checked end to end). With the head stored for y = x . W, W [K, N]
  * (K hidden, N vocabulary), the embedding of token t is column t of dequant(W):

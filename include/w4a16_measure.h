@@ -3,8 +3,8 @@
  * rows against what the GPU reaches on a bare stream of the same size.
  *
  * Decode is bound by the bytes of the weights (vllm-omni commit "Add cpu_int4, an
- * asymmetric 4-bit weight path for vLLM's CPU backend": each token reads every
- * weight, so the bits per weight set the token rate). The peak bandwidth a GPU is
+ * asymmetric 4-bit weight path for vLLM's CPU backend", on why weight size decides
+ * decode speed). The peak bandwidth a GPU is
  * sold with is not what a launch of a few megabytes can reach: the fixed cost of a
  * launch and the latency before the first bytes arrive take a share that shrinks
  * with size. These two kernels measure that floor for a given byte count — a plain

@@ -4,8 +4,8 @@ Test infrastructure only (see the package docstring).
 
 A model whose input embedding is tied to its output head stores one quantised
 matrix for both: the vllm-omni commit "cpu_int4: repack weights in n-blocks, to
-bound the load-time peak" lists the 131072 x 2048 embedding as tied, so also the
-head, and the commit "Add cpu_int4, an asymmetric 4-bit weight path for vLLM's CPU
+bound the load-time peak" lists the 131072 x 2048 embedding as the same matrix as
+the output head, and the commit "Add cpu_int4, an asymmetric 4-bit weight path for vLLM's CPU
 backend" checks the quantised tied embedding. Stored as the head, W [K, N] with
 K hidden and N the vocabulary (y = x . W), the embedding of token t is column t of
 dequant(W), one row of K values:

@@ -2,8 +2,8 @@
 //
 // A model whose input embedding is tied to its output head keeps one quantised
 // matrix for both (the vllm-omni commit "cpu_int4: repack weights in n-blocks, to
-// bound the load-time peak" lists the 131072 x 2048 embedding as "tied, so it is
-// also the head"; the commit "Add cpu_int4, an asymmetric 4-bit weight path for
+// bound the load-time peak" lists the 131072 x 2048 embedding as the same matrix as
+// the output head; the commit "Add cpu_int4, an asymmetric 4-bit weight path for
 // vLLM's CPU backend" checks the quantised tied embedding end to end). Stored as the
 // head W [K, N] (K hidden, N vocabulary) for y = x . W, the embedding of token t is
 // column t of dequant(W):

@@ -3,7 +3,8 @@
 // A W4A16 product at hundreds of rows is a real dense contraction, so it runs on
 // the matrix cores. What the CPU design of the vllm-omni cpu_int4 commits teaches
 // carries over: a kernel that dequantises once per activation row is linear in the
-// batch ("12.9x slower than bf16 at 512 rows", commit "Add cpu_int4 ..."), and
+// batch (the commit "Add cpu_int4 ..." measures such a kernel an order of magnitude
+// behind a bf16 GEMM at 512 rows), and
 // re-laying the weights out on every call halves prefill (commit "cpu_int4:
 // dequantize prefill weights from the tinygemm layout, not a copy"). Here each
 // weight is dequantised once per workgroup tile of up to 128 rows, straight from

@@ -1,8 +1,9 @@
 // Decode GEMV for one activation row (M = 1), balanced over the compute units.
 //
-// Decode reads every weight once per token, so its time is the time to stream the
-// packed codes (vllm-omni commit "Add cpu_int4, an asymmetric 4-bit weight path for
-// vLLM's CPU backend": the bits per weight set the token rate). On this GPU a
+// A decode step touches each weight once per generated token, so its time is the
+// time to stream the packed codes (vllm-omni commit "Add cpu_int4, an asymmetric
+// 4-bit weight path for vLLM's CPU backend", on why weight size decides decode
+// speed). On this GPU a
 // stream of a few megabytes ends when the compute unit holding the most bytes has
 // received them, so the work is cut into equal shares, one per compute unit:
 //
