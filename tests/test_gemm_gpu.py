@@ -347,12 +347,13 @@ def test_gemv_long_k(w, K, M):
                                          (8, 2048, 2048, "bf16")])
 def test_gemv_k_split_over_workgroups(w, M, K, N, dtype):
     # narrow outputs (at most 128 column blocks) with K >= 6144 split each block's K
-    # range over 2-4 workgroups from M = 6 when the workspace holds their partials
-    # (N = 2048: 2 ways, N = 1280: 3, N = 1000: 4; M = 1 and K = 2048 keep one
-    # workgroup per block): parity with the oracle, the
-    # same result on a second call, the counters left at zero, nothing written
-    # outside y (N = 1000: a ragged last block); without a workspace one workgroup
-    # per block gives a result within the same tolerance
+    # range over 2-4 workgroups from M = 9 when the workspace holds their partials
+    # (N = 2048: 2 ways, N = 1280: 3); M = 1 runs the balanced GEMV, M = 2 .. 8 the
+    # balanced matrix-core GEMV (M = 8 and M = 6 with N = 1000 here), K = 2048 keeps one
+    # workgroup per block, and none of those touch the workspace: parity with the
+    # oracle, the same result on a second call, the counters left at zero, nothing
+    # written outside y (N = 1000: a ragged last block); without a workspace one
+    # workgroup per block gives a result within the same tolerance
     print(f"gemv K split over workgroups M={M} K={K} N={N} {dtype}", flush=True)
     ws = synth.make_custom(150 + M, M, K, N, dtype, 128)
     packed = pack_on_gpu(w, ws)
@@ -374,8 +375,8 @@ def test_gemv_k_split_over_workgroups(w, M, K, N, dtype):
     assert np.array_equal(outs[0], outs[1])
     assert int(work[:512].count_nonzero()) == 0
     # the partials region shows whether the split ran: written by the split cases,
-    # untouched by M = 1 (the balanced M = 1 GEMV) and by K = 2048
-    splits = M >= 6 and K >= 6144
+    # untouched by the balanced GEMVs (M <= 8) and by K = 2048
+    splits = M > 8 and K >= 6144
     assert (int(work[512:].count_nonzero()) > 0) == splits, (M, K, N)
     assert ogemm.max_rel_error(numerics.half_bits_to_f64(outs[0], dtype), ref) <= TOL
     none = torch.empty(0, dtype=torch.uint8, device=DEV)
@@ -387,24 +388,25 @@ def test_gemv_k_split_over_workgroups(w, M, K, N, dtype):
 def test_gemv_needs_no_workspace(w):
     # a NULL workspace (an empty buffer; None would get the binding's default) on a
     # shape whose GEMV would split K over workgroups given one: one workgroup per block
-    ws = synth.make_custom(140, 8, 6656, 2048, "bf16", 128)
+    ws = synth.make_custom(140, 12, 6656, 2048, "bf16", 128)
     packed = pack_on_gpu(w, ws)
-    x = bits_to_device(ws.x_bits[8], "bf16")
+    x = bits_to_device(ws.x_bits[12], "bf16")
     none = torch.empty(0, dtype=torch.uint8, device=DEV)
     y = w.w4a16_gemm_ex(x, packed, 2048, 128, workspace=none, path="gemv")
     torch.cuda.synchronize()
-    assert ogemm.max_rel_error(y_to_f64(y, "bf16"), oracle_y(ws, ws.x_bits[8])) <= TOL
+    assert ogemm.max_rel_error(y_to_f64(y, "bf16"), oracle_y(ws, ws.x_bits[12])) <= TOL
 
 
-@pytest.mark.parametrize("K,M,N,dtype", [(2048, 1, 13296, "bf16"), (2048, 8, 13296, "bf16"),
+@pytest.mark.parametrize("K,M,N,dtype", [(2048, 1, 13296, "bf16"), (2048, 9, 13296, "bf16"),
                                          (2048, 3, 13296, "fp16"), (512, 2, 13296, "bf16"),
-                                         (1024, 5, 13296, "bf16"), (1024, 4, 16400, "bf16"),
+                                         (1024, 3, 13296, "bf16"), (1024, 4, 16400, "bf16"),
                                          (1024, 8, 16400, "fp16")])
 def test_gemv_several_column_blocks_per_workgroup(w, K, M, N, dtype):
-    # N = 13296 (831 column blocks) runs 2 blocks per workgroup at every M, N = 16400
-    # (1025 blocks) from M = 4: the last workgroup has a block past N, which repeats
-    # the last block and must store nothing. K = 512 has one wave per block (no K
-    # split), K = 1024 two.
+    # the 16-column GEMV: N = 13296 (831 column blocks) runs 2 blocks per workgroup at
+    # every M it takes (M = 4 .. 8 there go to the balanced matrix-core GEMV), N = 16400
+    # (1025 blocks, beyond that kernel's 8 units per lane) from M = 4: the last
+    # workgroup has a block past N, which repeats the last block and must store
+    # nothing. K = 512 has one wave per block (no K split), K = 1024 two.
     print(f"gemv 2 blocks per workgroup K={K} M={M} N={N} {dtype}", flush=True)
     ws = synth.make_custom(1000 + K // 128 + M, M, K, N, dtype, 128)
     packed = pack_on_gpu(w, ws)
@@ -482,5 +484,44 @@ def test_gemv_m1_balanced_half_blocks(w, K, N, dtype, G, bias):
     assert torch.all(b[:pad] == -7.0) and torch.all(b[-pad:] == -7.0), "write outside y"
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), "not run-to-run deterministic"
     err = ogemm.max_rel_error(y_to_f64(y, dtype), oracle_y(ws, ws.x_bits[1], bias_bits=bias_bits))
+    print(f"  max rel err {err:.3e}", flush=True)
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("M,K,N,dtype,G,bias", [
+    (2, 6656, 2048, "bf16", 128, True),    # 128 column blocks: M = 2 takes it; 26 units, 4 per wave
+    (8, 6656, 2048, "fp16", 128, False),   # the down_proj decode shape at M = 8
+    (5, 2048, 13312, "bf16", 128, True),   # 6 or 7 half blocks per workgroup, one unit each per wave
+    (4, 2048, 3072, "fp16", 128, False),   # 1 or 2 half blocks per workgroup
+    (7, 1152, 272, "bf16", 128, False),    # 9 row blocks: the last unit lacks its second row block
+    (6, 1408, 264, "bf16", 128, True),     # N % 16 == 8 (a last lower half block), 11 row blocks
+    (3, 1536, 1040, "bf16", -1, False),    # 65 column blocks: M = 3 takes it; one group of all K rows
+    (8, 16384, 520, "bf16", 256, True),    # 64 units per half block: 8 per wave; G = 256
+    (4, 128, 8, "fp16", 128, False),       # one workgroup, one unit with one row block
+    (8, 2048, 4104, "bf16", 128, False),   # 513 half blocks: workgroups of 2 and 3
+])
+def test_gemv_small_batch_matrix_cores(w, M, K, N, dtype, G, bias):
+    # the balanced matrix-core GEMV for 2 <= M <= 8: the whole output against the
+    # oracle, bias, run-to-run identical results, nothing written outside y
+    print(f"gemv small batch M={M} K={K} N={N} {dtype} G={G} bias={bias}", flush=True)
+    ws = synth.make_custom(1900 + M + K % 991 + N % 83, M, K, N, dtype, G)
+    packed = pack_on_gpu(w, ws)
+    bias_bits = None
+    bt = None
+    if bias:
+        rng = np.random.default_rng(N + M)
+        bias_bits = synth.f32_to_half_bits(rng.standard_normal(N, dtype=np.float32), dtype)
+        bt = bits_to_device(bias_bits, dtype)
+    x = bits_to_device(ws.x_bits[M], dtype)
+    pad = 4096
+    buf = torch.full((M * N + 2 * pad,), -7.0, dtype=TORCH_DTYPE[dtype], device=DEV)
+    y = buf[pad:pad + M * N].view(M, N)
+    w.w4a16_gemm_ex(x, packed, N, G, bias=bt, y=y, path="gemv")
+    y2 = w.w4a16_gemm(x, packed, N, G, bias=bt)
+    torch.cuda.synchronize()
+    b = buf.cpu()
+    assert torch.all(b[:pad] == -7.0) and torch.all(b[-pad:] == -7.0), "write outside y"
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), "not run-to-run deterministic"
+    err = ogemm.max_rel_error(y_to_f64(y, dtype), oracle_y(ws, ws.x_bits[M], bias_bits=bias_bits))
     print(f"  max rel err {err:.3e}", flush=True)
     assert err <= TOL

@@ -12,7 +12,7 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_NAME = "libw4a16.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["api.hip", "repack.hip", "gemv.hip", "gemv_strip.hip", "gemm.hip", "embedding.hip", "w4a8.hip", "measure.hip"]
+SOURCES = ["api.hip", "repack.hip", "gemv.hip", "gemv_strip.hip", "gemv_small.hip", "gemm.hip", "embedding.hip", "w4a8.hip", "measure.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

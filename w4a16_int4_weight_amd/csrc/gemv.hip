@@ -32,8 +32,10 @@
 //
 // One activation row (M = 1) takes the balanced GEMV of gemv_strip.hip instead when
 // the shape fits it (groups of 128 rows or more, K <= 8192, at most 16 of its code
-// loads per lane); this kernel runs the other M = 1 shapes (the LM head, K > 8192,
-// group sizes 32 and 64) and M = 2 .. 16.
+// loads per lane), and 4 <= M <= 8 (2 <= M <= 8 on outputs of at most 128 column
+// blocks) the balanced matrix-core GEMV of gemv_small.hip (groups of 128 rows or more,
+// at most 8 units in flight per lane); this kernel runs the other shapes: the LM
+// head, long K, group sizes 32 and 64, M = 2 and 3 on wide outputs, M = 9 .. 16.
 //
 // Two variants:
 //   staged  (the activations fit in LDS): the workgroup copies x to LDS and
@@ -482,6 +484,10 @@ GemvPlan plan_gemv(int64_t M, int64_t K, int64_t N, int64_t G, size_t workspace_
 hipError_t launch_gemv(const uint16_t* x, const uint8_t* packed, const uint16_t* bias, uint16_t* y,
                        int64_t M, int64_t K, int64_t N, int64_t G, bool bf16, void* workspace,
                        size_t workspace_bytes, hipStream_t stream) {
+    if (M >= 2) {
+        const SmallPlan sp = plan_gemv_small(M, K, N, G);
+        if (sp.ok) return launch_gemv_small(sp, x, packed, bias, y, M, K, N, G, bf16, stream);
+    }
     if (M == 1) {
         const StripPlan sp = plan_gemv_strip(M, K, N, G);
         if (sp.ok) return launch_gemv_strip(sp, x, packed, bias, y, K, N, G, bf16, stream);

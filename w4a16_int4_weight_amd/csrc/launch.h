@@ -56,6 +56,21 @@ StripPlan plan_gemv_strip(int64_t M, int64_t K, int64_t N, int64_t G);
 hipError_t launch_gemv_strip(const StripPlan& plan, const uint16_t* x, const uint8_t* packed, const uint16_t* bias,
                              uint16_t* y, int64_t K, int64_t N, int64_t G, bool bf16, hipStream_t stream);
 
+// Decode GEMV for 2 <= M <= 8 on the matrix cores over equal shares of 8-column half
+// blocks, one workgroup per compute unit (G >= 128). ok = false when the shape does
+// not fit it or the GEMV above is faster on it.
+struct SmallPlan {
+    bool ok;
+    int P;             // units (row-block pairs) per half block
+    int grid;          // workgroups
+    int smax;          // most half blocks of any workgroup
+    int JP;            // most units of one half block per wave
+};
+SmallPlan plan_gemv_small(int64_t M, int64_t K, int64_t N, int64_t G);
+
+hipError_t launch_gemv_small(const SmallPlan& plan, const uint16_t* x, const uint8_t* packed, const uint16_t* bias,
+                             uint16_t* y, int64_t M, int64_t K, int64_t N, int64_t G, bool bf16, hipStream_t stream);
+
 // Tied-embedding gather: out[t, :] = dequantised column ids[t] of the packed [K, N]
 // weight (zeros for ids outside [0, N)).
 hipError_t launch_embedding(const int32_t* ids, int64_t T, const uint8_t* packed, uint16_t* out, int64_t K,
