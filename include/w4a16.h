@@ -169,9 +169,10 @@ w4a16_status w4a16_parse_packed_header(const void* header, size_t header_bytes, 
  * (fp32) and one counter per output tile live there. Independent of the path that
  * w4a16_gemm_ex would choose: the value suffices for every path. The GEMV uses the
  * workspace too when one this large is passed, from M = 6 on outputs of at most 128
- * column blocks (N <= 2048) with K >= 6144, to split K over workgroups; with NULL it
- * runs one workgroup per column block (same result within the tolerance, not bit
- * for bit).
+ * column blocks (N <= 2048) with K >= 6144, to split K over workgroups, where its
+ * balanced variants do not take the shape (in practice from M = 9, or with groups of
+ * 32 or 64 rows); with NULL it runs one workgroup per column block (same result
+ * within the tolerance, not bit for bit).
  *
  * Layout: its first 512 bytes hold the tile counters for every shape (a split plan
  * has fewer than 128 output tiles), the partial sums follow.
@@ -208,8 +209,10 @@ w4a16_status w4a16_gemm(const void* x, const void* packed, size_t packed_bytes, 
  * W4A16_PATH_AUTO, M <= gemv_max_m takes the GEMV (gemv_max_m in 0..16; a
  * negative value selects the default, which w4a16_gemm uses: 8, raised to 12 when
  * the codes (K*N/2 bytes) take at most 16 MiB and to 15 at most 4 MiB or when
- * N <= 2048 and K >= 2048, for groups of 128 rows or more, where the GEMV was measured faster up
- * to those row counts).
+ * N <= 2048 and K >= 2048, and to 16 on outputs of at least 512 16-column blocks that
+ * the balanced matrix-core GEMV takes at M = 16 (at most 8 half blocks per compute
+ * unit), for groups of 128 rows or more, where the GEMV was measured faster up to those
+ * row counts).
  * W4A16_PATH_GEMV requires M <= 16. Both paths read the same packed buffer. */
 w4a16_status w4a16_gemm_ex(const void* x, const void* packed, size_t packed_bytes, w4a16_dtype dtype,
                            void* y, int64_t M, int64_t K, int64_t N, int64_t group_size,

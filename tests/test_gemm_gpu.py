@@ -203,8 +203,9 @@ def test_gemm_rejects_bad_calls(w):
 @pytest.mark.parametrize("M,K,N,path,G", [
     (8, 2048, 20480, "gemv", 128),     # M <= 8: the GEMV at every size
     (9, 2048, 20480, "mfma", 128),     # 20 MiB of codes: the MFMA GEMM from M = 9
-    (12, 2048, 13312, "gemv", 128),    # 13 MiB: the GEMV through M = 12
-    (13, 2048, 13312, "mfma", 128),
+    (12, 2048, 13312, "gemv", 128),    # 832 column blocks, at most 7 half blocks per compute unit:
+    (16, 2048, 13312, "gemv", 128),    # the balanced matrix-core GEMV through M = 16
+    (13, 2048, 16400, "mfma", 128),    # 15.6 MiB, 9 half blocks per compute unit: the MFMA GEMM from M = 13
     (15, 2048, 3072, "gemv", 128),     # 3 MiB: the GEMV through M = 15
     (16, 2048, 3072, "mfma", 128),     # M >= 16: the MFMA GEMM at every size
     (9, 2048, 3072, "mfma", 64),       # groups of 64 rows keep the stated M <= 8
@@ -499,9 +500,12 @@ def test_gemv_m1_balanced_half_blocks(w, K, N, dtype, G, bias):
     (8, 16384, 520, "bf16", 256, True),    # 64 units per half block: 8 per wave; G = 256
     (4, 128, 8, "fp16", 128, False),       # one workgroup, one unit with one row block
     (8, 2048, 4104, "bf16", 128, False),   # 513 half blocks: workgroups of 2 and 3
+    (12, 2048, 13312, "bf16", 128, True),  # two row groups (8 + 4 rows) on a wide output
+    (16, 1024, 8200, "fp16", 128, False),  # two full row groups; 1025 half blocks, 4 or 5 per workgroup
+    (9, 2304, 8192, "bf16", 128, True),    # a second group of one row; 9 units per half block
 ])
 def test_gemv_small_batch_matrix_cores(w, M, K, N, dtype, G, bias):
-    # the balanced matrix-core GEMV for 2 <= M <= 8: the whole output against the
+    # the balanced matrix-core GEMV for 2 <= M <= 16: the whole output against the
     # oracle, bias, run-to-run identical results, nothing written outside y
     print(f"gemv small batch M={M} K={K} N={N} {dtype} G={G} bias={bias}", flush=True)
     ws = synth.make_custom(1900 + M + K % 991 + N % 83, M, K, N, dtype, G)

@@ -25,9 +25,13 @@ constexpr int64_t kDefaultGemvMaxM = 8;
 // at 2048 x 131072), so the last GEMV row count follows the size of the codes. Outputs
 // of at most 128 column blocks (N <= 2048) and K >= 2048 keep it through M = 15
 // (2048 .. 8192 x 1024 .. 2048: 6-30% ahead of the MFMA GEMM at M = 12 .. 16, with
-// the GEMV's K split over workgroups where K >= 6144).
+// the GEMV's K split over workgroups where K >= 6144). Wide outputs that the balanced
+// matrix-core GEMV takes at M = 16 keep the GEMV through M = 16 (2048 x 13312: 7.96
+// against 10.2 us for the MFMA GEMM at M = 16, 7.95 against 9.9 us for the 16-column
+// GEMV at M = 12).
 int64_t default_gemv_max_m(int64_t K, int64_t N, int64_t G) {
     if (G % 128 != 0) return kDefaultGemvMaxM;        // group sizes 32, 64: not measured
+    if (w4a16::plan_gemv_small(kGemvMaxRows, K, N, G).ok) return kGemvMaxRows;
     if ((N + 15) / 16 <= 128 && K >= 2048) return 15;
     const int64_t code_bytes = K * N / 2;
     if (code_bytes <= (int64_t(4) << 20)) return 15;

@@ -33,9 +33,10 @@
 // One activation row (M = 1) takes the balanced GEMV of gemv_strip.hip instead when
 // the shape fits it (groups of 128 rows or more, K <= 8192, at most 16 of its code
 // loads per lane), and 4 <= M <= 8 (2 <= M <= 8 on outputs of at most 128 column
-// blocks) the balanced matrix-core GEMV of gemv_small.hip (groups of 128 rows or more,
-// at most 8 units in flight per lane); this kernel runs the other shapes: the LM
-// head, long K, group sizes 32 and 64, M = 2 and 3 on wide outputs, M = 9 .. 16.
+// blocks, up to M = 16 on outputs of at least 512) the balanced matrix-core GEMV of
+// gemv_small.hip (groups of 128 rows or more, at most 8 units in flight per lane); this
+// kernel runs the other shapes: the LM head, long K, group sizes 32 and 64, M = 2 and
+// 3 on wide outputs, M = 9 .. 16 on narrower ones.
 //
 // Two variants:
 //   staged  (the activations fit in LDS): the workgroup copies x to LDS and

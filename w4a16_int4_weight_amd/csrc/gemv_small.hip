@@ -1,4 +1,4 @@
-// Decode GEMV for small batches (2 <= M <= 8) on the matrix cores, balanced over the
+// Decode GEMV for small batches (2 <= M <= 16) on the matrix cores, balanced over the
 // compute units.
 //
 // Like the M = 1 GEMV, the work is cut into equal shares of 8-column half blocks over
@@ -9,8 +9,9 @@
 //
 //   * the MFMA's first operand is 16 weight columns x 32 rows: the half block's 8
 //     columns at row block 2p and the same 8 columns at row block 2p + 1 (a "unit").
-//     The second operand's 16 columns carry the M activation rows twice, once over
-//     each row block's k range; the cross terms are not used;
+//     The second operand's 16 columns carry up to 8 activation rows twice, once over
+//     each row block's k range; the cross terms are not used. M = 9 .. 16 runs two such
+//     row groups, each decoded operand feeding one MFMA per group;
 //   * lane (h, c) holds the 16 code bytes of its column at lane 16 h + c of the 1 KiB
 //     tile block, which is word i of the first operand for k step i: the layout is
 //     already in operand order. Its activations are four 16-byte loads from global
@@ -90,11 +91,12 @@ __device__ __forceinline__ float md_base_zero(uint32_t md) {
 }
 
 // kS >= half blocks of any workgroup, kJP >= units per wave per half block (powers of
-// two).
-template <bool kBF16, int kS, int kJP>
+// two), kG row groups of at most 8 activation rows (rows 8 g .. 8 g + 7; two for
+// M = 9 .. 16): each decoded operand serves one MFMA per group.
+template <bool kBF16, int kS, int kJP, int kG>
 __global__ __launch_bounds__(kThreads) void gemv_small_kernel(const SmallArgs a) {
     using Mg = Magic<kBF16>;
-    __shared__ f32x4 part[kS][kWaves][64];
+    __shared__ f32x4 part[kG][kS][kWaves][64];
     __shared__ __attribute__((aligned(16))) uint32_t mdx[kWaves][kS * kJP][16];
     constexpr int kItems = kS * kJP;
     constexpr uint32_t kOnes = kBF16 ? 0x3F803F80u : 0x3C003C00u;      // (1.0, 1.0)
@@ -110,30 +112,38 @@ __global__ __launch_bounds__(kThreads) void gemv_small_kernel(const SmallArgs a)
     const int h = lane >> 4;
     const int c8 = c & 7;
     const int hi = c >> 3;                   // first operand: the unit's second row block
-    // second operand column c: activation row mrow over the unit's first (bsel = 0) or
-    // second (bsel = 1) row block; columns past 2M load nothing
-    const int bsel = c >= M ? 1 : 0;
-    const int mrow = c - bsel * M;
-    const bool brow = mrow < M;
+    // group rg holds rows 8 rg .. 8 rg + R - 1 (R = min(8, M - 8 rg)); its second operand's
+    // column c is row 8 rg + c - bsel R over the unit's first (bsel = 0) or second
+    // (bsel = 1) row block; columns past 2R read row M - 1 and their outputs are not used
+    int R[kG], bsel[kG], mrow[kG];
+#pragma unroll
+    for (int rg = 0; rg < kG; ++rg) {
+        R[rg] = M - 8 * rg < 8 ? M - 8 * rg : 8;
+        bsel[rg] = c >= R[rg] ? 1 : 0;
+        const int r = c - bsel[rg] * R[rg];
+        mrow[rg] = r < R[rg] ? 8 * rg + r : M - 1;
+    }
     const uint8_t* meta_plane = a.packed + (size_t)KB * kRowsPerBlock * padded_cols(a.N) / 2;
 
     // 1. loads, all issued before the first is used and none under a branch: the
-    //    activations of each unit jp (they serve every half block), then per unit
-    //    j = (half block s = j / kJP, unit p = w + 8 (j % kJP)) the 16 code bytes and the
-    //    metadata word of the lane's first-operand column. Units past this workgroup's half blocks or
-    //    past P, and a unit's missing second row block, read a valid line and take
-    //    scale 0: their contribution is 0. Second-operand columns past 2M
-    //    read row M - 1; their outputs are not used.
-    uint4 xv[kJP][4];
+    //    activations of each unit jp and row group (they serve every half block), then
+    //    per unit j = (half block s = j / kJP, unit p = w + 8 (j % kJP)) the 16 code bytes
+    //    and the metadata word of the lane's first-operand column. Units past this
+    //    workgroup's half blocks or past P, and a unit's missing second row block, read a
+    //    valid line and take scale 0: their contribution is 0.
+    uint4 xv[kG][kJP][4];
 #pragma unroll
-    for (int jp = 0; jp < kJP; ++jp) {
-        const int p = w + kWaves * jp;
-        const int kbb = 2 * p + bsel;
-        const int kbc = kbb < KB ? kbb : KB - 1;
-        const int mr = mrow < M ? mrow : M - 1;
-        const uint4* xp = reinterpret_cast<const uint4*>(a.x + (size_t)mr * K + kRowsPerBlock * kbc + 8 * h);
+    for (int rg = 0; rg < kG; ++rg) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xv[jp][i] = xp[4 * i];
+        for (int jp = 0; jp < kJP; ++jp) {
+            const int p = w + kWaves * jp;
+            const int kbb = 2 * p + bsel[rg];
+            const int kbc = kbb < KB ? kbb : KB - 1;
+            const uint4* xp =
+                reinterpret_cast<const uint4*>(a.x + (size_t)mrow[rg] * K + kRowsPerBlock * kbc + 8 * h);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xv[rg][jp][i] = xp[4 * i];
+        }
     }
     uint4 wq[kItems];
     uint32_t md[kItems];
@@ -154,33 +164,38 @@ __global__ __launch_bounds__(kThreads) void gemv_small_kernel(const SmallArgs a)
     // nothing below moves above the loads
     __builtin_amdgcn_sched_barrier(0);
 
-    // 2. X of the lane's second-operand column per unit: its 32 values, then the sum
-    //    over the four lanes (h = 0..3) of the column
-    float xsum[kJP];
+    // 2. X of the lane's second-operand column per unit and group: its 32 values, then
+    //    the sum over the four lanes (h = 0..3) of the column
+    float xsum[kG][kJP];
 #pragma unroll
-    for (int jp = 0; jp < kJP; ++jp) {
-        float s0 = 0.f, s1 = 0.f;
+    for (int rg = 0; rg < kG; ++rg) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            s0 = dot2<kBF16>(xv[jp][i].x, kOnes, s0);
-            s1 = dot2<kBF16>(xv[jp][i].y, kOnes, s1);
-            s0 = dot2<kBF16>(xv[jp][i].z, kOnes, s0);
-            s1 = dot2<kBF16>(xv[jp][i].w, kOnes, s1);
+        for (int jp = 0; jp < kJP; ++jp) {
+            float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                s0 = dot2<kBF16>(xv[rg][jp][i].x, kOnes, s0);
+                s1 = dot2<kBF16>(xv[rg][jp][i].y, kOnes, s1);
+                s0 = dot2<kBF16>(xv[rg][jp][i].z, kOnes, s0);
+                s1 = dot2<kBF16>(xv[rg][jp][i].w, kOnes, s1);
+            }
+            float t = s0 + s1;
+            t += __shfl_xor(t, 16);
+            t += __shfl_xor(t, 32);
+            xsum[rg][jp] = t;
         }
-        float t = s0 + s1;
-        t += __shfl_xor(t, 16);
-        t += __shfl_xor(t, 32);
-        xsum[jp] = t;
     }
 
-    // 3. per unit: T = sum of (base + q) x over its k range, one MFMA per k step; the
-    //    tile is transposed (lane (h, c), register e: weight column 4 h + e against
-    //    second-operand column c); contribution s (T - (base + z) X) with the scale and
-    //    zero point of weight column 4 h + e
+    // 3. per unit: T = sum of (base + q) x over its k range, one MFMA per k step and
+    //    group; the tile is transposed (lane (h, c), register e: weight column 4 h + e
+    //    against second-operand column c); contribution s (T - (base + z) X) with the
+    //    scale and zero point of weight column 4 h + e
     const uint32_t mask = pair_mask_vgpr();
-    f32x4 acc[kS];
+    f32x4 acc[kG][kS];
 #pragma unroll
-    for (int s = 0; s < kS; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int rg = 0; rg < kG; ++rg)
+#pragma unroll
+        for (int s = 0; s < kS; ++s) acc[rg][s] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < kItems; ++j) {
         const int s = j / kJP;
@@ -191,39 +206,50 @@ __global__ __launch_bounds__(kThreads) void gemv_small_kernel(const SmallArgs a)
         if (h == 0) mdx[w][j][c] = md[j];
         const uint4 m4 = *reinterpret_cast<const uint4*>(&mdx[w][j][4 * h]);
         const uint32_t mdo[4] = {m4.x, m4.y, m4.z, m4.w};
-        f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 t[kG];
+#pragma unroll
+        for (int rg = 0; rg < kG; ++rg) t[rg] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const uint32_t v = pick(wq[j], i);
             const uint4 b = make_uint4((v & mask) | Mg::kBase2, ((v >> 4) & mask) | Mg::kBase2,
                                        ((v >> 8) & mask) | Mg::kBase2, ((v >> 12) & mask) | Mg::kBase2);
-            t = mfma16x16x32<kBF16>(b, xv[jp][i], t);
+#pragma unroll
+            for (int rg = 0; rg < kG; ++rg) t[rg] = mfma16x16x32<kBF16>(b, xv[rg][jp][i], t[rg]);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const float sc = mval[j] ? md_scale<kBF16>(mdo[e]) : 0.f;
-            acc[s][e] = fmaf(sc, fmaf(-md_base_zero<kBF16>(mdo[e]), xsum[jp], t[e]), acc[s][e]);
+            const float zb = md_base_zero<kBF16>(mdo[e]);
+#pragma unroll
+            for (int rg = 0; rg < kG; ++rg)
+                acc[rg][s][e] = fmaf(sc, fmaf(-zb, xsum[rg][jp], t[rg][e]), acc[rg][s][e]);
         }
     }
 #pragma unroll
-    for (int s = 0; s < kS; ++s) part[s][w][lane] = acc[s];
+    for (int rg = 0; rg < kG; ++rg)
+#pragma unroll
+        for (int s = 0; s < kS; ++s) part[rg][s][w][lane] = acc[rg][s];
     __syncthreads();
 
     // 4. output (row m, column 8 (u_lo + s) + jc): the waves' tiles added in wave order
     //    (a unit's two row blocks sit at weight columns jc and jc + 8, second-operand
-    //    columns m and m + M), bias, one rounding; 8 consecutive threads write one row's
-    //    16 contiguous bytes
+    //    columns r and r + R of row m = 8 rg + r), bias, one rounding; 8 consecutive
+    //    threads write one row's 16 contiguous bytes
     const int outs = S * 8 * M;
     for (int o = tid; o < outs; o += kThreads) {
         const int s = o / (8 * M);
-        const int r = o - s * 8 * M;
-        const int m = r >> 3;
-        const int jc = r & 7;
+        const int rr = o - s * 8 * M;
+        const int m = rr >> 3;
+        const int jc = rr & 7;
+        const int rg = kG > 1 ? m >> 3 : 0;
+        const int r = m - 8 * rg;
+        const int Rg = M - 8 * rg < 8 ? M - 8 * rg : 8;
         float sum = 0.f;
 #pragma unroll
         for (int ww = 0; ww < kWaves; ++ww) {
-            sum += part[s][ww][16 * (jc >> 2) + m][jc & 3];
-            sum += part[s][ww][16 * (2 + (jc >> 2)) + m + M][jc & 3];
+            sum += part[rg][s][ww][16 * (jc >> 2) + r][jc & 3];
+            sum += part[rg][s][ww][16 * (2 + (jc >> 2)) + r + Rg][jc & 3];
         }
         const int n = 8 * (u_lo + s) + jc;
         const float b = a.bias ? half_bits_to_f32<kBF16>(a.bias[n]) : 0.f;
@@ -231,27 +257,33 @@ __global__ __launch_bounds__(kThreads) void gemv_small_kernel(const SmallArgs a)
     }
 }
 
-template <bool kBF16, int kJP>
+template <bool kBF16, int kJP, int kG>
 void launch_jp(const SmallArgs& args, int smax, int grid, hipStream_t st) {
     constexpr int kMaxS = kMaxItems / kJP;
-    if (smax <= 1) hipLaunchKernelGGL((gemv_small_kernel<kBF16, 1, kJP>), dim3(grid), dim3(kThreads), 0, st, args);
+    if (smax <= 1) hipLaunchKernelGGL((gemv_small_kernel<kBF16, 1, kJP, kG>), dim3(grid), dim3(kThreads), 0, st, args);
     else if (smax <= 2 && kMaxS >= 2)
-        hipLaunchKernelGGL((gemv_small_kernel<kBF16, (kMaxS >= 2 ? 2 : 1), kJP>), dim3(grid), dim3(kThreads), 0, st,
+        hipLaunchKernelGGL((gemv_small_kernel<kBF16, (kMaxS >= 2 ? 2 : 1), kJP, kG>), dim3(grid), dim3(kThreads), 0, st,
                            args);
     else if (smax <= 4 && kMaxS >= 4)
-        hipLaunchKernelGGL((gemv_small_kernel<kBF16, (kMaxS >= 4 ? 4 : 1), kJP>), dim3(grid), dim3(kThreads), 0, st,
+        hipLaunchKernelGGL((gemv_small_kernel<kBF16, (kMaxS >= 4 ? 4 : 1), kJP, kG>), dim3(grid), dim3(kThreads), 0, st,
                            args);
     else if (kMaxS >= 8)
-        hipLaunchKernelGGL((gemv_small_kernel<kBF16, (kMaxS >= 8 ? 8 : 1), kJP>), dim3(grid), dim3(kThreads), 0, st,
+        hipLaunchKernelGGL((gemv_small_kernel<kBF16, (kMaxS >= 8 ? 8 : 1), kJP, kG>), dim3(grid), dim3(kThreads), 0, st,
                            args);
+}
+
+template <bool kBF16, int kG>
+void launch_groups(const SmallArgs& args, int JP, int smax, int grid, hipStream_t st) {
+    if (JP <= 1) launch_jp<kBF16, 1, kG>(args, smax, grid, st);
+    else if (JP <= 2) launch_jp<kBF16, 2, kG>(args, smax, grid, st);
+    else if (JP <= 4) launch_jp<kBF16, 4, kG>(args, smax, grid, st);
+    else if constexpr (kG == 1) launch_jp<kBF16, 8, kG>(args, smax, grid, st);
 }
 
 template <bool kBF16>
 void launch_typed(const SmallArgs& args, int JP, int smax, int grid, hipStream_t st) {
-    if (JP <= 1) launch_jp<kBF16, 1>(args, smax, grid, st);
-    else if (JP <= 2) launch_jp<kBF16, 2>(args, smax, grid, st);
-    else if (JP <= 4) launch_jp<kBF16, 4>(args, smax, grid, st);
-    else launch_jp<kBF16, 8>(args, smax, grid, st);
+    if (args.M <= 8) launch_groups<kBF16, 1>(args, JP, smax, grid, st);
+    else launch_groups<kBF16, 2>(args, JP, smax, grid, st);
 }
 
 int pow2_at_least(int64_t v) {
@@ -265,7 +297,7 @@ int pow2_at_least(int64_t v) {
 SmallPlan plan_gemv_small(int64_t M, int64_t K, int64_t N, int64_t G) {
     SmallPlan p{};
     p.ok = false;
-    if (M < 2 || M > 8 || G < kRowsPerBlock) return p;
+    if (M < 2 || M > 16 || G < kRowsPerBlock) return p;
     const int64_t U = N / 8;
     const int64_t KB = K / kRowsPerBlock;
     // At M = 2 and 3 the packed-dot-product GEMV is faster where it gives every compute
@@ -273,18 +305,26 @@ SmallPlan plan_gemv_small(int64_t M, int64_t K, int64_t N, int64_t G) {
     // qkv 2048 x 3072 3.6 against 3.8 us); from M = 4, and on outputs of at most 128
     // column blocks (down_proj 6656 x 2048 M = 2: 6.3 against 5.6 us), this kernel is.
     if (M < 4 && padded_cols(N) / kColsPerBlock > 128) return p;
+    // Two row groups (M = 9 .. 16) pay on wide outputs only: every workgroup reads all
+    // M x K activations for its half blocks (gate_up 2048 x 13312, M = 16: 7.96 against
+    // 10.2 us for the MFMA GEMM; qkv 2048 x 3072 5.0 against 5.0 us and down_proj
+    // 6656 x 2048 10.8 against 8.6 us for the 16-column GEMV).
+    if (M > 8 && padded_cols(N) / kColsPerBlock < 512) return p;
     p.P = (int)((KB + 1) / 2);
     p.grid = (int)(U < kTargetWorkgroups ? U : kTargetWorkgroups);
     p.smax = (int)((U + p.grid - 1) / p.grid);
     p.JP = (p.P + kWaves - 1) / kWaves;
     if ((int64_t)pow2_at_least(p.smax) * pow2_at_least(p.JP) > kMaxItems) return p;
+    // two row groups hold twice the activations: at most 4 units per wave
+    if (M > 8 && pow2_at_least(p.JP) > 4) return p;
     p.ok = true;
     return p;
 }
 
 hipError_t launch_gemv_small(const SmallPlan& plan, const uint16_t* x, const uint8_t* packed, const uint16_t* bias,
                              uint16_t* y, int64_t M, int64_t K, int64_t N, int64_t G, bool bf16, hipStream_t stream) {
-    if (!plan.ok || plan.smax < 1 || pow2_at_least(plan.smax) * pow2_at_least(plan.JP) > kMaxItems)
+    if (!plan.ok || plan.smax < 1 || pow2_at_least(plan.smax) * pow2_at_least(plan.JP) > kMaxItems ||
+        M < 2 || M > 16 || (M > 8 && pow2_at_least(plan.JP) > 4))
         return hipErrorInvalidValue;
     SmallArgs args;
     args.x = x;

@@ -56,7 +56,7 @@ StripPlan plan_gemv_strip(int64_t M, int64_t K, int64_t N, int64_t G);
 hipError_t launch_gemv_strip(const StripPlan& plan, const uint16_t* x, const uint8_t* packed, const uint16_t* bias,
                              uint16_t* y, int64_t K, int64_t N, int64_t G, bool bf16, hipStream_t stream);
 
-// Decode GEMV for 2 <= M <= 8 on the matrix cores over equal shares of 8-column half
+// Decode GEMV for 2 <= M <= 16 on the matrix cores over equal shares of 8-column half
 // blocks, one workgroup per compute unit (G >= 128). ok = false when the shape does
 // not fit it or the GEMV above is faster on it.
 struct SmallPlan {
