@@ -43,6 +43,10 @@
 extern "C" {
 #endif
 
+/* The enumerations below end in two range members that are not values: they give each
+ * type every 32-bit integer as a valid value, so an entry point can check and reject
+ * any value a caller passes without undefined behaviour in the C++ implementation. */
+
 typedef enum {
     W4A16_OK = 0,
     W4A16_ERR_NULL = 1,         /* a required pointer is NULL                       */
@@ -55,18 +59,24 @@ typedef enum {
     W4A16_ERR_DEVICE = 7,       /* the current device is not a gfx950 GPU            */
     W4A16_ERR_HIP = 8,          /* the HIP runtime reported an error at launch       */
     W4A16_ERR_PATH = 9,         /* unknown path, or the forced path cannot take M    */
-    W4A16_ERR_LAYOUT = 10       /* packed header bad, or from another layout version */
+    W4A16_ERR_LAYOUT = 10,      /* packed header bad, or from another layout version */
+    W4A16_STATUS_RANGE_MIN_ = -0x7FFFFFFF - 1,
+    W4A16_STATUS_RANGE_MAX_ = 0x7FFFFFFF
 } w4a16_status;
 
 typedef enum {
     W4A16_FP16 = 0,             /* IEEE binary16 activations, scales, bias, output  */
-    W4A16_BF16 = 1              /* bfloat16 activations, scales, bias, output       */
+    W4A16_BF16 = 1,             /* bfloat16 activations, scales, bias, output       */
+    W4A16_DTYPE_RANGE_MIN_ = -0x7FFFFFFF - 1,
+    W4A16_DTYPE_RANGE_MAX_ = 0x7FFFFFFF
 } w4a16_dtype;
 
 typedef enum {
     W4A16_PATH_AUTO = 0,        /* M <= gemv_max_m: GEMV, otherwise MFMA GEMM      */
     W4A16_PATH_GEMV = 1,        /* weight-streaming split-K GEMV, M <= 16          */
-    W4A16_PATH_MFMA = 2         /* LDS-staged dequantise -> MFMA GEMM, any M       */
+    W4A16_PATH_MFMA = 2,        /* LDS-staged dequantise -> MFMA GEMM, any M       */
+    W4A16_PATH_RANGE_MIN_ = -0x7FFFFFFF - 1,
+    W4A16_PATH_RANGE_MAX_ = 0x7FFFFFFF
 } w4a16_path;
 
 /* Version of the packed tile layout. A buffer written by one version must not be

@@ -222,12 +222,18 @@ def test_repack_validation_before_any_device_call(w):
 
 def test_missing_library_fails_loudly(monkeypatch):
     import w4a16_int4_weight_amd as mod
+    monkeypatch.delenv("W4A16_LIBRARY", raising=False)
     monkeypatch.setattr(mod, "LIB_PATH", "/nonexistent/libw4a16.so")
     monkeypatch.setattr(mod, "_lib", None)
     with pytest.raises(ImportError):
         mod.w4a16_packed_bytes(512, 512, 128)
     with pytest.raises(ImportError):
         mod.lib
+    # a library named through W4A16_LIBRARY that is missing is the same hard error
+    monkeypatch.setattr(mod, "LIB_PATH", os.path.join(ROOT, "w4a16_int4_weight_amd", "libw4a16.so"))
+    monkeypatch.setenv("W4A16_LIBRARY", "/nonexistent/libw4a16_other.so")
+    with pytest.raises(ImportError):
+        mod.w4a16_packed_bytes(512, 512, 128)
 
 
 def test_build_module_and_binding_agree_on_library_path():

@@ -74,10 +74,13 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m w4a16_int4_weight_amd.build` "
+    # W4A16_LIBRARY names another build of the same library (the host-sanitized one the
+    # CPU tests load); a missing file is the same hard error
+    path = os.environ.get("W4A16_LIBRARY") or LIB_PATH
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python -m w4a16_int4_weight_amd.build` "
                           "(the W4A16 path has no fallback)")
-    h = ctypes.CDLL(LIB_PATH)
+    h = ctypes.CDLL(path)
     _vp, _i64, _sz, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
     h.w4a16_layout_version.argtypes = []
     h.w4a16_layout_version.restype = _int

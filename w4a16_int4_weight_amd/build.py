@@ -30,10 +30,28 @@ def hipcc():
     raise RuntimeError("hipcc not found: the W4A16 library needs ROCm's hipcc to build")
 
 
-def build(verbose=False):
-    """Compiles every source into LIB_PATH (always recompiles). Returns the path."""
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc()] + HIPCC_FLAGS + ["-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES]
+# Host-side AddressSanitizer and UndefinedBehaviorSanitizer for the host code only (the
+# C ABI's validation, plans and launchers); the device code is built as usual. The
+# library then needs the ASan runtime preloaded into the process that loads it.
+SANITIZE_HOST_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=undefined"]
+
+
+def asan_runtime():
+    """Path of the ASan runtime a host-sanitized library needs preloaded."""
+    res = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = res.stdout.strip()
+    if res.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("the ASan runtime of the ROCm compiler was not found")
+    return path
+
+
+def build(verbose=False, out=None, sanitize_host=False):
+    """Compiles every source into LIB_PATH, or `out` (always recompiles). Returns the path.
+    sanitize_host: host code built with ASan and UBSan (see SANITIZE_HOST_FLAGS)."""
+    target = out or LIB_PATH
+    tmp = target + ".tmp"
+    flags = HIPCC_FLAGS + (SANITIZE_HOST_FLAGS if sanitize_host else [])
+    cmd = [hipcc()] + flags + ["-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -44,8 +62,8 @@ def build(verbose=False):
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs), flush=True)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, target)
+    return target
 
 
 if __name__ == "__main__":
