@@ -454,12 +454,15 @@ def test_gemm_tile_shapes(w, M, N, dtype):
 
 
 @pytest.mark.parametrize("K,N,dtype,G,bias", [
-    (2048, 13312, "bf16", 128, False),   # 1664 half blocks on 256 workgroups: 6 or 7 each, 1 pair per group
-    (6656, 2048, "bf16", 128, True),     # one half block per workgroup, 4 pairs per group
+    (2048, 13312, "bf16", 128, False),   # 1664 half blocks on 256 workgroups: 6 or 7 each, 1 row block per group
+    (6656, 2048, "bf16", 128, True),     # one half block per workgroup, 4 row blocks per group, 52 of 64 groups busy
     (128, 8, "fp16", 128, False),        # one workgroup, one half block, 4 of 64 groups busy
     (256, 24, "bf16", 128, True),        # a last half block (N % 16 == 8), 3 workgroups
-    (16384, 2056, "bf16", 128, False),   # 8 pairs per group, 257 half blocks: one workgroup takes 2
-    (4096, 4104, "fp16", 256, True),     # 2 pairs per group, 3 half blocks per workgroup, groups of 256
+    (16384, 2056, "bf16", 128, False),   # 8 row blocks per group would be needed: the 16-column GEMV runs
+    (4096, 4104, "fp16", 256, True),     # 2 row blocks per group, 3 half blocks per workgroup, groups of 256
+    (2176, 520, "fp16", 128, True),      # 17 row blocks in runs of 2: the last group has one
+    (6784, 1032, "bf16", 128, False),    # 53 row blocks in runs of 4: the last group has one; N % 16 == 8
+    (8192, 2048, "bf16", 128, True),     # 64 row blocks: every group busy with 4
     (1536, 1040, "bf16", -1, False),     # one group of all K rows
     (1024, 40000, "bf16", 128, False),   # 20 half blocks per workgroup: beyond the balanced GEMV, the
                                          # 16-column GEMV runs

@@ -15,18 +15,23 @@
 //   * workgroup g of G takes half blocks [g U / G, (g + 1) U / G) of the U = N / 8,
 //     so no compute unit holds more than one half block above the average (the
 //     16-column GEMV over 832 blocks leaves 160 compute units with two workgroups);
-//   * its 64 groups of 8 lanes take the (row block, lane quarter h) pairs of each
-//     half block in turn: lane c of a group loads the 16 bytes of column c (32 codes
-//     of rows 32i + 8h + e) with one nontemporal 128-bit load, every load of the
-//     workgroup issued before the first is used;
+//   * its 64 groups of 8 lanes split each half block's (row block, lane quarter h)
+//     pairs: group q takes quarter h = q % 4 of JP consecutive row blocks from
+//     JP (q / 4) on (JP = ceil(K / 2048), a power of two). Lane c of a group loads the
+//     16 bytes of column c (32 codes of rows 32i + 8h + e) per row block with one
+//     nontemporal 128-bit load, and the column's JP metadata words for those row
+//     blocks with one load; every load of the workgroup is issued before the first
+//     is used;
 //   * a code pair (rows 2t, 2t+1 sit in nibble slots t and t + 4) masked into the
 //     16-bit value 128.0 (bf16) or 1024.0 (fp16) gives base + q exactly, so one
 //     packed dot product with the matching activation pair sums x (base + q) with
 //     exact products; base and zero point leave in one correction per row block and
 //     lane quarter, s (T - (base + z) X) with X the sum of the same 32 activations;
-//   * the activations, their quarter sums X and the workgroup's metadata words (a
-//     contiguous range of the metadata plane) are staged in LDS by direct
-//     global -> LDS copies issued ahead of the code loads;
+//   * the activations a lane needs (32 per row block) sit in its registers: loaded
+//     directly with one row block per group, and with several read once from a copy
+//     of all K of them that the workgroup stages in LDS by direct global -> LDS
+//     copies issued ahead of the code loads (each value then serves the 8 lanes of
+//     its group without 8 separate global reads);
 //   * each group's partial per half block lands in its own LDS slot and the slots
 //     are added in group order: the result is run-to-run deterministic.
 #include "device_common.h"
@@ -39,7 +44,7 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kGroups = kThreads / 8;       // 8-lane groups, one column each lane
 constexpr int kMaxItems = 16;               // code loads in flight per lane
-constexpr int kMaxPairsPerGroup = 4;
+constexpr int kMaxPairsPerGroup = 4;        // row blocks per group (K <= 8192)
 constexpr int kTargetWorkgroups = 256;      // one per compute unit
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -86,24 +91,47 @@ struct StripArgs {
 };
 
 // LDS: the partials, smax half blocks x 8 columns x 64 group slots, fp32; then, with
-// several pairs per group, the activations (K 16-bit values, padded to 1 KiB)
+// several row blocks per group, the activations (K 16-bit values, padded to 1 KiB)
 __host__ __device__ inline int part_bytes(int smax) { return smax * 8 * kGroups * 4; }
 
 __device__ __forceinline__ uint32_t load4(const uint8_t* p) { return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p)); }
 
-// kS >= smax half blocks per workgroup and kJP pairs per group per half block, both
-// powers of two: kS * kJP items per lane. Every load of a lane is issued up front, in
-// this order: the activations of its pairs (4 x 16 bytes per pair, L2-resident after
-// the first workgroups read them), then per item the metadata word and the 16 code
-// bytes; no barrier precedes the arithmetic, so each item is used as soon as its
-// loads land.
+// n consecutive 32-bit words (n = 1, 2 or 4; the address a multiple of 4 n bytes) in
+// one load
+template <int n>
+__device__ __forceinline__ void load_words(const uint8_t* p, uint32_t (&w)[n]) {
+    if constexpr (n == 1) {
+        w[0] = load4(p);
+    } else if constexpr (n == 2) {
+        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+        w[0] = v.x;
+        w[1] = v.y;
+    } else {
+        static_assert(n == 4, "1, 2 or 4 words");
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+        w[0] = v.x;
+        w[1] = v.y;
+        w[2] = v.z;
+        w[3] = v.w;
+    }
+}
+
+// kS >= smax half blocks per workgroup and kJP row blocks per group per half block,
+// both powers of two: kS * kJP items per lane. Group q takes lane quarter h = q % 4 of
+// row blocks kJP (q / 4) .. kJP (q / 4) + kJP - 1, so the metadata words of a lane's
+// items in one column are consecutive: one load per half block. Every load of a lane
+// is issued up front, in this order: the activations (with one row block per group,
+// 4 x 16 bytes straight into registers, L2-resident after the first workgroups read
+// them; with several, the workgroup's copy of all of them into LDS), then per half
+// block the metadata words and the 16 code bytes of each row block.
 template <bool kBF16, int kS, int kJP>
 __global__ __launch_bounds__(kThreads) void gemv_strip_kernel(const StripArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     using Mg = Magic<kBF16>;
     constexpr int kItems = kS * kJP;
     constexpr uint32_t kOnes = kBF16 ? 0x3F803F80u : 0x3C003C00u;      // (1.0, 1.0)
-    const int K = a.K, KB = a.KB, UW = a.UW, P = a.P;
+    const int KB = a.KB, UW = a.UW;
     const int nwg = (int)gridDim.x;
     const int g = (int)blockIdx.x;
     const int u_lo = (int)((int64_t)g * a.U / nwg);
@@ -111,15 +139,15 @@ __global__ __launch_bounds__(kThreads) void gemv_strip_kernel(const StripArgs a)
     const int tid = (int)threadIdx.x;
     const int q = tid >> 3;            // group
     const int c = tid & 7;             // column of the half block
+    const int hq = q & 3;              // lane quarter of the tile block
+    const int rb0 = kJP * (q >> 2);    // the group's first row block
     float* part = reinterpret_cast<float*>(smem);
-    (void)K;
 
-    // 1. loads. One pair per group (kJP = 1): its activations, rows 128 kb + 8 h + 32 i
-    //    + 0..7, straight into registers. Several pairs: the activations are copied once
-    //    into LDS by the workgroup (direct copies, 64 chunks of 16 bytes per instruction)
-    //    and each item reads its 32 values from there.
+    // 1. loads; row blocks past the last (groups with nothing to do, or the last
+    //    group's tail) load a valid line and weigh 0, and such a group's metadata load
+    //    reads the column's last kJP words (UW is a multiple of 4)
     constexpr bool kXLds = kJP > 1;
-    uint4 xr[kXLds ? 1 : kJP][4];
+    uint4 xr[kJP][4];
     uint8_t* xs = smem + part_bytes(a.smax_pow2);
     if constexpr (kXLds) {
         const int nx = a.K / 8;
@@ -131,60 +159,53 @@ __global__ __launch_bounds__(kThreads) void gemv_strip_kernel(const StripArgs a)
             dma16(xb, 16u * (uint32_t)ch, lds_addr(xs) + 16u * (uint32_t)c0);
         }
     } else {
-        const int p = q < P ? q : P - 1;
-        const uint4* xp = reinterpret_cast<const uint4*>(a.x + 128 * (p >> 2) + 8 * (p & 3));
+        const int rb = rb0 < KB ? rb0 : KB - 1;
+        const uint4* xp = reinterpret_cast<const uint4*>(a.x + 128 * rb + 8 * hq);
 #pragma unroll
         for (int i = 0; i < 4; ++i) xr[0][i] = xp[4 * i];
     }
-    //    then per item j = (half block s = j / kJP, pair p = q + 64 (j % kJP)) its
-    //    metadata word and code bytes; items past this workgroup's half blocks or past
-    //    P load a valid line and weigh 0
     const uint8_t* meta_plane = a.packed + (size_t)KB * 128 * padded_cols(a.N) / 2;
-    uint32_t md[kItems];
+    const int rbm = rb0 + kJP <= UW ? rb0 : UW - kJP;
+    uint32_t md[kS][kJP];
     uint4 wq[kItems];
 #pragma unroll
-    for (int j = 0; j < kItems; ++j) {
-        const int s = j / kJP < S ? j / kJP : S - 1;
-        const int p0 = q + 64 * (j % kJP);
-        const int p = p0 < P ? p0 : P - 1;
-        const int u = u_lo + s;
-        const uint32_t blk = (uint32_t)(u >> 1) * (uint32_t)KB + (uint32_t)(p >> 2);    // < 2^27 (K N <= 2^37)
-        md[j] = load4(meta_plane + 4 * ((size_t)(8 * u + c) * UW + (p >> 2)));
-        wq[j] = load_once(a.packed + (size_t)blk * 1024 + (256 * (p & 3) + 128 * (u & 1) + 16 * c));
+    for (int s = 0; s < kS; ++s) {
+        const int u = u_lo + (s < S ? s : S - 1);
+        load_words<kJP>(meta_plane + 4 * ((size_t)(8 * u + c) * UW + rbm), md[s]);
+#pragma unroll
+        for (int jj = 0; jj < kJP; ++jj) {
+            const int rb = rb0 + jj < KB ? rb0 + jj : KB - 1;
+            const uint32_t blk = (uint32_t)(u >> 1) * (uint32_t)KB + (uint32_t)rb;    // < 2^27 (K N <= 2^37)
+            wq[s * kJP + jj] = load_once(a.packed + (size_t)blk * 1024 + (256 * hq + 128 * (u & 1) + 16 * c));
+        }
     }
 
-    // 2. X of each pair: the sum of its 32 activations, as packed dot products with (1, 1)
-    //    (with LDS activations: once this wave's copies have landed, i.e. with at most
-    //    the 2 kItems metadata and code loads outstanding, and a barrier for the other
-    //    waves' copies)
-    auto x_of = [&](int jj, uint4 (&v)[4]) {
-        if constexpr (kXLds) {
-            const int p0 = q + 64 * jj;
-            const int p = p0 < P ? p0 : P - 1;
-            const uint8_t* xp = xs + 2 * (128 * (p >> 2) + 8 * (p & 3));
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const uint4*>(xp + 64 * i);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = xr[0][i];
-        }
-    };
+    // 2. with LDS activations: once this wave's copies have landed (at most the
+    //    kS + kItems metadata and code loads outstanding) and a barrier for the other
+    //    waves' copies, each row block's 32 values of the lane quarter into registers,
+    //    read once. Then X of each row block: the sum of its 32 activations, as packed
+    //    dot products with (1, 1).
     if constexpr (kXLds) {
-        wait_vmcnt<2 * kItems>();
+        wait_vmcnt<kS + kItems>();
         lds_barrier();
+#pragma unroll
+        for (int jj = 0; jj < kJP; ++jj) {
+            const int rb = rb0 + jj < KB ? rb0 + jj : KB - 1;
+            const uint8_t* xp = xs + 2 * (128 * rb + 8 * hq);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xr[jj][i] = *reinterpret_cast<const uint4*>(xp + 64 * i);
+        }
     }
     float xsum[kJP];
 #pragma unroll
     for (int jj = 0; jj < kJP; ++jj) {
-        uint4 v[4];
-        x_of(jj, v);
         float s0 = 0.f, s1 = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            s0 = dot2<kBF16>(v[i].x, kOnes, s0);
-            s1 = dot2<kBF16>(v[i].y, kOnes, s1);
-            s0 = dot2<kBF16>(v[i].z, kOnes, s0);
-            s1 = dot2<kBF16>(v[i].w, kOnes, s1);
+            s0 = dot2<kBF16>(xr[jj][i].x, kOnes, s0);
+            s1 = dot2<kBF16>(xr[jj][i].y, kOnes, s1);
+            s0 = dot2<kBF16>(xr[jj][i].z, kOnes, s0);
+            s1 = dot2<kBF16>(xr[jj][i].w, kOnes, s1);
         }
         xsum[jj] = s0 + s1;
     }
@@ -198,20 +219,19 @@ __global__ __launch_bounds__(kThreads) void gemv_strip_kernel(const StripArgs a)
     for (int j = 0; j < kItems; ++j) {
         const int s = j / kJP;
         const int jj = j % kJP;
-        const bool valid = s < S && q + 64 * jj < P;
-        uint4 xv[4];
-        x_of(jj, xv);
+        const bool valid = s < S && rb0 + jj < KB;
         float t0 = 0.f, t1 = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const uint32_t v = pick(wq[j], i);
-            t0 = dot2<kBF16>((v & mask) | Mg::kBase2, xv[i].x, t0);
-            t1 = dot2<kBF16>(((v >> 4) & mask) | Mg::kBase2, xv[i].y, t1);
-            t0 = dot2<kBF16>(((v >> 8) & mask) | Mg::kBase2, xv[i].z, t0);
-            t1 = dot2<kBF16>(((v >> 12) & mask) | Mg::kBase2, xv[i].w, t1);
+            t0 = dot2<kBF16>((v & mask) | Mg::kBase2, xr[jj][i].x, t0);
+            t1 = dot2<kBF16>(((v >> 4) & mask) | Mg::kBase2, xr[jj][i].y, t1);
+            t0 = dot2<kBF16>(((v >> 8) & mask) | Mg::kBase2, xr[jj][i].z, t0);
+            t1 = dot2<kBF16>(((v >> 12) & mask) | Mg::kBase2, xr[jj][i].w, t1);
         }
-        const float sf = half_bits_to_f32<kBF16>(md[j] & 0xFFFFu);
-        const float zb = Mg::kBase + (float)((md[j] >> 16) & 0xFu);
+        const uint32_t m = md[s][jj];
+        const float sf = half_bits_to_f32<kBF16>(m & 0xFFFFu);
+        const float zb = Mg::kBase + (float)((m >> 16) & 0xFu);
         const float contrib = sf * ((t0 + t1) - zb * xsum[jj]);
         acc += valid ? contrib : 0.f;
         if (jj == kJP - 1) {
@@ -278,9 +298,10 @@ StripPlan plan_gemv_strip(int64_t M, int64_t K, int64_t N, int64_t G) {
     p.grid = (int)(U < kTargetWorkgroups ? U : kTargetWorkgroups);
     const int64_t smax = (U + p.grid - 1) / p.grid;
     const int64_t JP = (P + kGroups - 1) / kGroups;
-    // the kernel instantiations round both counts up to powers of two; at most 4
-    // pairs per group (K <= 8192): each lane holds the activations of its pairs in
-    // registers
+    // JP row blocks per group (the 64 groups cover K / 128 row blocks in 16 runs of
+    // JP, four lane quarters each); the kernel instantiations round both counts up to
+    // powers of two; at most 4 row blocks per group (K <= 8192): each lane holds the
+    // activations of its row blocks in registers
     if (JP > kMaxPairsPerGroup) return p;
     const int64_t items = (int64_t)pow2_at_least(smax) * pow2_at_least(JP);
     if (items > kMaxItems) return p;
