@@ -119,6 +119,9 @@ W4A8_CASES = [
     # 256 x 256 tiles (outputs of at least two rounds of them): ragged M, a half last
     # column block, fp16 with one group per column
     (257, 256, 65544, 128, "bf16"), (512, 384, 65536, -1, "fp16"),
+    # the zero-point operands staged in the ring (8 to 16 k blocks per workgroup): 16
+    # blocks per K split of 4, ragged M, a half last column block
+    (120, 8192, 2056, 128, "fp16"),
 ]
 
 
@@ -132,12 +135,19 @@ def test_w4a8_gemm_matches_oracle(w, M, K, N, G, dtype):
     assert err <= TOL
 
 
-def test_w4a8_bias(w):
-    ws = synth.make_custom(750, 24, 512, 48, "bf16", 128)
+@pytest.mark.parametrize("M,K,N,dtype", [
+    (24, 512, 48, "bf16"),
+    (130, 2048, 8200, "fp16"),     # zero-point operands and row scales staged in the ring
+])
+def test_w4a8_bias(w, M, K, N, dtype):
+    print(f"w4a8 bias M={M} K={K} N={N} {dtype}", flush=True)
+    ws = synth.make_custom(750 + M, M, K, N, dtype, 128)
     rng = np.random.default_rng(7)
-    bias_bits = synth.f32_to_half_bits(rng.standard_normal(48, dtype=np.float32), "bf16")
-    got = guarded_w4a8(w, ws, 24, bias_bits)
-    assert ogemm.max_rel_error(got, oracle_w4a8_y(ws, ws.x_bits[24], bias_bits=bias_bits)) <= TOL
+    bias_bits = synth.f32_to_half_bits(rng.standard_normal(N, dtype=np.float32), dtype)
+    got = guarded_w4a8(w, ws, M, bias_bits)
+    err = ogemm.max_rel_error(got, oracle_w4a8_y(ws, ws.x_bits[M], bias_bits=bias_bits))
+    print(f"  max rel err {err:.3e}", flush=True)
+    assert err <= TOL
 
 
 def test_w4a8_lm_head_whole_output(w):

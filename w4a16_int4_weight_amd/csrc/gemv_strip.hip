@@ -74,8 +74,6 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
         return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
 }
 
-__host__ __device__ constexpr int round_up(int v, int m) { return (v + m - 1) / m * m; }
-
 struct StripArgs {
     const uint16_t* x;
     const uint8_t* packed;

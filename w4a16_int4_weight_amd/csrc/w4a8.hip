@@ -145,7 +145,7 @@ __device__ __forceinline__ f32x4 mfma_fp8(const i32x8& a, const i32x8& b) {
 // the 16-bit GEMM. MFMA operands: weights first, activations second, so each lane
 // holds 4 adjacent output columns of one row (lane (c, h), register e -> row 16 r + c,
 // column 16 j + 4 h + e).
-template <bool kBF16, int MR, int CBW, int kWaves>
+template <bool kBF16, int MR, int CBW, int kWaves, bool kZpStaged>
 __global__ __launch_bounds__(64 * kWaves) void w4a8_gemm_kernel(
     const uint8_t* __restrict__ act, const float* __restrict__ row_scale, const float* __restrict__ block_sum,
     const uint8_t* __restrict__ packed, const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int M, int K,
@@ -224,6 +224,62 @@ __global__ __launch_bounds__(64 * kWaves) void w4a8_gemm_kernel(
     const uint8_t* mbase = uniform_ptr(meta_plane + (size_t)col0 * UW);
     const uint32_t ring_base = lds_addr(&ring[0]);
     const uint32_t mring_base = lds_addr(&mring[0][kGroupMeta ? w : 0]);
+
+    // Operands of the zero-point term (one batch of at most 16 k blocks: the tile rows'
+    // block sums and the tile columns' metadata words, 16 per row and column) are
+    // copied into the ring slot that the last k blocks leave free, two k blocks before
+    // the end, so the term's loads do not wait a memory latency after the loop.
+    constexpr int kBN = 16 * CBW * kWaves;
+    constexpr int kSumCopies = BM * 16 / 64 / kWaves;      // 4-byte copies per wave
+    constexpr int kZMetaCopies = 16 * CBW * 16 / 64;       // a wave's own columns
+    static_assert(kSumCopies >= 1 && kSumCopies * 64 * kWaves == BM * 16, "block sums must split over the waves");
+    constexpr int kRsCopies = (BM + 63) / 64;               // row scales: 4-byte copies, waves 0 ..
+    static_assert(kRsCopies <= kWaves, "one row-scale copy per wave at most");
+    static_assert((size_t)(BM + kBN) * 64 + (size_t)kRsCopies * 256 <= sizeof(StageT),
+                  "the zero-point operands and row scales fit one ring slot");
+    // kZpStaged: chosen by the host where every K split has 8 to 16 blocks (every
+    // row's and column's 16 words are copied, so with fewer k blocks the wasted copies
+    // cost more than the latency; the other instantiation keeps the loads after the
+    // loop, and its loop free of the staging code: both measured 2-3% slower otherwise)
+    constexpr bool zp_staged = kZpStaged;
+    const int zp_issue = nkb - 2;                           // step after whose barrier they are copied
+    const int zp_slot = nkb % kStages;                      // that of step nkb - 3, free from then on
+    const uint8_t* sbase = uniform_ptr(block_sum + (size_t)m0 * KB);
+    auto issue_zp = [&]() {
+        const uint32_t st = ring_base + (uint32_t)zp_slot * (uint32_t)sizeof(StageT);
+        // the copies' offsets are computed here, in the loop's one step that issues
+        // them (hoisted out of the loop they would hold 16 registers through it)
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        // block sums: word g = 16 r + u of [BM][16] is row m0 + r (rows past M read row
+        // M - 1) and block kb_begin + u (blocks past the split's end read its last:
+        // they are weighed 0)
+#pragma unroll
+        for (int i = 0; i < kSumCopies; ++i) {
+            const int g = (w * kSumCopies + i) * 64 + ln;
+            const int r = g >> 4, u = g & 15;
+            const int m = m0 + r < M ? m0 + r : M - 1;
+            const int kb = kb_begin + u < kb_end ? kb_begin + u : kb_end - 1;
+            dma4(sbase, ((uint32_t)(m - m0) * (uint32_t)KB + (uint32_t)kb) * 4u,
+                 st + (uint32_t)((w * kSumCopies + i) * 64) * 4u);
+        }
+        // metadata: word 16 cl + u of this wave's 16 CBW columns (past the last: the last)
+#pragma unroll
+        for (int i = 0; i < kZMetaCopies; ++i) {
+            const int g = i * 64 + ln;
+            const int cl = g >> 4, u = g & 15;
+            const int n = nbw * kColsPerBlock + cl < Np ? nbw * kColsPerBlock + cl : Np - 1;
+            const int kb = kb_begin + u < kb_end ? kb_begin + u : kb_end - 1;
+            dma4(mbase, ((uint32_t)(n - col0) * (uint32_t)UW + (uint32_t)kb) * 4u,
+                 st + (uint32_t)(BM * 64 + (w * 16 * CBW * 16 + i * 64) * 4));
+        }
+        // the tile rows' scales (rows past M read row M - 1), for the epilogue
+        if (w < kRsCopies) {
+            const int r = w * 64 + ln;
+            const int m = m0 + r < M ? m0 + r : M - 1;
+            dma4(uniform_ptr(row_scale), (uint32_t)m * 4u, st + (uint32_t)((BM + kBN) * 64 + w * 256));
+        }
+    };
     const int ncol = nbw * kColsPerBlock + (lane < 16 * CBW ? lane : 0);   // per-stage copies
     const uint32_t moff = (uint32_t)((ncol < Np ? ncol : Np - 1) - col0) * (uint32_t)UW * 4u;
 
@@ -274,6 +330,9 @@ __global__ __launch_bounds__(64 * kWaves) void w4a8_gemm_kernel(
         else wait_vmcnt<kDmaPerStage>();
         lds_barrier();
         if (t + 2 < nkb) issue((t + 2) % kStages, t + 2);
+        else if constexpr (zp_staged) {
+            if (t == zp_issue) issue_zp();
+        }
 
         const StageT& st = ring[t % kStages];
         // 512 s for this lane's 4 columns of each column block
@@ -319,11 +378,35 @@ __global__ __launch_bounds__(64 * kWaves) void w4a8_gemm_kernel(
 
     // zero-point term over this split's blocks: acc -= sum_kb (s z)[kb, n] * X[m, kb],
     // as 16x16x4 fp32 MFMAs, in batches of 16 blocks: in batch t0, MFMA u takes block
-    // t0 + 4 h + u in lane group h (blocks past the split's end contribute 0). A lane's
-    // four blocks are consecutive, so where they are 16-byte aligned its four block sums
-    // of a row and four metadata words of a column come in one load each (18 loads per
-    // batch instead of 72 4-byte ones), all issued before the batch's MFMAs.
-    for (int t0 = kb_begin; t0 < kb_end; t0 += 16) {
+    // t0 + 4 h + u in lane group h (blocks past the split's end contribute 0).
+    // One batch of 8 to 16 blocks: its operands are in the ring (copied during the
+    // loop, landed by its last barrier), read one block u at a time (MR + CBW values
+    // live beside the accumulators).
+    if constexpr (zp_staged) {
+        const uint8_t* zb = reinterpret_cast<const uint8_t*>(&ring[zp_slot]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int kb = 4 * h + u;                        // block of the batch
+            float zs[CBW], xs[MR];
+#pragma unroll
+            for (int j = 0; j < CBW; ++j) {
+                const uint32_t md = *reinterpret_cast<const uint32_t*>(zb + BM * 64 + ((16 * (w * CBW + j) + c) * 16 + kb) * 4);
+                zs[j] = kb < nkb ? -half_bits_to_f32<kBF16>(md & 0xFFFFu) * (float)((md >> 16) & 0xFu) : 0.f;
+            }
+#pragma unroll
+            for (int r = 0; r < MR; ++r) xs[r] = *reinterpret_cast<const float*>(zb + ((16 * r + c) * 16 + kb) * 4);
+#pragma unroll
+            for (int r = 0; r < MR; ++r)
+#pragma unroll
+                for (int j = 0; j < CBW; ++j)
+                    acc[r][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(zs[j], xs[r], acc[r][j], 0, 0, 0);
+        }
+    }
+    // More batches: from global memory. A lane's four blocks are consecutive, so where
+    // they are 16-byte aligned its four block sums of a row and four metadata words of a
+    // column come in one load each (18 loads per batch instead of 72 4-byte ones), all
+    // issued before the batch's MFMAs.
+    for (int t0 = kb_begin; !zp_staged && t0 < kb_end; t0 += 16) {
         const int kb4 = t0 + 4 * h;
         const bool vec = ((KB | kb4) & 3) == 0 && kb4 + 3 < kb_end;    // UW % 4 == 0 always
         float zs[4][CBW], xs[4][MR];
@@ -363,6 +446,16 @@ __global__ __launch_bounds__(64 * kWaves) void w4a8_gemm_kernel(
                     acc[r][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(zs[u][j], xs[u][r], acc[r][j], 0, 0, 0);
     }
 
+    // the row scales of this lane's rows: staged ones from the ring now, before the
+    // epilogue writes its output tile over it (the others after the barrier below)
+    float rs[MR];
+    if constexpr (zp_staged) {
+#pragma unroll
+        for (int r = 0; r < MR; ++r)
+            rs[r] = *reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(&ring[zp_slot]) +
+                                                    (BM + kBN) * 64 + (16 * r + c) * 4);
+    }
+
     // (tiles of more than 16 fragments per wave are only planned for outputs that need no
     // K split: their reduction would not fit in registers)
     if constexpr (MR * CBW <= 16) {
@@ -383,10 +476,10 @@ __global__ __launch_bounds__(64 * kWaves) void w4a8_gemm_kernel(
     static_assert((size_t)BM * kRowBytes <= kStages * sizeof(StageT), "the output tile fits in the ring");
     uint8_t* otile = reinterpret_cast<uint8_t*>(&ring[0]);
     lds_barrier();                           // every wave is done with the ring's operands
-    // the row scales of this lane's rows
-    float rs[MR];
+    if constexpr (!zp_staged) {
 #pragma unroll
-    for (int r = 0; r < MR; ++r) rs[r] = m0 + 16 * r + c < M ? row_scale[m0 + 16 * r + c] : 0.f;
+        for (int r = 0; r < MR; ++r) rs[r] = m0 + 16 * r + c < M ? row_scale[m0 + 16 * r + c] : 0.f;
+    }
 #pragma unroll
     for (int j = 0; j < CBW; ++j) {
         const int col = 16 * (w * CBW + j) + 4 * h;        // in the tile
@@ -424,8 +517,17 @@ void launch_cfg(const GemmPlan& p, const W4A8Act& a, const uint8_t* packed, cons
                 int M, int K, int N, uint32_t* counters, float* partials, hipStream_t stream) {
     const int tiles_n_pad = (p.tiles_n + kXcds - 1) / kXcds * kXcds;
     const dim3 grid((unsigned)(p.tiles_m * p.splits * tiles_n_pad));
-    hipLaunchKernelGGL((w4a8_gemm_kernel<kBF16, MR, CBW, W>), grid, dim3(64 * W), 0, stream, a.codes, a.row_scale,
-                       a.block_sum, packed, bias, y, M, K, N, p.tiles_m, p.tiles_n, p.splits, counters, partials);
+    // zero-point operands staged in the ring where every split has 8 to 16 k blocks
+    const int KB = K / kRowsPerBlock;
+    const bool staged = KB / p.splits >= 8 && (KB + p.splits - 1) / p.splits <= 16;
+    if (staged)
+        hipLaunchKernelGGL((w4a8_gemm_kernel<kBF16, MR, CBW, W, true>), grid, dim3(64 * W), 0, stream, a.codes,
+                           a.row_scale, a.block_sum, packed, bias, y, M, K, N, p.tiles_m, p.tiles_n, p.splits, counters,
+                           partials);
+    else
+        hipLaunchKernelGGL((w4a8_gemm_kernel<kBF16, MR, CBW, W, false>), grid, dim3(64 * W), 0, stream, a.codes,
+                           a.row_scale, a.block_sum, packed, bias, y, M, K, N, p.tiles_m, p.tiles_n, p.splits, counters,
+                           partials);
 }
 
 template <bool kBF16, int MR>
