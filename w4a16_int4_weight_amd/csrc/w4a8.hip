@@ -136,6 +136,20 @@ struct MetaGroupA8 {
 // cycle on gfx950.)
 __device__ __forceinline__ int row_swizzle(int r) { return ((r >> 2) & 1) | (r & 2) | (((r >> 3) & 1) << 2); }
 
+// v as two bf16 values (hi = v rounded to nearest even, lo = the rest rounded), packed
+// (lo half = hi): exact wherever v has at most 16 significant bits around hi's exponent
+__device__ __forceinline__ uint32_t bf16_split(float v) {
+    const float hi = __uint_as_float(pack2_rne<true>(v, 0.f) << 16);
+    return pack2_rne<true>(v, v - hi);
+}
+// v's two bf16 parts, each duplicated into both halves of a packed pair
+__device__ __forceinline__ void bf16_split_dup(float v, uint32_t& hi2, uint32_t& lo2) {
+    hi2 = pack2_rne<true>(v, v);
+    const float hi = __uint_as_float(hi2 << 16);
+    const float lo = v - hi;
+    lo2 = pack2_rne<true>(lo, lo);
+}
+
 __device__ __forceinline__ f32x4 mfma_fp8(const i32x8& a, const i32x8& b) {
     // format 0 (E4M3) for both operands, no block scales: the plain 16x16x128 fp8 MFMA
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
@@ -376,17 +390,52 @@ __global__ __launch_bounds__(64 * kWaves) void w4a8_gemm_kernel(
         }
     }
 
-    // zero-point term over this split's blocks: acc -= sum_kb (s z)[kb, n] * X[m, kb],
-    // as 16x16x4 fp32 MFMAs, in batches of 16 blocks: in batch t0, MFMA u takes block
-    // t0 + 4 h + u in lane group h (blocks past the split's end contribute 0).
-    // One batch of 8 to 16 blocks: its operands are in the ring (copied during the
-    // loop, landed by its last barrier), read one block u at a time (MR + CBW values
-    // live beside the accumulators).
-    if constexpr (zp_staged) {
+    // zero-point term over this split's blocks: acc -= sum_kb (s z)[kb, n] * X[m, kb].
+    // One batch of 8 to 16 blocks, its operands in the ring (copied during the loop,
+    // landed by its last barrier). Tiles of 16 or more fragments per wave run it on the
+    // bf16 matrix cores (smaller ones measured slower that way: qkv 11.6 -> 12.4 us, the
+    // splitting outweighs the saved MFMA time, so they take the fp32 16x16x4 MFMA of
+    // the unstaged path, on the staged operands): -s z has at most 12
+    // significant bits (s 8 or 11, z 4), so it is exactly the sum of two bf16 values
+    // (checked for every finite scale and zero point), and X is split the same way (the
+    // rest, below 2^-17 of X, is dropped); a block then contributes the four exact
+    // products of the parts, summed in fp32. In 16x16x32 MFMA q, lane group h takes
+    // blocks 8 q + 2 h and 8 q + 2 h + 1, k = 4 (block) + 2 a + b holding X part a and
+    // s z part b: two MFMAs per fragment instead of four fp32 16x16x4 ones, each of
+    // which costs as much as four 16-bit ones.
+    constexpr bool kZpBf16 = MR * CBW >= 16;
+    if constexpr (zp_staged && kZpBf16) {
+        const uint8_t* zb = reinterpret_cast<const uint8_t*>(&ring[zp_slot]);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int kb0 = 8 * q + 2 * h;                   // this lane's blocks kb0, kb0 + 1
+            uint4 av[CBW];                                   // per block (sz1, sz2, sz1, sz2)
+#pragma unroll
+            for (int j = 0; j < CBW; ++j) {
+                const uint2 md = *reinterpret_cast<const uint2*>(zb + BM * 64 + ((16 * (w * CBW + j) + c) * 16 + kb0) * 4);
+                const float s0 = kb0 < nkb ? -half_bits_to_f32<kBF16>(md.x & 0xFFFFu) * (float)((md.x >> 16) & 0xFu) : 0.f;
+                const float s1 = kb0 + 1 < nkb ? -half_bits_to_f32<kBF16>(md.y & 0xFFFFu) * (float)((md.y >> 16) & 0xFu) : 0.f;
+                const uint32_t p0 = bf16_split(s0), p1 = bf16_split(s1);
+                av[j] = make_uint4(p0, p0, p1, p1);
+            }
+#pragma unroll
+            for (int r = 0; r < MR; ++r) {
+                const float2 xv = *reinterpret_cast<const float2*>(zb + ((16 * r + c) * 16 + kb0) * 4);
+                uint32_t x1a, x2a, x1b, x2b;                 // per block (X1, X1) and (X2, X2)
+                bf16_split_dup(xv.x, x1a, x2a);
+                bf16_split_dup(xv.y, x1b, x2b);
+                const uint4 bv = make_uint4(x1a, x2a, x1b, x2b);
+#pragma unroll
+                for (int j = 0; j < CBW; ++j) acc[r][j] = mfma16x16x32<true>(av[j], bv, acc[r][j]);
+            }
+        }
+    }
+    if constexpr (zp_staged && !kZpBf16) {
+        // in 16x16x4 fp32 MFMA u, lane group h takes block 4 h + u
         const uint8_t* zb = reinterpret_cast<const uint8_t*>(&ring[zp_slot]);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int kb = 4 * h + u;                        // block of the batch
+            const int kb = 4 * h + u;
             float zs[CBW], xs[MR];
 #pragma unroll
             for (int j = 0; j < CBW; ++j) {
