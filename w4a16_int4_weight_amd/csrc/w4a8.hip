@@ -256,6 +256,16 @@ __global__ __launch_bounds__(64 * kWaves) void w4a8_gemm_kernel(
     // cost more than the latency; the other instantiation keeps the loads after the
     // loop, and its loop free of the staging code: both measured 2-3% slower otherwise)
     constexpr bool zp_staged = kZpStaged;
+    // Word u of row (or column) rho of the staged operands sits at 16 rho + (u ^ sw(rho)),
+    // sw from bits 2..3 of rho: unswizzled, lanes c, c + 4, c + 8, c + 12 of the term's
+    // reads (rows 16 r + c) met the same banks. The bf16 pass reads block pairs
+    // 8 q + 2 h + (0, 1) (sw on bits 2..3), the fp32 pass block 4 h + u (sw on bits 0..1):
+    // the 32 lanes served together then hit distinct banks, whether 64 or 128 of them.
+    constexpr bool kZpBf16 = MR * CBW >= 16;
+    auto zsw = [](int rho) {
+        const int k = (rho >> 2) & 3;
+        return kZpBf16 ? 4 * k : k;
+    };
     const int zp_issue = nkb - 2;                           // step after whose barrier they are copied
     const int zp_slot = nkb % kStages;                      // that of step nkb - 3, free from then on
     const uint8_t* sbase = uniform_ptr(block_sum + (size_t)m0 * KB);
@@ -271,7 +281,7 @@ __global__ __launch_bounds__(64 * kWaves) void w4a8_gemm_kernel(
 #pragma unroll
         for (int i = 0; i < kSumCopies; ++i) {
             const int g = (w * kSumCopies + i) * 64 + ln;
-            const int r = g >> 4, u = g & 15;
+            const int r = g >> 4, u = (g & 15) ^ zsw(g >> 4);
             const int m = m0 + r < M ? m0 + r : M - 1;
             const int kb = kb_begin + u < kb_end ? kb_begin + u : kb_end - 1;
             dma4(sbase, ((uint32_t)(m - m0) * (uint32_t)KB + (uint32_t)kb) * 4u,
@@ -281,7 +291,7 @@ __global__ __launch_bounds__(64 * kWaves) void w4a8_gemm_kernel(
 #pragma unroll
         for (int i = 0; i < kZMetaCopies; ++i) {
             const int g = i * 64 + ln;
-            const int cl = g >> 4, u = g & 15;
+            const int cl = g >> 4, u = (g & 15) ^ zsw(cl);      // tile column 16 w CBW + cl
             const int n = nbw * kColsPerBlock + cl < Np ? nbw * kColsPerBlock + cl : Np - 1;
             const int kb = kb_begin + u < kb_end ? kb_begin + u : kb_end - 1;
             dma4(mbase, ((uint32_t)(n - col0) * (uint32_t)UW + (uint32_t)kb) * 4u,
@@ -403,16 +413,17 @@ __global__ __launch_bounds__(64 * kWaves) void w4a8_gemm_kernel(
     // blocks 8 q + 2 h and 8 q + 2 h + 1, k = 4 (block) + 2 a + b holding X part a and
     // s z part b: two MFMAs per fragment instead of four fp32 16x16x4 ones, each of
     // which costs as much as four 16-bit ones.
-    constexpr bool kZpBf16 = MR * CBW >= 16;
     if constexpr (zp_staged && kZpBf16) {
         const uint8_t* zb = reinterpret_cast<const uint8_t*>(&ring[zp_slot]);
+        const int sw = zsw(c);                               // rows 16 r + c, columns 16 j' + c
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             const int kb0 = 8 * q + 2 * h;                   // this lane's blocks kb0, kb0 + 1
+            const int pos = kb0 ^ sw;                        // where the pair sits in its row
             uint4 av[CBW];                                   // per block (sz1, sz2, sz1, sz2)
 #pragma unroll
             for (int j = 0; j < CBW; ++j) {
-                const uint2 md = *reinterpret_cast<const uint2*>(zb + BM * 64 + ((16 * (w * CBW + j) + c) * 16 + kb0) * 4);
+                const uint2 md = *reinterpret_cast<const uint2*>(zb + BM * 64 + ((16 * (w * CBW + j) + c) * 16 + pos) * 4);
                 const float s0 = kb0 < nkb ? -half_bits_to_f32<kBF16>(md.x & 0xFFFFu) * (float)((md.x >> 16) & 0xFu) : 0.f;
                 const float s1 = kb0 + 1 < nkb ? -half_bits_to_f32<kBF16>(md.y & 0xFFFFu) * (float)((md.y >> 16) & 0xFu) : 0.f;
                 const uint32_t p0 = bf16_split(s0), p1 = bf16_split(s1);
@@ -420,7 +431,7 @@ __global__ __launch_bounds__(64 * kWaves) void w4a8_gemm_kernel(
             }
 #pragma unroll
             for (int r = 0; r < MR; ++r) {
-                const float2 xv = *reinterpret_cast<const float2*>(zb + ((16 * r + c) * 16 + kb0) * 4);
+                const float2 xv = *reinterpret_cast<const float2*>(zb + ((16 * r + c) * 16 + pos) * 4);
                 uint32_t x1a, x2a, x1b, x2b;                 // per block (X1, X1) and (X2, X2)
                 bf16_split_dup(xv.x, x1a, x2a);
                 bf16_split_dup(xv.y, x1b, x2b);
@@ -433,17 +444,19 @@ __global__ __launch_bounds__(64 * kWaves) void w4a8_gemm_kernel(
     if constexpr (zp_staged && !kZpBf16) {
         // in 16x16x4 fp32 MFMA u, lane group h takes block 4 h + u
         const uint8_t* zb = reinterpret_cast<const uint8_t*>(&ring[zp_slot]);
+        const int sw = zsw(c);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int kb = 4 * h + u;
+            const int pos = kb ^ sw;
             float zs[CBW], xs[MR];
 #pragma unroll
             for (int j = 0; j < CBW; ++j) {
-                const uint32_t md = *reinterpret_cast<const uint32_t*>(zb + BM * 64 + ((16 * (w * CBW + j) + c) * 16 + kb) * 4);
+                const uint32_t md = *reinterpret_cast<const uint32_t*>(zb + BM * 64 + ((16 * (w * CBW + j) + c) * 16 + pos) * 4);
                 zs[j] = kb < nkb ? -half_bits_to_f32<kBF16>(md & 0xFFFFu) * (float)((md >> 16) & 0xFu) : 0.f;
             }
 #pragma unroll
-            for (int r = 0; r < MR; ++r) xs[r] = *reinterpret_cast<const float*>(zb + ((16 * r + c) * 16 + kb) * 4);
+            for (int r = 0; r < MR; ++r) xs[r] = *reinterpret_cast<const float*>(zb + ((16 * r + c) * 16 + pos) * 4);
 #pragma unroll
             for (int r = 0; r < MR; ++r)
 #pragma unroll
