@@ -122,6 +122,9 @@ W4A8_CASES = [
     # the zero-point operands staged in the ring (8 to 16 k blocks per workgroup): 16
     # blocks per K split of 4, ragged M, a half last column block
     (120, 8192, 2056, 128, "fp16"),
+    # staged, with the term on the bf16 matrix cores (128 x 256 tiles, 16 fragments per
+    # wave) from fp16 scales: ragged M, a half last column block
+    (400, 2048, 10248, 128, "fp16"),
 ]
 
 
