@@ -18,7 +18,10 @@ Timing of every entry:
     have run over its just-written weight copies;
   * REPLAYS timed replays follow, each preceded by a 512 MiB streaming read of another
     buffer (the MALL scrub: the 256 MiB Infinity Cache then holds none of the copies)
-    and a device synchronisation, and bracketed by two events on the launch stream;
+    and bracketed by two events on the launch stream, the start event and the replay
+    enqueued while the scrub still runs (no host synchronisation after the scrub), so
+    the interval holds the GPU's execution of the K calls and not the host's
+    graph-launch latency;
   * per-launch time = replay time / K; the entry reports the median over replays (the
     value used everywhere), p10 and p90, the copies one replay touches and their bytes.
 So with the default K every call reads its weights from HBM, and with any K the first
@@ -155,14 +158,19 @@ class Timer:
         torch.cuda.synchronize()
         return g
 
-    def replay_ms(self, g, scrub=True):
+    def replay_ms(self, g):
+        """One timed replay after a scrub. The scrub (~80 us on the GPU) is enqueued
+        ahead of the start event with no host synchronisation in between, so the host
+        submits the replay while the scrub still runs: the start event completes when the
+        scrub does, the graph's first kernel follows at once, and the host's graph-launch
+        latency (~11 us, which a synchronisation there would leave the GPU idle for) is
+        not charged to the kernels."""
         import torch
-        if scrub:
-            self.scrub()
         stream = torch.cuda.current_stream()
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
+        self.scrub()
         start.record(stream)
         g.replay()
         end.record(stream)
