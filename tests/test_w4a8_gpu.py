@@ -196,3 +196,17 @@ def test_w4a8_rejects_small_groups(w):
     x = bits_to_device(ws.x_bits[4], "bf16")
     with pytest.raises(w.W4A16Error):
         w.w4a8_linear(x, packed, ws.N, 64)
+
+
+def test_w4a8_empty_batch(w):
+    # M = 0: quantisation and product launch nothing and return empty results
+    ws = synth.make_custom(770, 2, 512, 48, "bf16", 128)
+    qw, qz, sc = weights_to_device(ws)
+    packed = w.w4a16_repack(qw, qz, sc, ws.group_size)
+    x0 = torch.empty((0, 512), dtype=torch.bfloat16, device=DEV)
+    act = w.w4a8_quantize(x0)
+    y = w.w4a8_gemm(act, packed, 0, 512, 48, 128)
+    assert tuple(y.shape) == (0, 48)
+    y2 = w.w4a8_linear(x0, packed, 48, 128)
+    torch.cuda.synchronize()
+    assert tuple(y2.shape) == (0, 48)
