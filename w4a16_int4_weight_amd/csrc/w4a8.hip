@@ -47,7 +47,52 @@ constexpr int kQuantThreads = 256;
 
 // One workgroup per row. Pass 1: max |x|; pass 2: codes, in operand order (within each
 // 128-element block, byte 32 h + 8 i + j holds element 32 i + 8 h + (0,4,1,5,2,6,3,7)[j]),
-// and the block sums of the decoded codes.
+// and the block sums of the decoded codes. A thread keeps its first kQuantCached chunks
+// of 16 bytes (all of them for K <= 8192) in registers between the passes, so pass 2
+// reads nothing again.
+constexpr int kQuantCached = 4;
+
+template <bool kBF16>
+__device__ __forceinline__ float chunk_absmax(const uint4 v, float amax) {
+    const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        amax = fmaxf(amax, fabsf(half_bits_to_f32<kBF16>(wd[t] & 0xFFFFu)));
+        amax = fmaxf(amax, fabsf(half_bits_to_f32<kBF16>(wd[t] >> 16)));
+    }
+    return amax;
+}
+
+// chunk c of the row (8 elements): block c / 16, rows 8 (c % 16) .. +7 of it = step i,
+// lane group h. Its codes, and (by the first lane of its block's 16) the block's sum.
+template <bool kBF16>
+__device__ __forceinline__ void quantize_chunk(const uint4 v, int c, float scale, uint8_t* __restrict__ cr,
+                                               float* __restrict__ bs) {
+    const int kb = c >> 4, i = (c & 15) >> 2, h = c & 3;
+    const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+    float q[8];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        q[2 * t] = half_bits_to_f32<kBF16>(wd[t] & 0xFFFFu) / scale;
+        q[2 * t + 1] = half_bits_to_f32<kBF16>(wd[t] >> 16) / scale;
+    }
+    // bytes 0..3 = rows 0, 4, 1, 5; bytes 4..7 = rows 2, 6, 3, 7 (RNE, OCP E4M3)
+    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[4], 0, false);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[1], q[5], lo, true);
+    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[6], 0, false);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[3], q[7], hi, true);
+    *reinterpret_cast<uint2*>(cr + (size_t)kb * kRowsPerBlock + 32 * h + 8 * i) = make_uint2((uint32_t)lo, (uint32_t)hi);
+    float s = __builtin_amdgcn_cvt_f32_fp8(lo, 0) + __builtin_amdgcn_cvt_f32_fp8(lo, 1);
+    s += __builtin_amdgcn_cvt_f32_fp8(lo, 2) + __builtin_amdgcn_cvt_f32_fp8(lo, 3);
+    s += __builtin_amdgcn_cvt_f32_fp8(hi, 0) + __builtin_amdgcn_cvt_f32_fp8(hi, 1);
+    s += __builtin_amdgcn_cvt_f32_fp8(hi, 2) + __builtin_amdgcn_cvt_f32_fp8(hi, 3);
+    // the 16 chunks of a block sit in 16 consecutive lanes (K / 8 is a multiple of 16,
+    // so those lanes are all active or all idle together)
+#pragma unroll
+    for (int d = 8; d >= 1; d >>= 1) s += __shfl_xor(s, d, 16);
+    if ((c & 15) == 0) bs[kb] = s;
+}
+
 template <bool kBF16>
 __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(const uint16_t* __restrict__ x,
                                                                   uint8_t* __restrict__ codes,
@@ -55,56 +100,39 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(const uint16_t*
                                                                   float* __restrict__ block_sum, int K) {
     __shared__ float wave_max[kQuantThreads / 64];
     const int m = blockIdx.x;
+    const int tid = threadIdx.x;
     const uint16_t* xr = x + (size_t)m * K;
     const int chunks = K / 8;                  // 8 elements (16 bytes) each
     float amax = 0.f;
-    for (int c = threadIdx.x; c < chunks; c += kQuantThreads) {
-        const uint4 v = *reinterpret_cast<const uint4*>(xr + 8 * c);
-        const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+    uint4 cached[kQuantCached];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            amax = fmaxf(amax, fabsf(half_bits_to_f32<kBF16>(wd[t] & 0xFFFFu)));
-            amax = fmaxf(amax, fabsf(half_bits_to_f32<kBF16>(wd[t] >> 16)));
-        }
+    for (int k = 0; k < kQuantCached; ++k) {
+        const int c = tid + k * kQuantThreads;
+        cached[k] = c < chunks ? *reinterpret_cast<const uint4*>(xr + 8 * c) : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
+    for (int k = 0; k < kQuantCached; ++k) amax = chunk_absmax<kBF16>(cached[k], amax);
+    for (int c = tid + kQuantCached * kQuantThreads; c < chunks; c += kQuantThreads)
+        amax = chunk_absmax<kBF16>(*reinterpret_cast<const uint4*>(xr + 8 * c), amax);
+#pragma unroll
     for (int d = 32; d >= 1; d >>= 1) amax = fmaxf(amax, __shfl_xor(amax, d));
-    if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = amax;
+    if ((tid & 63) == 0) wave_max[tid >> 6] = amax;
     __syncthreads();
     amax = wave_max[0];
 #pragma unroll
     for (int i = 1; i < kQuantThreads / 64; ++i) amax = fmaxf(amax, wave_max[i]);
     const float scale = amax > 0.f ? amax / kE4M3Max : 1.f;     // IEEE division, as are the quotients
-    if (threadIdx.x == 0) row_scale[m] = scale;
+    if (tid == 0) row_scale[m] = scale;
 
     uint8_t* cr = codes + (size_t)m * K;
-    const int KB = K / kRowsPerBlock;
-    for (int c = threadIdx.x; c < chunks; c += kQuantThreads) {
-        // chunk c: block c / 16, rows 8 (c % 16) .. +7 of it = step i, lane group h
-        const int kb = c >> 4, i = (c & 15) >> 2, h = c & 3;
-        const uint4 v = *reinterpret_cast<const uint4*>(xr + 8 * c);
-        const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
-        float q[8];
+    float* bs = block_sum + (size_t)m * (K / kRowsPerBlock);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            q[2 * t] = half_bits_to_f32<kBF16>(wd[t] & 0xFFFFu) / scale;
-            q[2 * t + 1] = half_bits_to_f32<kBF16>(wd[t] >> 16) / scale;
-        }
-        // bytes 0..3 = rows 0, 4, 1, 5; bytes 4..7 = rows 2, 6, 3, 7 (RNE, OCP E4M3)
-        int lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[4], 0, false);
-        lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[1], q[5], lo, true);
-        int hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[6], 0, false);
-        hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[3], q[7], hi, true);
-        *reinterpret_cast<uint2*>(cr + (size_t)kb * kRowsPerBlock + 32 * h + 8 * i) = make_uint2((uint32_t)lo, (uint32_t)hi);
-        float s = __builtin_amdgcn_cvt_f32_fp8(lo, 0) + __builtin_amdgcn_cvt_f32_fp8(lo, 1);
-        s += __builtin_amdgcn_cvt_f32_fp8(lo, 2) + __builtin_amdgcn_cvt_f32_fp8(lo, 3);
-        s += __builtin_amdgcn_cvt_f32_fp8(hi, 0) + __builtin_amdgcn_cvt_f32_fp8(hi, 1);
-        s += __builtin_amdgcn_cvt_f32_fp8(hi, 2) + __builtin_amdgcn_cvt_f32_fp8(hi, 3);
-        // the 16 chunks of a block sit in 16 consecutive lanes (K / 8 is a multiple of 16)
-#pragma unroll
-        for (int d = 8; d >= 1; d >>= 1) s += __shfl_xor(s, d, 16);
-        if ((c & 15) == 0) block_sum[(size_t)m * KB + kb] = s;
+    for (int k = 0; k < kQuantCached; ++k) {
+        const int c = tid + k * kQuantThreads;
+        if (c < chunks) quantize_chunk<kBF16>(cached[k], c, scale, cr, bs);
     }
+    for (int c = tid + kQuantCached * kQuantThreads; c < chunks; c += kQuantThreads)
+        quantize_chunk<kBF16>(*reinterpret_cast<const uint4*>(xr + 8 * c), c, scale, cr, bs);
 }
 
 // ---------------------------------------------------------------- GEMM
