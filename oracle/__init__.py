@@ -13,8 +13,8 @@ Sources (pages, by title and section):
   * "Carga de capas cuantizadas: AWQ / GPTQ / Marlin / fp8" (vLLM architecture
     note), section "Flujo de datos": shapes of qweight int32 [K, N/8], qzeros
     int32 [K/G, N/8] and scales [K/G, N], packed along the output dimension with
-    pack factor 8; section "Motivación de diseño": AWQ packs in a non-standard
-    order along the output dimension and is reordered once after loading;
+    pack factor 8; section "Motivación de diseño": AWQ's order of the codes in a
+    word is not the ascending one, so vLLM reorders them once after loading;
     section "Límites y fallos": group_size = -1 means one group spanning all of K.
   * vllm-omni commit "Add cpu_int4, an asymmetric 4-bit weight path for vLLM's
     CPU backend": the method is asymmetric, group-wise, 4-bit weights with

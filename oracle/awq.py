@@ -7,7 +7,7 @@ and "Motivación de diseño"):
   * qweight is int32 [K, N/8] and qzeros is int32 [K/G, N/8]: each int32 carries
     8 four-bit codes of 8 consecutive output columns (packed_dim = 1, the output
     dimension, packed_factor = 8);
-  * AWQ uses a non-standard order of the codes inside the word.
+  * the codes inside an AWQ word are not in ascending column order.
 The order itself is that of the problem statement this library implements:
 "interleaved order 0,2,4,6,1,3,5,7". Reading taken (the plainest reading of a
 packing order): nibble slot s, i.e. bits 4s..4s+3 counted from the least

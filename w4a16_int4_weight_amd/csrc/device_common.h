@@ -44,6 +44,13 @@ __host__ __device__ constexpr int tile_row_of_slot(int s) { return 2 * (s & 3) +
 // the inverse of the interleave 0,2,4,6,1,3,5,7 (slot s holds column ORDER[s]).
 __host__ __device__ constexpr int awq_slot_of_column(int t) { return (t >> 1) + 4 * (t & 1); }
 
+// Workgroup ids go to the 8 XCDs in turn (the XCD of id is id % 8). Kernels that cut
+// their work into n ordered shares give workgroup id share (id % 8) (n / 8) + id / 8,
+// so that neighbouring shares run on one XCD; grids of other sizes keep share = id.
+__device__ __forceinline__ int xcd_share(int id, int n) {
+    return (n & 7) ? id : (id & 7) * (n >> 3) + (id >> 3);
+}
+
 // 16-bit "magic" encodings: OR-ing a code q (0..15) into the low mantissa bits
 // gives the exact value base + q.
 //   bf16 0x4300 = 128.0, mantissa step 1 on [128, 256)

@@ -1,7 +1,7 @@
 // One-time repack of AWQ int32 nibble packing into the packed tile layout.
 //
 // The AWQ checkpoint stores codes packed along the output dimension, eight per
-// int32 in a non-standard order, and vLLM reorders them once after loading (note
+// int32 but not in ascending column order, and vLLM reorders them once after loading (note
 // "Carga de capas cuantizadas: AWQ / GPTQ / Marlin / fp8", sections "Motivación de
 // diseño" and "Flujo de datos"). Here that reorder is a single coalesced pass on the
 // GPU: no int32 expansion of the codes is ever materialised (the CPU path of the
