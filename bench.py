@@ -17,13 +17,20 @@ Timing of every entry:
     reference) then replays the graph untimed, after scrubs, until SETTLE_CALLS calls
     have run over its just-written weight copies;
   * REPLAYS timed replays follow, each preceded by a 512 MiB streaming read of another
-    buffer (the MALL scrub: the 256 MiB Infinity Cache then holds none of the copies)
-    and bracketed by two events on the launch stream, the start event and the replay
-    enqueued while the scrub still runs (no host synchronisation after the scrub), so
-    the interval holds the GPU's execution of the K calls and not the host's
-    graph-launch latency;
-  * per-launch time = replay time / K; the entry reports the median over replays (the
-    value used everywhere), p10 and p90, the copies one replay touches and their bytes.
+    buffer (the MALL scrub: the 256 MiB Infinity Cache then holds none of the copies),
+    with a synchronisation before the scrub and after the replay;
+  * the interval is read from the GPU's wall clock (w4a16_clock_stamp, 100 MHz),
+    stamped by a one-lane kernel captured as the graph's first node and again as its
+    last: it holds the GPU's execution of the K calls plus one stamp kernel (3.7 us per
+    replay when no call sits between the stamps), and not the host's graph-launch
+    latency. HIP events cannot be recorded inside a graph with this PyTorch build, and
+    events recorded around the replay add ~9-11 us per replay (graphs of 0 to 200 calls:
+    15.0 us against 3.7 us with nothing between, 5.70 against 5.15 us per call at K = 20,
+    5.08 against 5.02 at K = 200); the event figure is reported beside the stamped one
+    (`us_per_launch_events`);
+  * per-launch time = stamped interval / K; the entry reports the median over replays
+    (the value used everywhere), p10 and p90, the copies one replay touches and their
+    bytes.
 So with the default K every call reads its weights from HBM, and with any K the first
 read of every copy in a replay does.
 
@@ -135,7 +142,7 @@ def pct(vals, q):
 
 
 class Timer:
-    """Graph capture, MALL scrub and event timing shared by every entry."""
+    """Graph capture, MALL scrub and GPU-clock timing shared by every entry."""
 
     def __init__(self, w, dev, steps, warmup, replays=REPLAYS):
         import torch
@@ -143,28 +150,34 @@ class Timer:
         self.settle = False          # switched on after the headline (see SETTLE_CALLS)
         self.scrub_buf = torch.empty(SCRUB_BYTES, dtype=torch.uint8, device=dev).fill_(1)
         self.scrub_sink = torch.empty(w.w4a16_stream_sink_bytes(SCRUB_BYTES), dtype=torch.uint8, device=dev)
+        self.stamps = torch.zeros(2, dtype=torch.int64, device=dev)
+        self.clock_hz = w.w4a16_wall_clock_hz()
 
     def scrub(self):
         self.w.w4a16_stream_read(self.scrub_buf, sink=self.scrub_sink)
 
     def capture(self, fns):
+        """A graph of the calls between two wall-clock stamps (first and last node)."""
         import torch
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
+            self.w.w4a16_clock_stamp(self.stamps, 0)
             for fn in fns:
                 fn()
+            self.w.w4a16_clock_stamp(self.stamps, 1)
         torch.cuda.synchronize()
         g.replay()                   # untimed: graph upload, first-use costs
         torch.cuda.synchronize()
         return g
 
+    def stamped_ms(self):
+        """The interval between the last replay's two stamps, in ms (after a sync)."""
+        a, b = self.stamps.cpu().tolist()
+        return (b - a) * 1e3 / self.clock_hz
+
     def replay_ms(self, g):
-        """One timed replay after a scrub. The scrub (~80 us on the GPU) is enqueued
-        ahead of the start event with no host synchronisation in between, so the host
-        submits the replay while the scrub still runs: the start event completes when the
-        scrub does, the graph's first kernel follows at once, and the host's graph-launch
-        latency (~11 us, which a synchronisation there would leave the GPU idle for) is
-        not charged to the kernels."""
+        """One timed replay after a scrub: (stamped interval, interval between events
+        recorded around the replay), in ms."""
         import torch
         stream = torch.cuda.current_stream()
         start = torch.cuda.Event(enable_timing=True)
@@ -175,7 +188,7 @@ class Timer:
         g.replay()
         end.record(stream)
         torch.cuda.synchronize()
-        return start.elapsed_time(end)
+        return self.stamped_ms(), start.elapsed_time(end)
 
     def time(self, rotation, copies, bytes_per_copy, calls=None, settle=None):
         """rotation[i] is a call reading copy i mod copies. Runs the warm-up, captures
@@ -193,31 +206,31 @@ class Timer:
         if settle:
             for _ in range(max(1, math.ceil(SETTLE_CALLS / n))):
                 self.replay_ms(g)
-        per = [self.replay_ms(g) * 1e3 / n for _ in range(self.replays)]
+        both = [self.replay_ms(g) for _ in range(self.replays)]
+        per = [s * 1e3 / n for s, _ in both]
+        per_events = [e * 1e3 / n for _, e in both]
         del g
         touched = min(n, copies)
         return {"us_per_launch": statistics.median(per), "us_p10": pct(per, 10), "us_p90": pct(per, 90),
+                "us_per_launch_events": statistics.median(per_events),
                 "replays": self.replays, "calls_per_replay": n, "copies": copies, "copies_touched_per_replay": touched,
                 "footprint_bytes_per_replay": touched * bytes_per_copy, "mall_scrub_bytes": SCRUB_BYTES,
                 "settle_calls": (max(1, math.ceil(SETTLE_CALLS / n)) * n) if settle else 0}
 
     def time_sustained(self, rotation, calls=SUSTAINED_CALLS):
-        """Three back-to-back replays of `calls` launches (no scrub, no gap); the third
-        is timed. Returns microseconds per launch."""
+        """Three back-to-back replays of `calls` launches (no scrub, no host
+        synchronisation between them); the third, read from its stamps, is timed.
+        Returns microseconds per launch."""
         import torch
         g = self.capture([rotation[i % len(rotation)] for i in range(calls)])
-        stream = torch.cuda.current_stream()
-        start = torch.cuda.Event(enable_timing=True)
-        end = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         g.replay()
         g.replay()
-        start.record(stream)
         g.replay()
-        end.record(stream)
         torch.cuda.synchronize()
+        us = self.stamped_ms() * 1e3 / calls
         del g
-        return start.elapsed_time(end) * 1e3 / calls
+        return us
 
     def stream_floor(self, nbytes, copy=False):
         """The streaming reference over `nbytes` algorithmic bytes: a read of nbytes, or
@@ -267,7 +280,7 @@ def packed_copies(w, ws, dev):
 
 
 def round_entry(e):
-    for k in ("us_per_launch", "us_p10", "us_p90"):
+    for k in ("us_per_launch", "us_p10", "us_p90", "us_per_launch_events"):
         if k in e:
             e[k] = round(e[k], 3)
     return e
@@ -293,7 +306,8 @@ def measure_gemm(T, w, workload, M, dev, path="auto", sustained=False):
         us_s = T.time_sustained(rotation)
         e["sustained"] = {"us_per_launch": round(us_s, 3), "GBps": round(nbytes / us_s / 1e3, 1),
                           "calls": SUSTAINED_CALLS,
-                          "timing": f"third of three back-to-back replays of {SUSTAINED_CALLS} calls"}
+                          "timing": f"third of three back-to-back replays of {SUSTAINED_CALLS} calls, "
+                                    "read from its stamps"}
     else:
         e.update(T.time(rotation, copies, packs[0].numel()))
     del packs, rotation
@@ -674,8 +688,11 @@ def main():
                    "footprint_bytes_per_replay": head["footprint_bytes_per_replay"],
                    "mall_scrub_bytes": SCRUB_BYTES, "replays": head["replays"],
                    "us_per_launch_p10": head["us_p10"], "us_per_launch_p90": head["us_p90"],
-                   "timing": "HIP graph of K calls; median over timed replays, each after a 512 MiB streaming "
-                             "read and bracketed by events on the launch stream"},
+                   "us_per_launch_events": head["us_per_launch_events"],
+                   "timing": "HIP graph of K calls between two GPU wall-clock stamps (first and last graph "
+                             "node); median over timed replays, each after a 512 MiB streaming read, "
+                             "synchronised before the scrub and after the replay; us_per_launch_events: "
+                             "events recorded around the replay, which add the host's graph-launch latency"},
         "roofline": roofline_hbm(head, head_floor, counter_traffic()),
         "cpu_baseline": cpu,
         "secondary": secondary,

@@ -21,6 +21,7 @@
 #define W4A16_MEASURE_H
 
 #include <stddef.h>
+#include <stdint.h>
 
 #include "w4a16.h"
 
@@ -44,6 +45,19 @@ w4a16_status w4a16_stream_read(const void* src, size_t bytes, void* sink, size_t
  * nontemporal, writes nontemporal). src and dst 16-byte aligned, not overlapping,
  * bytes % 16 == 0, bytes <= 2^40 (0 is a no-op). */
 w4a16_status w4a16_stream_copy(const void* src, void* dst, size_t bytes, void* stream);
+
+/* GPU-side timestamps for timing a stretch of work from inside a HIP graph (where the
+ * runtime records no timing events): a one-lane kernel on `stream` stores the GPU's
+ * wall clock, a device-wide counter read by the kernel when it runs, to dst[0]. Two
+ * such launches around captured work bound the GPU's execution of it, and not the
+ * host's graph-launch latency, which an event recorded before the replay includes.
+ *   dst   device memory, 8-byte aligned, one uint64 written (asynchronously).
+ * The counter's rate: w4a16_wall_clock_hz. */
+w4a16_status w4a16_clock_stamp(void* dst, void* stream);
+
+/* Rate of the counter w4a16_clock_stamp stores, in ticks per second, for the current
+ * device (*hz > 0 on W4A16_OK). */
+w4a16_status w4a16_wall_clock_hz(int64_t* hz);
 
 #ifdef __cplusplus
 }

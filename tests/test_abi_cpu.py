@@ -49,7 +49,8 @@ def measure_functions():
 def test_measure_header_entry_points_are_exported_and_bound(w):
     import subprocess
     from w4a16_int4_weight_amd.build import LIB_PATH
-    assert measure_functions() == ["w4a16_stream_copy", "w4a16_stream_read", "w4a16_stream_sink_bytes"]
+    assert measure_functions() == ["w4a16_clock_stamp", "w4a16_stream_copy", "w4a16_stream_read",
+                                   "w4a16_stream_sink_bytes", "w4a16_wall_clock_hz"]
     out = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
     for name in measure_functions():
@@ -76,6 +77,9 @@ def test_stream_validation_before_any_device_call(w):
     assert lib.w4a16_stream_copy(P(256), None, 32, None) == 1
     assert lib.w4a16_stream_copy(P(256), P(520), 32, None) == 5
     assert lib.w4a16_stream_copy(None, None, 0, None) == 0
+    assert lib.w4a16_clock_stamp(None, None) == 1
+    assert lib.w4a16_clock_stamp(P(260), None) == 5
+    assert lib.w4a16_wall_clock_hz(None) == 1
 
 
 def test_exports_are_c_symbols():

@@ -42,3 +42,31 @@ def test_stream_copy_is_exact_and_in_bounds(w, nbytes):
     torch.cuda.synchronize()
     assert torch.equal(dst[:nbytes], src[:nbytes])
     assert torch.all(dst[nbytes:] == 0xA5)
+
+
+def test_clock_stamps_bracket_captured_work(w):
+    """Two stamps captured around four 64 MiB reads in one graph: later than each other,
+    by at least what the reads take at 10 TB/s and at most the events around the replay
+    (which also hold the host's graph-launch latency); only dst[index] is written."""
+    hz = w.w4a16_wall_clock_hz()
+    assert hz > 0
+    src = torch.ones(64 << 20, dtype=torch.uint8, device=DEV)
+    sink = torch.empty(w.w4a16_stream_sink_bytes(src.numel()), dtype=torch.uint8, device=DEV)
+    stamps = torch.full((4,), -1, dtype=torch.int64, device=DEV)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        w.w4a16_clock_stamp(stamps, 1)
+        for _ in range(4):
+            w.w4a16_stream_read(src, sink=sink)
+        w.w4a16_clock_stamp(stamps, 2)
+    for _ in range(3):
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        g.replay()
+        end.record()
+        torch.cuda.synchronize()
+        v = stamps.cpu().tolist()
+        assert v[0] == -1 and v[3] == -1
+        span_us = (v[2] - v[1]) * 1e6 / hz
+        assert 4 * (64 << 20) / 10e12 * 1e6 <= span_us <= start.elapsed_time(end) * 1e3 + 1.0, span_us

@@ -44,7 +44,8 @@ __all__ = [
     "w4a16_repack", "w4a16_repack_gptq", "w4a16_repack_columns", "w4a16_repack_gptq_columns",
     "w4a16_packed_header", "w4a16_parse_packed_header", "repack_from_host", "save_packed", "load_packed",
     "w4a16_gemm", "w4a16_gemm_ex", "w4a16_gemm_noalloc", "w4a16_embedding", "w4a16_status_str", "STATUS", "PATHS",
-    "w4a16_stream_sink_bytes", "w4a16_stream_read", "w4a16_stream_copy",
+    "w4a16_stream_sink_bytes", "w4a16_stream_read", "w4a16_stream_copy", "w4a16_clock_stamp",
+    "w4a16_wall_clock_hz",
 ]
 
 STATUS = {
@@ -124,6 +125,10 @@ def _load():
     h.w4a16_stream_read.restype = _int
     h.w4a16_stream_copy.argtypes = [_vp, _vp, _sz, _vp]
     h.w4a16_stream_copy.restype = _int
+    h.w4a16_clock_stamp.argtypes = [_vp, _vp]
+    h.w4a16_clock_stamp.restype = _int
+    h.w4a16_wall_clock_hz.argtypes = [ctypes.POINTER(_i64)]
+    h.w4a16_wall_clock_hz.restype = _int
     h.w4a16_status_str.argtypes = [_int]
     h.w4a16_status_str.restype = ctypes.c_char_p
     _lib = h
@@ -509,6 +514,21 @@ def w4a16_stream_read(src, nbytes=None, sink=None, stream=None):
     _check(_load().w4a16_stream_read(_ptr(src), nbytes, _ptr(sink), sink.numel() * sink.element_size(),
                                      _stream(stream, src.device)), "w4a16_stream_read")
     return sink
+
+
+def w4a16_clock_stamp(dst, index=0, stream=None):
+    """Stores the GPU's wall clock, when the launch runs, into dst[index] (dst: an int64
+    device tensor); capturable in a HIP graph. Ticks per second: w4a16_wall_clock_hz()."""
+    if dst.dtype != torch.int64 or not 0 <= index < dst.numel() or not dst.is_contiguous():
+        raise ValueError("dst must be a contiguous int64 tensor holding `index`")
+    _check(_load().w4a16_clock_stamp(ctypes.c_void_p(dst.data_ptr() + 8 * index), _stream(stream, dst.device)),
+           "w4a16_clock_stamp")
+
+
+def w4a16_wall_clock_hz():
+    hz = ctypes.c_int64(0)
+    _check(_load().w4a16_wall_clock_hz(ctypes.byref(hz)), "w4a16_wall_clock_hz")
+    return int(hz.value)
 
 
 def w4a16_stream_copy(src, dst, nbytes=None, stream=None):

@@ -106,6 +106,12 @@ void launch_stream(const void* src, size_t bytes, void* out, hipStream_t stream)
                            (int64_t)(bytes / 16), o);
 }
 
+// One lane stores the wall clock (s_memrealtime: a read of the device-wide counter,
+// stored with an ordinary vector store).
+__global__ void clock_stamp_kernel(uint64_t* __restrict__ dst) {
+    if (threadIdx.x == 0) dst[0] = wall_clock64();
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 constexpr size_t kMaxBytes = (size_t)1 << 40;
@@ -127,6 +133,24 @@ w4a16_status w4a16_stream_read(const void* src, size_t bytes, void* sink, size_t
     if (sink_bytes < w4a16_stream_sink_bytes(bytes)) return W4A16_ERR_BUFFER_SIZE;
     launch_stream<false>(src, bytes, sink, static_cast<hipStream_t>(stream));
     return hipGetLastError() == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
+w4a16_status w4a16_clock_stamp(void* dst, void* stream) {
+    if (!dst) return W4A16_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(dst) & 7u) != 0) return W4A16_ERR_ALIGN;
+    hipLaunchKernelGGL(clock_stamp_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream),
+                       static_cast<uint64_t*>(dst));
+    return hipGetLastError() == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
+w4a16_status w4a16_wall_clock_hz(int64_t* hz) {
+    if (!hz) return W4A16_ERR_NULL;
+    int dev = 0, khz = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0)
+        return W4A16_ERR_HIP;
+    *hz = (int64_t)khz * 1000;
+    return W4A16_OK;
 }
 
 w4a16_status w4a16_stream_copy(const void* src, void* dst, size_t bytes, void* stream) {
