@@ -209,6 +209,16 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// One 16-byte output store: a streaming (nontemporal) store where `nt`, else an
+// ordinary one. Tile GEMMs whose grid fits the CUs in one round write streaming (their
+// output is read by nothing in the launch); those of several rounds write ordinary
+// stores (the streaming ones measured slower on one box for the W4A8 LM head).
+__device__ __forceinline__ void store_out16(void* dst, const uint4 v, bool nt) {
+    typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+    if (nt) __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t*>(dst));
+    else *reinterpret_cast<uint4*>(dst) = v;
+}
+
 // s_waitcnt with only lgkmcnt constrained, to zero: this wave's LDS accesses have
 // completed (vmcnt field at its maximum 63, expcnt 7).
 __device__ __forceinline__ void wait_lgkmcnt0() {

@@ -76,7 +76,7 @@ template <bool kBF16, int MR, int CBW, int kWaves, int kSub>
 __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed, const uint16_t* __restrict__ bias,
     uint16_t* __restrict__ y, int M, int K, int N, int tiles_m, int tiles_n, int splits,
-    uint32_t* __restrict__ counters, float* __restrict__ partials) {
+    uint32_t* __restrict__ counters, float* __restrict__ partials, int nt_out) {
     constexpr int BM = 16 * MR;
     constexpr int kSlabsPerWave = BM / 4 / kWaves;      // 1 KiB slabs (4 rows) of the x tile per wave
     static_assert(kSlabsPerWave * 4 * kWaves == BM, "x tile must split over the waves");
@@ -332,7 +332,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(
         const int ch = q - row * (BN / 8);
         const int m = m0 + row, n = n0 + 8 * ch;
         if (m < M && n < N)
-            *reinterpret_cast<uint4*>(y + (size_t)m * N + n) = *reinterpret_cast<const uint4*>(otile + row * kRowBytes + 16 * ch);
+            store_out16(y + (size_t)m * N + n, *reinterpret_cast<const uint4*>(otile + row * kRowBytes + 16 * ch), nt_out != 0);
     }
 }
 
@@ -343,8 +343,11 @@ void launch_cfg(const GemmPlan& p, const uint16_t* x, const uint8_t* packed, con
                 int M, int K, int N, uint32_t* counters, float* partials, hipStream_t stream) {
     const int tiles_n_pad = (p.tiles_n + kXcds - 1) / kXcds * kXcds;
     const dim3 grid((unsigned)(p.tiles_m * p.splits * tiles_n_pad));
+    // streaming output stores when every workgroup runs in the first round (qkv and
+    // gate_up prefill: 1-2% faster; the LM head, 8 rounds, unchanged)
+    const int nt_out = (int64_t)p.tiles_m * p.tiles_n * p.splits <= kTargetWorkgroups ? 1 : 0;
     hipLaunchKernelGGL((gemm_kernel<kBF16, MR, CBW, W, kSub>), grid, dim3(64 * W), 0, stream, x, packed, bias, y, M,
-                       K, N, p.tiles_m, p.tiles_n, p.splits, counters, partials);
+                       K, N, p.tiles_m, p.tiles_n, p.splits, counters, partials, nt_out);
 }
 
 template <bool kBF16, int MR>
