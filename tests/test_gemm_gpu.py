@@ -464,6 +464,10 @@ def test_gemm_tile_shapes(w, M, N, dtype):
     (6784, 1032, "bf16", 128, False),    # 53 row blocks in runs of 4: the last group has one; N % 16 == 8
     (8192, 2048, "bf16", 128, True),     # 64 row blocks: every group busy with 4
     (1536, 1040, "bf16", -1, False),     # one group of all K rows
+    # shares dealt over the XCDs (grids that are a multiple of 8; 65, 129 and 130 above are not)
+    (2048, 1024, "bf16", 128, True),     # 128 workgroups, one half block each
+    (3072, 512, "fp16", 128, False),     # 64 workgroups, 2 row blocks per group
+    (2048, 2064, "bf16", 128, True),     # 258 half blocks on 256 workgroups: two take two
     (1024, 40000, "bf16", 128, False),   # 20 half blocks per workgroup: beyond the balanced GEMV, the
                                          # 16-column GEMV runs
 ])
