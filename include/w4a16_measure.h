@@ -11,9 +11,13 @@
  * read and a plain copy with the access pattern of a tuned stream (16-byte
  * nontemporal accesses, every workgroup one contiguous share) — so the GEMV, the repack and the gather can be reported both against
  * the published peak and against this achievable figure. They compute nothing of
- * the method. Launch shape (measured best on MI355X): up to 64 MiB, 512-1024
- * workgroups each streaming one contiguous share, 4 loads per thread in flight;
- * beyond, one 32 KiB pass per workgroup, 8 loads per thread in flight.
+ * the method. Launch shape (measured best on MI355X): up to 64 MiB, 512, 768 or 1024
+ * workgroups (one per 16 KiB, rounded up to whole rounds of 256) each streaming one
+ * contiguous share, 4 loads per thread in flight; beyond, one 32 KiB pass per
+ * workgroup, 8 loads per thread in flight. The read ends with each workgroup's
+ * 16-byte XOR store, so that its result can be checked: a kernel of the same loads
+ * that writes nothing finishes ~0.5 us sooner (14.2 MB: 4.11 against 4.65 us), the
+ * wait for a launch's last store, which every kernel with an output pays.
  * Conventions of w4a16.h apply (device pointers owned by the caller,
  * asynchronous on `stream`, validation before any launch, status codes).
  */

@@ -61,8 +61,10 @@ def test_stream_validation_before_any_device_call(w):
     assert w.w4a16_stream_sink_bytes(0) == 0
     assert w.w4a16_stream_sink_bytes(24) == 0
     assert w.w4a16_stream_sink_bytes(16) == 16                       # one chunk: one workgroup
-    assert w.w4a16_stream_sink_bytes(32768) == 512 * 16               # 512 .. 1024 shares up to 64 MiB
-    assert w.w4a16_stream_sink_bytes(14_194_688) == 866 * 16
+    assert w.w4a16_stream_sink_bytes(32768) == 512 * 16               # 512, 768 or 1024 shares up to 64 MiB
+    assert w.w4a16_stream_sink_bytes(14_194_688) == 1024 * 16         # 866 16-KiB pieces: rounded up to 1024
+    assert w.w4a16_stream_sink_bytes(10 << 20) == 768 * 16            # 640: rounded up to 768
+    assert w.w4a16_stream_sink_bytes(7_099_392) == 512 * 16
     assert w.w4a16_stream_sink_bytes(64 << 20) == 1024 * 16
     assert w.w4a16_stream_sink_bytes((64 << 20) + 16) == ((64 << 20) // 16 + 1 + 2047) // 2048 * 16
     lib = w.lib

@@ -16,11 +16,14 @@ constexpr int64_t kSmallBytes = (int64_t)64 << 20;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-// Launch shape, measured on MI355X over 7-140 MB (graph replays, buffers rotated
-// through 1 GiB, Infinity Cache scrubbed): up to 64 MiB, 512-1024 workgroups each
-// streaming one contiguous share with 4 loads per thread in flight (14.2 MB: 3.83 us,
-// against 4.43 us for one 32 KiB pass per workgroup); beyond, one 32 KiB pass per
-// workgroup with 8 loads per thread in flight (140 MB: 21.8 us, against 22.4 us).
+// Launch shape, measured on MI355X over 2.7-140 MB (graph replays, buffers rotated
+// through 1 GiB, Infinity Cache scrubbed): up to 64 MiB, 512, 768 or 1024 workgroups
+// (one per 16 KiB, rounded up to whole rounds of 256, so that every CU holds the same
+// number) each streaming one contiguous share with 4 loads per thread in flight
+// (14.2 MB: 4.65-4.74 us on 1024 workgroups against 4.94-5.01 us on 866; 7.1 and
+// 8.4 MB: 512 as good as or better than 1024); beyond, one 32 KiB pass per workgroup
+// with 8 loads per thread in flight (140 MB: 22.6-22.8 us, against 23.0-24.0 us for
+// 256-1024 workgroups of 256-1024 threads).
 struct Shape {
     int64_t blocks;
     int unroll;
@@ -28,7 +31,7 @@ struct Shape {
 Shape shape_for(size_t bytes) {
     const int64_t chunks = (int64_t)(bytes / 16);
     if ((int64_t)bytes <= kSmallBytes) {
-        int64_t b = (int64_t)bytes / (16 << 10);
+        int64_t b = ((int64_t)bytes / (16 << 10) + 255) / 256 * 256;
         b = b < 512 ? 512 : b > 1024 ? 1024 : b;
         return {b < chunks ? b : chunks, 4};
     }
