@@ -30,11 +30,13 @@
 //     packed dot product with the matching activation pair sums x (base + q) with
 //     exact products; base and zero point leave in one correction per row block and
 //     lane quarter, s (T - (base + z) X) with X the sum of the same 32 activations;
-//   * the activations a lane needs (32 per row block) sit in its registers: loaded
-//     directly with one row block per group, and with several read once from a copy
-//     of all K of them that the workgroup stages in LDS by direct global -> LDS
-//     copies issued ahead of the code loads (each value then serves the 8 lanes of
-//     its group without 8 separate global reads);
+//   * the activations a lane needs (32 per row block) sit in its registers, read once
+//     from LDS: with one row block per group from the wave's own copy of its two row
+//     blocks (one direct global -> LDS copy per wave, no barrier; 2048 x 13312: 5.35
+//     -> 5.25 us against four 16-byte loads per lane), with several from a copy of all
+//     K of them that the workgroup stages (each value then serves the 8 lanes of its
+//     group without 8 separate global reads); both copies are issued ahead of the code
+//     loads;
 //   * each group's partial per half block lands in its own LDS slot and the slots
 //     are added in group order: the result is run-to-run deterministic.
 #include "device_common.h"
@@ -91,8 +93,9 @@ struct StripArgs {
     int smax_pow2;   // smax rounded up to a power of two (the partials' LDS rows)
 };
 
-// LDS: the partials, smax half blocks x 8 columns x 64 group slots, fp32; then, with
-// several row blocks per group, the activations (K 16-bit values, padded to 1 KiB)
+// LDS: the partials, smax half blocks x 8 columns x 64 group slots, fp32; then the
+// activations: with several row blocks per group all K 16-bit values (padded to 1 KiB),
+// with one a 1 KiB slot per wave for its two row blocks
 __host__ __device__ inline int part_bytes(int smax) { return smax * 8 * kGroups * 4; }
 
 __device__ __forceinline__ uint32_t load4(const uint8_t* p) { return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p)); }
@@ -123,9 +126,9 @@ __device__ __forceinline__ void load_words(const uint8_t* p, uint32_t (&w)[n]) {
 // row blocks kJP (q / 4) .. kJP (q / 4) + kJP - 1, so the metadata words of a lane's
 // items in one column are consecutive: one load per half block. Every load of a lane
 // is issued up front, in this order: the activations (with one row block per group,
-// 4 x 16 bytes straight into registers, L2-resident after the first workgroups read
-// them; with several, the workgroup's copy of all of them into LDS), then per half
-// block the metadata words and the 16 code bytes of each row block.
+// each wave's copy of its two row blocks into its own LDS slot, L2-resident after the
+// first workgroups read them; with several, the workgroup's copy of all of them into
+// LDS), then per half block the metadata words and the 16 code bytes of each row block.
 template <bool kBF16, int kS, int kJP>
 __global__ __launch_bounds__(kThreads) void gemv_strip_kernel(const StripArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -160,10 +163,15 @@ __global__ __launch_bounds__(kThreads) void gemv_strip_kernel(const StripArgs a)
             dma16(xb, 16u * (uint32_t)ch, lds_addr(xs) + 16u * (uint32_t)c0);
         }
     } else {
-        const int rb = rb0 < KB ? rb0 : KB - 1;
-        const uint4* xp = reinterpret_cast<const uint4*>(a.x + 128 * rb + 8 * hq);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) xr[0][i] = xp[4 * i];
+        // with one row block per group, wave w's groups use row blocks 2w and 2w + 1:
+        // 512 contiguous bytes of x, copied into the wave's own 1 KiB LDS slot with one
+        // copy (lanes past 32, and row blocks past the last, copy the last valid chunk)
+        // instead of four 16-byte loads per lane; only this wave reads the slot
+        const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int lane = tid & 63;
+        const int nx = a.K / 8;                                   // 16-byte chunks of x
+        const int ch = 32 * w + (lane & 31) < nx ? 32 * w + (lane & 31) : nx - 1;
+        dma16(uniform_ptr(a.x), 16u * (uint32_t)ch, lds_addr(xs) + 1024u * (uint32_t)w);
     }
     const uint8_t* meta_plane = a.packed + (size_t)KB * 128 * padded_cols(a.N) / 2;
     const int rbm = rb0 + kJP <= UW ? rb0 : UW - kJP;
@@ -186,6 +194,14 @@ __global__ __launch_bounds__(kThreads) void gemv_strip_kernel(const StripArgs a)
     //    waves' copies, each row block's 32 values of the lane quarter into registers,
     //    read once. Then X of each row block: the sum of its 32 activations, as packed
     //    dot products with (1, 1).
+    if constexpr (!kXLds) {
+        // this wave's copy has landed once at most the kS metadata and kItems code loads
+        // issued after it are outstanding; no other wave's copy is read, so no barrier
+        wait_vmcnt<kS + kItems>();
+        const uint8_t* xp = xs + 1024 * (tid >> 6) + 2 * (128 * (rb0 & 1) + 8 * hq);   // rb0 = 2w or 2w + 1
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xr[0][i] = *reinterpret_cast<const uint4*>(xp + 64 * i);
+    }
     if constexpr (kXLds) {
         wait_vmcnt<kS + kItems>();
         lds_barrier();
@@ -307,7 +323,10 @@ StripPlan plan_gemv_strip(int64_t M, int64_t K, int64_t N, int64_t G) {
     const int64_t items = (int64_t)pow2_at_least(smax) * pow2_at_least(JP);
     if (items > kMaxItems) return p;
     p.items = (int)items;
-    p.lds_bytes = (size_t)part_bytes((int)pow2_at_least(smax)) + (JP > 1 ? (size_t)((K * 2 + 1023) / 1024 * 1024) : 0);
+    // after the partials: the activations, all K of them with several row blocks per
+    // group, each wave's two row blocks (a 1 KiB slot per wave) with one
+    p.lds_bytes = (size_t)part_bytes((int)pow2_at_least(smax)) +
+                  (JP > 1 ? (size_t)((K * 2 + 1023) / 1024 * 1024) : (size_t)kWaves * 1024);
     if (p.lds_bytes > 64 * 1024) return p;
     p.ok = true;
     return p;
