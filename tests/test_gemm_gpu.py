@@ -468,6 +468,8 @@ def test_gemm_tile_shapes(w, M, N, dtype):
     (2048, 1024, "bf16", 128, True),     # 128 workgroups, one half block each
     (3072, 512, "fp16", 128, False),     # 64 workgroups, 2 row blocks per group
     (2048, 2064, "bf16", 128, True),     # 258 half blocks on 256 workgroups: two take two
+    (2048, 10240, "fp16", 128, False),   # 5 half blocks per workgroup
+    (1024, 12288, "bf16", 128, True),    # 6 half blocks per workgroup
     (1024, 40000, "bf16", 128, False),   # 20 half blocks per workgroup: beyond the balanced GEMV, the
                                          # 16-column GEMV runs
 ])
