@@ -90,8 +90,8 @@ __device__ __forceinline__ float md_base_zero(uint32_t md) {
                  : __uint_as_float(((md >> 3) & 0x0001E000u) | 0x44800000u);      // 1024 + z
 }
 
-// kS >= half blocks of any workgroup, kJP >= units per wave per half block (powers of
-// two), kG row groups of at most 8 activation rows (rows 8 g .. 8 g + 7; two for
+// kS >= half blocks of any workgroup (exactly), kJP >= units per wave per half block
+// (a power of two), kG row groups of at most 8 activation rows (rows 8 g .. 8 g + 7; two for
 // M = 9 .. 16): each decoded operand serves one MFMA per group.
 template <bool kBF16, int kS, int kJP, int kG>
 __global__ __launch_bounds__(kThreads) void gemv_small_kernel(const SmallArgs a) {
@@ -257,15 +257,29 @@ __global__ __launch_bounds__(kThreads) void gemv_small_kernel(const SmallArgs a)
     }
 }
 
+// kS = the most half blocks of any workgroup, exactly (3, 5, 6 and 7 included: a power
+// of two above it would issue loads of clamped units that weigh nothing)
 template <bool kBF16, int kJP, int kG>
 void launch_jp(const SmallArgs& args, int smax, int grid, hipStream_t st) {
     constexpr int kMaxS = kMaxItems / kJP;
     if (smax <= 1) hipLaunchKernelGGL((gemv_small_kernel<kBF16, 1, kJP, kG>), dim3(grid), dim3(kThreads), 0, st, args);
-    else if (smax <= 2 && kMaxS >= 2)
+    else if (smax == 2 && kMaxS >= 2)
         hipLaunchKernelGGL((gemv_small_kernel<kBF16, (kMaxS >= 2 ? 2 : 1), kJP, kG>), dim3(grid), dim3(kThreads), 0, st,
                            args);
-    else if (smax <= 4 && kMaxS >= 4)
+    else if (smax == 3 && kMaxS >= 4)
+        hipLaunchKernelGGL((gemv_small_kernel<kBF16, (kMaxS >= 4 ? 3 : 1), kJP, kG>), dim3(grid), dim3(kThreads), 0, st,
+                           args);
+    else if (smax == 4 && kMaxS >= 4)
         hipLaunchKernelGGL((gemv_small_kernel<kBF16, (kMaxS >= 4 ? 4 : 1), kJP, kG>), dim3(grid), dim3(kThreads), 0, st,
+                           args);
+    else if (smax == 5 && kMaxS >= 8)
+        hipLaunchKernelGGL((gemv_small_kernel<kBF16, (kMaxS >= 8 ? 5 : 1), kJP, kG>), dim3(grid), dim3(kThreads), 0, st,
+                           args);
+    else if (smax == 6 && kMaxS >= 8)
+        hipLaunchKernelGGL((gemv_small_kernel<kBF16, (kMaxS >= 8 ? 6 : 1), kJP, kG>), dim3(grid), dim3(kThreads), 0, st,
+                           args);
+    else if (smax == 7 && kMaxS >= 8)
+        hipLaunchKernelGGL((gemv_small_kernel<kBF16, (kMaxS >= 8 ? 7 : 1), kJP, kG>), dim3(grid), dim3(kThreads), 0, st,
                            args);
     else if (kMaxS >= 8)
         hipLaunchKernelGGL((gemv_small_kernel<kBF16, (kMaxS >= 8 ? 8 : 1), kJP, kG>), dim3(grid), dim3(kThreads), 0, st,
