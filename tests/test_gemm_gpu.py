@@ -117,6 +117,32 @@ def test_small_integer_case_is_exact(w, path):
     assert np.array_equal(got, numerics.f64_to_half_bits_rne(oracle_y(ws, xb), "bf16"))
 
 
+# More tiles than compute units on a tile whose LDS holds one workgroup per CU: the
+# grid is one workgroup per CU, each taking a tile per round and copying the next
+# tile's first k block while it writes the current output. Ragged rows, a last half
+# block of columns, N tiles that are not a multiple of 8 (ids without a tile), bias.
+@pytest.mark.parametrize("M,K,N,dtype,with_bias", [
+    (200, 1024, 32776, "bf16", True),     # 128 x 128 tiles, 2 x 257
+    (300, 256, 36872, "fp16", False),     # 64 x 256 tiles, 5 x 145
+    (1000, 256, 8200, "bf16", True),      # 128 x 128 tiles, 8 x 65
+])
+def test_gemm_more_tiles_than_cus(w, M, K, N, dtype, with_bias):
+    print(f"gemm M={M} K={K} N={N} {dtype} bias={with_bias}", flush=True)
+    ws = synth.make_custom(700 + M, M, K, N, dtype, 128)
+    packed = pack_on_gpu(w, ws)
+    bias_bits = None
+    bias = None
+    if with_bias:
+        rng = np.random.default_rng(M)
+        bias_bits = numerics.f64_to_half_bits_rne(rng.standard_normal(N), dtype)
+        bias = bits_to_device(bias_bits, dtype)
+    y = run(w, ws, packed, ws.x_bits[M], path="mfma", bias=bias)
+    y2 = run(w, ws, packed, ws.x_bits[M], path="mfma", bias=bias)
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    got = y_to_f64(y, dtype)
+    assert ogemm.max_rel_error(got, oracle_y(ws, ws.x_bits[M], bias_bits=bias_bits)) <= TOL
+
+
 @pytest.mark.parametrize("path", ["gemv", "mfma"])
 def test_bias(w, path):
     ws = synth.make_custom(60, 8, 1024, 272, "bf16", 128)
