@@ -33,8 +33,8 @@
 // the packed codes through that XCD's L2. A tile that holds one workgroup per CU runs
 // persistent when there are more tiles than CUs: each workgroup takes a tile per
 // round and copies the next tile's first k block while it writes the current output
-// (gate_up at M = 2048 138 -> 134 us, the LM head at M = 256 155 -> 151 us; the LM
-// head at M = 512 unchanged within run-to-run spread).
+// (same box, three runs each: the LM head at M = 512 270.7-274.4 -> 268.1-269.7 us,
+// gate_up at M = 2048 129.0 -> 126.2 us).
 // Epilogue: bias in fp32, one rounding to the dtype.
 #include <stddef.h>
 
@@ -76,7 +76,7 @@ struct MetaGroup {
 // owning CBW column blocks and all rows. `splits` > 1 splits the K range over
 // workgroups; their fp32 partial tiles meet in `workspace` and the last workgroup of
 // a tile to finish adds them in split order (deterministic) and writes y.
-template <bool kBF16, int MR, int CBW, int kWaves, int kSub>
+template <bool kBF16, int MR, int CBW, int kWaves, int kSub, bool kPersist>
 __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed, const uint16_t* __restrict__ bias,
     uint16_t* __restrict__ y, int M, int K, int N, int tiles_m, int tiles_n, int splits,
@@ -191,9 +191,10 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(
         }
     };
 
-    // A workgroup runs the tiles of ids blockIdx.x, + gridDim.x, ... (one id per
-    // workgroup when the grid covers them all). With several, the next tile's first
-    // stage is copied while the current tile's output is written.
+    // A workgroup runs the tile of id blockIdx.x and, when persistent (a grid smaller
+    // than the ids), those of + gridDim.x, ...: the next tile's first stage is copied
+    // while the current tile's output is written. (Compiled without the tile loop
+    // where the grid covers every id: with it, single-round launches ran 2-3% slower.)
     Src cur;
     int id = next_tile((int)blockIdx.x, cur);
     if (id >= total_ids) return;
@@ -324,29 +325,37 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(
                                                           cur.split, splits))
             return;
 
-        // bias of this wave's columns, read while no copy is in flight
+        // bias of this wave's columns; a persistent tile reads it before the next
+        // tile's copies are issued (a wait for it would then wait for them too)
         float bv[CBW][4];
+        auto load_bias = [&]() {
 #pragma unroll
-        for (int j = 0; j < CBW; ++j) {
-            const int n = (nbw + j) * kColsPerBlock + 4 * h;
+            for (int j = 0; j < CBW; ++j) {
+                const int n = (nbw + j) * kColsPerBlock + 4 * h;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) bv[j][e] = bias && n < N ? half_bits_to_f32<kBF16>(bias[n + e]) : 0.f;
-        }
+                for (int e = 0; e < 4; ++e) bv[j][e] = bias && n < N ? half_bits_to_f32<kBF16>(bias[n + e]) : 0.f;
+            }
+        };
+        if constexpr (kPersist) load_bias();
         Src nxt;
-        const int nid = next_tile(id + (int)gridDim.x, nxt);
+        int nid = total_ids;
+        if constexpr (kPersist) nid = next_tile(id + (int)gridDim.x, nxt);
         const bool more = nid < total_ids;
 
-        // Epilogue through LDS: the lanes write their rounded outputs into ring slots 1..2
-        // as a row-major [BM][BN] tile (rows padded by 16 bytes against bank conflicts), and
-        // the waves store whole rows, 16 bytes per lane and 1 KiB per instruction, instead of
-        // each wave writing half of every 128-byte line it touches. Slot 0 meanwhile takes
-        // the next tile's first stage.
+        // Epilogue through LDS: the lanes write their rounded outputs into the ring as a
+        // row-major [BM][BN] tile (rows padded by 16 bytes against bank conflicts), and
+        // the waves store whole rows, 16 bytes per lane and 1 KiB per instruction, instead
+        // of each wave writing half of every 128-byte line it touches. A persistent tile
+        // stages it in slots 1..2, while slot 0 takes the next tile's first stage.
         constexpr int BN = 16 * CBW * kWaves;
         constexpr int kRowBytes = BN * 2 + 16;
-        static_assert((size_t)BM * kRowBytes <= (kStages - 1) * sizeof(StageT), "the output tile fits in slots 1..2");
-        uint8_t* otile = reinterpret_cast<uint8_t*>(&ring[1]);
+        static_assert(!kPersist || (size_t)BM * kRowBytes <= (kStages - 1) * sizeof(StageT),
+                      "the output tile fits in slots 1..2");
+        static_assert((size_t)BM * kRowBytes <= kStages * sizeof(StageT), "the output tile fits in the ring");
+        uint8_t* otile = reinterpret_cast<uint8_t*>(&ring[kPersist ? 1 : 0]);
         lds_barrier();                           // every wave is done with the ring's operands
         if (more) issue(nxt, 0, 0);
+        if constexpr (!kPersist) load_bias();
 #pragma unroll
         for (int j = 0; j < CBW; ++j) {
             const int col = 16 * (w * CBW + j) + 4 * h;        // in the tile
@@ -389,12 +398,19 @@ void launch_cfg(const GemmPlan& p, const uint16_t* x, const uint8_t* packed, con
     // workgroup takes stays on its XCD) takes a tile per round.
     constexpr size_t kLds = 3 * sizeof(Stage<16 * MR, CBW, W, kSub>) + 2 * W * sizeof(MetaGroup<CBW, kSub>);
     const bool persistent = kLds > 80 * 1024 && p.splits == 1 && total_ids > kTargetWorkgroups;
-    const dim3 grid((unsigned)(persistent ? kTargetWorkgroups : total_ids));
     // streaming output stores when every workgroup runs in the first round (qkv and
     // gate_up prefill: 1-2% faster; the LM head, 8 rounds, unchanged)
     const int nt_out = (int64_t)p.tiles_m * p.tiles_n * p.splits <= kTargetWorkgroups ? 1 : 0;
-    hipLaunchKernelGGL((gemm_kernel<kBF16, MR, CBW, W, kSub>), grid, dim3(64 * W), 0, stream, x, packed, bias, y, M,
-                       K, N, p.tiles_m, p.tiles_n, p.splits, counters, partials, nt_out, total_ids);
+    if constexpr (kLds > 80 * 1024) {
+        if (persistent) {
+            hipLaunchKernelGGL((gemm_kernel<kBF16, MR, CBW, W, kSub, true>), dim3(kTargetWorkgroups), dim3(64 * W), 0,
+                               stream, x, packed, bias, y, M, K, N, p.tiles_m, p.tiles_n, p.splits, counters, partials,
+                               nt_out, total_ids);
+            return;
+        }
+    }
+    hipLaunchKernelGGL((gemm_kernel<kBF16, MR, CBW, W, kSub, false>), dim3((unsigned)total_ids), dim3(64 * W), 0, stream,
+                       x, packed, bias, y, M, K, N, p.tiles_m, p.tiles_n, p.splits, counters, partials, nt_out, total_ids);
 }
 
 template <bool kBF16, int MR>
